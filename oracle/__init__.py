@@ -1,0 +1,153 @@
+"""fp64 CPU oracle for single-token paged decode attention over an fp8 KV cache.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's CPU
+baseline leg use it; the product library never imports, links or calls it.
+It shares no code with the HIP path.  The arithmetic lives in ``pa_oracle.c``
+(plain loops in double precision, written from the definition), built by
+:func:`build` with gcc into ``liboracle.so`` and called through ctypes.
+
+Every function is pinned in ``tests/test_oracle_pins.py`` against things
+other than itself: torch's own fp8 decoding, a dense attention computed by
+``torch.nn.functional.scaled_dot_product_attention`` in fp64 on K/V gathered
+by array indexing, closed forms, hand-worked fixtures and invariants.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "pa_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build() -> str:
+    """Compile pa_oracle.c into liboracle.so (gcc, -O2, OpenMP)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+           "-o", _LIB + ".tmp", _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    i32 = ctypes.c_int
+    f32 = ctypes.c_float
+    lib.pa_oracle_fp8_e4m3fn.argtypes = [ctypes.c_uint8]
+    lib.pa_oracle_fp8_e4m3fn.restype = ctypes.c_double
+    lib.pa_oracle_bf16.argtypes = [ctypes.c_uint16]
+    lib.pa_oracle_bf16.restype = ctypes.c_double
+    lib.pa_oracle_bf16_rne.argtypes = [ctypes.c_double]
+    lib.pa_oracle_bf16_rne.restype = ctypes.c_uint16
+    lib.pa_oracle_decode.argtypes = [P, P, P, P, P, i32, i32, i32, i32,
+                                     f32, f32, f32, P, i32]
+    lib.pa_oracle_decode.restype = i32
+    lib.pa_oracle_decode_partitioned.argtypes = [P, P, P, P, P, i32, i32, i32, i32,
+                                                 f32, f32, f32, i32, P]
+    lib.pa_oracle_decode_partitioned.restype = i32
+    _lib = lib
+    return lib
+
+
+def fp8_e4m3fn_value(byte: int) -> float:
+    """Value of one fp8 e4m3fn byte (OCP format, from its definition)."""
+    return _load().pa_oracle_fp8_e4m3fn(byte & 0xFF)
+
+
+def fp8_table() -> np.ndarray:
+    """Values of all 256 fp8 e4m3fn codes, float64."""
+    lib = _load()
+    return np.array([lib.pa_oracle_fp8_e4m3fn(b) for b in range(256)], dtype=np.float64)
+
+
+def bf16_value(bits: int) -> float:
+    return _load().pa_oracle_bf16(bits & 0xFFFF)
+
+
+def bf16_rne(x: np.ndarray) -> np.ndarray:
+    """Correctly rounded bfloat16 bit patterns (uint16) of float64 values."""
+    lib = _load()
+    flat = np.ascontiguousarray(x, dtype=np.float64).ravel()
+    out = np.fromiter((lib.pa_oracle_bf16_rne(float(v)) for v in flat),
+                      dtype=np.uint16, count=flat.size)
+    return out.reshape(np.shape(x))
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact float64 values of bf16 bit patterns (plain bit placement)."""
+    u = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+def _check(q_bits, k_cache, v_cache, block_tables, seq_lens):
+    q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    k_cache = np.ascontiguousarray(k_cache, dtype=np.uint8)
+    v_cache = np.ascontiguousarray(v_cache, dtype=np.uint8)
+    block_tables = np.ascontiguousarray(block_tables, dtype=np.int32)
+    seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    if q_bits.ndim != 3 or q_bits.shape[2] != 128:
+        raise ValueError("q must be [S, Hq, 128] bf16 bits")
+    S, Hq, _ = q_bits.shape
+    if k_cache.ndim != 5 or k_cache.shape[2:] != (8, 16, 16):
+        raise ValueError("k_cache must be [NB, Hkv, 8, 16, 16] bytes")
+    NB, Hkv = k_cache.shape[:2]
+    if v_cache.reshape(-1).size != NB * Hkv * 128 * 16:
+        raise ValueError("v_cache must hold [NB, Hkv, 128, 16] bytes")
+    if block_tables.ndim != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must be [S, W]")
+    if seq_lens.shape != (S,):
+        raise ValueError("seq_lens must be [S]")
+    W = block_tables.shape[1]
+    for s in range(S):
+        used = block_tables[s, : (int(seq_lens[s]) + 15) // 16]
+        if used.size and (used.min() < 0 or used.max() >= NB):
+            raise ValueError(f"sequence {s}: block id out of range")
+    return q_bits, k_cache, v_cache, block_tables, seq_lens, S, Hq, Hkv, W
+
+
+def decode(q_bits, k_cache, v_cache, block_tables, seq_lens, scale, k_scale,
+           v_scale, num_threads: int | None = None) -> np.ndarray:
+    """fp64 paged decode attention.  Returns float64 [S, Hq, 128].
+
+    q_bits: uint16 bf16 patterns [S, Hq, 128]; k_cache: uint8 [NB, Hkv, 8, 16, 16];
+    v_cache: uint8 [NB, Hkv, 128, 16] (or the same bytes with an extra unit dim);
+    block_tables: int32 [S, W]; seq_lens: int32 [S]; scale, k_scale, v_scale: the
+    fp32 values the caller passes.
+    """
+    q_bits, k_cache, v_cache, bt, sl, S, Hq, Hkv, W = _check(
+        q_bits, k_cache, v_cache, block_tables, seq_lens)
+    out = np.zeros((S, Hq, 128), dtype=np.float64)
+    nt = num_threads if num_threads else (os.cpu_count() or 1)
+    rc = _load().pa_oracle_decode(
+        q_bits.ctypes.data, k_cache.ctypes.data, v_cache.ctypes.data, bt.ctypes.data,
+        sl.ctypes.data, S, Hq, Hkv, W, float(scale), float(k_scale), float(v_scale),
+        out.ctypes.data, int(nt))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return out
+
+
+def decode_partitioned(q_bits, k_cache, v_cache, block_tables, seq_lens, scale,
+                       k_scale, v_scale, tokens_per_part: int) -> np.ndarray:
+    """The same quantity via per-partition partials and a log-sum-exp merge."""
+    q_bits, k_cache, v_cache, bt, sl, S, Hq, Hkv, W = _check(
+        q_bits, k_cache, v_cache, block_tables, seq_lens)
+    out = np.zeros((S, Hq, 128), dtype=np.float64)
+    rc = _load().pa_oracle_decode_partitioned(
+        q_bits.ctypes.data, k_cache.ctypes.data, v_cache.ctypes.data, bt.ctypes.data,
+        sl.ctypes.data, S, Hq, Hkv, W, float(scale), float(k_scale), float(v_scale),
+        int(tokens_per_part), out.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return out

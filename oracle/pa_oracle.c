@@ -1,0 +1,239 @@
+/*
+ * pa_oracle.c -- fp64 CPU oracle for single-token paged decode attention over
+ * an fp8-e4m3fn KV cache.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
+ * calls this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline leg do.  It shares no code, header or table with the HIP path.
+ *
+ * What it computes (the plain definition, evaluated in double precision):
+ *
+ *   For every sequence s, query head h and output dim d, with G = Hq / Hkv,
+ *   kv head k = floor(h / G) and n = seq_lens[s] cached tokens:
+ *     token t lives in physical block  p_t = block_tables[s][t / 16]
+ *                        at slot       j   = t % 16
+ *     K_t[e] = fp8(k_cache[p_t][k][e / 16][j][e % 16]) * k_scale
+ *     V_t[e] = fp8(v_cache[p_t][k][e][j])              * v_scale
+ *     z_t    = scale * sum_e q[s][h][e] * K_t[e]
+ *     out[s][h][d] = sum_t exp(z_t - max z) V_t[d] / sum_t exp(z_t - max z)
+ *
+ * Sources (cited by page title and section):
+ *  - vLLM pull request lishuoshuo-amd/vllm #3 (ROCM_ATTN asm decode),
+ *    Overview and Details > Layout:
+ *    paged fp8 cache with 16-token blocks; K cache laid out as
+ *    [blocks, kv_heads, head_size/16, 16, 16], V cache as
+ *    [blocks, kv_heads, head_size, 16]; pages addressed by a dense stride.
+ *  - API page "vllm.v1.attention.backends.rocm_aiter_unified_attn",
+ *    RocmAiterUnifiedAttentionImpl.forward: query [num_tokens, num_heads,
+ *    head_size], seqused_k (tokens per sequence), block_table, softmax_scale,
+ *    k_descale / v_descale (per-tensor scales multiplied on read).
+ *
+ * Readings where the pages leave a step open:
+ *  - query head h reads kv head floor(h / G) (consecutive heads share);
+ *  - fp8 is the OCP e4m3fn format: bias 7, 3 mantissa bits, subnormals
+ *    m * 2^-9, largest finite 448, no infinities, S.1111.111 is NaN;
+ *  - scales multiply the decoded value;
+ *  - seq_lens[s] == 0 gives an all-zero output row;
+ *  - tokens at or beyond seq_lens[s] and table entries past
+ *    ceil(seq_lens[s] / 16) are never read;
+ *  - seq_lens[s] > 16 * max_blocks_per_seq is a caller error (return -3).
+ *
+ * The split-KV variant (pa_oracle_decode_partitioned) evaluates the same
+ * quantity as a log-sum-exp merge of per-partition partial results; it exists
+ * to pin that merge formula against the unsplit definition.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define PA_HEAD_DIM 128
+#define PA_BLOCK 16
+
+/* Value of one OCP fp8 e4m3fn byte, from the format's definition. */
+double pa_oracle_fp8_e4m3fn(uint8_t b) {
+  const int sign = (b >> 7) & 1;
+  const int e = (b >> 3) & 0xF;
+  const int m = b & 0x7;
+  double mag;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    mag = ldexp((double)m / 8.0, -6); /* subnormal: 0.m * 2^(1 - 7) */
+  else
+    mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sign ? -mag : mag;
+}
+
+/* Value of one bfloat16 (upper half of an IEEE binary32). */
+double pa_oracle_bf16(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* Correctly rounded (nearest, ties to even) bfloat16 of a double. */
+uint16_t pa_oracle_bf16_rne(double x) {
+  uint16_t sign = signbit(x) ? 0x8000u : 0u;
+  double a = fabs(x);
+  if (isnan(x)) return 0x7FC0u;
+  if (a == 0.0) return sign;
+  /* bf16: 8 significant bits, normal exponents -126..127, subnormal step 2^-133 */
+  int e;
+  (void)frexp(a, &e); /* a = f * 2^e, 0.5 <= f < 1; leading bit weight 2^(e-1) */
+  int step_exp = (e - 1) - 7;
+  if (step_exp < -133) step_exp = -133;
+  double q = nearbyint(ldexp(a, -step_exp)); /* default rounding mode: ties even */
+  double r = ldexp(q, step_exp);
+  if (r > ldexp(2.0 - ldexp(1.0, -7), 127))
+    return sign | 0x7F80u; /* rounds past the largest finite bf16: infinity */
+  float f = (float)r;      /* exact: r has at most 8 significant bits */
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return sign | (uint16_t)(u >> 16);
+}
+
+/* Gather + dequantise token t of sequence s for kv head k (one row of K and V). */
+static void load_token(const uint8_t* k_cache, const uint8_t* v_cache,
+                       const int32_t* bt_row, int num_kv_heads, int k, int t,
+                       double k_scale, double v_scale, double* K, double* V) {
+  const int64_t p = bt_row[t / PA_BLOCK];
+  const int j = t % PA_BLOCK;
+  const uint8_t* kpage = k_cache + (p * num_kv_heads + k) * (int64_t)(PA_HEAD_DIM * PA_BLOCK);
+  const uint8_t* vpage = v_cache + (p * num_kv_heads + k) * (int64_t)(PA_HEAD_DIM * PA_BLOCK);
+  for (int e = 0; e < PA_HEAD_DIM; ++e) {
+    /* K page is [head_size/16][16 slots][16 dims]; V page is [head_size][16 slots] */
+    K[e] = pa_oracle_fp8_e4m3fn(kpage[(e / 16) * (PA_BLOCK * 16) + j * 16 + (e % 16)]) * k_scale;
+    V[e] = pa_oracle_fp8_e4m3fn(vpage[e * PA_BLOCK + j]) * v_scale;
+  }
+}
+
+static int check_args(int S, int Hq, int Hkv, int W, const int32_t* seq_lens) {
+  if (S < 0 || Hq <= 0 || Hkv <= 0 || W < 0) return -1;
+  if (Hq % Hkv != 0) return -2;
+  for (int s = 0; s < S; ++s)
+    if (seq_lens[s] < 0 || seq_lens[s] > PA_BLOCK * W) return -3;
+  return 0;
+}
+
+/*
+ * out: [S][Hq][128] doubles.  q_bits: bf16 bit patterns [S][Hq][128].
+ * Returns 0, or a negative code for bad arguments (nothing is written then).
+ */
+int pa_oracle_decode(const uint16_t* q_bits, const uint8_t* k_cache,
+                     const uint8_t* v_cache, const int32_t* block_tables,
+                     const int32_t* seq_lens, int S, int Hq, int Hkv, int W,
+                     float scale, float k_scale, float v_scale, double* out,
+                     int num_threads) {
+  int rc = check_args(S, Hq, Hkv, W, seq_lens);
+  if (rc) return rc;
+  const int G = Hq / Hkv;
+  (void)num_threads;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1) num_threads(num_threads > 0 ? num_threads : 1)
+  for (int s = 0; s < S; ++s) {
+    for (int h = 0; h < Hq; ++h) {
+      const int n = seq_lens[s];
+      const int k = h / G;
+      double* o = out + ((int64_t)s * Hq + h) * PA_HEAD_DIM;
+      double q[PA_HEAD_DIM], K[PA_HEAD_DIM], V[PA_HEAD_DIM];
+      for (int e = 0; e < PA_HEAD_DIM; ++e)
+        q[e] = pa_oracle_bf16(q_bits[((int64_t)s * Hq + h) * PA_HEAD_DIM + e]);
+      for (int d = 0; d < PA_HEAD_DIM; ++d) o[d] = 0.0;
+      if (n == 0) continue;
+      double* z = (double*)malloc(sizeof(double) * (size_t)n);
+      const int32_t* bt_row = block_tables + (int64_t)s * W;
+      /* logits */
+      double zmax = -INFINITY;
+      for (int t = 0; t < n; ++t) {
+        load_token(k_cache, v_cache, bt_row, Hkv, k, t, k_scale, v_scale, K, V);
+        double dot = 0.0;
+        for (int e = 0; e < PA_HEAD_DIM; ++e) dot += q[e] * K[e];
+        z[t] = (double)scale * dot;
+        if (z[t] > zmax) zmax = z[t];
+      }
+      /* softmax-weighted sum of V */
+      double den = 0.0;
+      for (int t = 0; t < n; ++t) {
+        load_token(k_cache, v_cache, bt_row, Hkv, k, t, k_scale, v_scale, K, V);
+        const double w = exp(z[t] - zmax);
+        den += w;
+        for (int d = 0; d < PA_HEAD_DIM; ++d) o[d] += w * V[d];
+      }
+      for (int d = 0; d < PA_HEAD_DIM; ++d) o[d] /= den;
+      free(z);
+    }
+  }
+  return 0;
+}
+
+/*
+ * Same quantity, computed as independent partitions of `tokens_per_part`
+ * consecutive tokens followed by a log-sum-exp merge:
+ *   partition p keeps  m_p = max z,  l_p = sum exp(z - m_p),
+ *                      a_p[d] = sum exp(z - m_p) V[d];
+ *   merge:  M = max_p m_p,  w_p = exp(m_p - M)  (partitions with no tokens
+ *           are skipped),  out = sum_p w_p a_p / sum_p w_p l_p.
+ */
+int pa_oracle_decode_partitioned(const uint16_t* q_bits, const uint8_t* k_cache,
+                                 const uint8_t* v_cache, const int32_t* block_tables,
+                                 const int32_t* seq_lens, int S, int Hq, int Hkv, int W,
+                                 float scale, float k_scale, float v_scale,
+                                 int tokens_per_part, double* out) {
+  int rc = check_args(S, Hq, Hkv, W, seq_lens);
+  if (rc) return rc;
+  if (tokens_per_part <= 0) return -4;
+  const int G = Hq / Hkv;
+  for (int s = 0; s < S; ++s) {
+    for (int h = 0; h < Hq; ++h) {
+      const int n = seq_lens[s];
+      const int k = h / G;
+      const int nparts = (n + tokens_per_part - 1) / tokens_per_part;
+      double* o = out + ((int64_t)s * Hq + h) * PA_HEAD_DIM;
+      double q[PA_HEAD_DIM], K[PA_HEAD_DIM], V[PA_HEAD_DIM];
+      for (int e = 0; e < PA_HEAD_DIM; ++e)
+        q[e] = pa_oracle_bf16(q_bits[((int64_t)s * Hq + h) * PA_HEAD_DIM + e]);
+      for (int d = 0; d < PA_HEAD_DIM; ++d) o[d] = 0.0;
+      if (n == 0) continue;
+      double* m = (double*)malloc(sizeof(double) * (size_t)nparts);
+      double* l = (double*)malloc(sizeof(double) * (size_t)nparts);
+      double* a = (double*)calloc((size_t)nparts * PA_HEAD_DIM, sizeof(double));
+      const int32_t* bt_row = block_tables + (int64_t)s * W;
+      for (int p = 0; p < nparts; ++p) {
+        const int t0 = p * tokens_per_part;
+        const int t1 = (t0 + tokens_per_part < n) ? t0 + tokens_per_part : n;
+        double zmax = -INFINITY;
+        for (int t = t0; t < t1; ++t) {
+          load_token(k_cache, v_cache, bt_row, Hkv, k, t, k_scale, v_scale, K, V);
+          double dot = 0.0;
+          for (int e = 0; e < PA_HEAD_DIM; ++e) dot += q[e] * K[e];
+          double zt = (double)scale * dot;
+          if (zt > zmax) zmax = zt;
+        }
+        m[p] = zmax;
+        l[p] = 0.0;
+        for (int t = t0; t < t1; ++t) {
+          load_token(k_cache, v_cache, bt_row, Hkv, k, t, k_scale, v_scale, K, V);
+          double dot = 0.0;
+          for (int e = 0; e < PA_HEAD_DIM; ++e) dot += q[e] * K[e];
+          const double w = exp((double)scale * dot - zmax);
+          l[p] += w;
+          for (int d = 0; d < PA_HEAD_DIM; ++d) a[(int64_t)p * PA_HEAD_DIM + d] += w * V[d];
+        }
+      }
+      double M = -INFINITY;
+      for (int p = 0; p < nparts; ++p)
+        if (m[p] > M) M = m[p];
+      double den = 0.0;
+      for (int p = 0; p < nparts; ++p) {
+        const double w = exp(m[p] - M);
+        den += w * l[p];
+        for (int d = 0; d < PA_HEAD_DIM; ++d) o[d] += w * a[(int64_t)p * PA_HEAD_DIM + d];
+      }
+      for (int d = 0; d < PA_HEAD_DIM; ++d) o[d] /= den;
+      free(m);
+      free(l);
+      free(a);
+    }
+  }
+  return 0;
+}

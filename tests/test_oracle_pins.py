@@ -1,0 +1,332 @@
+"""Pins of the fp64 oracle against things other than itself (CPU only).
+
+* fp8 decoding: torch's own float8_e4m3fn conversion on all 256 codes, and
+  values worked out by hand from the OCP e4m3fn definition.
+* Attention: two independent dense routes on K/V gathered by array indexing
+  (torch's scaled_dot_product_attention in fp64, and a numpy softmax), closed
+  forms (one token, constant V, zero query, a hand-worked two-token fixture),
+  and invariants (physical block placement, sequence order, NaN poison in
+  memory the method must not read, exact power-of-two scalings).
+* The split-KV log-sum-exp merge against the unsplit definition.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# --------------------------------------------------------------------------
+# fp8 / bf16 decoding
+
+def test_fp8_table_matches_torch_all_codes(oracle_lib):
+    ours = oracle.fp8_table()
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ours[ok], ref[ok])
+    # signed zero survives
+    assert math.copysign(1.0, ours[0x80]) == -1.0
+
+
+@pytest.mark.parametrize("code,value", [
+    (0x00, 0.0), (0x01, 2.0 ** -9), (0x07, 7 * 2.0 ** -9), (0x08, 2.0 ** -6),
+    (0x30, 0.5), (0x38, 1.0), (0x3C, 1.5), (0x40, 2.0), (0x77, 240.0),
+    (0x7E, 448.0), (0xFE, -448.0), (0xB8, -1.0), (0x81, -(2.0 ** -9)),
+])
+def test_fp8_values_from_format_definition(oracle_lib, code, value):
+    assert oracle.fp8_e4m3fn_value(code) == value
+
+
+def test_fp8_nan_codes(oracle_lib):
+    t = oracle.fp8_table()
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF])
+    assert np.isnan(t).sum() == 2
+
+
+def test_bf16_value_and_rounding(oracle_lib):
+    assert oracle.bf16_value(0x3F80) == 1.0
+    assert oracle.bf16_value(0xC000) == -2.0
+    assert oracle.bf16_value(0x0001) == 2.0 ** -133
+    # ties go to even, both directions
+    bits = oracle.bf16_rne(np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 1 + 2 ** -8 + 2 ** -30]))
+    assert list(bits) == [0x3F80, 0x3F82, 0xBF80, 0x3F81]
+    # subnormal step, zero, overflow, NaN
+    assert list(oracle.bf16_rne(np.array([2.0 ** -133, 2.0 ** -134, 1.5 * 2.0 ** -133, 0.0]))) == [1, 0, 2, 0]
+    assert list(oracle.bf16_rne(np.array([3.5e38, -3.5e38]))) == [0x7F80, 0xFF80]
+    assert oracle.bf16_rne(np.array([float("nan")]))[0] == 0x7FC0
+
+
+def test_bf16_rne_matches_torch_on_float32_exact_values(oracle_lib):
+    g = torch.Generator().manual_seed(1)
+    x = (torch.randn(4096, generator=g) * torch.exp2(torch.randint(-20, 20, (4096,), generator=g).float()))
+    ref = x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    ours = oracle.bf16_rne(x.double().numpy())
+    assert np.array_equal(ours, ref)
+
+
+# --------------------------------------------------------------------------
+# independent dense routes (gather by array indexing, dequantise with torch)
+
+def gather_dense(case, s):
+    """K, V of sequence s as float64 [L, Hkv, 128] via numpy fancy indexing."""
+    L = int(case.seq_lens[s])
+    t = np.arange(L)
+    blocks = case.block_tables.numpy()[s, t // 16]
+    slots = t % 16
+    kb = case.k_cache.numpy()[blocks, :, :, slots, :]      # [L, Hkv, 8, 16]
+    vb = case.v_cache.numpy()[blocks, :, :, slots]         # [L, Hkv, 128]
+    kb = kb.reshape(L, case.num_kv_heads, 128)
+    K = torch.from_numpy(np.ascontiguousarray(kb)).view(torch.float8_e4m3fn).to(torch.float64) * case.k_scale
+    V = torch.from_numpy(np.ascontiguousarray(vb)).view(torch.float8_e4m3fn).to(torch.float64) * case.v_scale
+    return K, V
+
+
+def sdpa_reference(case):
+    S, Hq, Hkv = case.num_seqs, case.num_heads, case.num_kv_heads
+    G = Hq // Hkv
+    out = np.zeros((S, Hq, 128))
+    q = case.q.to(torch.float64)
+    for s in range(S):
+        if int(case.seq_lens[s]) == 0:
+            continue
+        K, V = gather_dense(case, s)
+        Kr = K.permute(1, 0, 2).repeat_interleave(G, dim=0)   # [Hq, L, 128]
+        Vr = V.permute(1, 0, 2).repeat_interleave(G, dim=0)
+        o = torch.nn.functional.scaled_dot_product_attention(
+            q[s][:, None, :].contiguous(), Kr.contiguous(), Vr.contiguous(), scale=case.scale)
+        out[s] = o[:, 0, :].numpy()
+    return out
+
+
+def numpy_reference(case):
+    S, Hq, Hkv = case.num_seqs, case.num_heads, case.num_kv_heads
+    G = Hq // Hkv
+    out = np.zeros((S, Hq, 128))
+    q = case.q.to(torch.float64).numpy()
+    for s in range(S):
+        if int(case.seq_lens[s]) == 0:
+            continue
+        K, V = gather_dense(case, s)
+        K, V = K.numpy(), V.numpy()
+        for h in range(Hq):
+            z = case.scale * (K[:, h // G, :] @ q[s, h])
+            w = np.exp(z - z.max())
+            out[s, h] = (w[:, None] * V[:, h // G, :]).sum(0) / w.sum()
+    return out
+
+
+def run_oracle(case, **kw):
+    return oracle.decode(case.q_bits(), case.k_cache.numpy(), case.v_cache.numpy(),
+                         case.block_tables.numpy(), case.seq_lens.numpy(), case.scale,
+                         case.k_scale, case.v_scale, **kw)
+
+
+def small_cases():
+    yield workloads.tiny(0)
+    yield workloads.tiny(5)
+    yield workloads.make_case(16, 2, [3, 16, 31, 100, 257], 3, name="g8")
+    yield workloads.make_case(5, 1, [1, 2, 15, 16, 17, 48], 4, name="g5")
+    yield workloads.make_case(16, 1, [70, 1], 7, name="g16")
+    yield workloads.make_case(4, 4, [40, 0, 9], 8, max_blocks=5, name="mha_with_empty")
+    for (hq, hkv) in workloads.RAGGED_LAYOUTS:
+        lens = workloads.ragged_lens(6, seed=hq + hkv)
+        yield workloads.make_case(hq, hkv, [min(x, 600) for x in lens], 11,
+                                  name=f"ragged_sub_{hq}x{hkv}")
+
+
+@pytest.mark.parametrize("case", list(small_cases()), ids=lambda c: c.name)
+def test_oracle_matches_sdpa_fp64(oracle_lib, case):
+    ours = run_oracle(case)
+    ref = sdpa_reference(case)
+    assert np.isfinite(ours).all()
+    np.testing.assert_allclose(ours, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("case", list(small_cases())[:4], ids=lambda c: c.name)
+def test_oracle_matches_numpy_softmax(oracle_lib, case):
+    np.testing.assert_allclose(run_oracle(case), numpy_reference(case), rtol=0, atol=1e-12)
+
+
+def test_oracle_threads_do_not_change_result(oracle_lib):
+    case = workloads.make_case(16, 2, [33, 500, 7], 2)
+    assert np.array_equal(run_oracle(case, num_threads=1), run_oracle(case, num_threads=4))
+
+
+# --------------------------------------------------------------------------
+# closed forms
+
+def _two_token_fixture():
+    kv = {}
+    with open(os.path.join(GOLDEN, "two_token_case.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                k, v = line.split()
+                kv[k] = v
+    return kv
+
+
+def test_golden_two_token_hand_worked(oracle_lib):
+    kv = _two_token_fixture()
+    nb = int(kv["num_blocks"])
+    p = int(kv["physical_block"])
+    q = np.zeros((1, 1, 128), np.uint16)
+    q[0, 0, 0] = int(kv["q_dim0_bits"], 16)
+    k = np.zeros((nb, 1, 8, 16, 16), np.uint8)
+    v = np.zeros((nb, 1, 128, 16), np.uint8)
+    k[p, 0, 0, 0, 0] = int(kv["k_tok0_dim0"], 16)
+    k[p, 0, 0, 1, 0] = int(kv["k_tok1_dim0"], 16)
+    v[p, 0, :, 0] = int(kv["v_tok0"], 16)
+    v[p, 0, :, 1] = int(kv["v_tok1"], 16)
+    k[p, 0, :, 2:, :] = 0x7F   # slots past seq_len hold NaN and must not be read
+    v[p, 0, :, 2:] = 0x7F
+    bt = np.array([[p]], np.int32)
+    sl = np.array([int(kv["seq_len"])], np.int32)
+    out = oracle.decode(q, k, v, bt, sl, float(kv["scale"]), float(kv["k_scale"]), float(kv["v_scale"]))
+    expected = float(kv["expected_every_dim"])
+    np.testing.assert_allclose(out[0, 0], expected, rtol=1e-15, atol=0)
+    # the same number from the closed form sigma(z0 - z1) V0 + (1 - sigma) V1
+    sig = 1.0 / (1.0 + math.exp(-(2.0 - 1.0)))
+    assert abs(expected - (sig * 1.0 + (1 - sig) * 2.0)) < 1e-15
+
+
+def test_one_token_context_returns_v0(oracle_lib):
+    case = workloads.make_case(8, 2, [1, 1, 17], 21)
+    out = run_oracle(case)
+    for s in range(3):
+        L = int(case.seq_lens[s])
+        _, V = gather_dense(case, s)
+        if L == 1:
+            for h in range(8):
+                assert np.array_equal(out[s, h], V[0, h // 4].numpy())
+
+
+def test_constant_v_gives_that_v(oracle_lib):
+    case = workloads.make_case(8, 2, [5, 64, 200], 22)
+    v = case.v_cache.clone()
+    code = 0x3B   # 1.375
+    for s in range(3):
+        L = int(case.seq_lens[s])
+        for b in range((L + 15) // 16):
+            v[int(case.block_tables[s, b])] = code
+    case.v_cache = v
+    out = run_oracle(case)
+    np.testing.assert_allclose(out, 1.375 * case.v_scale, rtol=1e-13, atol=0)  # n-term summation rounding
+
+
+def test_zero_query_gives_mean_of_v(oracle_lib):
+    case = workloads.make_case(8, 2, [3, 50, 129], 23)
+    case.q = torch.zeros_like(case.q)
+    out = run_oracle(case)
+    for s in range(3):
+        _, V = gather_dense(case, s)
+        mean = V.mean(0).numpy()               # [Hkv, 128]
+        for h in range(8):
+            np.testing.assert_allclose(out[s, h], mean[h // 4], rtol=0, atol=1e-13)
+
+
+def test_identical_heads_give_identical_outputs(oracle_lib):
+    case = workloads.make_case(8, 2, [77], 24)
+    q = case.q.clone()
+    q[0, 1:4] = q[0, 0]
+    case.q = q
+    out = run_oracle(case)
+    for h in range(1, 4):
+        assert np.array_equal(out[0, h], out[0, 0])
+    assert not np.array_equal(out[0, 4], out[0, 0])
+
+
+# --------------------------------------------------------------------------
+# invariants
+
+def test_block_placement_invariance(oracle_lib):
+    case = workloads.make_case(8, 2, [33, 90, 16, 1], 31)
+    base = run_oracle(case)
+    NB = case.k_cache.shape[0]
+    g = torch.Generator().manual_seed(99)
+    perm = torch.randperm(NB, generator=g)          # block b moves to perm[b]
+    k2 = torch.empty_like(case.k_cache)
+    v2 = torch.empty_like(case.v_cache)
+    k2[perm] = case.k_cache
+    v2[perm] = case.v_cache
+    bt2 = perm[case.block_tables.long()].to(torch.int32)
+    moved = workloads.Case("moved", case.q, k2, v2, bt2, case.seq_lens, case.scale,
+                           case.k_scale, case.v_scale)
+    assert np.array_equal(run_oracle(moved), base)
+
+
+def test_sequence_order_permutes_outputs(oracle_lib):
+    case = workloads.make_case(8, 2, [33, 90, 16, 1, 0], 32, max_blocks=8)
+    base = run_oracle(case)
+    order = torch.tensor([3, 0, 4, 2, 1])
+    perm_case = workloads.Case("perm", case.q[order], case.k_cache, case.v_cache,
+                               case.block_tables[order], case.seq_lens[order],
+                               case.scale, case.k_scale, case.v_scale)
+    assert np.array_equal(run_oracle(perm_case), base[order.numpy()])
+
+
+def test_nan_poison_outside_context_is_never_read(oracle_lib):
+    lens = [1, 17, 33, 64, 5]
+    a = workloads.make_case(8, 2, lens, 33, max_blocks=6, poison=True)
+    b = workloads.make_case(8, 2, lens, 33, max_blocks=6, poison=False)
+    assert (a.k_cache == 0x7F).sum() > 0
+    ra, rb = run_oracle(a), run_oracle(b)
+    assert np.isfinite(ra).all()
+    assert np.array_equal(ra, rb)
+
+
+def test_nan_inside_context_propagates_to_its_head_only(oracle_lib):
+    case = workloads.make_case(8, 2, [20, 20], 34)
+    q = case.q.clone()
+    q[1, 5, 7] = float("nan")
+    case.q = q
+    out = run_oracle(case)
+    assert np.isnan(out[1, 5]).all()
+    mask = np.ones((2, 8), bool)
+    mask[1, 5] = False
+    assert np.isfinite(out[mask]).all()
+
+
+def test_power_of_two_scalings_are_exact(oracle_lib):
+    case = workloads.make_case(8, 2, [40, 3], 35)
+    base = run_oracle(case)
+    v2 = run_oracle(workloads.Case("v2", case.q, case.k_cache, case.v_cache, case.block_tables,
+                                   case.seq_lens, case.scale, case.k_scale, 2 * case.v_scale))
+    assert np.array_equal(v2, 2 * base)
+    k2 = run_oracle(workloads.Case("k2", case.q, case.k_cache, case.v_cache, case.block_tables,
+                                   case.seq_lens, case.scale, 2 * case.k_scale, case.v_scale))
+    s2 = run_oracle(workloads.Case("s2", case.q, case.k_cache, case.v_cache, case.block_tables,
+                                   case.seq_lens, 2 * case.scale, case.k_scale, case.v_scale))
+    assert np.array_equal(k2, s2)
+    assert not np.array_equal(k2, base)
+
+
+def test_empty_sequence_gives_zeros_and_overlong_is_rejected(oracle_lib):
+    case = workloads.make_case(4, 1, [0, 9], 36, max_blocks=2)
+    out = run_oracle(case)
+    assert np.array_equal(out[0], np.zeros((4, 128)))
+    bad = case.seq_lens.clone()
+    bad[1] = 33            # 2 blocks hold at most 32 tokens
+    with pytest.raises(ValueError):
+        oracle.decode(case.q_bits(), case.k_cache.numpy(), case.v_cache.numpy(),
+                      case.block_tables.numpy(), bad.numpy(), case.scale, case.k_scale, case.v_scale)
+
+
+# --------------------------------------------------------------------------
+# split-KV merge
+
+@pytest.mark.parametrize("tpp", [16, 48, 64, 1000])
+def test_partition_merge_equals_unsplit(oracle_lib, tpp):
+    case = workloads.make_case(10, 2, [1, 15, 16, 17, 100, 1024, 0, 333], 41, max_blocks=64)
+    whole = run_oracle(case)
+    split = oracle.decode_partitioned(case.q_bits(), case.k_cache.numpy(), case.v_cache.numpy(),
+                                      case.block_tables.numpy(), case.seq_lens.numpy(),
+                                      case.scale, case.k_scale, case.v_scale, tpp)
+    np.testing.assert_allclose(split, whole, rtol=0, atol=1e-12)
