@@ -1,0 +1,226 @@
+"""Benchmark: fp8 paged decode attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one call of the library (decode kernel, plus the log-sum-exp merge
+kernel when the plan splits) over one batch already resident in HBM.  The
+default workload is 40 query / 8 kv heads, head_dim 128, 256 sequences of
+4096 tokens, fp8-e4m3fn K/V in 16-token blocks with a shuffled block table
+(2.15 GB of K/V per call, far beyond the 256 MB Infinity Cache, so every call
+streams from HBM).
+
+Prints one JSON line: achieved algorithmic HBM GB/s (value), µs/call, the
+roofline object for the decode kernel (HIP-event timing on its launch stream;
+counter traffic from the committed rocprofv3 summary when it matches the
+current kernel source), and the fp64 CPU oracle timed on a bounded sample.
+
+Other modes:
+    --workload all          also print one line per workload of the suite to stderr
+    --copy-calibration      time a plain 1 GiB device copy (for scaling PMC counters)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode attention µs/call and achieved HBM GB/s (% of MI355X peak)"
+PEAK_GBS = 8000.0          # MI355X HBM3E, AMD's published peak
+PAGES_ASM_US = 363.04      # pa_fwd_asm, 40/8 ctx 4096 256 seqs, MI355X (the pages' table)
+PAGES_HIP_US = 448.27      # ROCM_ATTN HIP paged attention, same row
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "pa_decode_kernel_40x8_ctx4096_s256_pmc.md")
+KERNEL_SRC = os.path.join(ROOT, "paged_attention_decode_03_amd", "csrc", "pa_decode_kernels.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counter_traffic():
+    """HBM bytes per launch from the committed PMC summary, or None when the
+    summary is missing or was taken on a different kernel source."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    text = open(PMC_SUMMARY).read()
+    h = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not h or not t or h.group(1) != kernel_source_hash():
+        return None
+    return float(t.group(1))
+
+
+def make_workload(name, device):
+    import workloads
+    if name == "target":
+        hq, hkv, s, ctx = workloads.TARGET
+        return workloads.dense(hq, hkv, s, ctx, seed=0, device=device)
+    m = re.fullmatch(r"dense_(\d+)x(\d+)_ctx(\d+)_s(\d+)", name)
+    if m:
+        hq, hkv, ctx, s = map(int, m.groups())
+        return workloads.dense(hq, hkv, s, ctx, seed=0, device=device)
+    m = re.fullmatch(r"ragged_(\d+)x(\d+)_seed(\d+)", name)
+    if m:
+        hq, hkv, seed = map(int, m.groups())
+        return workloads.ragged(hq, hkv, seed, device=device)
+    raise SystemExit(f"unknown workload {name}")
+
+
+def suite_names():
+    import workloads
+    names = [f"dense_{a}x{b}_ctx{c}_s{s}" for (a, b, s, c) in workloads.DENSE_1K + workloads.DENSE_4K]
+    names += ["target", "dense_20x4_ctx4096_s256"]
+    names += [f"ragged_{a}x{b}_seed0" for (a, b) in workloads.RAGGED_LAYOUTS]
+    names += [f"dense_{a}x{b}_ctx{c}_s{s}" for (a, b, s, c) in workloads.LOW_BATCH]
+    return names
+
+
+def time_calls(case, steps, warmup, rotate=1):
+    """Average µs per call over `steps` back-to-back calls, HIP events on the launch stream."""
+    import torch
+    import paged_attention_decode_03_amd as pa
+    dev = case.q.device
+    ks = torch.tensor([case.k_scale], dtype=torch.float32, device=dev)
+    vs = torch.tensor([case.v_scale], dtype=torch.float32, device=dev)
+    out = torch.empty_like(case.q)
+    stream = torch.cuda.Stream(dev)
+
+    def call():
+        pa.paged_decode_attention(case.q, case.k_cache, case.v_cache, case.block_tables,
+                                  case.seq_lens, case.scale, ks, vs, out=out, stream=stream)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize(dev)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        call()
+    end.record(stream)
+    torch.cuda.synchronize(dev)
+    return start.elapsed_time(end) * 1e3 / steps
+
+
+def cpu_baseline(sample_seqs=16):
+    """The fp64 oracle on a bounded sample of the same workload (host cores)."""
+    import numpy as np
+    import oracle
+    import workloads
+    hq, hkv, _, ctx = workloads.TARGET
+    case = workloads.dense(hq, hkv, sample_seqs, ctx, seed=1, device="cpu")
+    cores = os.cpu_count() or 1
+    args = (case.q_bits(), case.k_cache.numpy(), case.v_cache.numpy(), case.block_tables.numpy(),
+            case.seq_lens.numpy(), case.scale, case.k_scale, case.v_scale)
+    t0 = time.perf_counter()
+    oracle.decode(*args, num_threads=cores)
+    dt = time.perf_counter() - t0
+    return {"value": round(case.algorithmic_bytes() / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{sample_seqs} of 256 sequences of the same shape (40/8 heads, ctx {ctx}), "
+                      f"all heads; {dt:.2f} s wall on {cores} threads"}
+
+
+def copy_calibration(steps):
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "us_per_copy": dt * 1e6,
+                      "GBps_read_plus_write": 2 * n / dt / 1e9}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="target")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; the kernel works on one GPU's share of "
+              "heads/sequences and has no cross-GPU path (see the sharding notes in DESIGN.md).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
+
+    import paged_attention_decode_03_amd as pa
+    pa.load_library()
+
+    if args.workload == "all":
+        for name in suite_names():
+            case = make_workload(name, "cuda")
+            us = time_calls(case, max(10, args.steps // 4), 5)
+            P, ppp, _ = pa.pa_decode_plan(case.num_seqs, case.num_heads, case.num_kv_heads,
+                                          case.max_blocks, 256)
+            b = case.algorithmic_bytes()
+            print(json.dumps({"workload": name, "us_per_call": round(us, 2),
+                              "GBps": round(b / us / 1e3, 1), "frac_of_peak": round(b / us / 1e3 / PEAK_GBS, 4),
+                              "bytes": b, "partitions": P, "pages_per_partition": ppp}),
+                  file=sys.stderr, flush=True)
+            del case
+            torch.cuda.empty_cache()
+        args.workload = "target"
+
+    case = make_workload(args.workload, "cuda")
+    us = time_calls(case, args.steps, args.warmup)
+    B = case.algorithmic_bytes()
+    gbs = B / us / 1e3
+    P, ppp, _ = pa.pa_decode_plan(case.num_seqs, case.num_heads, case.num_kv_heads, case.max_blocks, 256)
+    traffic = counter_traffic() if args.workload == "target" else None
+    line = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 6),
+        "us_per_call": round(us, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(PAGES_ASM_US / us, 4) if args.workload == "target" else None,
+        "vs_baseline_ref": "pages' MI355X pa_fwd_asm 363.04 us/call at this workload (ratio of call times)",
+        "vs_pages_hip": round(PAGES_HIP_US / us, 4) if args.workload == "target" else None,
+        "dtype": "fp8_e4m3fn KV, bf16 q/out, bf16/fp16 MFMA, fp32 accumulate",
+        "data": "synthetic (seeded N(0,1) q, K, V; per-tensor fp8 scales; shuffled block table)",
+        "config": {"workload": args.workload if args.workload != "target" else
+                   "40q/8kv heads, head_dim 128, 256 seqs x ctx 4096, fp8 e4m3fn KV, 16-token blocks",
+                   "num_seqs": case.num_seqs, "num_heads": case.num_heads,
+                   "num_kv_heads": case.num_kv_heads, "max_blocks_per_seq": case.max_blocks,
+                   "partitions": P, "pages_per_partition": ppp, "algorithmic_bytes": B},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_GBS, 4), "traffic": traffic},
+    }
+    del case
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,137 @@
+/*
+ * paged_attention.h -- C ABI of libpagedattn.so: single-token (decode) attention
+ * over a paged fp8-e4m3fn KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (vLLM pull request lishuoshuo-amd/vllm #3, Overview and
+ * Details > Layout; API page vllm.v1.attention.backends.rocm_aiter_unified_attn,
+ * RocmAiterUnifiedAttentionImpl.forward):
+ *
+ *   for every sequence s and query head h, with G = num_heads / num_kv_heads,
+ *   kv head k = h / G and n = seq_lens[s]:
+ *     token t (0 <= t < n) sits in physical block block_tables[s][t / 16], slot t % 16
+ *     K_t = fp8(k_cache[block][k][:, slot, :]) * k_scale     (128 values)
+ *     V_t = fp8(v_cache[block][k][:, slot])    * v_scale     (128 values)
+ *     out[s][h] = sum_t softmax_t(scale * q[s][h] . K_t) * V_t
+ *
+ * fp8 is the OCP e4m3fn format (largest finite 448, NaN = 0x7F / 0xFF).
+ * Accumulation is fp32; out is rounded to bf16 (nearest even).  A sequence with
+ * seq_lens[s] == 0 gets an all-zero output row.
+ *
+ * Memory: every pointer is device memory of the current HIP device, owned by
+ * the caller and not retained after the call returns.  Calls are asynchronous:
+ * they validate their arguments on the host, enqueue work on `stream` and
+ * return; they never read device memory on the host and never synchronise, so
+ * they may be captured into a HIP graph.  Split-KV scratch is owned by the
+ * library (one buffer per device, grown with hipMalloc outside capture only;
+ * see pa_decode_reserve_workspace).  Two calls that run concurrently on one
+ * device (different streams or threads) must not both need the split-KV
+ * scratch: they would share it.
+ *
+ * Errors: every check runs before any launch.  A failing call returns a
+ * negative pa_status, launches nothing, and leaves a message for
+ * pa_last_error() (thread-local).  No exception crosses the ABI; nothing aborts.
+ * Conditions that only device memory could reveal are not checked: seq_lens
+ * above 16 * max_blocks_per_seq are clamped to that, and block ids are trusted
+ * (an id outside [0, num_blocks) reads outside the caches).
+ */
+#ifndef PAGED_ATTENTION_H_
+#define PAGED_ATTENTION_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,        /* a required pointer is NULL                            */
+  PA_ERR_SHAPE = -2,       /* a size is negative or sizes disagree                  */
+  PA_ERR_UNSUPPORTED = -3, /* head_size != 128, block_size != 16 or group > 16      */
+  PA_ERR_ALIAS = -4,       /* out overlaps an input                                 */
+  PA_ERR_WORKSPACE = -5,   /* split-KV scratch too small while `stream` captures    */
+  PA_ERR_HIP = -6          /* a HIP runtime call or a kernel launch failed          */
+} pa_status;
+
+/*
+ * Paged decode attention (see the top of this file for the operation).
+ *
+ *   q             bf16  [num_seqs][num_heads][head_size], dense
+ *   k_cache       fp8   [num_blocks][num_kv_heads][head_size/16][16][16], dense:
+ *                       per (block, kv head) one 2048-byte page holding, for each
+ *                       16-dim chunk, the 16 slots' 16 dims
+ *   v_cache       fp8   [num_blocks][num_kv_heads][head_size][16], dense: per
+ *                       (block, kv head) one 2048-byte page holding, for each dim,
+ *                       the 16 slots (the 5-D view [.., 1, head_size, 16] has the
+ *                       same bytes)
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq], dense; logical block j of
+ *                       sequence s is physical block block_tables[s][j]; entries at
+ *                       or past ceil(seq_lens[s] / 16) are never read
+ *   seq_lens      int32 [num_seqs], tokens cached per sequence (current one included)
+ *   num_heads     query heads; a positive multiple of num_kv_heads, group <= 16
+ *   head_size     must be 128;  block_size must be 16
+ *   num_blocks    physical blocks in each cache (sizes the caches for the alias check)
+ *   scale         softmax scale applied to q.K (e.g. 1/sqrt(128)), host value
+ *   k_scale       fp32 [1], device: dequantisation scale of the K cache
+ *   v_scale       fp32 [1], device: dequantisation scale of the V cache
+ *   out           bf16  [num_seqs][num_heads][head_size], dense, written in full;
+ *                       must not overlap any input
+ *   stream        hipStream_t to enqueue on (NULL: the default stream)
+ *
+ * num_seqs == 0 is a no-op returning PA_OK.
+ */
+int paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* seq_lens,
+                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                           int32_t head_size, int32_t block_size,
+                           int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                           const float* k_scale, const float* v_scale, void* out,
+                           void* stream);
+
+/*
+ * The same operation with an explicit split-KV partition size: each sequence's
+ * blocks are cut into partitions of `pages_per_partition` 16-token blocks,
+ * computed independently and merged by a log-sum-exp reduction.  0 lets the
+ * library choose (what paged_decode_attention does).  Results of different
+ * partition sizes agree to rounding, not bit for bit; one size always gives
+ * the same bits for the same inputs.
+ */
+int paged_decode_attention_split(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, const int32_t* seq_lens,
+                                 int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_size, int32_t block_size,
+                                 int32_t max_blocks_per_seq, int64_t num_blocks,
+                                 float scale, const float* k_scale, const float* v_scale,
+                                 void* out, void* stream, int32_t pages_per_partition);
+
+/*
+ * Launch plan for the given shapes (host arithmetic only; no device access).
+ * num_compute_units: the device's CU count (256 on MI355X).
+ * pages_per_partition: as in paged_decode_attention_split (0 = library's choice).
+ * Outputs (any may be NULL): number of partitions per sequence, blocks per
+ * partition, and the split-KV scratch bytes that plan needs (0 when it has one
+ * partition).  Returns PA_OK or PA_ERR_SHAPE.
+ */
+int pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                   int32_t max_blocks_per_seq, int32_t num_compute_units,
+                   int32_t pages_per_partition, int32_t* num_partitions,
+                   int32_t* pages_per_part, size_t* workspace_bytes);
+
+/*
+ * Make the current device's split-KV scratch at least `bytes` large.
+ * Growing it frees the old buffer (hipFree, which waits for the device) and
+ * allocates a new one (hipMalloc), so do it outside graph capture: call it
+ * before capturing a graph whose calls need scratch (pa_decode_plan gives the
+ * size).  Returns PA_OK or PA_ERR_HIP (allocation failed).
+ */
+int pa_decode_reserve_workspace(size_t bytes);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTENTION_H_ */

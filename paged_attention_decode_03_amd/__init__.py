@@ -1,0 +1,188 @@
+"""MI355X (gfx950) paged decode attention over an fp8-e4m3fn KV cache.
+
+A thin binding of ``libpagedattn.so`` (declared in ``include/paged_attention.h``):
+it turns torch tensors into pointers and sizes and calls the C ABI; every step
+of the computation runs in the library's HIP kernels.  torch supplies device
+memory and streams only.  If the library has not been built, importing works
+but every call raises: there is no fallback path.
+
+The operation, for each sequence s and query head h (G = num_heads / num_kv_heads,
+kv head h // G, n = seq_lens[s] tokens in 16-token blocks found through
+block_tables[s]):
+
+    out[s, h] = softmax(scale * q[s, h] . K^T) V,
+    K = fp8(k_cache) * k_scale,  V = fp8(v_cache) * v_scale
+
+with the cache layouts of the vLLM pull request lishuoshuo-amd/vllm #3
+(Details > Layout): K ``[num_blocks, num_kv_heads, 8, 16, 16]``, V
+``[num_blocks, num_kv_heads, 128, 16]`` (or ``[.., 1, 128, 16]``), fp8 e4m3fn.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "paged_decode_attention", "paged_decode_attention_split", "pa_decode_plan",
+    "pa_decode_reserve_workspace", "pa_last_error", "PagedAttentionError", "library_path",
+    "load_library",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libpagedattn.so")
+
+STATUS_NAMES = {
+    0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_UNSUPPORTED",
+    -4: "PA_ERR_ALIAS", -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_HIP",
+}
+
+_lib = None
+
+
+class PagedAttentionError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(code, code)}: {message}")
+        self.code = code
+
+
+def load_library():
+    """Load libpagedattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise RuntimeError(
+            f"{library_path} is missing: build it with "
+            "`python -m paged_attention_decode_03_amd.build` (there is no fallback path)")
+    lib = ctypes.CDLL(library_path)
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    common = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i64, f32, vp, vp, vp, vp]
+    lib.paged_decode_attention.argtypes = common
+    lib.paged_decode_attention.restype = ctypes.c_int
+    lib.paged_decode_attention_split.argtypes = common + [i32]
+    lib.paged_decode_attention_split.restype = ctypes.c_int
+    lib.pa_decode_plan.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(i32),
+                                   ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_size_t)]
+    lib.pa_decode_plan.restype = ctypes.c_int
+    lib.pa_decode_reserve_workspace.argtypes = [ctypes.c_size_t]
+    lib.pa_decode_reserve_workspace.restype = ctypes.c_int
+    lib.pa_last_error.argtypes = []
+    lib.pa_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def pa_last_error() -> str:
+    return load_library().pa_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise PagedAttentionError(rc, pa_last_error())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _scale_tensor(x, device):
+    if isinstance(x, torch.Tensor):
+        if x.dtype != torch.float32 or x.numel() != 1 or x.device != device:
+            raise TypeError("k_scale / v_scale must be one-element float32 tensors on the q device")
+        return x
+    return torch.tensor([float(x)], dtype=torch.float32, device=device)
+
+
+def _args(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale, v_scale, out, stream):
+    if q.dtype != torch.bfloat16 or q.dim() != 3:
+        raise TypeError("q must be a bfloat16 tensor [num_seqs, num_heads, head_size]")
+    dev = q.device
+    if dev.type != "cuda":
+        raise TypeError("tensors must be on a GPU")
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise TypeError(f"{name} must be uint8 or float8_e4m3fn")
+        if t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous and on {dev}")
+    if k_cache.dim() != 5:
+        raise ValueError("k_cache must be [num_blocks, num_kv_heads, head_size/16, 16, 16]")
+    if v_cache.dim() == 5:
+        if v_cache.shape[2] != 1:
+            raise ValueError("a 5-D v_cache must be [num_blocks, num_kv_heads, 1, head_size, 16]")
+        v_cache = v_cache.squeeze(2)
+    if v_cache.dim() != 4 or v_cache.shape[:2] != k_cache.shape[:2]:
+        raise ValueError("v_cache must be [num_blocks, num_kv_heads, head_size, block_size]")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.device != dev:
+        raise TypeError("block_tables must be int32 [num_seqs, max_blocks_per_seq] on the q device")
+    if seq_lens.dtype != torch.int32 or seq_lens.dim() != 1 or seq_lens.device != dev:
+        raise TypeError("seq_lens must be int32 [num_seqs] on the q device")
+    if not (q.is_contiguous() and block_tables.is_contiguous() and seq_lens.is_contiguous()):
+        raise ValueError("q, block_tables and seq_lens must be contiguous")
+    S, Hq, D = q.shape
+    NB, Hkv = k_cache.shape[:2]
+    bs = k_cache.shape[3]
+    if k_cache.shape[2] * k_cache.shape[4] != D or v_cache.shape[2] != D or v_cache.shape[3] != bs:
+        raise ValueError("cache shapes disagree with head_size / block_size")
+    if block_tables.shape[0] != S or seq_lens.shape[0] != S:
+        raise ValueError("block_tables / seq_lens disagree with num_seqs")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.dtype != torch.bfloat16 or out.shape != q.shape or not out.is_contiguous() or out.device != dev:
+        raise ValueError("out must be a contiguous bfloat16 tensor shaped like q")
+    ks = _scale_tensor(k_scale, dev)
+    vs = _scale_tensor(v_scale, dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    c_args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens),
+              S, Hq, Hkv, D, bs, block_tables.shape[1], NB, float(scale), _ptr(ks), _ptr(vs),
+              _ptr(out), handle)
+    return dev, out, c_args, (ks, vs)
+
+
+def paged_decode_attention(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale, v_scale,
+                           out=None, stream=None):
+    """Enqueue paged decode attention on `stream` (default: torch's current stream).
+
+    Returns ``out`` (allocated like q when not given).  k_scale / v_scale are
+    one-element float32 device tensors (a Python float is copied to the device).
+    """
+    lib = load_library()
+    dev, out, c_args, keep = _args(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale,
+                                   v_scale, out, stream)
+    with torch.cuda.device(dev):
+        _check(lib.paged_decode_attention(*c_args))
+    return out
+
+
+def paged_decode_attention_split(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale,
+                                 v_scale, pages_per_partition: int, out=None, stream=None):
+    """paged_decode_attention with an explicit split-KV partition size (blocks; 0 = auto)."""
+    lib = load_library()
+    dev, out, c_args, keep = _args(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale,
+                                   v_scale, out, stream)
+    with torch.cuda.device(dev):
+        _check(lib.paged_decode_attention_split(*c_args, int(pages_per_partition)))
+    return out
+
+
+def pa_decode_plan(num_seqs, num_heads, num_kv_heads, max_blocks_per_seq, num_compute_units=256,
+                   pages_per_partition=0):
+    """(num_partitions, pages_per_partition, workspace_bytes) the library would use."""
+    lib = load_library()
+    P = ctypes.c_int32()
+    ppp = ctypes.c_int32()
+    ws = ctypes.c_size_t()
+    _check(lib.pa_decode_plan(num_seqs, num_heads, num_kv_heads, max_blocks_per_seq,
+                              num_compute_units, pages_per_partition, ctypes.byref(P),
+                              ctypes.byref(ppp), ctypes.byref(ws)))
+    return P.value, ppp.value, ws.value
+
+
+def pa_decode_reserve_workspace(nbytes: int, device=None):
+    """Grow the split-KV scratch of `device` (default: current) to at least nbytes."""
+    lib = load_library()
+    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+        _check(lib.pa_decode_reserve_workspace(int(nbytes)))

@@ -1,0 +1,264 @@
+// C ABI of libpagedattn.so (declared in include/paged_attention.h): argument
+// validation, the shape-only split-KV planner, the per-device split-KV
+// scratch, and the launch.
+//
+// Every check runs on the host before any HIP call, so a rejected call touches
+// no device and needs no GPU.  Nothing here reads device memory or
+// synchronises on the call path (vLLM pull request lishuoshuo-amd/vllm #3,
+// Validation: no host synchronisation under torch's sync check; Details > Cut
+// and precision: the kernel choice is made on the host from shapes so one
+// captured graph uses one kernel).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "paged_attention.h"
+#include "pa_decode_kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+// Planner constants.
+constexpr int kWavesPerCU = 8;           // the decode kernel runs 2 waves per SIMD
+constexpr int kDefaultCUs = 256;         // MI355X
+
+struct Plan {
+  int32_t num_parts;
+  int32_t pages_per_part;
+  size_t workspace_bytes;
+};
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Shape-only plan.  Enough partitions that every wave slot of the device gets
+// a work item; none longer than pa::kMaxPagesPerPart blocks.
+int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t W, int32_t num_cus, int32_t ppp_req,
+              Plan* plan) {
+  if (S < 0 || Hq <= 0 || Hkv <= 0 || W < 0 || ppp_req < 0)
+    return fail(PA_ERR_SHAPE, "plan: negative or zero size (S=%d Hq=%d Hkv=%d W=%d ppp=%d)", S, Hq,
+                Hkv, W, ppp_req);
+  const int64_t Wc = W > 0 ? W : 1;
+  int64_t ppp;
+  if (ppp_req > 0) {
+    ppp = ppp_req < Wc ? ppp_req : Wc;
+  } else {
+    const int64_t items = (int64_t)(S > 0 ? S : 1) * Hkv;
+    const int64_t slots = (int64_t)(num_cus > 0 ? num_cus : kDefaultCUs) * kWavesPerCU;
+    int64_t parts = ceil_div(slots, items);
+    if (parts < 1) parts = 1;
+    if (parts > Wc) parts = Wc;
+    ppp = ceil_div(Wc, parts);
+  }
+  if (ppp > pa::kMaxPagesPerPart) ppp = pa::kMaxPagesPerPart;
+  const int64_t parts = ceil_div(Wc, ppp);
+  plan->num_parts = (int32_t)parts;
+  plan->pages_per_part = (int32_t)ppp;
+  plan->workspace_bytes =
+      parts > 1 ? (size_t)S * Hq * parts * (pa::kHeadDim + 2) * sizeof(float) : 0;
+  return PA_OK;
+}
+
+// Per-device split-KV scratch.
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::vector<Workspace> g_ws;
+std::vector<int> g_cus;
+
+int device_cus(int dev) {
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  if ((int)g_cus.size() <= dev) g_cus.resize(dev + 1, 0);
+  if (g_cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = kDefaultCUs;
+    g_cus[dev] = n;
+  }
+  return g_cus[dev];
+}
+
+int ensure_workspace(int dev, size_t bytes, hipStream_t stream, bool check_capture, void** out) {
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
+  Workspace& ws = g_ws[dev];
+  if (ws.bytes >= bytes) {
+    *out = ws.ptr;
+    return PA_OK;
+  }
+  if (check_capture) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &st) != hipSuccess)
+      return fail(PA_ERR_HIP, "hipStreamIsCapturing failed");
+    if (st != hipStreamCaptureStatusNone)
+      return fail(PA_ERR_WORKSPACE,
+                  "split-KV scratch needs %zu bytes but %zu are reserved and the stream is "
+                  "capturing; call pa_decode_reserve_workspace before capture",
+                  bytes, ws.bytes);
+  }
+  const size_t grow = (bytes + (size_t(1) << 20) - 1) & ~((size_t(1) << 20) - 1);
+  if (ws.ptr) {
+    if (hipFree(ws.ptr) != hipSuccess) return fail(PA_ERR_HIP, "hipFree of the old scratch failed");
+    ws.ptr = nullptr;
+    ws.bytes = 0;
+  }
+  void* p = nullptr;
+  if (hipMalloc(&p, grow) != hipSuccess) return fail(PA_ERR_HIP, "hipMalloc(%zu) for scratch failed", grow);
+  ws.ptr = p;
+  ws.bytes = grow;
+  *out = p;
+  return PA_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return na && nb && a0 < b0 + nb && b0 < a0 + na;
+}
+
+int decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+           const int32_t* seq_lens, int32_t S, int32_t Hq, int32_t Hkv, int32_t head_size,
+           int32_t block_size, int32_t W, int64_t NB, float scale, const float* k_scale,
+           const float* v_scale, void* out, void* stream_ptr, int32_t ppp_req) {
+  g_last_error[0] = '\0';
+  if (head_size != pa::kHeadDim)
+    return fail(PA_ERR_UNSUPPORTED, "head_size %d unsupported (only %d)", head_size, pa::kHeadDim);
+  if (block_size != pa::kBlockTokens)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d unsupported (only %d)", block_size,
+                pa::kBlockTokens);
+  if (S < 0 || Hq <= 0 || Hkv <= 0 || W < 0 || NB < 0 || ppp_req < 0)
+    return fail(PA_ERR_SHAPE,
+                "negative or zero size: num_seqs=%d num_heads=%d num_kv_heads=%d "
+                "max_blocks_per_seq=%d num_blocks=%lld pages_per_partition=%d",
+                S, Hq, Hkv, W, (long long)NB, ppp_req);
+  if (Hq % Hkv != 0)
+    return fail(PA_ERR_SHAPE, "num_heads %d is not a multiple of num_kv_heads %d", Hq, Hkv);
+  const int32_t G = Hq / Hkv;
+  if (G > pa::kMaxGroup)
+    return fail(PA_ERR_UNSUPPORTED, "group size %d exceeds %d query heads per kv head", G,
+                pa::kMaxGroup);
+  if (!isfinite(scale)) return fail(PA_ERR_SHAPE, "scale is not finite");
+  if (S == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !k_scale || !v_scale || !out)
+    return fail(PA_ERR_NULL, "a required pointer is NULL");
+  if (W == 0 || NB == 0)
+    return fail(PA_ERR_SHAPE, "max_blocks_per_seq and num_blocks must be positive when num_seqs > 0");
+
+  const size_t q_bytes = (size_t)S * Hq * pa::kHeadDim * 2;
+  const size_t cache_bytes = (size_t)NB * Hkv * pa::kPageBytes;
+  if (overlaps(out, q_bytes, q, q_bytes) || overlaps(out, q_bytes, k_cache, cache_bytes) ||
+      overlaps(out, q_bytes, v_cache, cache_bytes) ||
+      overlaps(out, q_bytes, block_tables, (size_t)S * W * 4) ||
+      overlaps(out, q_bytes, seq_lens, (size_t)S * 4) || overlaps(out, q_bytes, k_scale, 4) ||
+      overlaps(out, q_bytes, v_scale, 4))
+    return fail(PA_ERR_ALIAS, "out overlaps an input");
+  if (((uintptr_t)q & 15) || ((uintptr_t)k_cache & 15) || ((uintptr_t)v_cache & 3) ||
+      ((uintptr_t)out & 7) || ((uintptr_t)block_tables & 3) || ((uintptr_t)seq_lens & 3))
+    return fail(PA_ERR_SHAPE, "misaligned pointer (q, k_cache: 16 B; out: 8 B; others: 4 B)");
+
+  // --- past this point HIP is called
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice failed");
+  Plan plan;
+  int rc = make_plan(S, Hq, Hkv, W, device_cus(dev), ppp_req, &plan);
+  if (rc) return rc;
+  hipStream_t stream = (hipStream_t)stream_ptr;
+
+  pa::DecodeParams p;
+  p.q = (const uint16_t*)q;
+  p.k_cache = (const uint8_t*)k_cache;
+  p.v_cache = (const uint8_t*)v_cache;
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.out = (uint16_t*)out;
+  p.part_acc = nullptr;
+  p.part_ml = nullptr;
+  p.num_seqs = S;
+  p.num_heads = Hq;
+  p.num_kv_heads = Hkv;
+  p.group = G;
+  p.max_blocks = W;
+  p.num_parts = plan.num_parts;
+  p.pages_per_part = plan.pages_per_part;
+  p.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  if (plan.workspace_bytes) {
+    void* ws = nullptr;
+    rc = ensure_workspace(dev, plan.workspace_bytes, stream, true, &ws);
+    if (rc) return rc;
+    p.part_acc = (float*)ws;
+    p.part_ml = (float*)ws + (size_t)S * Hq * plan.num_parts * pa::kHeadDim;
+  }
+  const hipError_t err = pa::launch_decode(p, stream);
+  if (err != hipSuccess) return fail(PA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                           int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                           int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                           float scale, const float* k_scale, const float* v_scale, void* out,
+                           void* stream) {
+  return decode(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads, num_kv_heads,
+                head_size, block_size, max_blocks_per_seq, num_blocks, scale, k_scale, v_scale, out,
+                stream, 0);
+}
+
+int paged_decode_attention_split(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, const int32_t* seq_lens,
+                                 int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
+                                 int64_t num_blocks, float scale, const float* k_scale,
+                                 const float* v_scale, void* out, void* stream,
+                                 int32_t pages_per_partition) {
+  return decode(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads, num_kv_heads,
+                head_size, block_size, max_blocks_per_seq, num_blocks, scale, k_scale, v_scale, out,
+                stream, pages_per_partition);
+}
+
+int pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                   int32_t max_blocks_per_seq, int32_t num_compute_units,
+                   int32_t pages_per_partition, int32_t* num_partitions, int32_t* pages_per_part,
+                   size_t* workspace_bytes) {
+  g_last_error[0] = '\0';
+  Plan plan;
+  const int rc = make_plan(num_seqs, num_heads, num_kv_heads, max_blocks_per_seq, num_compute_units,
+                           pages_per_partition, &plan);
+  if (rc) return rc;
+  if (num_partitions) *num_partitions = plan.num_parts;
+  if (pages_per_part) *pages_per_part = plan.pages_per_part;
+  if (workspace_bytes) *workspace_bytes = plan.workspace_bytes;
+  return PA_OK;
+}
+
+int pa_decode_reserve_workspace(size_t bytes) {
+  g_last_error[0] = '\0';
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice failed");
+  void* p = nullptr;
+  return ensure_workspace(dev, bytes, nullptr, false, &p);
+}
+
+const char* pa_last_error(void) { return g_last_error; }
+
+}  // extern "C"

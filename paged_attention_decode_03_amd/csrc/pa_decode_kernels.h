@@ -1,0 +1,40 @@
+// Internal interface between the C-ABI layer (pa_api.hip) and the gfx950
+// kernels (pa_decode_kernels.hip).  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kHeadDim = 128;
+constexpr int kBlockTokens = 16;
+constexpr int kPageBytes = kHeadDim * kBlockTokens;  // one (block, kv head) page of fp8
+constexpr int kMaxGroup = 16;                         // query heads per kv head (MFMA N)
+constexpr int kMaxPagesPerPart = 256;                 // blocks per work item (LDS id buffer)
+
+struct DecodeParams {
+  const uint16_t* q;         // bf16 [S][Hq][128]
+  const uint8_t* k_cache;    // fp8  [NB][Hkv][8][16][16]
+  const uint8_t* v_cache;    // fp8  [NB][Hkv][128][16]
+  const int32_t* block_tables;  // [S][W]
+  const int32_t* seq_lens;      // [S]
+  const float* k_scale;      // [1]
+  const float* v_scale;      // [1]
+  uint16_t* out;             // bf16 [S][Hq][128]
+  float* part_acc;           // [S][Hq][P][128] unnormalised partial outputs (P > 1 only)
+  float* part_ml;            // [S][Hq][P][2]   (running max in log2 units, sum of weights)
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t group;             // num_heads / num_kv_heads, 1..16
+  int32_t max_blocks;        // W, block-table row length
+  int32_t num_parts;         // P, partitions per sequence
+  int32_t pages_per_part;    // blocks per partition
+  float scale_log2e;         // softmax scale * log2(e)
+};
+
+// Enqueue the decode (and, when num_parts > 1, the merge) on `stream`.
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+
+}  // namespace pa

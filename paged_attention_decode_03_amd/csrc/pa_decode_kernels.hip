@@ -1,0 +1,329 @@
+// gfx950 kernels for single-token paged decode attention over an fp8-e4m3fn
+// KV cache (16-token blocks, head_dim 128, GQA groups of up to 16 query heads).
+//
+// The operation follows the vLLM pull request lishuoshuo-amd/vllm #3
+// (Overview; Details > Layout: K pages [head_size/16][16][16], V pages
+// [head_size][16], addressed by a dense page stride) and the API page
+// vllm.v1.attention.backends.rocm_aiter_unified_attn
+// (RocmAiterUnifiedAttentionImpl.forward: block_table, seqused_k,
+// softmax_scale, k_descale / v_descale).
+//
+// One wavefront owns one work item (sequence, kv head, partition) and keeps
+// every query head of the kv head's group in the 16 columns of its MFMA tiles,
+// so each fp8 K/V byte is fetched from HBM once and used by the whole group.
+//
+//   QK^T  v_mfma_f32_16x16x32_bf16: A = K page (16 tokens x 32 dims, fp8 -> bf16
+//         exactly), B = q^T (32 dims x 16 heads).  Four per page.
+//   PV    v_mfma_f32_16x16x16_f16:  A = V^T (16 dims x 16 tokens, fp8 -> fp16
+//         exactly), B = P^T (16 tokens x 16 heads, fp16).  Eight per page,
+//         plus one with A = ones that accumulates the softmax denominator from
+//         the same rounded P.
+//
+// The D layout of both MFMAs puts head (lane & 15) and rows 4*(lane >> 4)+i in
+// lane `lane`, so the QK^T result is already the B operand of PV and every
+// per-head softmax quantity (running max, rescale factor) is lane-local; the
+// only cross-lane step is a max over the four 16-lane rows (permlane swaps).
+//
+// Loads go straight from HBM into VGPRs, in the layouts the MFMAs want:
+//   K: two fully coalesced 1 KiB dwordx4 loads per page (lane l: token l & 15,
+//      16-dim chunks l >> 4 and 4 + (l >> 4)),
+//   V: eight dword loads per page, each a contiguous 256 B (16 dims x 16 slots).
+// Pages are software-pipelined PPS at a time, one stage ahead.
+#include <math.h>
+
+#include "pa_decode_kernels.h"
+
+namespace pa {
+namespace {
+
+typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef _Float16 f16x2 __attribute__((__vector_size__(2 * sizeof(_Float16))));
+typedef _Float16 f16x4 __attribute__((__vector_size__(4 * sizeof(_Float16))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+
+constexpr int kPagesPerStage = 4;
+
+// Wave-uniform load through the scalar data cache (read-only data).
+template <typename T>
+__device__ __forceinline__ T scalar_load(const T* ptr) {
+  return *(const __attribute__((address_space(4))) T*)(ptr);
+}
+
+// Eight fp8 e4m3fn codes (two dwords, byte order) -> eight bf16, exactly.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  bf16x8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  return r;
+}
+
+// Four fp8 e4m3fn codes (one dword, byte order) -> four fp16, exactly.
+__device__ __forceinline__ f16x4 fp8x4_to_f16(uint32_t v) {
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, false);
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, true);
+  f16x4 r = {a[0], a[1], b[0], b[1]};
+  return r;
+}
+
+// Max of x over lanes l, l^16, l^32, l^48 (the four 16-lane rows).
+__device__ __forceinline__ float max_over_rows(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const __bf16 x = (__bf16)a;
+  const __bf16 y = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+__device__ __forceinline__ int clamp_len(int len, int max_blocks) {
+  return min(max(len, 0), max_blocks * kBlockTokens);
+}
+
+template <int PPS>
+struct Stage {
+  u32x4 k[PPS][2];     // per page: 16 bytes of chunk (l >> 4) and of chunk 4 + (l >> 4)
+  uint32_t v[PPS][8];  // per page: 4 slots of one dim in each of the 8 16-dim blocks
+};
+
+template <int PPS>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pa_decode_kernel(const DecodeParams p) {
+  const int lane = threadIdx.x;
+  const int col = lane & 15;  // MFMA column (query head in group); K load row (token)
+  const int rq = lane >> 4;   // row quad: rows 4*rq .. 4*rq+3 of the 16x16 tiles
+
+  const int item = blockIdx.x;
+  const int part = item % p.num_parts;
+  const int sk = item / p.num_parts;
+  const int kvh = sk % p.num_kv_heads;
+  const int s = sk / p.num_kv_heads;
+
+  const int L = clamp_len(scalar_load(p.seq_lens + s), p.max_blocks);
+  const int npages = (L + kBlockTokens - 1) / kBlockTokens;
+  const int ppp = p.pages_per_part;
+  const int nused = (npages + ppp - 1) / ppp;  // partitions holding tokens
+  if (part > 0 && part >= nused) return;
+  const bool direct = nused <= 1;  // one partition: write the final output here
+
+  const int h = kvh * p.group + col;
+  const bool hvalid = col < p.group;
+  const size_t orow = ((size_t)s * p.num_heads + h) * kHeadDim;
+
+  if (L == 0) {  // empty context: an all-zero row
+    if (hvalid) {
+#pragma unroll
+      for (int jd = 0; jd < 8; ++jd)
+        *(uint2*)(p.out + orow + jd * 16 + rq * 4) = make_uint2(0u, 0u);
+    }
+    return;
+  }
+
+  const int pbeg = part * ppp;
+  const int pend = min(pbeg + ppp, npages);
+  const int tend = min(L, pend * kBlockTokens);  // first token this item must not use
+
+  // B operand of QK^T: q^T, 8 dims per MFMA.  Element e of qop[h2][c] is dim
+  // 16 * (4 * h2 + rq) + 8 * c + e, matching the K bytes this lane loads.
+  bf16x8 qop[2][2];
+  if (hvalid) {
+    const uint16_t* qrow = p.q + orow;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        qop[h2][c] = *(const bf16x8*)(qrow + 16 * (4 * h2 + rq) + 8 * c);
+  } else {
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+        qop[h2][c] = bf16x8{};
+  }
+
+  // logits in log2 units: z * scale * k_scale * log2(e)
+  const float c_log2 = p.scale_log2e * scalar_load(p.k_scale);
+
+  const int32_t* bt = p.block_tables + (size_t)s * p.max_blocks;
+  const size_t page_stride = (size_t)p.num_kv_heads * kPageBytes;
+  const uint8_t* kbase = p.k_cache + (size_t)kvh * kPageBytes + lane * 16;
+  const uint8_t* vbase = p.v_cache + (size_t)kvh * kPageBytes + col * 16 + rq * 4;
+
+  f32x4 acc[8];  // O^T tiles: dims 16*jd + 4*rq + i for head `col`
+#pragma unroll
+  for (int jd = 0; jd < 8; ++jd) acc[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 accl = {0.f, 0.f, 0.f, 0.f};  // softmax denominator (same value in every element)
+  float m_run = -INFINITY;
+  const f16x4 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
+
+  // The partition's physical block ids, staged once in LDS.  Entries past the
+  // partition repeat its last id, so a stage never needs a bounds check: those
+  // pages are re-reads whose tokens the last stage masks.
+  __shared__ __attribute__((aligned(16))) int32_t ids[kMaxPagesPerPart + PPS];
+  const int npg = pend - pbeg;
+  const int npg_pad = (npg + PPS - 1) / PPS * PPS;
+  for (int i = lane; i < npg_pad; i += 64) ids[i] = bt[pbeg + min(i, npg - 1)];
+  __syncthreads();
+
+  auto load = [&](Stage<PPS>& st, int j0) {
+    int32_t pid[PPS];
+    if constexpr (PPS == 4) {
+      const int4 v = *(const int4*)(ids + (j0 - pbeg));
+      pid[0] = v.x; pid[1] = v.y; pid[2] = v.z; pid[3] = v.w;
+    } else {
+#pragma unroll
+      for (int pp = 0; pp < PPS; ++pp) pid[pp] = ids[j0 - pbeg + pp];
+    }
+#pragma unroll
+    for (int pp = 0; pp < PPS; ++pp) {
+      const size_t off = (size_t)__builtin_amdgcn_readfirstlane(pid[pp]) * page_stride;
+      const uint8_t* kp = kbase + off;
+      st.k[pp][0] = *(const u32x4*)(kp);
+      st.k[pp][1] = *(const u32x4*)(kp + 1024);
+      const uint8_t* vp = vbase + off;
+#pragma unroll
+      for (int jd = 0; jd < 8; ++jd) st.v[pp][jd] = *(const uint32_t*)(vp + jd * 256);
+    }
+    // keep the scheduler from hoisting compute above these loads
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  auto compute = [&](const Stage<PPS>& st, int j0, bool last) {
+    f32x4 z[PPS];
+#pragma unroll
+    for (int pp = 0; pp < PPS; ++pp) {
+      f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const u32x4 kk = st.k[pp][h2];
+        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(kk[0], kk[1]), qop[h2][0], t, 0, 0, 0);
+        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(kk[2], kk[3]), qop[h2][1], t, 0, 0, 0);
+      }
+      z[pp] = t;
+    }
+    // scale, mask, running max
+    float mx = -INFINITY;
+#pragma unroll
+    for (int pp = 0; pp < PPS; ++pp) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = z[pp][i] * c_log2;
+        if (last) {
+          const int t = (j0 + pp) * kBlockTokens + rq * 4 + i;
+          v = (t < tend) ? v : -INFINITY;
+        }
+        z[pp][i] = v;
+        mx = fmaxf(mx, v);
+      }
+    }
+    mx = max_over_rows(mx);
+    const float m_new = fmaxf(m_run, mx);
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run)) {
+      const float alpha = (m_new == m_run) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+      for (int jd = 0; jd < 8; ++jd) acc[jd] *= alpha;
+      accl *= alpha;
+      m_run = m_new;
+    }
+    // P = 2^(z - m) in fp16, then PV
+#pragma unroll
+    for (int pp = 0; pp < PPS; ++pp) {
+      f16x4 pb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pb[i] = (_Float16)__builtin_amdgcn_exp2f(z[pp][i] - m_run);
+      uint32_t vmask = 0xFFFFFFFFu;
+      if (last) {
+        // slots past the context may hold anything (even NaN): zero their V bytes
+        const int nv = tend - ((j0 + pp) * kBlockTokens + rq * 4);
+        vmask = nv >= 4 ? 0xFFFFFFFFu : (nv <= 0 ? 0u : ((1u << (8 * nv)) - 1u));
+      }
+#pragma unroll
+      for (int jd = 0; jd < 8; ++jd)
+        acc[jd] = __builtin_amdgcn_mfma_f32_16x16x16f16(fp8x4_to_f16(st.v[pp][jd] & vmask), pb, acc[jd], 0, 0, 0);
+      accl = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pb, accl, 0, 0, 0);
+    }
+  };
+
+  const int nsteps = npg_pad / PPS;
+  Stage<PPS> sa, sb;
+  load(sa, pbeg);
+  int st = 0;
+  for (; st + 2 < nsteps; st += 2) {
+    load(sb, pbeg + (st + 1) * PPS);
+    compute(sa, pbeg + st * PPS, false);
+    load(sa, pbeg + (st + 2) * PPS);
+    compute(sb, pbeg + (st + 1) * PPS, false);
+  }
+  if (st + 1 < nsteps) {
+    load(sb, pbeg + (st + 1) * PPS);
+    compute(sa, pbeg + st * PPS, false);
+    compute(sb, pbeg + (st + 1) * PPS, true);
+  } else {
+    compute(sa, pbeg + st * PPS, true);
+  }
+
+  if (!hvalid) return;
+  const float lsum = accl[0];
+  if (direct) {
+    const float inv = scalar_load(p.v_scale) / lsum;
+    uint16_t* o = p.out + orow + rq * 4;
+#pragma unroll
+    for (int jd = 0; jd < 8; ++jd) {
+      const f32x4 a = acc[jd];
+      *(uint2*)(o + jd * 16) = make_uint2(pack_bf16x2(a[0] * inv, a[1] * inv), pack_bf16x2(a[2] * inv, a[3] * inv));
+    }
+  } else {
+    const size_t prow = ((size_t)s * p.num_heads + h) * p.num_parts + part;
+    float* a = p.part_acc + prow * kHeadDim + rq * 4;
+#pragma unroll
+    for (int jd = 0; jd < 8; ++jd) *(f32x4*)(a + jd * 16) = acc[jd];
+    if (rq == 0) *(float2*)(p.part_ml + prow * 2) = make_float2(m_run, lsum);
+  }
+}
+
+// Log-sum-exp merge of the partitions of one (sequence, query head):
+//   M = max_p m_p,  w_p = 2^(m_p - M),  out = v_scale * sum_p w_p a_p / sum_p w_p l_p.
+// Sequences whose context fits one partition were finished by the main kernel.
+__global__ __launch_bounds__(64) void pa_merge_kernel(const DecodeParams p) {
+  const int lane = threadIdx.x;
+  const int sh = blockIdx.x;
+  const int s = sh / p.num_heads;
+  const int L = clamp_len(scalar_load(p.seq_lens + s), p.max_blocks);
+  const int npages = (L + kBlockTokens - 1) / kBlockTokens;
+  const int nused = (npages + p.pages_per_part - 1) / p.pages_per_part;
+  if (nused <= 1) return;
+
+  const float* ml = p.part_ml + (size_t)sh * p.num_parts * 2;
+  float M = -INFINITY;
+  for (int i = 0; i < nused; ++i) M = fmaxf(M, scalar_load(ml + 2 * i));
+  float den = 0.f, n0 = 0.f, n1 = 0.f;
+  const float* a = p.part_acc + (size_t)sh * p.num_parts * kHeadDim + 2 * lane;
+  for (int i = 0; i < nused; ++i) {
+    const float w = __builtin_amdgcn_exp2f(scalar_load(ml + 2 * i) - M);
+    den += w * scalar_load(ml + 2 * i + 1);
+    const float2 v = *(const float2*)(a + (size_t)i * kHeadDim);
+    n0 += w * v.x;
+    n1 += w * v.y;
+  }
+  const float inv = scalar_load(p.v_scale) / den;
+  *(uint32_t*)(p.out + (size_t)sh * kHeadDim + 2 * lane) = pack_bf16x2(n0 * inv, n1 * inv);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
+  const size_t items = (size_t)p.num_seqs * p.num_kv_heads * p.num_parts;
+  hipLaunchKernelGGL(pa_decode_kernel<kPagesPerStage>, dim3((unsigned)items), dim3(64), 0, stream, p);
+  if (p.num_parts > 1)
+    hipLaunchKernelGGL(pa_merge_kernel, dim3((unsigned)((size_t)p.num_seqs * p.num_heads)), dim3(64), 0,
+                       stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace pa

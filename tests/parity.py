@@ -1,0 +1,88 @@
+"""Helpers shared by the GPU parity tests: run the HIP library through its
+binding, run the fp64 oracle on the same bytes, compare."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+
+# Bound for bf16 output against the fp64 oracle: max abs 1e-2, mean abs 5e-4.
+MAX_ABS = 1e-2
+MEAN_ABS = 5e-4
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(case, pages_per_partition=None, out=None, stream=None):
+    import paged_attention_decode_03_amd as pa
+    c = case if case.q.is_cuda else case.to("cuda")
+    ks = torch.tensor([case.k_scale], dtype=torch.float32, device="cuda")
+    vs = torch.tensor([case.v_scale], dtype=torch.float32, device="cuda")
+    if pages_per_partition is None:
+        o = pa.paged_decode_attention(c.q, c.k_cache, c.v_cache, c.block_tables, c.seq_lens,
+                                      c.scale, ks, vs, out=out, stream=stream)
+    else:
+        o = pa.paged_decode_attention_split(c.q, c.k_cache, c.v_cache, c.block_tables, c.seq_lens,
+                                            c.scale, ks, vs, pages_per_partition, out=out,
+                                            stream=stream)
+    torch.cuda.synchronize()
+    return o
+
+
+def run_oracle(case, seqs=None):
+    """fp64 oracle output for the sequences `seqs` (all when None): [len(seqs), Hq, 128]."""
+    h = case.host() if case.q.is_cuda else case
+    idx = np.arange(h.num_seqs) if seqs is None else np.asarray(seqs)
+    q_bits = h.q_bits()[idx]
+    return oracle.decode(q_bits, h.k_cache.numpy(), h.v_cache.numpy(),
+                         h.block_tables.numpy()[idx], h.seq_lens.numpy()[idx],
+                         h.scale, h.k_scale, h.v_scale)
+
+
+def compare(gpu_out, ref, label, seqs=None, max_abs=MAX_ABS, mean_abs=MEAN_ABS):
+    """Check bf16 GPU output against the fp64 oracle.
+
+    The bound (max abs <= 1e-2, mean abs <= 5e-4) is applied to |gpu - oracle|
+    wherever a bf16 output can meet it at all, i.e. wherever the correctly
+    rounded oracle output does; it is always applied to |gpu - bf16(oracle)|,
+    the distance from the best bf16 answer.  (Short contexts with |out| near 1,
+    such as a one-token sequence, have a bf16 rounding floor above 5e-4 mean.)
+    """
+    g = gpu_out.float().cpu().double().numpy()
+    if seqs is not None:
+        g = g[np.asarray(seqs)]
+    assert g.shape == ref.shape, (g.shape, ref.shape)
+    assert np.isfinite(g).all(), f"{label}: non-finite output"
+    err = np.abs(g - ref)
+    rne = oracle.bf16_bits_to_f64(oracle.bf16_rne(ref))
+    floor = np.abs(rne - ref)
+    err_rne = np.abs(g - rne)
+    log(f"[{label}] vs fp64: max={err.max():.3e} mean={err.mean():.3e} | "
+        f"vs bf16(oracle): max={err_rne.max():.3e} mean={err_rne.mean():.3e} | "
+        f"bf16 floor: max={floor.max():.3e} mean={floor.mean():.3e} | n={err.size}")
+    assert err_rne.max() <= max_abs, f"{label}: max error vs bf16(oracle) {err_rne.max():.3e} > {max_abs}"
+    assert err_rne.mean() <= mean_abs, f"{label}: mean error vs bf16(oracle) {err_rne.mean():.3e} > {mean_abs}"
+    if floor.max() <= max_abs:
+        assert err.max() <= max_abs, f"{label}: max abs error {err.max():.3e} > {max_abs}"
+    if floor.mean() <= mean_abs:
+        assert err.mean() <= mean_abs, f"{label}: mean abs error {err.mean():.3e} > {mean_abs}"
+    return err
+
+
+def sample_seqs(case, n, seed=0):
+    """n sequences spread over the batch, always including the longest and shortest."""
+    S = case.num_seqs
+    if n >= S:
+        return list(range(S))
+    lens = case.seq_lens.cpu().numpy()
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(S, size=n - 2, replace=False).tolist())
+    pick.add(int(lens.argmax()))
+    pick.add(int(lens.argmin()))
+    return sorted(pick)

@@ -1,0 +1,97 @@
+"""The C ABI without a GPU: the library loads, exports what the header declares,
+plans from shapes alone, and rejects bad arguments before touching HIP."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_attention.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import paged_attention_decode_03_amd as pa
+    if not os.path.exists(pa.library_path):
+        from paged_attention_decode_03_amd import build
+        build.build()
+    return pa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("paged_decode_attention", "paged_decode_attention_split", "pa_decode_plan",
+              "pa_decode_reserve_workspace", "pa_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def plan(lib, S, Hq, Hkv, W, cus=256, ppp=0):
+    P, n, ws = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_size_t()
+    rc = lib.pa_decode_plan(S, Hq, Hkv, W, cus, ppp, ctypes.byref(P), ctypes.byref(n), ctypes.byref(ws))
+    return rc, P.value, n.value, ws.value
+
+
+def test_plan_large_batch_is_unsplit(lib):
+    # 40/8 heads, 256 sequences, ctx 4096: 2048 work items fill 256 CUs x 8 waves
+    assert plan(lib, 256, 40, 8, 256) == (0, 1, 256, 0)
+
+
+def test_plan_small_batch_splits_long_context(lib):
+    rc, P, n, ws = plan(lib, 1, 40, 8, 2048)        # one sequence of 32768 tokens
+    assert rc == 0 and P * n >= 2048 and P == 256 and n == 8
+    assert ws == 1 * 40 * P * 130 * 4
+
+
+def test_plan_caps_partition_length(lib):
+    rc, P, n, ws = plan(lib, 4096, 32, 8, 2048)     # huge batch, 32K table: still <= 256 blocks
+    assert rc == 0 and n <= 256 and P * n >= 2048
+
+
+def test_plan_explicit_partition_size(lib):
+    assert plan(lib, 4, 8, 2, 4, ppp=1)[:3] == (0, 4, 1)
+    assert plan(lib, 4, 8, 2, 4, ppp=3)[:3] == (0, 2, 3)
+    assert plan(lib, 4, 8, 2, 4, ppp=100)[:3] == (0, 1, 4)
+
+
+def test_plan_rejects_bad_shapes(lib):
+    assert plan(lib, -1, 8, 2, 4)[0] == -2
+    assert plan(lib, 1, 8, 0, 4)[0] == -2
+
+
+FAKE = 1 << 20   # host never dereferences device pointers: any aligned address will do
+
+
+def call(lib, S=2, Hq=8, Hkv=2, D=128, bs=16, W=4, NB=16, scale=0.088, out=None, q=FAKE,
+         k=FAKE * 16, v=FAKE * 32, bt=FAKE * 48, sl=FAKE * 50, ks=FAKE * 52, vs=FAKE * 53):
+    out = FAKE * 64 if out is None else out
+    vp = ctypes.c_void_p
+    return lib.paged_decode_attention(vp(q), vp(k), vp(v), vp(bt), vp(sl), S, Hq, Hkv, D, bs, W, NB,
+                                      ctypes.c_float(scale), vp(ks), vp(vs), vp(out), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=64), -3), (dict(bs=32), -3), (dict(Hq=34, Hkv=2), -3),
+    (dict(Hq=9, Hkv=2), -2), (dict(S=-1), -2), (dict(Hkv=0), -2), (dict(W=0), -2),
+    (dict(q=0), -1), (dict(ks=0), -1), (dict(out=0), -1),
+    (dict(out=FAKE), -4), (dict(out=FAKE * 16 + 4096), -4),
+    (dict(scale=float("inf")), -2), (dict(q=FAKE + 8), -2),
+])
+def test_invalid_arguments_fail_before_any_launch(lib, kw, code):
+    assert call(lib, **kw) == code
+    assert lib.pa_last_error().decode() != ""
+
+
+def test_empty_batch_is_a_noop(lib):
+    assert call(lib, S=0, q=0, k=0, v=0, bt=0, sl=0, out=0) == 0

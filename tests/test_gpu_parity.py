@@ -1,0 +1,237 @@
+"""Parity of the HIP library with the fp64 oracle on MI355X (gfx950).
+
+Small cases are compared element by element in full; the full-size workloads
+(dense 1K/4K, the 256-sequence ragged mix over four head layouts and three
+seeds, the low-batch long-context grid, and 40/8 heads x 4096 tokens x 256
+sequences in the benchmark's launch configuration) are compared on sampled
+sequences.  Bound: max abs error <= 1e-2 and mean abs error <= 5e-4 against
+the fp64 oracle, for bf16 output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from parity import compare, log, run_gpu, run_oracle, sample_seqs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_attention_decode_03_amd as pa
+    pa.load_library()   # raises if the library is missing: no fallback
+
+
+# ---------------------------------------------------------------- small, full
+
+def test_tiny():
+    case = workloads.tiny(0)
+    log("tiny: 4 seqs ctx {1,17,33,64}, 8/2 heads, 32 blocks")
+    compare(run_gpu(case), run_oracle(case), "tiny")
+
+
+SMALL = [
+    (8, 2, [1, 15, 16, 17, 63, 64, 65, 200]),
+    (5, 1, [1, 2, 31, 32, 33, 500]),
+    (40, 8, [1, 100, 1000, 17]),
+    (32, 4, [64, 65, 129, 255, 256, 257]),
+    (16, 1, [1, 333, 48]),
+    (8, 8, [7, 90, 16]),
+    (16, 16, [40, 3]),
+    (2, 1, [1024, 5]),
+]
+
+
+@pytest.mark.parametrize("hq,hkv,lens", SMALL, ids=lambda x: str(x))
+def test_small_layouts(hq, hkv, lens):
+    case = workloads.make_case(hq, hkv, lens, seed=hq * 7 + hkv)
+    log(f"small {hq}/{hkv} lens={lens}")
+    compare(run_gpu(case), run_oracle(case), f"small {hq}/{hkv}")
+
+
+@pytest.mark.parametrize("ppp", [1, 2, 3, 5, 7, 64, 256])
+def test_forced_partition_sizes(ppp):
+    case = workloads.make_case(16, 2, [1, 15, 16, 17, 100, 1000, 0, 333, 4000], seed=3,
+                               max_blocks=250)
+    log(f"split ppp={ppp}")
+    compare(run_gpu(case, pages_per_partition=ppp), run_oracle(case), f"split ppp={ppp}")
+
+
+def test_empty_sequences_give_zero_rows():
+    case = workloads.make_case(8, 2, [0, 37, 0, 1], seed=5, max_blocks=4)
+    out = run_gpu(case)
+    assert torch.count_nonzero(out[0]) == 0 and torch.count_nonzero(out[2]) == 0
+    compare(out, run_oracle(case), "with empty sequences")
+    out_split = run_gpu(case, pages_per_partition=1)
+    assert torch.count_nonzero(out_split[0]) == 0
+    compare(out_split, run_oracle(case), "with empty sequences, split")
+
+
+def test_all_fp8_codes_through_v_are_exact():
+    """One-token contexts return V_0 * v_scale; with v_scale = 1 every finite
+    fp8 value is a bf16 value, so the output must equal it exactly (the sum
+    that forms the output starts from +0, so the code for -0 gives +0, as in
+    the oracle)."""
+    case = workloads.make_case(4, 1, [1, 1], seed=9, max_blocks=1, extra_blocks=2)
+    codes = np.arange(256, dtype=np.uint8)
+    codes[codes == 0x7F] = 0
+    codes[codes == 0xFF] = 0
+    v = case.v_cache.clone()
+    for s in range(2):
+        blk = int(case.block_tables[s, 0])
+        v[blk, 0, :, 0] = torch.from_numpy(codes[s * 128:(s + 1) * 128].copy())
+    case.v_cache = v
+    case.v_scale = 1.0
+    out = run_gpu(case).cpu()
+    expect = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).float().to(torch.bfloat16).view(2, 128)
+    for s in range(2):
+        for h in range(4):
+            assert torch.equal(out[s, h].float(), expect[s].float()), (s, h)
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_run_to_run_bitwise_determinism():
+    case = workloads.ragged(40, 8, seed=0, num_seqs=64, device="cuda")
+    a = run_gpu(case).clone()
+    b = run_gpu(case)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_block_placement_invariance_bitwise():
+    case = workloads.make_case(8, 2, [33, 90, 16, 1, 700], seed=31)
+    base = run_gpu(case).cpu()
+    NB = case.k_cache.shape[0]
+    perm = torch.randperm(NB, generator=torch.Generator().manual_seed(99))
+    k2 = torch.empty_like(case.k_cache)
+    v2 = torch.empty_like(case.v_cache)
+    k2[perm] = case.k_cache
+    v2[perm] = case.v_cache
+    moved = workloads.Case("moved", case.q, k2, v2, perm[case.block_tables.long()].to(torch.int32),
+                           case.seq_lens, case.scale, case.k_scale, case.v_scale)
+    assert torch.equal(run_gpu(moved).cpu().view(torch.int16), base.view(torch.int16))
+
+
+def test_sequence_order_permutes_outputs_bitwise():
+    case = workloads.make_case(8, 2, [33, 90, 16, 1, 0, 250], seed=32, max_blocks=16)
+    base = run_gpu(case).cpu()
+    order = torch.tensor([3, 0, 5, 4, 2, 1])
+    pc = workloads.Case("perm", case.q[order], case.k_cache, case.v_cache, case.block_tables[order],
+                        case.seq_lens[order], case.scale, case.k_scale, case.v_scale)
+    assert torch.equal(run_gpu(pc).cpu().view(torch.int16), base[order].view(torch.int16))
+
+
+def test_nan_poison_outside_context_is_never_read():
+    lens = [1, 17, 33, 64, 5, 250]
+    a = workloads.make_case(8, 2, lens, 33, max_blocks=20, poison=True)
+    b = workloads.make_case(8, 2, lens, 33, max_blocks=20, poison=False)
+    for ppp in (None, 1, 3):
+        oa, ob = run_gpu(a, ppp).cpu(), run_gpu(b, ppp).cpu()
+        assert torch.isfinite(oa.float()).all()
+        assert torch.equal(oa.view(torch.int16), ob.view(torch.int16))
+
+
+def test_split_and_unsplit_agree():
+    case = workloads.make_case(40, 8, [4096, 1, 2000, 3001], seed=12)
+    ref = run_oracle(case)
+    outs = {ppp: run_gpu(case, ppp).cpu() for ppp in (0, 1, 8, 64, 256)}
+    for ppp, o in outs.items():
+        compare(o, ref, f"ppp={ppp}")
+    d = (outs[1].float() - outs[256].float()).abs().max().item()
+    assert d <= 2e-2
+
+
+def test_non_default_stream():
+    case = workloads.make_case(8, 2, [300, 20], seed=13).to("cuda")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out = run_gpu(case, stream=s)
+    compare(out, run_oracle(case), "side stream")
+
+
+def test_graph_capture_replays_match_eager():
+    import paged_attention_decode_03_amd as pa
+    cases = [workloads.make_case(40, 8, [4096, 33], seed=14).to("cuda"),       # split path
+             workloads.make_case(8, 2, [1, 17, 200], seed=15).to("cuda")]
+    ks = [torch.tensor([c.k_scale], device="cuda") for c in cases]
+    vs = [torch.tensor([c.v_scale], device="cuda") for c in cases]
+    outs = [torch.empty_like(c.q) for c in cases]
+
+    def step():
+        for c, k, v, o in zip(cases, ks, vs, outs):
+            pa.paged_decode_attention(c.q, c.k_cache, c.v_cache, c.block_tables, c.seq_lens,
+                                      c.scale, k, v, out=o)
+
+    step()   # eager: also sizes the split-KV scratch before capture
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step()
+    torch.cuda.synchronize()
+    for r in range(4):
+        for o in outs:
+            o.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o.view(torch.int16), e.view(torch.int16)), f"replay {r}"
+        step()   # eager work between replays
+        torch.cuda.synchronize()
+    compare(outs[1], run_oracle(cases[1]), "graph replay")
+
+
+# ---------------------------------------------------------------- full sizes, sampled
+
+@pytest.mark.parametrize("hq,hkv,s,ctx", workloads.DENSE_1K + workloads.DENSE_4K,
+                         ids=lambda x: str(x))
+def test_dense_full_size(hq, hkv, s, ctx):
+    log(f"dense {hq}/{hkv} seqs={s} ctx={ctx}")
+    case = workloads.dense(hq, hkv, s, ctx, seed=0, device="cuda")
+    out = run_gpu(case)
+    seqs = sample_seqs(case, 6)
+    compare(out, run_oracle(case, seqs), f"dense {hq}/{hkv} s{s} ctx{ctx}", seqs)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("hq,hkv", workloads.RAGGED_LAYOUTS, ids=lambda x: str(x))
+def test_ragged_full_size(hq, hkv, seed):
+    log(f"ragged {hq}/{hkv} seed={seed}")
+    case = workloads.ragged(hq, hkv, seed=seed, device="cuda")
+    out = run_gpu(case)
+    seqs = sample_seqs(case, 16, seed)
+    compare(out, run_oracle(case, seqs), f"ragged {hq}/{hkv} seed {seed}", seqs)
+
+
+@pytest.mark.parametrize("hq,hkv,s,ctx", workloads.LOW_BATCH, ids=lambda x: str(x))
+def test_low_batch_long_context(hq, hkv, s, ctx):
+    log(f"low batch {hq}/{hkv} seqs={s} ctx={ctx}")
+    case = workloads.dense(hq, hkv, s, ctx, seed=s, device="cuda")
+    out = run_gpu(case)
+    seqs = [s - 1]
+    compare(out, run_oracle(case, seqs), f"low-batch s{s} ctx{ctx}", seqs)
+
+
+def test_target_40x8_ctx4096_256seqs():
+    """The benchmark's workload and launch configuration."""
+    hq, hkv, s, ctx = workloads.TARGET
+    case = workloads.dense(hq, hkv, s, ctx, seed=0, device="cuda")
+    out = run_gpu(case)
+    seqs = sample_seqs(case, 8)
+    compare(out, run_oracle(case, seqs), "target 40/8 ctx4096 s256", seqs)
+    again = run_gpu(case)
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16))
+
+
+def test_tp2_share_20x4_ctx4096_256seqs():
+    case = workloads.dense(20, 4, 256, 4096, seed=0, device="cuda")
+    out = run_gpu(case)
+    seqs = sample_seqs(case, 6)
+    compare(out, run_oracle(case, seqs), "20/4 ctx4096 s256", seqs)
