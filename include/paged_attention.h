@@ -67,7 +67,8 @@ typedef enum pa_status {
  *                       same bytes)
  *   block_tables  int32 [num_seqs][max_blocks_per_seq], dense; logical block j of
  *                       sequence s is physical block block_tables[s][j]; entries at
- *                       or past ceil(seq_lens[s] / 16) are never read
+ *                       or past ceil(seq_lens[s] / 16) may be read but are never
+ *                       used, so they may hold anything
  *   seq_lens      int32 [num_seqs], tokens cached per sequence (current one included)
  *   num_heads     query heads; a positive multiple of num_kv_heads, group <= 16
  *   head_size     must be 128;  block_size must be 16

@@ -33,8 +33,10 @@ int fail(int code, const char* fmt, ...) {
 }
 
 // Planner constants.
-constexpr int kWavesPerCU = 8;           // the decode kernel runs 2 waves per SIMD
-constexpr int kDefaultCUs = 256;         // MI355X
+constexpr int kWavesPerCU = 8;        // the decode kernel runs 2 waves per SIMD
+constexpr int kDefaultCUs = 256;      // MI355X
+constexpr int kMinPagesPerPart = 8;   // shorter partitions cost more in start-up and merge than they gain
+constexpr int kStagePages = 4;        // the decode kernel loads 4 blocks per pipeline stage
 
 struct Plan {
   int32_t num_parts;
@@ -44,8 +46,14 @@ struct Plan {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Shape-only plan.  Enough partitions that every wave slot of the device gets
-// a work item; none longer than pa::kMaxPagesPerPart blocks.
+// Shape-only plan (no device data: it must not depend on seq_lens).  One
+// partition per (sequence, kv head) when that already gives a quarter of the
+// device's wave slots (2 waves per CU) a work item: measured on MI355X, a wave
+// streaming one long partition sustains ~12 GB/s, so 512 of them already
+// saturate HBM, and every extra partition costs a start-up and a merge.
+// Otherwise split each sequence's blocks so that about that many items exist,
+// with partitions of at least kMinPagesPerPart blocks, whole pipeline stages,
+// and never more than pa::kMaxPagesPerPart blocks.
 int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t W, int32_t num_cus, int32_t ppp_req,
               Plan* plan) {
   if (S < 0 || Hq <= 0 || Hkv <= 0 || W < 0 || ppp_req < 0)
@@ -57,11 +65,15 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t W, int32_t num_cus, in
     ppp = ppp_req < Wc ? ppp_req : Wc;
   } else {
     const int64_t items = (int64_t)(S > 0 ? S : 1) * Hkv;
-    const int64_t slots = (int64_t)(num_cus > 0 ? num_cus : kDefaultCUs) * kWavesPerCU;
-    int64_t parts = ceil_div(slots, items);
-    if (parts < 1) parts = 1;
+    const int64_t target = (int64_t)(num_cus > 0 ? num_cus : kDefaultCUs) * kWavesPerCU / 4;
+    int64_t parts = ceil_div(target, items);
     if (parts > Wc) parts = Wc;
-    ppp = ceil_div(Wc, parts);
+    ppp = ceil_div(Wc, parts < 1 ? 1 : parts);
+    if (ppp < Wc) {
+      if (ppp < kMinPagesPerPart) ppp = kMinPagesPerPart;
+      ppp = ceil_div(ppp, kStagePages) * kStagePages;
+      if (ppp > Wc) ppp = Wc;
+    }
   }
   if (ppp > pa::kMaxPagesPerPart) ppp = pa::kMaxPagesPerPart;
   const int64_t parts = ceil_div(Wc, ppp);

@@ -43,7 +43,28 @@ typedef _Float16 f16x4 __attribute__((__vector_size__(4 * sizeof(_Float16))));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 
-constexpr int kPagesPerStage = 4;
+// Tuning (compile time): pages per pipeline stage, waves per SIMD the register
+// budget is sized for, and whether K/V loads are marked nontemporal (streamed
+// once, so they need not stay in the caches).
+#ifndef PA_PAGES_PER_STAGE
+#define PA_PAGES_PER_STAGE 4
+#endif
+#ifndef PA_WAVES_PER_EU
+#define PA_WAVES_PER_EU 2
+#endif
+#ifndef PA_NT_LOADS
+#define PA_NT_LOADS 1
+#endif
+constexpr int kPagesPerStage = PA_PAGES_PER_STAGE;
+
+template <typename T>
+__device__ __forceinline__ T stream_load(const T* ptr) {
+#if PA_NT_LOADS
+  return __builtin_nontemporal_load(ptr);
+#else
+  return *ptr;
+#endif
+}
 
 // Wave-uniform load through the scalar data cache (read-only data).
 template <typename T>
@@ -94,7 +115,7 @@ struct Stage {
 };
 
 template <int PPS>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pa_decode_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU))) void pa_decode_kernel(const DecodeParams p) {
   const int lane = threadIdx.x;
   const int col = lane & 15;  // MFMA column (query head in group); K load row (token)
   const int rq = lane >> 4;   // row quad: rows 4*rq .. 4*rq+3 of the 16x16 tiles
@@ -104,30 +125,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pa
   const int sk = item / p.num_parts;
   const int kvh = sk % p.num_kv_heads;
   const int s = sk / p.num_kv_heads;
-
-  const int L = clamp_len(scalar_load(p.seq_lens + s), p.max_blocks);
-  const int npages = (L + kBlockTokens - 1) / kBlockTokens;
   const int ppp = p.pages_per_part;
-  const int nused = (npages + ppp - 1) / ppp;  // partitions holding tokens
-  if (part > 0 && part >= nused) return;
-  const bool direct = nused <= 1;  // one partition: write the final output here
+  const int pbeg = part * ppp;  // < max_blocks: the planner never makes an empty partition range
 
   const int h = kvh * p.group + col;
   const bool hvalid = col < p.group;
   const size_t orow = ((size_t)s * p.num_heads + h) * kHeadDim;
 
-  if (L == 0) {  // empty context: an all-zero row
-    if (hvalid) {
+  // Start the three independent reads of the prologue together: this
+  // partition's slice of the block-table row (its length is not known yet, so
+  // entries past the context are read too and discarded below), the sequence
+  // length, and q.
+  const int32_t* bt = p.block_tables + (size_t)s * p.max_blocks;
+  const int span = min(ppp, p.max_blocks - pbeg);
+  int32_t idv[kMaxPagesPerPart / 64];
 #pragma unroll
-      for (int jd = 0; jd < 8; ++jd)
-        *(uint2*)(p.out + orow + jd * 16 + rq * 4) = make_uint2(0u, 0u);
-    }
-    return;
-  }
-
-  const int pbeg = part * ppp;
-  const int pend = min(pbeg + ppp, npages);
-  const int tend = min(L, pend * kBlockTokens);  // first token this item must not use
+  for (int k = 0; k < kMaxPagesPerPart / 64; ++k)
+    idv[k] = (k * 64 < span) ? bt[pbeg + min(k * 64 + lane, span - 1)] : 0;
 
   // B operand of QK^T: q^T, 8 dims per MFMA.  Element e of qop[h2][c] is dim
   // 16 * (4 * h2 + rq) + 8 * c + e, matching the K bytes this lane loads.
@@ -147,10 +161,27 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pa
         qop[h2][c] = bf16x8{};
   }
 
+  const int L = clamp_len(scalar_load(p.seq_lens + s), p.max_blocks);
+  const int npages = (L + kBlockTokens - 1) / kBlockTokens;
+  const int nused = (npages + ppp - 1) / ppp;  // partitions holding tokens
+  if (part > 0 && part >= nused) return;
+  const bool direct = nused <= 1;  // one partition: write the final output here
+
+  if (L == 0) {  // empty context: an all-zero row
+    if (hvalid) {
+#pragma unroll
+      for (int jd = 0; jd < 8; ++jd)
+        *(uint2*)(p.out + orow + jd * 16 + rq * 4) = make_uint2(0u, 0u);
+    }
+    return;
+  }
+
+  const int pend = min(pbeg + ppp, npages);
+  const int tend = min(L, pend * kBlockTokens);  // first token this item must not use
+
   // logits in log2 units: z * scale * k_scale * log2(e)
   const float c_log2 = p.scale_log2e * scalar_load(p.k_scale);
 
-  const int32_t* bt = p.block_tables + (size_t)s * p.max_blocks;
   const size_t page_stride = (size_t)p.num_kv_heads * kPageBytes;
   const uint8_t* kbase = p.k_cache + (size_t)kvh * kPageBytes + lane * 16;
   const uint8_t* vbase = p.v_cache + (size_t)kvh * kPageBytes + col * 16 + rq * 4;
@@ -162,20 +193,38 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pa
   float m_run = -INFINITY;
   const f16x4 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
 
-  // The partition's physical block ids, staged once in LDS.  Entries past the
-  // partition repeat its last id, so a stage never needs a bounds check: those
+  // The partition's physical block ids, staged in LDS.  Entries past the
+  // context repeat its last id, so a stage never needs a bounds check: those
   // pages are re-reads whose tokens the last stage masks.
   __shared__ __attribute__((aligned(16))) int32_t ids[kMaxPagesPerPart + PPS];
   const int npg = pend - pbeg;
   const int npg_pad = (npg + PPS - 1) / PPS * PPS;
-  for (int i = lane; i < npg_pad; i += 64) ids[i] = bt[pbeg + min(i, npg - 1)];
+  int32_t last_id;
+  {
+    const int k = (npg - 1) >> 6, l = (npg - 1) & 63;
+    last_id = __builtin_amdgcn_readlane(idv[0], l);
+#pragma unroll
+    for (int kk = 1; kk < kMaxPagesPerPart / 64; ++kk)
+      if (k == kk) last_id = __builtin_amdgcn_readlane(idv[kk], l);
+  }
+#pragma unroll
+  for (int k = 0; k < kMaxPagesPerPart / 64; ++k) {
+    const int i = k * 64 + lane;
+    if (k * 64 < npg_pad && i < npg_pad) ids[i] = (i < npg) ? idv[k] : last_id;
+  }
   __syncthreads();
 
   auto load = [&](Stage<PPS>& st, int j0) {
     int32_t pid[PPS];
-    if constexpr (PPS == 4) {
-      const int4 v = *(const int4*)(ids + (j0 - pbeg));
-      pid[0] = v.x; pid[1] = v.y; pid[2] = v.z; pid[3] = v.w;
+    if constexpr (PPS % 4 == 0) {
+#pragma unroll
+      for (int c = 0; c < PPS / 4; ++c) {
+        const int4 v = *(const int4*)(ids + (j0 - pbeg) + 4 * c);
+        pid[4 * c] = v.x;
+        pid[4 * c + 1] = v.y;
+        pid[4 * c + 2] = v.z;
+        pid[4 * c + 3] = v.w;
+      }
     } else {
 #pragma unroll
       for (int pp = 0; pp < PPS; ++pp) pid[pp] = ids[j0 - pbeg + pp];
@@ -184,11 +233,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pa
     for (int pp = 0; pp < PPS; ++pp) {
       const size_t off = (size_t)__builtin_amdgcn_readfirstlane(pid[pp]) * page_stride;
       const uint8_t* kp = kbase + off;
-      st.k[pp][0] = *(const u32x4*)(kp);
-      st.k[pp][1] = *(const u32x4*)(kp + 1024);
+      st.k[pp][0] = stream_load((const u32x4*)(kp));
+      st.k[pp][1] = stream_load((const u32x4*)(kp + 1024));
       const uint8_t* vp = vbase + off;
 #pragma unroll
-      for (int jd = 0; jd < 8; ++jd) st.v[pp][jd] = *(const uint32_t*)(vp + jd * 256);
+      for (int jd = 0; jd < 8; ++jd) st.v[pp][jd] = stream_load((const uint32_t*)(vp + jd * 256));
     }
     // keep the scheduler from hoisting compute above these loads
     __builtin_amdgcn_sched_barrier(0);
@@ -289,30 +338,76 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pa
 
 // Log-sum-exp merge of the partitions of one (sequence, query head):
 //   M = max_p m_p,  w_p = 2^(m_p - M),  out = v_scale * sum_p w_p a_p / sum_p w_p l_p.
-// Sequences whose context fits one partition were finished by the main kernel.
-__global__ __launch_bounds__(64) void pa_merge_kernel(const DecodeParams p) {
-  const int lane = threadIdx.x;
+// Sequences whose context fits one partition were finished by the decode kernel.
+// 256 threads: thread t owns dims 4*(t & 31) .. +3 of partitions p = t >> 5 (mod 8);
+// the eight partial sums are combined in LDS.
+constexpr int kMergeThreads = 256;
+
+__device__ __forceinline__ float wave_max(float x) {
+  x = max_over_rows(x);  // lanes l, l^16, l^32, l^48
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+__global__ __launch_bounds__(kMergeThreads) void pa_merge_kernel(const DecodeParams p) {
+  const int t = threadIdx.x;
   const int sh = blockIdx.x;
   const int s = sh / p.num_heads;
   const int L = clamp_len(scalar_load(p.seq_lens + s), p.max_blocks);
   const int npages = (L + kBlockTokens - 1) / kBlockTokens;
   const int nused = (npages + p.pages_per_part - 1) / p.pages_per_part;
-  if (nused <= 1) return;
+  if (nused <= 1) return;  // uniform over the block
 
-  const float* ml = p.part_ml + (size_t)sh * p.num_parts * 2;
-  float M = -INFINITY;
-  for (int i = 0; i < nused; ++i) M = fmaxf(M, scalar_load(ml + 2 * i));
-  float den = 0.f, n0 = 0.f, n1 = 0.f;
-  const float* a = p.part_acc + (size_t)sh * p.num_parts * kHeadDim + 2 * lane;
-  for (int i = 0; i < nused; ++i) {
-    const float w = __builtin_amdgcn_exp2f(scalar_load(ml + 2 * i) - M);
-    den += w * scalar_load(ml + 2 * i + 1);
-    const float2 v = *(const float2*)(a + (size_t)i * kHeadDim);
-    n0 += w * v.x;
-    n1 += w * v.y;
+  __shared__ float red_max[kMergeThreads / 64];
+  __shared__ float4 red_acc[8][32];
+  __shared__ float red_den[8];
+
+  const float2* ml = (const float2*)(p.part_ml + (size_t)sh * p.num_parts * 2);
+  float mx = -INFINITY;
+  for (int i = t; i < nused; i += kMergeThreads) mx = fmaxf(mx, ml[i].x);
+  mx = wave_max(mx);
+  if ((t & 63) == 0) red_max[t >> 6] = mx;
+  __syncthreads();
+  float M = red_max[0];
+#pragma unroll
+  for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, red_max[w]);
+
+  const int d4 = t & 31;
+  const int pl = t >> 5;
+  const float4* acc = (const float4*)(p.part_acc + (size_t)sh * p.num_parts * kHeadDim) + d4;
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+  float den = 0.f;
+#pragma unroll 4
+  for (int i = pl; i < nused; i += 8) {
+    const float2 m_l = ml[i];  // every partition in use holds >= 1 token: m is finite
+    const float w = __builtin_amdgcn_exp2f(m_l.x - M);
+    const float4 a = acc[(size_t)i * (kHeadDim / 4)];
+    den += w * m_l.y;
+    num.x += w * a.x;
+    num.y += w * a.y;
+    num.z += w * a.z;
+    num.w += w * a.w;
   }
-  const float inv = scalar_load(p.v_scale) / den;
-  *(uint32_t*)(p.out + (size_t)sh * kHeadDim + 2 * lane) = pack_bf16x2(n0 * inv, n1 * inv);
+  red_acc[pl][d4] = num;
+  if (d4 == 0) red_den[pl] = den;
+  __syncthreads();
+  if (t < 32) {
+    float4 n = red_acc[0][t];
+    float dsum = red_den[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) {
+      const float4 a = red_acc[k][t];
+      n.x += a.x;
+      n.y += a.y;
+      n.z += a.z;
+      n.w += a.w;
+      dsum += red_den[k];
+    }
+    const float inv = scalar_load(p.v_scale) / dsum;
+    *(uint2*)(p.out + (size_t)sh * kHeadDim + 4 * t) =
+        make_uint2(pack_bf16x2(n.x * inv, n.y * inv), pack_bf16x2(n.z * inv, n.w * inv));
+  }
 }
 
 }  // namespace
@@ -321,8 +416,8 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const size_t items = (size_t)p.num_seqs * p.num_kv_heads * p.num_parts;
   hipLaunchKernelGGL(pa_decode_kernel<kPagesPerStage>, dim3((unsigned)items), dim3(64), 0, stream, p);
   if (p.num_parts > 1)
-    hipLaunchKernelGGL(pa_merge_kernel, dim3((unsigned)((size_t)p.num_seqs * p.num_heads)), dim3(64), 0,
-                       stream, p);
+    hipLaunchKernelGGL(pa_merge_kernel, dim3((unsigned)((size_t)p.num_seqs * p.num_heads)),
+                       dim3(kMergeThreads), 0, stream, p);
   return hipGetLastError();
 }
 

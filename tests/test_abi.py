@@ -50,8 +50,17 @@ def test_plan_large_batch_is_unsplit(lib):
 
 def test_plan_small_batch_splits_long_context(lib):
     rc, P, n, ws = plan(lib, 1, 40, 8, 2048)        # one sequence of 32768 tokens
-    assert rc == 0 and P * n >= 2048 and P == 256 and n == 8
+    assert rc == 0 and P * n >= 2048 and (P, n) == (64, 32)
     assert ws == 1 * 40 * P * 130 * 4
+    rc, P, n, ws = plan(lib, 1, 40, 8, 256)         # one sequence of 4096 tokens
+    assert rc == 0 and (P, n) == (32, 8)            # never below 8 blocks per partition
+
+
+def test_plan_partitions_are_whole_stages(lib):
+    for S, W in [(3, 256), (24, 256), (5, 100), (2, 37)]:
+        rc, P, n, ws = plan(lib, S, 40, 8, W)
+        assert rc == 0 and P * n >= W
+        assert P == 1 or (n % 4 == 0 and n >= 8)
 
 
 def test_plan_caps_partition_length(lib):
