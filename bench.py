@@ -109,6 +109,43 @@ def time_calls(case, steps, warmup, rotate=1):
     return start.elapsed_time(end) * 1e3 / steps
 
 
+def time_graph(case, replays=50, calls_per_graph=10):
+    """Average µs per call when `calls_per_graph` calls are captured in one HIP
+    graph and the graph is replayed (the way the pages time impl.forward)."""
+    import torch
+    import paged_attention_decode_03_amd as pa
+    dev = case.q.device
+    ks = torch.tensor([case.k_scale], dtype=torch.float32, device=dev)
+    vs = torch.tensor([case.v_scale], dtype=torch.float32, device=dev)
+    out = torch.empty_like(case.q)
+
+    def call():
+        pa.paged_decode_attention(case.q, case.k_cache, case.v_cache, case.block_tables,
+                                  case.seq_lens, case.scale, ks, vs, out=out)
+
+    stream = torch.cuda.Stream(dev)
+    stream.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            call()          # sizes the split-KV scratch before capture
+    torch.cuda.synchronize(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(calls_per_graph):
+            call()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize(dev)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(replays):
+        g.replay()
+    end.record()
+    torch.cuda.synchronize(dev)
+    return start.elapsed_time(end) * 1e3 / (replays * calls_per_graph)
+
+
 def cpu_baseline(sample_seqs=16):
     """The fp64 oracle on a bounded sample of the same workload (host cores)."""
     import numpy as np
@@ -174,10 +211,12 @@ def main():
         for name in suite_names():
             case = make_workload(name, "cuda")
             us = time_calls(case, max(10, args.steps // 4), 5)
+            us_graph = time_graph(case)
             P, ppp, _ = pa.pa_decode_plan(case.num_seqs, case.num_heads, case.num_kv_heads,
                                           case.max_blocks, 256)
             b = case.algorithmic_bytes()
             print(json.dumps({"workload": name, "us_per_call": round(us, 2),
+                              "us_per_call_graph": round(us_graph, 2),
                               "GBps": round(b / us / 1e3, 1), "frac_of_peak": round(b / us / 1e3 / PEAK_GBS, 4),
                               "bytes": b, "partitions": P, "pages_per_partition": ppp}),
                   file=sys.stderr, flush=True)

@@ -43,28 +43,26 @@ typedef _Float16 f16x4 __attribute__((__vector_size__(4 * sizeof(_Float16))));
 typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
 typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 
-// Tuning (compile time): pages per pipeline stage, waves per SIMD the register
-// budget is sized for, and whether K/V loads are marked nontemporal (streamed
-// once, so they need not stay in the caches).
+// Tuning (compile time): pages per pipeline stage, depth of the register ring
+// of stages (depth - 1 stages are in flight while one is computed), waves per
+// SIMD the register budget is sized for, and the cache-policy bits of the K/V
+// loads (gfx950 buffer-load aux: 2 = nt, i.e. streamed once, not kept).
 #ifndef PA_PAGES_PER_STAGE
 #define PA_PAGES_PER_STAGE 4
+#endif
+#ifndef PA_RING_DEPTH
+#define PA_RING_DEPTH 2
 #endif
 #ifndef PA_WAVES_PER_EU
 #define PA_WAVES_PER_EU 2
 #endif
-#ifndef PA_NT_LOADS
-#define PA_NT_LOADS 1
+#ifndef PA_LOAD_AUX
+#define PA_LOAD_AUX 2
 #endif
 constexpr int kPagesPerStage = PA_PAGES_PER_STAGE;
-
-template <typename T>
-__device__ __forceinline__ T stream_load(const T* ptr) {
-#if PA_NT_LOADS
-  return __builtin_nontemporal_load(ptr);
-#else
-  return *ptr;
-#endif
-}
+constexpr int kRingDepth = PA_RING_DEPTH;
+// Word 3 of a raw buffer resource (no format conversion, no swizzle).
+constexpr int kRsrcWord3 = 0x00020000;
 
 // Wave-uniform load through the scalar data cache (read-only data).
 template <typename T>
@@ -114,7 +112,7 @@ struct Stage {
   uint32_t v[PPS][8];  // per page: 4 slots of one dim in each of the 8 16-dim blocks
 };
 
-template <int PPS>
+template <int PPS, int NB>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU))) void pa_decode_kernel(const DecodeParams p) {
   const int lane = threadIdx.x;
   const int col = lane & 15;  // MFMA column (query head in group); K load row (token)
@@ -183,8 +181,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
   const float c_log2 = p.scale_log2e * scalar_load(p.k_scale);
 
   const size_t page_stride = (size_t)p.num_kv_heads * kPageBytes;
-  const uint8_t* kbase = p.k_cache + (size_t)kvh * kPageBytes + lane * 16;
-  const uint8_t* vbase = p.v_cache + (size_t)kvh * kPageBytes + col * 16 + rq * 4;
+  const uint8_t* kpage0 = p.k_cache + (size_t)kvh * kPageBytes;
+  const uint8_t* vpage0 = p.v_cache + (size_t)kvh * kPageBytes;
+  const int koff = lane * 16;            // K: token lane & 15, chunks lane >> 4 and 4 + (lane >> 4)
+  const int voff = col * 16 + rq * 4;    // V: dim col (+16 jd), slots 4 rq .. 4 rq + 3
 
   f32x4 acc[8];  // O^T tiles: dims 16*jd + 4*rq + i for head `col`
 #pragma unroll
@@ -193,57 +193,66 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
   float m_run = -INFINITY;
   const f16x4 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
 
-  // The partition's physical block ids, staged in LDS.  Entries past the
-  // context repeat its last id, so a stage never needs a bounds check: those
-  // pages are re-reads whose tokens the last stage masks.
-  __shared__ __attribute__((aligned(16))) int32_t ids[kMaxPagesPerPart + PPS];
+  // The partition's physical block ids, staged in LDS.  A load of a page past
+  // the partition gets a buffer descriptor of zero bytes: it is still issued
+  // (so the pipeline's wait counts do not depend on the data) but it returns
+  // zeros without touching memory.  Those ids are therefore never used.
   const int npg = pend - pbeg;
-  const int npg_pad = (npg + PPS - 1) / PPS * PPS;
-  int32_t last_id;
-  {
-    const int k = (npg - 1) >> 6, l = (npg - 1) & 63;
-    last_id = __builtin_amdgcn_readlane(idv[0], l);
+  const int nsteps = (npg + PPS - 1) / PPS;
+  constexpr int kIdsCap = kMaxPagesPerPart + NB * PPS;
+  __shared__ __attribute__((aligned(16))) int32_t ids[kIdsCap];
+  const int ids_fill = (nsteps + NB - 1) * PPS;  // every index a load can reach
 #pragma unroll
-    for (int kk = 1; kk < kMaxPagesPerPart / 64; ++kk)
-      if (k == kk) last_id = __builtin_amdgcn_readlane(idv[kk], l);
-  }
-#pragma unroll
-  for (int k = 0; k < kMaxPagesPerPart / 64; ++k) {
+  for (int k = 0; k < (kIdsCap + 63) / 64; ++k) {
     const int i = k * 64 + lane;
-    if (k * 64 < npg_pad && i < npg_pad) ids[i] = (i < npg) ? idv[k] : last_id;
+    const int32_t v = (k < kMaxPagesPerPart / 64) ? idv[k < kMaxPagesPerPart / 64 ? k : 0] : 0;
+    if (k * 64 < ids_fill && i < ids_fill) ids[i] = (i < npg) ? v : 0;
   }
   __syncthreads();
 
-  auto load = [&](Stage<PPS>& st, int j0) {
+  auto load = [&](Stage<PPS>& st, int stage) {
+    const int i0 = stage * PPS;
     int32_t pid[PPS];
     if constexpr (PPS % 4 == 0) {
 #pragma unroll
       for (int c = 0; c < PPS / 4; ++c) {
-        const int4 v = *(const int4*)(ids + (j0 - pbeg) + 4 * c);
+        const int4 v = *(const int4*)(ids + i0 + 4 * c);
         pid[4 * c] = v.x;
         pid[4 * c + 1] = v.y;
         pid[4 * c + 2] = v.z;
         pid[4 * c + 3] = v.w;
       }
+    } else if constexpr (PPS % 2 == 0) {
+#pragma unroll
+      for (int c = 0; c < PPS / 2; ++c) {
+        const int2 v = *(const int2*)(ids + i0 + 2 * c);
+        pid[2 * c] = v.x;
+        pid[2 * c + 1] = v.y;
+      }
     } else {
 #pragma unroll
-      for (int pp = 0; pp < PPS; ++pp) pid[pp] = ids[j0 - pbeg + pp];
+      for (int pp = 0; pp < PPS; ++pp) pid[pp] = ids[i0 + pp];
     }
 #pragma unroll
     for (int pp = 0; pp < PPS; ++pp) {
+      const int bytes = (i0 + pp < npg) ? kPageBytes : 0;
       const size_t off = (size_t)__builtin_amdgcn_readfirstlane(pid[pp]) * page_stride;
-      const uint8_t* kp = kbase + off;
-      st.k[pp][0] = stream_load((const u32x4*)(kp));
-      st.k[pp][1] = stream_load((const u32x4*)(kp + 1024));
-      const uint8_t* vp = vbase + off;
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(kpage0 + off), (short)0, bytes, kRsrcWord3);
+      const __amdgpu_buffer_rsrc_t rv =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(vpage0 + off), (short)0, bytes, kRsrcWord3);
+      st.k[pp][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, 0, PA_LOAD_AUX));
+      st.k[pp][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 1024, 0, PA_LOAD_AUX));
 #pragma unroll
-      for (int jd = 0; jd < 8; ++jd) st.v[pp][jd] = stream_load((const uint32_t*)(vp + jd * 256));
+      for (int jd = 0; jd < 8; ++jd)
+        st.v[pp][jd] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff + jd * 256, 0, PA_LOAD_AUX);
     }
     // keep the scheduler from hoisting compute above these loads
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  auto compute = [&](const Stage<PPS>& st, int j0, bool last) {
+  auto compute = [&](const Stage<PPS>& st, int stage, bool last) {
+    const int j0 = pbeg + stage * PPS;
     f32x4 z[PPS];
 #pragma unroll
     for (int pp = 0; pp < PPS; ++pp) {
@@ -299,22 +308,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
     }
   };
 
-  const int nsteps = npg_pad / PPS;
-  Stage<PPS> sa, sb;
-  load(sa, pbeg);
-  int st = 0;
-  for (; st + 2 < nsteps; st += 2) {
-    load(sb, pbeg + (st + 1) * PPS);
-    compute(sa, pbeg + st * PPS, false);
-    load(sa, pbeg + (st + 2) * PPS);
-    compute(sb, pbeg + (st + 1) * PPS, false);
-  }
-  if (st + 1 < nsteps) {
-    load(sb, pbeg + (st + 1) * PPS);
-    compute(sa, pbeg + st * PPS, false);
-    compute(sb, pbeg + (st + 1) * PPS, true);
-  } else {
-    compute(sa, pbeg + st * PPS, true);
+  // Register ring of NB stages: NB - 1 stages are in flight while one is
+  // computed.  Loads past the last stage are empty (see above).
+  Stage<PPS> ring[NB];
+#pragma unroll
+  for (int k = 0; k < NB - 1; ++k) load(ring[k], k);
+  for (int st = 0; st < nsteps; st += NB) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      if (st + k >= nsteps) break;
+      load(ring[(k + NB - 1) % NB], st + k + NB - 1);
+      compute(ring[k], st + k, st + k == nsteps - 1);
+    }
   }
 
   if (!hvalid) return;
@@ -414,7 +419,7 @@ __global__ __launch_bounds__(kMergeThreads) void pa_merge_kernel(const DecodePar
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const size_t items = (size_t)p.num_seqs * p.num_kv_heads * p.num_parts;
-  hipLaunchKernelGGL(pa_decode_kernel<kPagesPerStage>, dim3((unsigned)items), dim3(64), 0, stream, p);
+  hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth>), dim3((unsigned)items), dim3(64), 0, stream, p);
   if (p.num_parts > 1)
     hipLaunchKernelGGL(pa_merge_kernel, dim3((unsigned)((size_t)p.num_seqs * p.num_heads)),
                        dim3(kMergeThreads), 0, stream, p);
