@@ -56,6 +56,11 @@ def _load():
     lib.pa_oracle_decode_partitioned.argtypes = [P, P, P, P, P, i32, i32, i32, i32,
                                                  f32, f32, f32, i32, P]
     lib.pa_oracle_decode_partitioned.restype = i32
+    lib.pa_oracle_fp8_e4m3fn_encode.argtypes = [ctypes.c_float]
+    lib.pa_oracle_fp8_e4m3fn_encode.restype = ctypes.c_uint8
+    lib.pa_oracle_cache_write.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, P, P, P, i32, i32,
+                                          ctypes.c_int64, f32, f32]
+    lib.pa_oracle_cache_write.restype = i32
     _lib = lib
     return lib
 
@@ -151,3 +156,40 @@ def decode_partitioned(q_bits, k_cache, v_cache, block_tables, seq_lens, scale,
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (code {rc})")
     return out
+
+
+def fp8_encode(values) -> np.ndarray:
+    """fp8 e4m3fn codes (uint8) of float32 values: nearest-even, saturating at 448."""
+    lib = _load()
+    flat = np.ascontiguousarray(values, dtype=np.float32).ravel()
+    out = np.fromiter((lib.pa_oracle_fp8_e4m3fn_encode(float(v)) for v in flat),
+                      dtype=np.uint8, count=flat.size)
+    return out.reshape(np.shape(values))
+
+
+def cache_write(key_bits, value_bits, k_cache, v_cache, slot_mapping, k_scale, v_scale):
+    """Quantise and scatter new tokens into (copies of) the caches.
+
+    key_bits / value_bits: uint16 bf16 patterns [T, Hkv, 128] (any token stride);
+    k_cache uint8 [NB, Hkv, 8, 16, 16]; v_cache uint8 [NB, Hkv, 128, 16];
+    slot_mapping int64 [T] (negative: skip).  Returns the new (k_cache, v_cache).
+    """
+    key_bits = np.asarray(key_bits, dtype=np.uint16)
+    value_bits = np.asarray(value_bits, dtype=np.uint16)
+    T, Hkv, D = key_bits.shape
+    if D != 128 or value_bits.shape != key_bits.shape:
+        raise ValueError("key/value must be [T, Hkv, 128]")
+    kb = np.ascontiguousarray(key_bits)
+    vb = np.ascontiguousarray(value_bits)
+    kc = np.array(k_cache, dtype=np.uint8, copy=True, order="C")
+    vc = np.array(v_cache, dtype=np.uint8, copy=True, order="C")
+    sm = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    NB = kc.shape[0]
+    if kc.shape[1] != Hkv or vc.size != kc.size:
+        raise ValueError("cache shapes disagree with key/value")
+    rc = _load().pa_oracle_cache_write(kb.ctypes.data, vb.ctypes.data, Hkv * 128, Hkv * 128,
+                                       kc.ctypes.data, vc.ctypes.data, sm.ctypes.data, T, Hkv, NB,
+                                       float(k_scale), float(v_scale))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return kc, vc

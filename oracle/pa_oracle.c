@@ -41,6 +41,17 @@
  * The split-KV variant (pa_oracle_decode_partitioned) evaluates the same
  * quantity as a log-sum-exp merge of per-partition partial results; it exists
  * to pin that merge formula against the unsplit definition.
+ *
+ * Cache write (pa_oracle_cache_write): the step that fills the cache the
+ * decode reads (API page, do_kv_cache_update: new tokens' key and value, the
+ * two caches, slot_mapping and the per-tensor k/v scales go to the cache
+ * writer; pull request #3, Details > Layout, for the page layout).  For every
+ * token t with slot_mapping[t] >= 0, block = slot / 16, slot in block = slot % 16:
+ *   k_cache[block][kvh][d / 16][slot % 16][d % 16] = fp8(key[t][kvh][d] / k_scale)
+ *   v_cache[block][kvh][d][slot % 16]             = fp8(value[t][kvh][d] / v_scale)
+ * Readings: the division is done in fp32 (the precision the kernel decides the
+ * code in), fp8() rounds to nearest even and saturates to +-448 (infinities
+ * too), NaN stays NaN with its sign, and a negative slot means "not cached".
  */
 #include <math.h>
 #include <stdint.h>
@@ -62,6 +73,30 @@ double pa_oracle_fp8_e4m3fn(uint8_t b) {
   else
     mag = ldexp(1.0 + (double)m / 8.0, e - 7);
   return sign ? -mag : mag;
+}
+
+/* fp8 e4m3fn code of an fp32 value: nearest, ties to even; magnitudes above
+ * 448 (including infinity) saturate to 448; NaN gives S.1111.111. */
+uint8_t pa_oracle_fp8_e4m3fn_encode(float y) {
+  const uint8_t sign = signbit(y) ? 0x80u : 0u;
+  if (isnan(y)) return sign | 0x7Fu;
+  const double a = fabs((double)y);
+  if (a > 448.0) return sign | 0x7Eu;
+  if (a < ldexp(1.0, -6)) {
+    /* subnormal range: multiples of 2^-9; q = 8 is the smallest normal, code 0x08 */
+    const double q = nearbyint(ldexp(a, 9));
+    return sign | (uint8_t)q;
+  }
+  int e;
+  (void)frexp(a, &e);
+  e -= 1;                                   /* a = 1.f * 2^e, -6 <= e <= 8 */
+  double m = nearbyint((ldexp(a, -e) - 1.0) * 8.0);
+  if (m == 8.0) {
+    m = 0.0;
+    e += 1;
+  }
+  if (e + 7 > 15 || (e + 7 == 15 && m == 7.0)) return sign | 0x7Eu;
+  return sign | (uint8_t)(((e + 7) << 3) | (int)m);
 }
 
 /* Value of one bfloat16 (upper half of an IEEE binary32). */
@@ -233,6 +268,36 @@ int pa_oracle_decode_partitioned(const uint16_t* q_bits, const uint8_t* k_cache,
       free(m);
       free(l);
       free(a);
+    }
+  }
+  return 0;
+}
+
+/*
+ * key, value: bf16 bit patterns, token t / kv head k / dim d at
+ * [t * key_stride + k * 128 + d] (value_stride likewise).  Returns 0, or -3 if a
+ * slot points past the caches (nothing is written for that call then).
+ */
+int pa_oracle_cache_write(const uint16_t* key, const uint16_t* value, int64_t key_stride,
+                          int64_t value_stride, uint8_t* k_cache, uint8_t* v_cache,
+                          const int64_t* slot_mapping, int T, int Hkv, int64_t num_blocks,
+                          float k_scale, float v_scale) {
+  for (int t = 0; t < T; ++t)
+    if (slot_mapping[t] >= num_blocks * PA_BLOCK) return -3;
+  for (int t = 0; t < T; ++t) {
+    const int64_t slot = slot_mapping[t];
+    if (slot < 0) continue;
+    const int64_t block = slot / PA_BLOCK;
+    const int j = (int)(slot % PA_BLOCK);
+    for (int k = 0; k < Hkv; ++k) {
+      uint8_t* kpage = k_cache + (block * Hkv + k) * (int64_t)(PA_HEAD_DIM * PA_BLOCK);
+      uint8_t* vpage = v_cache + (block * Hkv + k) * (int64_t)(PA_HEAD_DIM * PA_BLOCK);
+      for (int d = 0; d < PA_HEAD_DIM; ++d) {
+        const float xk = (float)pa_oracle_bf16(key[t * key_stride + k * PA_HEAD_DIM + d]);
+        const float xv = (float)pa_oracle_bf16(value[t * value_stride + k * PA_HEAD_DIM + d]);
+        kpage[(d / 16) * (PA_BLOCK * 16) + j * 16 + (d % 16)] = pa_oracle_fp8_e4m3fn_encode(xk / k_scale);
+        vpage[d * PA_BLOCK + j] = pa_oracle_fp8_e4m3fn_encode(xv / v_scale);
+      }
     }
   }
   return 0;
