@@ -16,6 +16,8 @@ current kernel source), and the fp64 CPU oracle timed on a bounded sample.
 
 Other modes:
     --workload all          also print one line per workload of the suite to stderr
+                            (decode workloads, and the fp8 cache write for a decode step
+                            and for a prefill-sized batch)
     --copy-calibration      time a plain 1 GiB device copy (for scaling PMC counters)
 """
 from __future__ import annotations
@@ -146,6 +148,55 @@ def time_graph(case, replays=50, calls_per_graph=10):
     return start.elapsed_time(end) * 1e3 / (replays * calls_per_graph)
 
 
+def cache_write_case(num_tokens, num_kv_heads=8, seed=0, prefill=True):
+    """New keys/values (bf16 N(0,1), per-tensor scale amax/448) for `num_tokens`
+    tokens.  prefill: sequences of 2048 new tokens, each filling its own shuffled
+    blocks in order; otherwise one token per sequence at a random slot (a decode
+    step).  The cache has 25% spare blocks."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    nb = (num_tokens + 15) // 16 * 5 // 4 + 1
+    key = torch.randn(num_tokens, num_kv_heads, 128, generator=g, device="cuda").to(torch.bfloat16)
+    value = torch.randn(num_tokens, num_kv_heads, 128, generator=g, device="cuda").to(torch.bfloat16)
+    if prefill:
+        blocks = torch.randperm(nb, generator=g, device="cuda")[:(num_tokens + 15) // 16]
+        t = torch.arange(num_tokens, device="cuda")
+        slots = blocks[t // 16] * 16 + t % 16
+    else:
+        slots = torch.randperm(nb * 16, generator=g, device="cuda")[:num_tokens]
+    slots = slots.to(torch.int64)
+    k_cache = torch.zeros(nb, num_kv_heads, 8, 16, 16, dtype=torch.uint8, device="cuda")
+    v_cache = torch.zeros(nb, num_kv_heads, 128, 16, dtype=torch.uint8, device="cuda")
+    ks = (key.float().abs().max() / 448).reshape(1)
+    vs = (value.float().abs().max() / 448).reshape(1)
+    return key, value, k_cache, v_cache, slots, ks, vs
+
+
+def cache_write_bytes(num_tokens, num_kv_heads=8):
+    """Algorithmic bytes of one cache write: bf16 key and value in, fp8 key and
+    value out, the int64 slots and the two scales."""
+    return num_tokens * num_kv_heads * 128 * (2 + 2 + 1 + 1) + 8 * num_tokens + 8
+
+
+def time_cache_write(num_tokens, steps, warmup, num_kv_heads=8, prefill=True):
+    import torch
+    import paged_attention_decode_03_amd as pa
+    key, value, kc, vc, slots, ks, vs = cache_write_case(num_tokens, num_kv_heads, prefill=prefill)
+    stream = torch.cuda.Stream()
+    for _ in range(warmup):
+        pa.paged_kv_cache_write(key, value, kc, vc, slots, ks, vs, stream=stream)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        pa.paged_kv_cache_write(key, value, kc, vc, slots, ks, vs, stream=stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) * 1e3 / steps
+
+
 def cpu_baseline(sample_seqs=16):
     """The fp64 oracle on a bounded sample of the same workload (host cores)."""
     import numpy as np
@@ -222,6 +273,14 @@ def main():
                   file=sys.stderr, flush=True)
             del case
             torch.cuda.empty_cache()
+        for name, T, pre in (("cache_write_decode_256x8", 256, False),
+                             ("cache_write_prefill_32768x8", 32768, True)):
+            us = time_cache_write(T, max(10, args.steps // 4), 5, prefill=pre)
+            b = cache_write_bytes(T)
+            print(json.dumps({"workload": name, "us_per_call": round(us, 2),
+                              "GBps": round(b / us / 1e3, 1),
+                              "frac_of_peak": round(b / us / 1e3 / PEAK_GBS, 4), "bytes": b}),
+                  file=sys.stderr, flush=True)
         args.workload = "target"
 
     case = make_workload(args.workload, "cuda")

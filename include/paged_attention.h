@@ -128,6 +128,38 @@ int pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
  */
 int pa_decode_reserve_workspace(size_t bytes);
 
+/*
+ * Fill the paged fp8 cache with new tokens (the cache update that precedes the
+ * decode: API page vllm.v1.attention.backends.rocm_aiter_unified_attn,
+ * do_kv_cache_update, which hands key, value, both caches, slot_mapping and the
+ * per-tensor k/v scales to the cache writer; page layout as in the vLLM pull
+ * request lishuoshuo-amd/vllm #3, Details > Layout).  For every token t with
+ * slot = slot_mapping[t] >= 0, block = slot / 16, s = slot % 16, kv head k, dim d:
+ *   k_cache[block][k][d/16][s][d%16] = fp8(key[t][k][d]   / k_scale)
+ *   v_cache[block][k][d][s]          = fp8(value[t][k][d] / v_scale)
+ * with the division in fp32 and fp8() = OCP e4m3fn, round to nearest even,
+ * saturating to +-448 (infinities too); NaN stays NaN with its sign.
+ *
+ *   key, value        bf16, token t / kv head k / dim d at [t * stride + k * 128 + d];
+ *                     4-byte aligned
+ *   key_token_stride, value_token_stride
+ *                     elements between consecutive tokens (even, >= num_kv_heads * 128:
+ *                     key and value may be slices of a fused projection output)
+ *   k_cache, v_cache  as for paged_decode_attention; only the addressed slots change
+ *   slot_mapping      int64 [num_tokens]; negative = token not cached; a slot at or past
+ *                     num_blocks * 16 cannot be reported without a device read and is
+ *                     skipped
+ *   num_tokens        0 is a no-op
+ *   k_scale, v_scale  fp32 [1], device
+ * Two tokens with the same slot race (one of them wins).  Asynchronous like
+ * paged_decode_attention; errors as there.
+ */
+int paged_kv_cache_write(const void* key, const void* value, int64_t key_token_stride,
+                         int64_t value_token_stride, void* k_cache, void* v_cache,
+                         const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                         int32_t head_size, int32_t block_size, int64_t num_blocks,
+                         const float* k_scale, const float* v_scale, void* stream);
+
 /* Message of the last failing call on this thread ("" if none). */
 const char* pa_last_error(void);
 

@@ -26,7 +26,8 @@ import torch
 
 __all__ = [
     "paged_decode_attention", "paged_decode_attention_split", "pa_decode_plan",
-    "pa_decode_reserve_workspace", "pa_last_error", "PagedAttentionError", "library_path",
+    "pa_decode_reserve_workspace", "paged_kv_cache_write", "pa_last_error",
+    "PagedAttentionError", "library_path",
     "load_library",
 ]
 
@@ -68,6 +69,9 @@ def load_library():
     lib.pa_decode_plan.restype = ctypes.c_int
     lib.pa_decode_reserve_workspace.argtypes = [ctypes.c_size_t]
     lib.pa_decode_reserve_workspace.restype = ctypes.c_int
+    lib.paged_kv_cache_write.argtypes = [vp, vp, i64, i64, vp, vp, vp, i32, i32, i32, i32, i64,
+                                         vp, vp, vp]
+    lib.paged_kv_cache_write.restype = ctypes.c_int
     lib.pa_last_error.argtypes = []
     lib.pa_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -186,3 +190,42 @@ def pa_decode_reserve_workspace(nbytes: int, device=None):
     lib = load_library()
     with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
         _check(lib.pa_decode_reserve_workspace(int(nbytes)))
+
+
+def paged_kv_cache_write(key, value, k_cache, v_cache, slot_mapping, k_scale, v_scale,
+                         stream=None):
+    """Quantise new tokens' keys/values to fp8 and scatter them into the caches.
+
+    key, value: bfloat16 [num_tokens, num_kv_heads, 128] with dense rows (any
+    token stride); k_cache / v_cache as for paged_decode_attention (modified in
+    place); slot_mapping: int64 [num_tokens] (negative = not cached).
+    """
+    lib = load_library()
+    for name, t in (("key", key), ("value", value)):
+        if t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+            raise TypeError(f"{name} must be bfloat16 [num_tokens, num_kv_heads, head_size] "
+                            "with dense rows")
+    if key.shape != value.shape:
+        raise ValueError("key and value shapes differ")
+    T, Hkv, D = key.shape
+    dev = key.device
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn) or t.device != dev or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous uint8 / float8_e4m3fn tensor on {dev}")
+    if k_cache.dim() != 5 or k_cache.shape[1] != Hkv:
+        raise ValueError("k_cache must be [num_blocks, num_kv_heads, head_size/16, 16, 16]")
+    if v_cache.numel() != k_cache.numel():
+        raise ValueError("v_cache must hold as many bytes as k_cache")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,) or slot_mapping.device != dev \
+            or not slot_mapping.is_contiguous():
+        raise TypeError("slot_mapping must be a contiguous int64 [num_tokens] tensor on the key device")
+    ks = _scale_tensor(k_scale, dev)
+    vs = _scale_tensor(v_scale, dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(dev):
+        _check(lib.paged_kv_cache_write(
+            _ptr(key), _ptr(value), key.stride(0) if T else Hkv * D, value.stride(0) if T else Hkv * D,
+            _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), T, Hkv, D, k_cache.shape[3],
+            k_cache.shape[0], _ptr(ks), _ptr(vs), handle))

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpagedattn.so")
-SOURCES = ["pa_decode_kernels.hip", "pa_api.hip"]
+SOURCES = ["pa_decode_kernels.hip", "pa_cache_write.hip", "pa_api.hip"]
 ARCH = "gfx950"
 
 

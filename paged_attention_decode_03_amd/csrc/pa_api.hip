@@ -18,6 +18,7 @@
 #include <vector>
 
 #include "paged_attention.h"
+#include "pa_cache_write.h"
 #include "pa_decode_kernels.h"
 
 namespace {
@@ -269,6 +270,64 @@ int pa_decode_reserve_workspace(size_t bytes) {
   if (hipGetDevice(&dev) != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice failed");
   void* p = nullptr;
   return ensure_workspace(dev, bytes, nullptr, false, &p);
+}
+
+int paged_kv_cache_write(const void* key, const void* value, int64_t key_token_stride,
+                         int64_t value_token_stride, void* k_cache, void* v_cache,
+                         const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                         int32_t head_size, int32_t block_size, int64_t num_blocks,
+                         const float* k_scale, const float* v_scale, void* stream) {
+  g_last_error[0] = '\0';
+  if (head_size != pa::kHeadDim)
+    return fail(PA_ERR_UNSUPPORTED, "head_size %d unsupported (only %d)", head_size, pa::kHeadDim);
+  if (block_size != pa::kBlockTokens)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %d unsupported (only %d)", block_size,
+                pa::kBlockTokens);
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0)
+    return fail(PA_ERR_SHAPE, "negative or zero size: num_tokens=%d num_kv_heads=%d num_blocks=%lld",
+                num_tokens, num_kv_heads, (long long)num_blocks);
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping || !k_scale || !v_scale)
+    return fail(PA_ERR_NULL, "a required pointer is NULL");
+  const int64_t row = (int64_t)num_kv_heads * pa::kHeadDim;
+  if (key_token_stride < row || value_token_stride < row || (key_token_stride & 1) ||
+      (value_token_stride & 1))
+    return fail(PA_ERR_SHAPE,
+                "token strides (%lld, %lld) must be even and at least num_kv_heads * 128 = %lld",
+                (long long)key_token_stride, (long long)value_token_stride, (long long)row);
+  if (num_blocks == 0) return fail(PA_ERR_SHAPE, "num_blocks must be positive");
+  if (((uintptr_t)key & 3) || ((uintptr_t)value & 3) || ((uintptr_t)k_cache & 1) ||
+      ((uintptr_t)slot_mapping & 7))
+    return fail(PA_ERR_SHAPE, "misaligned pointer (key, value: 4 B; k_cache: 2 B; slot_mapping: 8 B)");
+  const size_t cache_bytes = (size_t)num_blocks * num_kv_heads * pa::kPageBytes;
+  const size_t key_bytes = ((size_t)(num_tokens - 1) * key_token_stride + row) * 2;
+  const size_t value_bytes = ((size_t)(num_tokens - 1) * value_token_stride + row) * 2;
+  if (overlaps(k_cache, cache_bytes, v_cache, cache_bytes))
+    return fail(PA_ERR_ALIAS, "k_cache and v_cache overlap");
+  for (const void* c : {(const void*)k_cache, (const void*)v_cache})
+    if (overlaps(c, cache_bytes, key, key_bytes) || overlaps(c, cache_bytes, value, value_bytes) ||
+        overlaps(c, cache_bytes, slot_mapping, (size_t)num_tokens * 8) ||
+        overlaps(c, cache_bytes, k_scale, 4) || overlaps(c, cache_bytes, v_scale, 4))
+      return fail(PA_ERR_ALIAS, "a cache overlaps an input");
+
+  pa::CacheWriteParams p;
+  p.key = (const uint16_t*)key;
+  p.value = (const uint16_t*)value;
+  p.key_stride = key_token_stride;
+  p.value_stride = value_token_stride;
+  p.k_cache = (uint8_t*)k_cache;
+  p.v_cache = (uint8_t*)v_cache;
+  p.slot_mapping = slot_mapping;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.num_tokens = num_tokens;
+  p.num_kv_heads = num_kv_heads;
+  p.num_blocks = num_blocks;
+  p.vec16 = !((uintptr_t)key & 15) && !((uintptr_t)value & 15) && !(key_token_stride & 7) &&
+            !(value_token_stride & 7) && !((uintptr_t)k_cache & 15) && !((uintptr_t)v_cache & 15);
+  const hipError_t err = pa::launch_cache_write(p, (hipStream_t)stream);
+  if (err != hipSuccess) return fail(PA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+  return PA_OK;
 }
 
 const char* pa_last_error(void) { return g_last_error; }

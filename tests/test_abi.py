@@ -28,7 +28,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("paged_decode_attention", "paged_decode_attention_split", "pa_decode_plan",
-              "pa_decode_reserve_workspace", "pa_last_error"):
+              "pa_decode_reserve_workspace", "paged_kv_cache_write", "pa_last_error"):
         assert n in names
 
 
@@ -104,3 +104,25 @@ def test_invalid_arguments_fail_before_any_launch(lib, kw, code):
 
 def test_empty_batch_is_a_noop(lib):
     assert call(lib, S=0, q=0, k=0, v=0, bt=0, sl=0, out=0) == 0
+
+
+def cw(lib, T=4, Hkv=2, D=128, bs=16, NB=8, ks_=256, vs_=256, key=FAKE, value=FAKE * 2,
+       kc=FAKE * 16, vc=FAKE * 32, sm=FAKE * 48, ksc=FAKE * 50, vsc=FAKE * 51):
+    vp = ctypes.c_void_p
+    return lib.paged_kv_cache_write(vp(key), vp(value), ks_, vs_, vp(kc), vp(vc), vp(sm), T, Hkv, D,
+                                    bs, NB, vp(ksc), vp(vsc), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=64), -3), (dict(bs=8), -3), (dict(T=-1), -2), (dict(Hkv=0), -2), (dict(NB=0), -2),
+    (dict(ks_=200), -2), (dict(vs_=257), -2), (dict(key=0), -1), (dict(sm=0), -1),
+    (dict(vsc=0), -1), (dict(vc=FAKE * 16 + 2048), -4), (dict(kc=FAKE * 2), -4),
+    (dict(key=FAKE + 2), -2), (dict(sm=FAKE * 48 + 4), -2),
+])
+def test_cache_write_rejects_bad_arguments(lib, kw, code):
+    assert cw(lib, **kw) == code
+    assert lib.pa_last_error().decode() != ""
+
+
+def test_cache_write_empty_is_a_noop(lib):
+    assert cw(lib, T=0, key=0, value=0, kc=0, vc=0, sm=0) == 0
