@@ -56,6 +56,8 @@ def _load():
     lib.pa_oracle_decode_partitioned.argtypes = [P, P, P, P, P, i32, i32, i32, i32,
                                                  f32, f32, f32, i32, P]
     lib.pa_oracle_decode_partitioned.restype = i32
+    lib.pa_oracle_decode_slot_scales.argtypes = [P, P, P, P, P, i32, i32, i32, i32, f32, P, P, P, i32]
+    lib.pa_oracle_decode_slot_scales.restype = i32
     lib.pa_oracle_fp8_e4m3fn_encode.argtypes = [ctypes.c_float]
     lib.pa_oracle_fp8_e4m3fn_encode.restype = ctypes.c_uint8
     lib.pa_oracle_cache_write.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, P, P, P, i32, i32,
@@ -138,6 +140,26 @@ def decode(q_bits, k_cache, v_cache, block_tables, seq_lens, scale, k_scale,
         q_bits.ctypes.data, k_cache.ctypes.data, v_cache.ctypes.data, bt.ctypes.data,
         sl.ctypes.data, S, Hq, Hkv, W, float(scale), float(k_scale), float(v_scale),
         out.ctypes.data, int(nt))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return out
+
+
+def decode_slot_scales(q_bits, k_cache, v_cache, block_tables, seq_lens, scale, k_scales,
+                       v_scales, num_threads: int | None = None) -> np.ndarray:
+    """fp64 paged decode with per-slot scale tables k_scales / v_scales
+    (float32 [NB, Hkv, 16]) instead of per-tensor scales."""
+    q_bits, k_cache, v_cache, bt, sl, S, Hq, Hkv, W = _check(
+        q_bits, k_cache, v_cache, block_tables, seq_lens)
+    ks = np.ascontiguousarray(k_scales, dtype=np.float32)
+    vs = np.ascontiguousarray(v_scales, dtype=np.float32)
+    if ks.shape != (k_cache.shape[0], Hkv, 16) or vs.shape != ks.shape:
+        raise ValueError("scale tables must be float32 [NB, Hkv, 16]")
+    out = np.zeros((S, Hq, 128), dtype=np.float64)
+    rc = _load().pa_oracle_decode_slot_scales(
+        q_bits.ctypes.data, k_cache.ctypes.data, v_cache.ctypes.data, bt.ctypes.data,
+        sl.ctypes.data, S, Hq, Hkv, W, float(scale), ks.ctypes.data, vs.ctypes.data,
+        out.ctypes.data, int(num_threads if num_threads else (os.cpu_count() or 1)))
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (code {rc})")
     return out

@@ -42,6 +42,12 @@
  * quantity as a log-sum-exp merge of per-partition partial results; it exists
  * to pin that merge formula against the unsplit definition.
  *
+ * Per-slot scales (pa_oracle_decode_slot_scales): the same quantity with K_t
+ * and V_t dequantised by k_scales[p_t][k][j] and v_scales[p_t][k][j], one fp32
+ * scale per (block, kv head, slot) instead of one per tensor (pull request
+ * #3, Details > Scale tables: the asm kernel reads [blocks, kv_heads,
+ * block_size] tables).
+ *
  * Cache write (pa_oracle_cache_write): the step that fills the cache the
  * decode reads (API page, do_kv_cache_update: new tokens' key and value, the
  * two caches, slot_mapping and the per-tensor k/v scales go to the cache
@@ -128,12 +134,25 @@ uint16_t pa_oracle_bf16_rne(double x) {
   return sign | (uint16_t)(u >> 16);
 }
 
+/* Dequantisation scales: one per tensor, or (when the tables are not NULL) one
+ * per (block, kv head, slot) from tables [num_blocks][num_kv_heads][16]. */
+typedef struct {
+  double k_scale, v_scale;
+  const float* k_slot;
+  const float* v_slot;
+} scales_t;
+
 /* Gather + dequantise token t of sequence s for kv head k (one row of K and V). */
 static void load_token(const uint8_t* k_cache, const uint8_t* v_cache,
                        const int32_t* bt_row, int num_kv_heads, int k, int t,
-                       double k_scale, double v_scale, double* K, double* V) {
+                       const scales_t* sc, double* K, double* V) {
   const int64_t p = bt_row[t / PA_BLOCK];
   const int j = t % PA_BLOCK;
+  double k_scale = sc->k_scale, v_scale = sc->v_scale;
+  if (sc->k_slot) {
+    k_scale = sc->k_slot[(p * num_kv_heads + k) * PA_BLOCK + j];
+    v_scale = sc->v_slot[(p * num_kv_heads + k) * PA_BLOCK + j];
+  }
   const uint8_t* kpage = k_cache + (p * num_kv_heads + k) * (int64_t)(PA_HEAD_DIM * PA_BLOCK);
   const uint8_t* vpage = v_cache + (p * num_kv_heads + k) * (int64_t)(PA_HEAD_DIM * PA_BLOCK);
   for (int e = 0; e < PA_HEAD_DIM; ++e) {
@@ -151,15 +170,10 @@ static int check_args(int S, int Hq, int Hkv, int W, const int32_t* seq_lens) {
   return 0;
 }
 
-/*
- * out: [S][Hq][128] doubles.  q_bits: bf16 bit patterns [S][Hq][128].
- * Returns 0, or a negative code for bad arguments (nothing is written then).
- */
-int pa_oracle_decode(const uint16_t* q_bits, const uint8_t* k_cache,
-                     const uint8_t* v_cache, const int32_t* block_tables,
-                     const int32_t* seq_lens, int S, int Hq, int Hkv, int W,
-                     float scale, float k_scale, float v_scale, double* out,
-                     int num_threads) {
+static int decode_impl(const uint16_t* q_bits, const uint8_t* k_cache, const uint8_t* v_cache,
+                       const int32_t* block_tables, const int32_t* seq_lens, int S, int Hq,
+                       int Hkv, int W, float scale, const scales_t* sc, double* out,
+                       int num_threads) {
   int rc = check_args(S, Hq, Hkv, W, seq_lens);
   if (rc) return rc;
   const int G = Hq / Hkv;
@@ -180,7 +194,7 @@ int pa_oracle_decode(const uint16_t* q_bits, const uint8_t* k_cache,
       /* logits */
       double zmax = -INFINITY;
       for (int t = 0; t < n; ++t) {
-        load_token(k_cache, v_cache, bt_row, Hkv, k, t, k_scale, v_scale, K, V);
+        load_token(k_cache, v_cache, bt_row, Hkv, k, t, sc, K, V);
         double dot = 0.0;
         for (int e = 0; e < PA_HEAD_DIM; ++e) dot += q[e] * K[e];
         z[t] = (double)scale * dot;
@@ -189,7 +203,7 @@ int pa_oracle_decode(const uint16_t* q_bits, const uint8_t* k_cache,
       /* softmax-weighted sum of V */
       double den = 0.0;
       for (int t = 0; t < n; ++t) {
-        load_token(k_cache, v_cache, bt_row, Hkv, k, t, k_scale, v_scale, K, V);
+        load_token(k_cache, v_cache, bt_row, Hkv, k, t, sc, K, V);
         const double w = exp(z[t] - zmax);
         den += w;
         for (int d = 0; d < PA_HEAD_DIM; ++d) o[d] += w * V[d];
@@ -199,6 +213,31 @@ int pa_oracle_decode(const uint16_t* q_bits, const uint8_t* k_cache,
     }
   }
   return 0;
+}
+
+/*
+ * out: [S][Hq][128] doubles.  q_bits: bf16 bit patterns [S][Hq][128].
+ * Returns 0, or a negative code for bad arguments (nothing is written then).
+ */
+int pa_oracle_decode(const uint16_t* q_bits, const uint8_t* k_cache,
+                     const uint8_t* v_cache, const int32_t* block_tables,
+                     const int32_t* seq_lens, int S, int Hq, int Hkv, int W,
+                     float scale, float k_scale, float v_scale, double* out,
+                     int num_threads) {
+  const scales_t sc = {k_scale, v_scale, NULL, NULL};
+  return decode_impl(q_bits, k_cache, v_cache, block_tables, seq_lens, S, Hq, Hkv, W, scale, &sc,
+                     out, num_threads);
+}
+
+/* pa_oracle_decode with per-slot scale tables [num_blocks][Hkv][16] (fp32). */
+int pa_oracle_decode_slot_scales(const uint16_t* q_bits, const uint8_t* k_cache,
+                                 const uint8_t* v_cache, const int32_t* block_tables,
+                                 const int32_t* seq_lens, int S, int Hq, int Hkv, int W,
+                                 float scale, const float* k_scales, const float* v_scales,
+                                 double* out, int num_threads) {
+  const scales_t sc = {1.0, 1.0, k_scales, v_scales};
+  return decode_impl(q_bits, k_cache, v_cache, block_tables, seq_lens, S, Hq, Hkv, W, scale, &sc,
+                     out, num_threads);
 }
 
 /*
@@ -218,6 +257,7 @@ int pa_oracle_decode_partitioned(const uint16_t* q_bits, const uint8_t* k_cache,
   if (rc) return rc;
   if (tokens_per_part <= 0) return -4;
   const int G = Hq / Hkv;
+  const scales_t sc = {k_scale, v_scale, NULL, NULL};
   for (int s = 0; s < S; ++s) {
     for (int h = 0; h < Hq; ++h) {
       const int n = seq_lens[s];
@@ -238,7 +278,7 @@ int pa_oracle_decode_partitioned(const uint16_t* q_bits, const uint8_t* k_cache,
         const int t1 = (t0 + tokens_per_part < n) ? t0 + tokens_per_part : n;
         double zmax = -INFINITY;
         for (int t = t0; t < t1; ++t) {
-          load_token(k_cache, v_cache, bt_row, Hkv, k, t, k_scale, v_scale, K, V);
+          load_token(k_cache, v_cache, bt_row, Hkv, k, t, &sc, K, V);
           double dot = 0.0;
           for (int e = 0; e < PA_HEAD_DIM; ++e) dot += q[e] * K[e];
           double zt = (double)scale * dot;
@@ -247,7 +287,7 @@ int pa_oracle_decode_partitioned(const uint16_t* q_bits, const uint8_t* k_cache,
         m[p] = zmax;
         l[p] = 0.0;
         for (int t = t0; t < t1; ++t) {
-          load_token(k_cache, v_cache, bt_row, Hkv, k, t, k_scale, v_scale, K, V);
+          load_token(k_cache, v_cache, bt_row, Hkv, k, t, &sc, K, V);
           double dot = 0.0;
           for (int e = 0; e < PA_HEAD_DIM; ++e) dot += q[e] * K[e];
           const double w = exp((double)scale * dot - zmax);

@@ -330,3 +330,44 @@ def test_partition_merge_equals_unsplit(oracle_lib, tpp):
                                       case.block_tables.numpy(), case.seq_lens.numpy(),
                                       case.scale, case.k_scale, case.v_scale, tpp)
     np.testing.assert_allclose(split, whole, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# per-slot scale tables
+
+def test_slot_scales_equal_to_tensor_scales_reproduce_per_tensor_decode(oracle_lib):
+    case = workloads.make_case(8, 2, [1, 17, 90, 33], 51)
+    NB = case.k_cache.shape[0]
+    ks = np.full((NB, 2, 16), case.k_scale, np.float32)
+    vs = np.full((NB, 2, 16), case.v_scale, np.float32)
+    a = oracle.decode_slot_scales(case.q_bits(), case.k_cache.numpy(), case.v_cache.numpy(),
+                                  case.block_tables.numpy(), case.seq_lens.numpy(), case.scale, ks, vs)
+    assert np.array_equal(a, run_oracle(case))
+
+
+@pytest.mark.parametrize("hq,hkv,lens", [(8, 2, [1, 17, 33, 64]), (40, 8, [100, 3, 257]),
+                                         (16, 1, [48, 1])])
+def test_slot_scales_match_sdpa(oracle_lib, hq, hkv, lens):
+    case = workloads.make_case(hq, hkv, lens, 52, scale_mode="per_slot")
+    ks, vs = case.k_slot_scales.numpy(), case.v_slot_scales.numpy()
+    assert np.isnan(ks).any()            # unused slots carry NaN scales
+    ours = oracle.decode_slot_scales(case.q_bits(), case.k_cache.numpy(), case.v_cache.numpy(),
+                                     case.block_tables.numpy(), case.seq_lens.numpy(), case.scale,
+                                     ks, vs)
+    assert np.isfinite(ours).all()
+    G = hq // hkv
+    q = case.q.to(torch.float64)
+    for s, L in enumerate(lens):
+        t = np.arange(L)
+        blocks = case.block_tables.numpy()[s, t // 16]
+        slots = t % 16
+        kb = case.k_cache.numpy()[blocks, :, :, slots, :].reshape(L, hkv, 128)
+        vb = case.v_cache.numpy()[blocks, :, :, slots]
+        K = torch.from_numpy(np.ascontiguousarray(kb)).view(torch.float8_e4m3fn).double() * \
+            torch.from_numpy(ks[blocks, :, slots]).double()[:, :, None]
+        V = torch.from_numpy(np.ascontiguousarray(vb)).view(torch.float8_e4m3fn).double() * \
+            torch.from_numpy(vs[blocks, :, slots]).double()[:, :, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q[s][:, None, :].contiguous(), K.permute(1, 0, 2).repeat_interleave(G, 0).contiguous(),
+            V.permute(1, 0, 2).repeat_interleave(G, 0).contiguous(), scale=case.scale)[:, 0]
+        np.testing.assert_allclose(ours[s], ref.numpy(), rtol=0, atol=1e-12)

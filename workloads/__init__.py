@@ -45,9 +45,11 @@ class Case:
     block_tables: torch.Tensor   # int32 [S, W]
     seq_lens: torch.Tensor       # int32 [S]
     scale: float                 # softmax scale (an fp32 value)
-    k_scale: float               # fp32 value
+    k_scale: float               # fp32 value (1.0 when per-slot tables are used)
     v_scale: float               # fp32 value
     meta: dict = field(default_factory=dict)
+    k_slot_scales: torch.Tensor | None = None   # float32 [NB, Hkv, 16], per-slot mode only
+    v_slot_scales: torch.Tensor | None = None
 
     @property
     def num_seqs(self) -> int:
@@ -67,15 +69,15 @@ class Case:
 
     def host(self) -> "Case":
         """A copy with every tensor on the CPU."""
-        return Case(self.name, self.q.cpu(), self.k_cache.cpu(), self.v_cache.cpu(),
-                    self.block_tables.cpu(), self.seq_lens.cpu(), self.scale,
-                    self.k_scale, self.v_scale, dict(self.meta))
+        return self.to("cpu")
 
     def to(self, device) -> "Case":
+        opt = (lambda t: None if t is None else t.to(device))
         return Case(self.name, self.q.to(device), self.k_cache.to(device),
                     self.v_cache.to(device), self.block_tables.to(device),
                     self.seq_lens.to(device), self.scale, self.k_scale,
-                    self.v_scale, dict(self.meta))
+                    self.v_scale, dict(self.meta), opt(self.k_slot_scales),
+                    opt(self.v_slot_scales))
 
     def q_bits(self):
         """q as uint16 bf16 bit patterns (numpy), for the oracle."""
@@ -109,11 +111,34 @@ def _quantise(x: torch.Tensor, scale_mode: str):
     return codes, s
 
 
+def _quantise_per_slot(x: torch.Tensor, layout: str):
+    """Per-(block, kv head, slot) fp8 quantisation of one cache's fp32 values,
+    given as [NB, Hkv, 2048] in page order -> (uint8 codes, float32 [NB, Hkv, 16])."""
+    NB, Hkv = x.shape[:2]
+    if layout == "k":          # page = [8 chunks][16 slots][16 dims]
+        v = x.view(NB, Hkv, 8, BLOCK, 16)
+        amax = v.abs().amax(dim=(2, 4))
+        s = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax))
+        q = (v / s[:, :, None, :, None]).clamp_(-FP8_MAX, FP8_MAX)
+    else:                      # page = [128 dims][16 slots]
+        v = x.view(NB, Hkv, HEAD_DIM, BLOCK)
+        amax = v.abs().amax(dim=2)
+        s = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax))
+        q = (v / s[:, :, None, :]).clamp_(-FP8_MAX, FP8_MAX)
+    codes = q.to(torch.float8_e4m3fn).view(torch.uint8).reshape(NB * Hkv * 2048)
+    return codes, s.to(torch.float32).contiguous()
+
+
 def make_case(num_heads: int, num_kv_heads: int, seq_lens, seed: int = 0, *,
               device="cpu", max_blocks: int | None = None, extra_blocks: int | None = None,
               scale_mode: str = "amax", poison: bool = True, name: str = "case",
               softmax_scale: float | None = None) -> Case:
-    """Build one seeded case.  ``seq_lens`` is a list/tensor of per-sequence token counts."""
+    """Build one seeded case.  ``seq_lens`` is a list/tensor of per-sequence token counts.
+
+    scale_mode: "amax" / "pow2" (per-tensor scales), or "per_slot": each token's
+    K and V get a random magnitude 2^U(-4, 4) and their own scale amax/448 per
+    (block, kv head, slot), returned as k_slot_scales / v_slot_scales (slots
+    outside every context get NaN scales)."""
     device = torch.device(device)
     g = torch.Generator(device=device)
     g.manual_seed(int(seed))
@@ -142,12 +167,25 @@ def make_case(num_heads: int, num_kv_heads: int, seq_lens, seed: int = 0, *,
             # entries past the last block point at (NaN-filled) blocks no sequence owns
             bt[s, n:] = poison_ids[torch.arange(W - n) % poison_ids.numel()]
 
-    kx = torch.randn(NB * num_kv_heads * HEAD_DIM * BLOCK, generator=g, device=device)
-    k_codes, k_scale = _quantise(kx, scale_mode)
-    del kx
-    vx = torch.randn(NB * num_kv_heads * HEAD_DIM * BLOCK, generator=g, device=device)
-    v_codes, v_scale = _quantise(vx, scale_mode)
-    del vx
+    ks_tab = vs_tab = None
+    if scale_mode == "per_slot":
+        n = NB * num_kv_heads * HEAD_DIM * BLOCK
+        kx = torch.randn(n, generator=g, device=device).view(NB, num_kv_heads, 8, BLOCK, 16)
+        kx *= torch.exp2(torch.rand(NB, num_kv_heads, 1, BLOCK, 1, generator=g, device=device) * 8 - 4)
+        k_codes, ks_tab = _quantise_per_slot(kx.reshape(NB, num_kv_heads, 2048), "k")
+        del kx
+        vx = torch.randn(n, generator=g, device=device).view(NB, num_kv_heads, HEAD_DIM, BLOCK)
+        vx *= torch.exp2(torch.rand(NB, num_kv_heads, 1, BLOCK, generator=g, device=device) * 8 - 4)
+        v_codes, vs_tab = _quantise_per_slot(vx.reshape(NB, num_kv_heads, 2048), "v")
+        del vx
+        k_scale = v_scale = 1.0
+    else:
+        kx = torch.randn(NB * num_kv_heads * HEAD_DIM * BLOCK, generator=g, device=device)
+        k_codes, k_scale = _quantise(kx, scale_mode)
+        del kx
+        vx = torch.randn(NB * num_kv_heads * HEAD_DIM * BLOCK, generator=g, device=device)
+        v_codes, v_scale = _quantise(vx, scale_mode)
+        del vx
     k_cache = k_codes.view(NB, num_kv_heads, HEAD_DIM // 16, BLOCK, 16)
     v_cache = v_codes.view(NB, num_kv_heads, HEAD_DIM, BLOCK)
 
@@ -155,19 +193,26 @@ def make_case(num_heads: int, num_kv_heads: int, seq_lens, seed: int = 0, *,
         pid = poison_ids.to(device=device, dtype=torch.int64)
         k_cache[pid] = FP8_NAN
         v_cache[pid] = FP8_NAN
+        if ks_tab is not None:
+            ks_tab[pid] = float("nan")
+            vs_tab[pid] = float("nan")
         for s in range(S):
             L = int(lens[s])
             if L % BLOCK:
                 last = int(bt[s, L // BLOCK])
                 k_cache[last, :, :, L % BLOCK:, :] = FP8_NAN
                 v_cache[last, :, :, L % BLOCK:] = FP8_NAN
+                if ks_tab is not None:
+                    ks_tab[last, :, L % BLOCK:] = float("nan")
+                    vs_tab[last, :, L % BLOCK:] = float("nan")
 
     scale = softmax_scale if softmax_scale is not None else 1.0 / math.sqrt(HEAD_DIM)
     scale = float(torch.tensor(scale, dtype=torch.float32).item())
     return Case(name=name, q=q, k_cache=k_cache, v_cache=v_cache,
                 block_tables=bt.to(device), seq_lens=lens.to(torch.int32).to(device),
                 scale=scale, k_scale=float(k_scale), v_scale=float(v_scale),
-                meta=dict(seed=seed, num_blocks=NB, used_blocks=used, scale_mode=scale_mode))
+                meta=dict(seed=seed, num_blocks=NB, used_blocks=used, scale_mode=scale_mode),
+                k_slot_scales=ks_tab, v_slot_scales=vs_tab)
 
 
 # ----------------------------------------------------------------------------
