@@ -68,6 +68,11 @@ def make_workload(name, device):
     if m:
         hq, hkv, ctx, s = map(int, m.groups())
         return workloads.dense(hq, hkv, s, ctx, seed=0, device=device)
+    m = re.fullmatch(r"slotscales_(\d+)x(\d+)_ctx(\d+)_s(\d+)", name)
+    if m:
+        hq, hkv, ctx, s = map(int, m.groups())
+        return workloads.make_case(hq, hkv, [ctx] * s, seed=0, device=device, scale_mode="per_slot",
+                                   name=name)
     m = re.fullmatch(r"ragged_(\d+)x(\d+)_seed(\d+)", name)
     if m:
         hq, hkv, seed = map(int, m.groups())
@@ -79,6 +84,7 @@ def suite_names():
     import workloads
     names = [f"dense_{a}x{b}_ctx{c}_s{s}" for (a, b, s, c) in workloads.DENSE_1K + workloads.DENSE_4K]
     names += ["target", "dense_20x4_ctx4096_s256"]
+    names += ["slotscales_40x8_ctx4096_s256"]
     names += [f"ragged_{a}x{b}_seed0" for (a, b) in workloads.RAGGED_LAYOUTS]
     names += [f"dense_{a}x{b}_ctx{c}_s{s}" for (a, b, s, c) in workloads.LOW_BATCH]
     return names
@@ -95,8 +101,14 @@ def time_calls(case, steps, warmup, rotate=1):
     stream = torch.cuda.Stream(dev)
 
     def call():
-        pa.paged_decode_attention(case.q, case.k_cache, case.v_cache, case.block_tables,
-                                  case.seq_lens, case.scale, ks, vs, out=out, stream=stream)
+        if case.k_slot_scales is not None:
+            pa.paged_decode_attention_slot_scales(case.q, case.k_cache, case.v_cache,
+                                                  case.block_tables, case.seq_lens, case.scale,
+                                                  case.k_slot_scales, case.v_slot_scales,
+                                                  out=out, stream=stream)
+        else:
+            pa.paged_decode_attention(case.q, case.k_cache, case.v_cache, case.block_tables,
+                                      case.seq_lens, case.scale, ks, vs, out=out, stream=stream)
 
     for _ in range(warmup):
         call()
@@ -122,8 +134,13 @@ def time_graph(case, replays=50, calls_per_graph=10):
     out = torch.empty_like(case.q)
 
     def call():
-        pa.paged_decode_attention(case.q, case.k_cache, case.v_cache, case.block_tables,
-                                  case.seq_lens, case.scale, ks, vs, out=out)
+        if case.k_slot_scales is not None:
+            pa.paged_decode_attention_slot_scales(case.q, case.k_cache, case.v_cache,
+                                                  case.block_tables, case.seq_lens, case.scale,
+                                                  case.k_slot_scales, case.v_slot_scales, out=out)
+        else:
+            pa.paged_decode_attention(case.q, case.k_cache, case.v_cache, case.block_tables,
+                                      case.seq_lens, case.scale, ks, vs, out=out)
 
     stream = torch.cuda.Stream(dev)
     stream.wait_stream(torch.cuda.current_stream(dev))
@@ -266,6 +283,8 @@ def main():
             P, ppp, _ = pa.pa_decode_plan(case.num_seqs, case.num_heads, case.num_kv_heads,
                                           case.max_blocks, 256)
             b = case.algorithmic_bytes()
+            if case.k_slot_scales is not None:
+                b += case.kv_bytes() // 128 * 4   # one fp32 K or V scale per cached token and kv head
             print(json.dumps({"workload": name, "us_per_call": round(us, 2),
                               "us_per_call_graph": round(us_graph, 2),
                               "GBps": round(b / us / 1e3, 1), "frac_of_peak": round(b / us / 1e3 / PEAK_GBS, 4),

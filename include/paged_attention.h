@@ -107,6 +107,25 @@ int paged_decode_attention_split(const void* q, const void* k_cache, const void*
                                  void* out, void* stream, int32_t pages_per_partition);
 
 /*
+ * paged_decode_attention with per-slot dequantisation scales: one fp32 K scale
+ * and one V scale per (block, kv head, slot) instead of one per tensor (the
+ * tables the asm decode of the vLLM pull request lishuoshuo-amd/vllm #3 reads,
+ * Details > Scale tables):
+ *   K_t = fp8(k_cache[...]) * k_slot_scales[block][kv head][slot], V likewise.
+ *   k_slot_scales, v_slot_scales  fp32 [num_blocks][num_kv_heads][16], device,
+ *                                 16-byte aligned; entries of slots outside every
+ *                                 context are never used (they may hold NaN)
+ * Other arguments, plan, scratch and errors as for paged_decode_attention.
+ */
+int paged_decode_attention_slot_scales(const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, const int32_t* seq_lens,
+                                       int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                       int32_t head_size, int32_t block_size,
+                                       int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                                       const float* k_slot_scales, const float* v_slot_scales,
+                                       void* out, void* stream);
+
+/*
  * Launch plan for the given shapes (host arithmetic only; no device access).
  * num_compute_units: the device's CU count (256 on MI355X).
  * pages_per_partition: as in paged_decode_attention_split (0 = library's choice).

@@ -26,7 +26,8 @@ import torch
 
 __all__ = [
     "paged_decode_attention", "paged_decode_attention_split", "pa_decode_plan",
-    "pa_decode_reserve_workspace", "paged_kv_cache_write", "pa_last_error",
+    "pa_decode_reserve_workspace", "paged_kv_cache_write", "paged_decode_attention_slot_scales",
+    "pa_last_error",
     "PagedAttentionError", "library_path",
     "load_library",
 ]
@@ -64,6 +65,8 @@ def load_library():
     lib.paged_decode_attention.restype = ctypes.c_int
     lib.paged_decode_attention_split.argtypes = common + [i32]
     lib.paged_decode_attention_split.restype = ctypes.c_int
+    lib.paged_decode_attention_slot_scales.argtypes = common
+    lib.paged_decode_attention_slot_scales.restype = ctypes.c_int
     lib.pa_decode_plan.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(i32),
                                    ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_size_t)]
     lib.pa_decode_plan.restype = ctypes.c_int
@@ -169,6 +172,26 @@ def paged_decode_attention_split(q, k_cache, v_cache, block_tables, seq_lens, sc
                                    v_scale, out, stream)
     with torch.cuda.device(dev):
         _check(lib.paged_decode_attention_split(*c_args, int(pages_per_partition)))
+    return out
+
+
+def paged_decode_attention_slot_scales(q, k_cache, v_cache, block_tables, seq_lens, scale,
+                                       k_slot_scales, v_slot_scales, out=None, stream=None):
+    """paged_decode_attention with per-slot scale tables (float32
+    [num_blocks, num_kv_heads, 16] device tensors) instead of per-tensor scales."""
+    lib = load_library()
+    NB, Hkv = k_cache.shape[:2]
+    for name, t in (("k_slot_scales", k_slot_scales), ("v_slot_scales", v_slot_scales)):
+        if (t.dtype != torch.float32 or tuple(t.shape) != (NB, Hkv, k_cache.shape[3])
+                or not t.is_contiguous() or t.device != q.device):
+            raise TypeError(f"{name} must be a contiguous float32 [num_blocks, num_kv_heads, "
+                            "block_size] tensor on the q device")
+    one = torch.ones(1, dtype=torch.float32, device=q.device)
+    dev, out, c_args, keep = _args(q, k_cache, v_cache, block_tables, seq_lens, scale, one, one,
+                                   out, stream)
+    c_args = c_args[:13] + (_ptr(k_slot_scales), _ptr(v_slot_scales)) + c_args[15:]
+    with torch.cuda.device(dev):
+        _check(lib.paged_decode_attention_slot_scales(*c_args))
     return out
 
 

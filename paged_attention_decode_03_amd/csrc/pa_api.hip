@@ -146,7 +146,8 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 int decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
            const int32_t* seq_lens, int32_t S, int32_t Hq, int32_t Hkv, int32_t head_size,
            int32_t block_size, int32_t W, int64_t NB, float scale, const float* k_scale,
-           const float* v_scale, void* out, void* stream_ptr, int32_t ppp_req) {
+           const float* v_scale, void* out, void* stream_ptr, int32_t ppp_req,
+           bool slot_scales = false) {
   g_last_error[0] = '\0';
   if (head_size != pa::kHeadDim)
     return fail(PA_ERR_UNSUPPORTED, "head_size %d unsupported (only %d)", head_size, pa::kHeadDim);
@@ -179,9 +180,14 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
       overlaps(out, q_bytes, seq_lens, (size_t)S * 4) || overlaps(out, q_bytes, k_scale, 4) ||
       overlaps(out, q_bytes, v_scale, 4))
     return fail(PA_ERR_ALIAS, "out overlaps an input");
+  if (slot_scales && (overlaps(out, q_bytes, k_scale, (size_t)NB * Hkv * 64) ||
+                      overlaps(out, q_bytes, v_scale, (size_t)NB * Hkv * 64)))
+    return fail(PA_ERR_ALIAS, "out overlaps a scale table");
   if (((uintptr_t)q & 15) || ((uintptr_t)k_cache & 15) || ((uintptr_t)v_cache & 3) ||
       ((uintptr_t)out & 7) || ((uintptr_t)block_tables & 3) || ((uintptr_t)seq_lens & 3))
     return fail(PA_ERR_SHAPE, "misaligned pointer (q, k_cache: 16 B; out: 8 B; others: 4 B)");
+  if (slot_scales && (((uintptr_t)k_scale & 15) || ((uintptr_t)v_scale & 15)))
+    return fail(PA_ERR_SHAPE, "scale tables must be 16-byte aligned");
 
   // --- past this point HIP is called
   int dev = 0;
@@ -197,8 +203,10 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   p.v_cache = (const uint8_t*)v_cache;
   p.block_tables = block_tables;
   p.seq_lens = seq_lens;
-  p.k_scale = k_scale;
-  p.v_scale = v_scale;
+  p.k_scale = slot_scales ? nullptr : k_scale;
+  p.v_scale = slot_scales ? nullptr : v_scale;
+  p.k_slot_scales = slot_scales ? k_scale : nullptr;
+  p.v_slot_scales = slot_scales ? v_scale : nullptr;
   p.out = (uint16_t*)out;
   p.part_acc = nullptr;
   p.part_ml = nullptr;
@@ -247,6 +255,18 @@ int paged_decode_attention_split(const void* q, const void* k_cache, const void*
   return decode(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads, num_kv_heads,
                 head_size, block_size, max_blocks_per_seq, num_blocks, scale, k_scale, v_scale, out,
                 stream, pages_per_partition);
+}
+
+int paged_decode_attention_slot_scales(const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, const int32_t* seq_lens,
+                                       int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                       int32_t head_size, int32_t block_size,
+                                       int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
+                                       const float* k_slot_scales, const float* v_slot_scales,
+                                       void* out, void* stream) {
+  return decode(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads, num_kv_heads,
+                head_size, block_size, max_blocks_per_seq, num_blocks, scale, k_slot_scales,
+                v_slot_scales, out, stream, 0, true);
 }
 
 int pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,

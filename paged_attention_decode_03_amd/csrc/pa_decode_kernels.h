@@ -19,8 +19,10 @@ struct DecodeParams {
   const uint8_t* v_cache;    // fp8  [NB][Hkv][128][16]
   const int32_t* block_tables;  // [S][W]
   const int32_t* seq_lens;      // [S]
-  const float* k_scale;      // [1]
+  const float* k_scale;      // [1] (per-tensor scales)
   const float* v_scale;      // [1]
+  const float* k_slot_scales;  // [NB][Hkv][16] per-slot scales, or null for per-tensor
+  const float* v_slot_scales;
   uint16_t* out;             // bf16 [S][Hq][128]
   float* part_acc;           // [S][Hq][P][128] unnormalised partial outputs (P > 1 only)
   float* part_ml;            // [S][Hq][P][2]   (running max in log2 units, sum of weights)

@@ -61,6 +61,9 @@ typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 #endif
 constexpr int kPagesPerStage = PA_PAGES_PER_STAGE;
 constexpr int kRingDepth = PA_RING_DEPTH;
+// The per-slot-scale variant keeps 8 more VGPRs per page in flight; 2 pages per
+// stage keep it at 2 waves per SIMD.
+constexpr int kSlotScalePagesPerStage = 2;
 // Word 3 of a raw buffer resource (no format conversion, no swizzle).
 constexpr int kRsrcWord3 = 0x00020000;
 
@@ -110,9 +113,18 @@ template <int PPS>
 struct Stage {
   u32x4 k[PPS][2];     // per page: 16 bytes of chunk (l >> 4) and of chunk 4 + (l >> 4)
   uint32_t v[PPS][8];  // per page: 4 slots of one dim in each of the 8 16-dim blocks
+  u32x4 ks[PPS];       // per-slot scales of slots 4 rq .. 4 rq + 3 (per-slot variant only)
+  u32x4 vs[PPS];
 };
 
-template <int PPS, int NB>
+// SS: per-slot scale tables instead of per-tensor scales.  K scales multiply
+// the logits token by token; V scales multiply the fp16 weights that feed PV
+// (the denominator keeps the plain weights).  So that p * v_scale stays in
+// fp16's normal range, every weight of a work item is also multiplied by one
+// exact power of two, 2^-e with e the exponent of the item's first V scale,
+// and the epilogue divides it out exactly.  (Scales more than 2^14 above the
+// first one would saturate the fp16 weights.)
+template <int PPS, int NB, bool SS>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU))) void pa_decode_kernel(const DecodeParams p) {
   const int lane = threadIdx.x;
   const int col = lane & 15;  // MFMA column (query head in group); K load row (token)
@@ -177,8 +189,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
   const int pend = min(pbeg + ppp, npages);
   const int tend = min(L, pend * kBlockTokens);  // first token this item must not use
 
-  // logits in log2 units: z * scale * k_scale * log2(e)
-  const float c_log2 = p.scale_log2e * scalar_load(p.k_scale);
+  // logits in log2 units: z * scale * k_scale * log2(e) (k_scale per slot when SS)
+  const float c_log2 = SS ? p.scale_log2e : p.scale_log2e * scalar_load(p.k_scale);
 
   const size_t page_stride = (size_t)p.num_kv_heads * kPageBytes;
   const uint8_t* kpage0 = p.k_cache + (size_t)kvh * kPageBytes;
@@ -192,6 +204,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
   f32x4 accl = {0.f, 0.f, 0.f, 0.f};  // softmax denominator (same value in every element)
   float m_run = -INFINITY;
   const f16x4 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
+  float vnorm = 1.0f, vnorm_inv = 1.0f;  // per-slot variant: power-of-two weight factor
 
   // The partition's physical block ids, staged in LDS.  A load of a page past
   // the partition gets a buffer descriptor of zero bytes: it is still issued
@@ -241,6 +254,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
           __builtin_amdgcn_make_buffer_rsrc((void*)(kpage0 + off), (short)0, bytes, kRsrcWord3);
       const __amdgpu_buffer_rsrc_t rv =
           __builtin_amdgcn_make_buffer_rsrc((void*)(vpage0 + off), (short)0, bytes, kRsrcWord3);
+      if constexpr (SS) {
+        const size_t srow = ((size_t)__builtin_amdgcn_readfirstlane(pid[pp]) * p.num_kv_heads + kvh) * kBlockTokens;
+        const int sbytes = (i0 + pp < npg) ? kBlockTokens * 4 : 0;
+        const __amdgpu_buffer_rsrc_t rks =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(p.k_slot_scales + srow), (short)0, sbytes, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rvs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(p.v_slot_scales + srow), (short)0, sbytes, kRsrcWord3);
+        st.ks[pp] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rks, rq * 16, 0, 0));
+        st.vs[pp] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rvs, rq * 16, 0, 0));
+      }
       st.k[pp][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, 0, PA_LOAD_AUX));
       st.k[pp][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 1024, 0, PA_LOAD_AUX));
 #pragma unroll
@@ -272,6 +295,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float v = z[pp][i] * c_log2;
+        if constexpr (SS) v *= __uint_as_float(st.ks[pp][i]);
         if (last) {
           const int t = (j0 + pp) * kBlockTokens + rq * 4 + i;
           v = (t < tend) ? v : -INFINITY;
@@ -290,21 +314,46 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
       m_run = m_new;
     }
     // P = 2^(z - m) in fp16, then PV
+    if constexpr (SS) {
+      if (stage == 0) {
+        // 2^-e for the exponent e of the item's first V scale (token 0 is always
+        // in the context); clamped so that the factor and its inverse are normal
+        const uint32_t eb = min(max((__builtin_amdgcn_readfirstlane(st.vs[0][0]) >> 23) & 0xFFu, 1u), 253u);
+        vnorm = __uint_as_float((254u - eb) << 23);
+        vnorm_inv = __uint_as_float(eb << 23);
+      }
+    }
 #pragma unroll
     for (int pp = 0; pp < PPS; ++pp) {
-      f16x4 pb;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pb[i] = (_Float16)__builtin_amdgcn_exp2f(z[pp][i] - m_run);
       uint32_t vmask = 0xFFFFFFFFu;
       if (last) {
         // slots past the context may hold anything (even NaN): zero their V bytes
         const int nv = tend - ((j0 + pp) * kBlockTokens + rq * 4);
         vmask = nv >= 4 ? 0xFFFFFFFFu : (nv <= 0 ? 0u : ((1u << (8 * nv)) - 1u));
       }
+      if constexpr (SS) {
+        f16x4 pb, pv;
 #pragma unroll
-      for (int jd = 0; jd < 8; ++jd)
-        acc[jd] = __builtin_amdgcn_mfma_f32_16x16x16f16(fp8x4_to_f16(st.v[pp][jd] & vmask), pb, acc[jd], 0, 0, 0);
-      accl = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pb, accl, 0, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+          const float e = __builtin_amdgcn_exp2f(z[pp][i] - m_run);
+          pb[i] = (_Float16)e;
+          // masked tokens have e == 0; their scale may be NaN and must not reach PV
+          const float w = e == 0.0f ? 0.0f : fminf(e * __uint_as_float(st.vs[pp][i]) * vnorm, 65504.0f);
+          pv[i] = (_Float16)w;
+        }
+#pragma unroll
+        for (int jd = 0; jd < 8; ++jd)
+          acc[jd] = __builtin_amdgcn_mfma_f32_16x16x16f16(fp8x4_to_f16(st.v[pp][jd] & vmask), pv, acc[jd], 0, 0, 0);
+        accl = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pb, accl, 0, 0, 0);
+      } else {
+        f16x4 pb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pb[i] = (_Float16)__builtin_amdgcn_exp2f(z[pp][i] - m_run);
+#pragma unroll
+        for (int jd = 0; jd < 8; ++jd)
+          acc[jd] = __builtin_amdgcn_mfma_f32_16x16x16f16(fp8x4_to_f16(st.v[pp][jd] & vmask), pb, acc[jd], 0, 0, 0);
+        accl = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pb, accl, 0, 0, 0);
+      }
     }
   };
 
@@ -325,7 +374,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
   if (!hvalid) return;
   const float lsum = accl[0];
   if (direct) {
-    const float inv = scalar_load(p.v_scale) / lsum;
+    const float inv = (SS ? vnorm_inv : scalar_load(p.v_scale)) / lsum;
     uint16_t* o = p.out + orow + rq * 4;
 #pragma unroll
     for (int jd = 0; jd < 8; ++jd) {
@@ -336,7 +385,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
     const size_t prow = ((size_t)s * p.num_heads + h) * p.num_parts + part;
     float* a = p.part_acc + prow * kHeadDim + rq * 4;
 #pragma unroll
-    for (int jd = 0; jd < 8; ++jd) *(f32x4*)(a + jd * 16) = acc[jd];
+    for (int jd = 0; jd < 8; ++jd) *(f32x4*)(a + jd * 16) = acc[jd] * vnorm_inv;
     if (rq == 0) *(float2*)(p.part_ml + prow * 2) = make_float2(m_run, lsum);
   }
 }
@@ -409,7 +458,7 @@ __global__ __launch_bounds__(kMergeThreads) void pa_merge_kernel(const DecodePar
       n.w += a.w;
       dsum += red_den[k];
     }
-    const float inv = scalar_load(p.v_scale) / dsum;
+    const float inv = (p.v_slot_scales ? 1.0f : scalar_load(p.v_scale)) / dsum;
     *(uint2*)(p.out + (size_t)sh * kHeadDim + 4 * t) =
         make_uint2(pack_bf16x2(n.x * inv, n.y * inv), pack_bf16x2(n.z * inv, n.w * inv));
   }
@@ -419,7 +468,12 @@ __global__ __launch_bounds__(kMergeThreads) void pa_merge_kernel(const DecodePar
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const size_t items = (size_t)p.num_seqs * p.num_kv_heads * p.num_parts;
-  hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth>), dim3((unsigned)items), dim3(64), 0, stream, p);
+  if (p.k_slot_scales)
+    hipLaunchKernelGGL((pa_decode_kernel<kSlotScalePagesPerStage, kRingDepth, true>), dim3((unsigned)items),
+                       dim3(64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false>), dim3((unsigned)items), dim3(64),
+                       0, stream, p);
   if (p.num_parts > 1)
     hipLaunchKernelGGL(pa_merge_kernel, dim3((unsigned)((size_t)p.num_seqs * p.num_heads)),
                        dim3(kMergeThreads), 0, stream, p);

@@ -28,7 +28,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("paged_decode_attention", "paged_decode_attention_split", "pa_decode_plan",
-              "pa_decode_reserve_workspace", "paged_kv_cache_write", "pa_last_error"):
+              "pa_decode_reserve_workspace", "paged_kv_cache_write",
+              "paged_decode_attention_slot_scales", "pa_last_error"):
         assert n in names
 
 
@@ -126,3 +127,13 @@ def test_cache_write_rejects_bad_arguments(lib, kw, code):
 
 def test_cache_write_empty_is_a_noop(lib):
     assert cw(lib, T=0, key=0, value=0, kc=0, vc=0, sm=0) == 0
+
+
+def test_slot_scale_decode_checks_its_tables(lib):
+    vp = ctypes.c_void_p
+    args = lambda ks, vs, out=FAKE * 64: (vp(FAKE), vp(FAKE * 16), vp(FAKE * 32), vp(FAKE * 48),
+                                          vp(FAKE * 50), 2, 8, 2, 128, 16, 4, 16,
+                                          ctypes.c_float(0.088), vp(ks), vp(vs), vp(out), None)
+    assert lib.paged_decode_attention_slot_scales(*args(0, FAKE * 80)) == -1
+    assert lib.paged_decode_attention_slot_scales(*args(FAKE * 80 + 4, FAKE * 90)) == -2
+    assert lib.paged_decode_attention_slot_scales(*args(FAKE * 64 + 256, FAKE * 90)) == -4

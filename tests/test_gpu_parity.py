@@ -235,3 +235,58 @@ def test_tp2_share_20x4_ctx4096_256seqs():
     out = run_gpu(case)
     seqs = sample_seqs(case, 6)
     compare(out, run_oracle(case, seqs), "20/4 ctx4096 s256", seqs)
+
+
+# ---------------------------------------------------------------- per-slot scales
+
+def run_gpu_slot(case):
+    import paged_attention_decode_03_amd as pa
+    c = case if case.q.is_cuda else case.to("cuda")
+    out = pa.paged_decode_attention_slot_scales(c.q, c.k_cache, c.v_cache, c.block_tables,
+                                                c.seq_lens, c.scale, c.k_slot_scales,
+                                                c.v_slot_scales)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_slot(case, seqs=None):
+    import oracle
+    h = case.host()
+    idx = np.arange(h.num_seqs) if seqs is None else np.asarray(seqs)
+    return oracle.decode_slot_scales(h.q_bits()[idx], h.k_cache.numpy(), h.v_cache.numpy(),
+                                     h.block_tables.numpy()[idx], h.seq_lens.numpy()[idx],
+                                     h.scale, h.k_slot_scales.numpy(), h.v_slot_scales.numpy())
+
+
+@pytest.mark.parametrize("hq,hkv,lens", [(8, 2, [1, 17, 33, 64]), (40, 8, [1, 100, 1000, 17]),
+                                         (16, 1, [1, 333, 48]), (5, 1, [2, 31, 500])],
+                         ids=lambda x: str(x))
+def test_slot_scales_small(hq, hkv, lens):
+    case = workloads.make_case(hq, hkv, lens, seed=hq + 3 * hkv, scale_mode="per_slot")
+    compare(run_gpu_slot(case), oracle_slot(case), f"slot scales {hq}/{hkv}", relative=True)
+
+
+def test_slot_scales_equal_to_tensor_scales_match_per_tensor_path():
+    case = workloads.make_case(40, 8, [4096, 77, 1], seed=61)
+    NB = case.k_cache.shape[0]
+    case.k_slot_scales = torch.full((NB, 8, 16), case.k_scale, dtype=torch.float32)
+    case.v_slot_scales = torch.full((NB, 8, 16), case.v_scale, dtype=torch.float32)
+    ref = run_oracle(case)
+    compare(run_gpu_slot(case), ref, "slot scales = tensor scales")
+
+
+@pytest.mark.parametrize("hq,hkv,s,ctx", [(40, 8, 256, 4096), (40, 8, 1, 32768), (40, 8, 4, 4096)],
+                         ids=lambda x: str(x))
+def test_slot_scales_full_size(hq, hkv, s, ctx):
+    case = workloads.make_case(hq, hkv, [ctx] * s, seed=62, device="cuda", scale_mode="per_slot")
+    out = run_gpu_slot(case)
+    seqs = sample_seqs(case, 4)
+    compare(out, oracle_slot(case, seqs), f"slot scales {hq}/{hkv} s{s} ctx{ctx}", seqs, relative=True)
+
+
+def test_slot_scales_ragged_with_poison():
+    case = workloads.make_case(32, 8, workloads.ragged_lens(64, seed=5), seed=63, device="cuda",
+                               max_blocks=250, scale_mode="per_slot")
+    out = run_gpu_slot(case)
+    seqs = sample_seqs(case, 8)
+    compare(out, oracle_slot(case, seqs), "slot scales ragged", seqs, relative=True)
