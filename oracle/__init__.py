@@ -58,6 +58,8 @@ def _load():
     lib.pa_oracle_decode_partitioned.restype = i32
     lib.pa_oracle_decode_slot_scales.argtypes = [P, P, P, P, P, i32, i32, i32, i32, f32, P, P, P, i32]
     lib.pa_oracle_decode_slot_scales.restype = i32
+    lib.pa_oracle_attend_multi.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, f32, f32, f32, P, i32]
+    lib.pa_oracle_attend_multi.restype = i32
     lib.pa_oracle_fp8_e4m3fn_encode.argtypes = [ctypes.c_float]
     lib.pa_oracle_fp8_e4m3fn_encode.restype = ctypes.c_uint8
     lib.pa_oracle_cache_write.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, P, P, P, i32, i32,
@@ -160,6 +162,32 @@ def decode_slot_scales(q_bits, k_cache, v_cache, block_tables, seq_lens, scale, 
         q_bits.ctypes.data, k_cache.ctypes.data, v_cache.ctypes.data, bt.ctypes.data,
         sl.ctypes.data, S, Hq, Hkv, W, float(scale), ks.ctypes.data, vs.ctypes.data,
         out.ctypes.data, int(num_threads if num_threads else (os.cpu_count() or 1)))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return out
+
+
+def attend_multi(q_bits, cu_seqlens_q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale,
+                 v_scale, num_threads: int | None = None) -> np.ndarray:
+    """Causal attention of several new tokens per sequence over the cache.
+
+    q_bits: uint16 bf16 [T, Hq, 128]; cu_seqlens_q: int32 [S + 1] query row
+    offsets (cu[0] = 0, cu[S] = T).  Query i of sequence s sees cache tokens
+    0 .. seq_lens[s] - q_len + i.  Returns float64 [T, Hq, 128]."""
+    q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    cu = np.ascontiguousarray(cu_seqlens_q, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    S = sl.shape[0]
+    if cu.shape != (S + 1,) or q_bits.ndim != 3 or q_bits.shape[0] != int(cu[-1]):
+        raise ValueError("cu_seqlens_q must be [S+1] with cu[S] = number of query rows")
+    _, Hq, _ = q_bits.shape
+    fake_q = np.zeros((S, Hq, 128), np.uint16)
+    _, k_cache, v_cache, bt, sl, S, Hq, Hkv, W = _check(fake_q, k_cache, v_cache, block_tables, sl)
+    out = np.zeros((q_bits.shape[0], Hq, 128), dtype=np.float64)
+    rc = _load().pa_oracle_attend_multi(
+        q_bits.ctypes.data, cu.ctypes.data, k_cache.ctypes.data, v_cache.ctypes.data,
+        bt.ctypes.data, sl.ctypes.data, S, Hq, Hkv, W, float(scale), float(k_scale),
+        float(v_scale), out.ctypes.data, int(num_threads if num_threads else (os.cpu_count() or 1)))
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (code {rc})")
     return out

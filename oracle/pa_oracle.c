@@ -48,6 +48,14 @@
  * #3, Details > Scale tables: the asm kernel reads [blocks, kv_heads,
  * block_size] tables).
  *
+ * Several query tokens per sequence (pa_oracle_attend_multi): sequence s owns
+ * query rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1, its q_len newest tokens,
+ * already in the cache (API page, RocmAiterUnifiedAttentionImpl.forward:
+ * cu_seqlens_q / query_start_loc, seqused_k, causal=True; the cache update
+ * runs before it).  Reading of the causal mask: query i (0-based) of a sequence
+ * with n = seq_lens[s] tokens sits at position n - q_len + i and sees tokens
+ * 0 .. n - q_len + i.  q_len > n is a caller error (return -5).
+ *
  * Cache write (pa_oracle_cache_write): the step that fills the cache the
  * decode reads (API page, do_kv_cache_update: new tokens' key and value, the
  * two caches, slot_mapping and the per-tensor k/v scales go to the cache
@@ -170,6 +178,37 @@ static int check_args(int S, int Hq, int Hkv, int W, const int32_t* seq_lens) {
   return 0;
 }
 
+/* One output row: query row q_row (bf16 bits) of kv head k against the first
+ * n tokens of the sequence whose block-table row is bt_row. */
+static void attend_row(const uint16_t* q_row, const uint8_t* k_cache, const uint8_t* v_cache,
+                       const int32_t* bt_row, int Hkv, int k, int n, float scale,
+                       const scales_t* sc, double* o) {
+  double q[PA_HEAD_DIM], K[PA_HEAD_DIM], V[PA_HEAD_DIM];
+  for (int e = 0; e < PA_HEAD_DIM; ++e) q[e] = pa_oracle_bf16(q_row[e]);
+  for (int d = 0; d < PA_HEAD_DIM; ++d) o[d] = 0.0;
+  if (n <= 0) return;
+  double* z = (double*)malloc(sizeof(double) * (size_t)n);
+  /* logits */
+  double zmax = -INFINITY;
+  for (int t = 0; t < n; ++t) {
+    load_token(k_cache, v_cache, bt_row, Hkv, k, t, sc, K, V);
+    double dot = 0.0;
+    for (int e = 0; e < PA_HEAD_DIM; ++e) dot += q[e] * K[e];
+    z[t] = (double)scale * dot;
+    if (z[t] > zmax) zmax = z[t];
+  }
+  /* softmax-weighted sum of V */
+  double den = 0.0;
+  for (int t = 0; t < n; ++t) {
+    load_token(k_cache, v_cache, bt_row, Hkv, k, t, sc, K, V);
+    const double w = exp(z[t] - zmax);
+    den += w;
+    for (int d = 0; d < PA_HEAD_DIM; ++d) o[d] += w * V[d];
+  }
+  for (int d = 0; d < PA_HEAD_DIM; ++d) o[d] /= den;
+  free(z);
+}
+
 static int decode_impl(const uint16_t* q_bits, const uint8_t* k_cache, const uint8_t* v_cache,
                        const int32_t* block_tables, const int32_t* seq_lens, int S, int Hq,
                        int Hkv, int W, float scale, const scales_t* sc, double* out,
@@ -179,39 +218,11 @@ static int decode_impl(const uint16_t* q_bits, const uint8_t* k_cache, const uin
   const int G = Hq / Hkv;
   (void)num_threads;
 #pragma omp parallel for collapse(2) schedule(dynamic, 1) num_threads(num_threads > 0 ? num_threads : 1)
-  for (int s = 0; s < S; ++s) {
-    for (int h = 0; h < Hq; ++h) {
-      const int n = seq_lens[s];
-      const int k = h / G;
-      double* o = out + ((int64_t)s * Hq + h) * PA_HEAD_DIM;
-      double q[PA_HEAD_DIM], K[PA_HEAD_DIM], V[PA_HEAD_DIM];
-      for (int e = 0; e < PA_HEAD_DIM; ++e)
-        q[e] = pa_oracle_bf16(q_bits[((int64_t)s * Hq + h) * PA_HEAD_DIM + e]);
-      for (int d = 0; d < PA_HEAD_DIM; ++d) o[d] = 0.0;
-      if (n == 0) continue;
-      double* z = (double*)malloc(sizeof(double) * (size_t)n);
-      const int32_t* bt_row = block_tables + (int64_t)s * W;
-      /* logits */
-      double zmax = -INFINITY;
-      for (int t = 0; t < n; ++t) {
-        load_token(k_cache, v_cache, bt_row, Hkv, k, t, sc, K, V);
-        double dot = 0.0;
-        for (int e = 0; e < PA_HEAD_DIM; ++e) dot += q[e] * K[e];
-        z[t] = (double)scale * dot;
-        if (z[t] > zmax) zmax = z[t];
-      }
-      /* softmax-weighted sum of V */
-      double den = 0.0;
-      for (int t = 0; t < n; ++t) {
-        load_token(k_cache, v_cache, bt_row, Hkv, k, t, sc, K, V);
-        const double w = exp(z[t] - zmax);
-        den += w;
-        for (int d = 0; d < PA_HEAD_DIM; ++d) o[d] += w * V[d];
-      }
-      for (int d = 0; d < PA_HEAD_DIM; ++d) o[d] /= den;
-      free(z);
-    }
-  }
+  for (int s = 0; s < S; ++s)
+    for (int h = 0; h < Hq; ++h)
+      attend_row(q_bits + ((int64_t)s * Hq + h) * PA_HEAD_DIM, k_cache, v_cache,
+                 block_tables + (int64_t)s * W, Hkv, h / G, seq_lens[s], scale, sc,
+                 out + ((int64_t)s * Hq + h) * PA_HEAD_DIM);
   return 0;
 }
 
@@ -338,6 +349,39 @@ int pa_oracle_cache_write(const uint16_t* key, const uint16_t* value, int64_t ke
         kpage[(d / 16) * (PA_BLOCK * 16) + j * 16 + (d % 16)] = pa_oracle_fp8_e4m3fn_encode(xk / k_scale);
         vpage[d * PA_BLOCK + j] = pa_oracle_fp8_e4m3fn_encode(xv / v_scale);
       }
+    }
+  }
+  return 0;
+}
+
+/*
+ * q_bits: bf16 [T][Hq][128] with T = cu_seqlens_q[S]; out: [T][Hq][128] doubles.
+ */
+int pa_oracle_attend_multi(const uint16_t* q_bits, const int32_t* cu_seqlens_q,
+                           const uint8_t* k_cache, const uint8_t* v_cache,
+                           const int32_t* block_tables, const int32_t* seq_lens, int S, int Hq,
+                           int Hkv, int W, float scale, float k_scale, float v_scale, double* out,
+                           int num_threads) {
+  int rc = check_args(S, Hq, Hkv, W, seq_lens);
+  if (rc) return rc;
+  if (cu_seqlens_q[0] != 0) return -5;
+  for (int s = 0; s < S; ++s) {
+    const int q_len = cu_seqlens_q[s + 1] - cu_seqlens_q[s];
+    if (q_len < 0 || q_len > seq_lens[s]) return -5;
+  }
+  const int G = Hq / Hkv;
+  const scales_t sc = {k_scale, v_scale, NULL, NULL};
+  (void)num_threads;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(num_threads > 0 ? num_threads : 1)
+  for (int s = 0; s < S; ++s) {
+    const int q0 = cu_seqlens_q[s];
+    const int q_len = cu_seqlens_q[s + 1] - q0;
+    for (int i = 0; i < q_len; ++i) {
+      const int visible = seq_lens[s] - q_len + i + 1;
+      for (int h = 0; h < Hq; ++h)
+        attend_row(q_bits + ((int64_t)(q0 + i) * Hq + h) * PA_HEAD_DIM, k_cache, v_cache,
+                   block_tables + (int64_t)s * W, Hkv, h / G, visible, scale, &sc,
+                   out + ((int64_t)(q0 + i) * Hq + h) * PA_HEAD_DIM);
     }
   }
   return 0;

@@ -371,3 +371,63 @@ def test_slot_scales_match_sdpa(oracle_lib, hq, hkv, lens):
             q[s][:, None, :].contiguous(), K.permute(1, 0, 2).repeat_interleave(G, 0).contiguous(),
             V.permute(1, 0, 2).repeat_interleave(G, 0).contiguous(), scale=case.scale)[:, 0]
         np.testing.assert_allclose(ours[s], ref.numpy(), rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# several query tokens per sequence (causal)
+
+def run_multi(case):
+    return oracle.attend_multi(case.q_bits(), case.cu_seqlens_q.numpy(), case.k_cache.numpy(),
+                               case.v_cache.numpy(), case.block_tables.numpy(),
+                               case.seq_lens.numpy(), case.scale, case.k_scale, case.v_scale)
+
+
+def test_multi_with_one_query_per_sequence_is_decode(oracle_lib):
+    lens = [1, 17, 90, 33, 0]
+    case = workloads.make_multi_case(8, 2, lens, [1, 1, 1, 1, 0], 71, max_blocks=8)
+    dec = workloads.Case("d", case.q[[0, 1, 2, 3]], case.k_cache, case.v_cache,
+                         case.block_tables[:4], case.seq_lens[:4], case.scale, case.k_scale,
+                         case.v_scale)
+    assert np.array_equal(run_multi(case), run_oracle(dec))
+
+
+@pytest.mark.parametrize("hq,hkv,lens,qlens", [
+    (8, 2, [5, 40, 17], [5, 3, 16]), (40, 8, [100, 33], [4, 1]), (16, 1, [64, 2], [7, 2]),
+    (5, 1, [300, 16, 1], [2, 16, 1]),
+])
+def test_multi_matches_causal_sdpa(oracle_lib, hq, hkv, lens, qlens):
+    case = workloads.make_multi_case(hq, hkv, lens, qlens, 72)
+    ours = run_multi(case)
+    G = hq // hkv
+    cu = case.cu_seqlens_q.numpy()
+    q = case.q.to(torch.float64)
+    for s, (L, ql) in enumerate(zip(lens, qlens)):
+        K, V = gather_dense(case, s)
+        Q = q[cu[s]:cu[s + 1]].permute(1, 0, 2).contiguous()             # [Hq, ql, 128]
+        i = torch.arange(ql)[:, None]
+        t = torch.arange(L)[None, :]
+        mask = t <= (L - ql + i)                                          # bottom-right causal
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            Q, K.permute(1, 0, 2).repeat_interleave(G, 0).contiguous(),
+            V.permute(1, 0, 2).repeat_interleave(G, 0).contiguous(), attn_mask=mask,
+            scale=case.scale)                                             # [Hq, ql, 128]
+        np.testing.assert_allclose(ours[cu[s]:cu[s + 1]], ref.permute(1, 0, 2).numpy(),
+                                   rtol=0, atol=1e-12)
+
+
+def test_multi_first_query_of_a_fresh_sequence_sees_token_zero(oracle_lib):
+    case = workloads.make_multi_case(4, 1, [9], [9], 73)
+    out = run_multi(case)
+    _, V = gather_dense(case, 0)
+    for h in range(4):
+        assert np.array_equal(out[0, h], V[0, 0].numpy())
+
+
+def test_multi_rejects_more_queries_than_context(oracle_lib):
+    case = workloads.make_multi_case(4, 1, [9], [9], 74)
+    bad = case.seq_lens.clone()
+    bad[0] = 8
+    with pytest.raises(ValueError):
+        oracle.attend_multi(case.q_bits(), case.cu_seqlens_q.numpy(), case.k_cache.numpy(),
+                            case.v_cache.numpy(), case.block_tables.numpy(), bad.numpy(),
+                            case.scale, case.k_scale, case.v_scale)

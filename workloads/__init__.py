@@ -50,6 +50,7 @@ class Case:
     meta: dict = field(default_factory=dict)
     k_slot_scales: torch.Tensor | None = None   # float32 [NB, Hkv, 16], per-slot mode only
     v_slot_scales: torch.Tensor | None = None
+    cu_seqlens_q: torch.Tensor | None = None    # int32 [S + 1]: several query rows per sequence
 
     @property
     def num_seqs(self) -> int:
@@ -77,7 +78,7 @@ class Case:
                     self.v_cache.to(device), self.block_tables.to(device),
                     self.seq_lens.to(device), self.scale, self.k_scale,
                     self.v_scale, dict(self.meta), opt(self.k_slot_scales),
-                    opt(self.v_slot_scales))
+                    opt(self.v_slot_scales), opt(self.cu_seqlens_q))
 
     def q_bits(self):
         """q as uint16 bf16 bit patterns (numpy), for the oracle."""
@@ -213,6 +214,26 @@ def make_case(num_heads: int, num_kv_heads: int, seq_lens, seed: int = 0, *,
                 scale=scale, k_scale=float(k_scale), v_scale=float(v_scale),
                 meta=dict(seed=seed, num_blocks=NB, used_blocks=used, scale_mode=scale_mode),
                 k_slot_scales=ks_tab, v_slot_scales=vs_tab)
+
+
+def make_multi_case(num_heads: int, num_kv_heads: int, seq_lens, q_lens, seed: int = 0,
+                    **kw) -> Case:
+    """Several new query tokens per sequence: sequence s has seq_lens[s] cached
+    tokens, the last q_lens[s] of which are its queries (q rows
+    cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1, N(0,1) rounded to bf16)."""
+    base = make_case(num_heads, num_kv_heads, seq_lens, seed, **kw)
+    ql = torch.as_tensor(q_lens, dtype=torch.int64)
+    if ql.numel() != base.num_seqs or bool((ql < 0).any()) or \
+            bool((ql > torch.as_tensor(seq_lens, dtype=torch.int64)).any()):
+        raise ValueError("need 0 <= q_lens[s] <= seq_lens[s] for every sequence")
+    cu = torch.zeros(base.num_seqs + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(ql, 0).to(torch.int32)
+    g = torch.Generator(device=base.q.device)
+    g.manual_seed(int(seed) + 7919)
+    base.q = torch.randn(int(cu[-1]), num_heads, HEAD_DIM, generator=g,
+                         device=base.q.device).to(torch.bfloat16)
+    base.cu_seqlens_q = cu.to(base.q.device)
+    return base
 
 
 # ----------------------------------------------------------------------------
