@@ -73,6 +73,11 @@ def make_workload(name, device):
         hq, hkv, ctx, s = map(int, m.groups())
         return workloads.make_case(hq, hkv, [ctx] * s, seed=0, device=device, scale_mode="per_slot",
                                    name=name)
+    m = re.fullmatch(r"specdec_(\d+)x(\d+)_ctx(\d+)_s(\d+)_q(\d+)", name)
+    if m:
+        hq, hkv, ctx, s, ql = map(int, m.groups())
+        return workloads.make_multi_case(hq, hkv, [ctx] * s, [ql] * s, seed=0, device=device,
+                                         name=name)
     m = re.fullmatch(r"ragged_(\d+)x(\d+)_seed(\d+)", name)
     if m:
         hq, hkv, seed = map(int, m.groups())
@@ -85,31 +90,41 @@ def suite_names():
     names = [f"dense_{a}x{b}_ctx{c}_s{s}" for (a, b, s, c) in workloads.DENSE_1K + workloads.DENSE_4K]
     names += ["target", "dense_20x4_ctx4096_s256"]
     names += ["slotscales_40x8_ctx4096_s256"]
+    names += [f"specdec_40x8_ctx4096_s256_q{q}" for q in (2, 3, 4, 8)]
     names += [f"ragged_{a}x{b}_seed0" for (a, b) in workloads.RAGGED_LAYOUTS]
     names += [f"dense_{a}x{b}_ctx{c}_s{s}" for (a, b, s, c) in workloads.LOW_BATCH]
     return names
 
 
-def time_calls(case, steps, warmup, rotate=1):
-    """Average µs per call over `steps` back-to-back calls, HIP events on the launch stream."""
+def make_call(case, out, stream=None):
+    """One call of the entry point that serves `case` (per-tensor scales, per-slot
+    scales, or several queries per sequence), writing `out`."""
     import torch
     import paged_attention_decode_03_amd as pa
     dev = case.q.device
     ks = torch.tensor([case.k_scale], dtype=torch.float32, device=dev)
     vs = torch.tensor([case.v_scale], dtype=torch.float32, device=dev)
+    if case.k_slot_scales is not None:
+        return lambda: pa.paged_decode_attention_slot_scales(
+            case.q, case.k_cache, case.v_cache, case.block_tables, case.seq_lens, case.scale,
+            case.k_slot_scales, case.v_slot_scales, out=out, stream=stream)
+    if case.cu_seqlens_q is not None:
+        max_q = int((case.cu_seqlens_q[1:] - case.cu_seqlens_q[:-1]).max().item())
+        return lambda: pa.paged_multi_query_attention(
+            case.q, case.cu_seqlens_q, max_q, case.k_cache, case.v_cache, case.block_tables,
+            case.seq_lens, case.scale, ks, vs, out=out, stream=stream)
+    return lambda: pa.paged_decode_attention(case.q, case.k_cache, case.v_cache, case.block_tables,
+                                             case.seq_lens, case.scale, ks, vs, out=out,
+                                             stream=stream)
+
+
+def time_calls(case, steps, warmup):
+    """Average µs per call, HIP events recorded on the stream the kernels run on."""
+    import torch
+    dev = case.q.device
     out = torch.empty_like(case.q)
     stream = torch.cuda.Stream(dev)
-
-    def call():
-        if case.k_slot_scales is not None:
-            pa.paged_decode_attention_slot_scales(case.q, case.k_cache, case.v_cache,
-                                                  case.block_tables, case.seq_lens, case.scale,
-                                                  case.k_slot_scales, case.v_slot_scales,
-                                                  out=out, stream=stream)
-        else:
-            pa.paged_decode_attention(case.q, case.k_cache, case.v_cache, case.block_tables,
-                                      case.seq_lens, case.scale, ks, vs, out=out, stream=stream)
-
+    call = make_call(case, out, stream)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize(dev)
@@ -127,21 +142,9 @@ def time_graph(case, replays=50, calls_per_graph=10):
     """Average µs per call when `calls_per_graph` calls are captured in one HIP
     graph and the graph is replayed (the way the pages time impl.forward)."""
     import torch
-    import paged_attention_decode_03_amd as pa
     dev = case.q.device
-    ks = torch.tensor([case.k_scale], dtype=torch.float32, device=dev)
-    vs = torch.tensor([case.v_scale], dtype=torch.float32, device=dev)
     out = torch.empty_like(case.q)
-
-    def call():
-        if case.k_slot_scales is not None:
-            pa.paged_decode_attention_slot_scales(case.q, case.k_cache, case.v_cache,
-                                                  case.block_tables, case.seq_lens, case.scale,
-                                                  case.k_slot_scales, case.v_slot_scales, out=out)
-        else:
-            pa.paged_decode_attention(case.q, case.k_cache, case.v_cache, case.block_tables,
-                                      case.seq_lens, case.scale, ks, vs, out=out)
-
+    call = make_call(case, out)
     stream = torch.cuda.Stream(dev)
     stream.wait_stream(torch.cuda.current_stream(dev))
     with torch.cuda.stream(stream):
@@ -285,11 +288,13 @@ def main():
             b = case.algorithmic_bytes()
             if case.k_slot_scales is not None:
                 b += case.kv_bytes() // 128 * 4   # one fp32 K or V scale per cached token and kv head
-            print(json.dumps({"workload": name, "us_per_call": round(us, 2),
-                              "us_per_call_graph": round(us_graph, 2),
-                              "GBps": round(b / us / 1e3, 1), "frac_of_peak": round(b / us / 1e3 / PEAK_GBS, 4),
-                              "bytes": b, "partitions": P, "pages_per_partition": ppp}),
-                  file=sys.stderr, flush=True)
+            row = {"workload": name, "us_per_call": round(us, 2),
+                   "us_per_call_graph": round(us_graph, 2),
+                   "GBps": round(b / us / 1e3, 1), "frac_of_peak": round(b / us / 1e3 / PEAK_GBS, 4),
+                   "bytes": b}
+            if case.cu_seqlens_q is None:   # the exported planner covers one query per sequence
+                row.update({"partitions": P, "pages_per_partition": ppp})
+            print(json.dumps(row), file=sys.stderr, flush=True)
             del case
             torch.cuda.empty_cache()
         for name, T, pre in (("cache_write_decode_256x8", 256, False),

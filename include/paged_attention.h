@@ -107,6 +107,37 @@ int paged_decode_attention_split(const void* q, const void* k_cache, const void*
                                  void* out, void* stream, int32_t pages_per_partition);
 
 /*
+ * Attention of several new query tokens per sequence over the paged cache,
+ * causal (the multi-token form of the operation: API page
+ * vllm.v1.attention.backends.rocm_aiter_unified_attn,
+ * RocmAiterUnifiedAttentionImpl.forward with cu_seqlens_q / query_start_loc,
+ * max_seqlen_q, seqused_k and causal=True; the new tokens' K/V are already in
+ * the cache, e.g. written by paged_kv_cache_write).
+ *
+ * Sequence s owns query rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1: its q_len
+ * newest tokens.  Query i of a sequence with n = seq_lens[s] tokens sits at
+ * position n - q_len + i and attends to cache tokens 0 .. n - q_len + i.
+ *
+ *   q, out          bf16 [num_q_tokens][num_heads][head_size], dense
+ *   cu_seqlens_q    int32 [num_seqs + 1], device: cu[0] = 0, cu[num_seqs] = num_q_tokens,
+ *                   non-decreasing
+ *   max_seqlen_q    host bound on every q_len (the plan is sized from it; queries past it
+ *                   are not computed); 0 < q_len <= seq_lens[s] is the caller's contract
+ *                   (a query that would see no token gets zeros)
+ * Each work item holds floor(16 / group) query tokens of one sequence (all the
+ * group's heads for each), so the kernel is at its best for short q_len
+ * (speculative or mixed decode); K/V are read once per query tile.  Other
+ * arguments, scales, plan, scratch and errors as for paged_decode_attention.
+ */
+int paged_multi_query_attention(const void* q, const int32_t* cu_seqlens_q, int32_t num_q_tokens,
+                                int32_t max_seqlen_q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, const int32_t* seq_lens,
+                                int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
+                                int64_t num_blocks, float scale, const float* k_scale,
+                                const float* v_scale, void* out, void* stream);
+
+/*
  * paged_decode_attention with per-slot dequantisation scales: one fp32 K scale
  * and one V scale per (block, kv head, slot) instead of one per tensor (the
  * tables the asm decode of the vLLM pull request lishuoshuo-amd/vllm #3 reads,

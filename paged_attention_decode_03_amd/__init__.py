@@ -67,6 +67,9 @@ def load_library():
     lib.paged_decode_attention_split.restype = ctypes.c_int
     lib.paged_decode_attention_slot_scales.argtypes = common
     lib.paged_decode_attention_slot_scales.restype = ctypes.c_int
+    lib.paged_multi_query_attention.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, i32,
+                                                i32, i32, i64, f32, vp, vp, vp, vp]
+    lib.paged_multi_query_attention.restype = ctypes.c_int
     lib.pa_decode_plan.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(i32),
                                    ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_size_t)]
     lib.pa_decode_plan.restype = ctypes.c_int
@@ -102,9 +105,12 @@ def _scale_tensor(x, device):
     return torch.tensor([float(x)], dtype=torch.float32, device=device)
 
 
-def _args(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale, v_scale, out, stream):
+def _args(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale, v_scale, out, stream,
+          q_rows_free=False):
+    """Validate and marshal the shared arguments.  With q_rows_free, q's first
+    dimension counts query tokens and need not equal num_seqs."""
     if q.dtype != torch.bfloat16 or q.dim() != 3:
-        raise TypeError("q must be a bfloat16 tensor [num_seqs, num_heads, head_size]")
+        raise TypeError("q must be a bfloat16 tensor [rows, num_heads, head_size]")
     dev = q.device
     if dev.type != "cuda":
         raise TypeError("tensors must be on a GPU")
@@ -127,7 +133,8 @@ def _args(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale, v_scale, 
         raise TypeError("seq_lens must be int32 [num_seqs] on the q device")
     if not (q.is_contiguous() and block_tables.is_contiguous() and seq_lens.is_contiguous()):
         raise ValueError("q, block_tables and seq_lens must be contiguous")
-    S, Hq, D = q.shape
+    _, Hq, D = q.shape
+    S = seq_lens.shape[0] if q_rows_free else q.shape[0]
     NB, Hkv = k_cache.shape[:2]
     bs = k_cache.shape[3]
     if k_cache.shape[2] * k_cache.shape[4] != D or v_cache.shape[2] != D or v_cache.shape[3] != bs:
@@ -192,6 +199,29 @@ def paged_decode_attention_slot_scales(q, k_cache, v_cache, block_tables, seq_le
     c_args = c_args[:13] + (_ptr(k_slot_scales), _ptr(v_slot_scales)) + c_args[15:]
     with torch.cuda.device(dev):
         _check(lib.paged_decode_attention_slot_scales(*c_args))
+    return out
+
+
+def paged_multi_query_attention(q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache, block_tables,
+                                seq_lens, scale, k_scale, v_scale, out=None, stream=None):
+    """Causal attention of several new query tokens per sequence.
+
+    q: bfloat16 [num_q_tokens, num_heads, head_size]; cu_seqlens_q: int32
+    [num_seqs + 1] row offsets on the q device; max_seqlen_q: host int bounding
+    every sequence's query count.  Other arguments as paged_decode_attention.
+    """
+    lib = load_library()
+    dev, out, c_args, keep = _args(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale,
+                                   v_scale, out, stream, q_rows_free=True)
+    S = c_args[5]
+    if (cu_seqlens_q.dtype != torch.int32 or tuple(cu_seqlens_q.shape) != (S + 1,)
+            or cu_seqlens_q.device != dev or not cu_seqlens_q.is_contiguous()):
+        raise TypeError("cu_seqlens_q must be a contiguous int32 [num_seqs + 1] tensor on the q device")
+    (_, kc, vc, bt, sl, _, Hq, Hkv, D, bs, W, NB, sc, ks, vs, _, handle) = c_args
+    with torch.cuda.device(dev):
+        _check(lib.paged_multi_query_attention(
+            _ptr(q), _ptr(cu_seqlens_q), q.shape[0], int(max_seqlen_q), kc, vc, bt, sl, S, Hq,
+            Hkv, D, bs, W, NB, sc, ks, vs, _ptr(out), handle))
     return out
 
 

@@ -56,7 +56,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // with partitions of at least kMinPagesPerPart blocks, whole pipeline stages,
 // and never more than pa::kMaxPagesPerPart blocks.
 int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t W, int32_t num_cus, int32_t ppp_req,
-              Plan* plan) {
+              Plan* plan, int32_t q_tiles = 1, int64_t q_rows = -1) {
   if (S < 0 || Hq <= 0 || Hkv <= 0 || W < 0 || ppp_req < 0)
     return fail(PA_ERR_SHAPE, "plan: negative or zero size (S=%d Hq=%d Hkv=%d W=%d ppp=%d)", S, Hq,
                 Hkv, W, ppp_req);
@@ -65,7 +65,7 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t W, int32_t num_cus, in
   if (ppp_req > 0) {
     ppp = ppp_req < Wc ? ppp_req : Wc;
   } else {
-    const int64_t items = (int64_t)(S > 0 ? S : 1) * Hkv;
+    const int64_t items = (int64_t)(S > 0 ? S : 1) * Hkv * (q_tiles > 0 ? q_tiles : 1);
     const int64_t target = (int64_t)(num_cus > 0 ? num_cus : kDefaultCUs) * kWavesPerCU / 4;
     int64_t parts = ceil_div(target, items);
     if (parts > Wc) parts = Wc;
@@ -80,8 +80,9 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t W, int32_t num_cus, in
   const int64_t parts = ceil_div(Wc, ppp);
   plan->num_parts = (int32_t)parts;
   plan->pages_per_part = (int32_t)ppp;
+  const int64_t rows = q_rows >= 0 ? q_rows : S;
   plan->workspace_bytes =
-      parts > 1 ? (size_t)S * Hq * parts * (pa::kHeadDim + 2) * sizeof(float) : 0;
+      parts > 1 ? (size_t)rows * Hq * parts * (pa::kHeadDim + 2) * sizeof(float) : 0;
   return PA_OK;
 }
 
@@ -147,7 +148,8 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
            const int32_t* seq_lens, int32_t S, int32_t Hq, int32_t Hkv, int32_t head_size,
            int32_t block_size, int32_t W, int64_t NB, float scale, const float* k_scale,
            const float* v_scale, void* out, void* stream_ptr, int32_t ppp_req,
-           bool slot_scales = false) {
+           bool slot_scales = false, const int32_t* cu_seqlens_q = nullptr, int32_t num_q_rows = 0,
+           int32_t max_seqlen_q = 1) {
   g_last_error[0] = '\0';
   if (head_size != pa::kHeadDim)
     return fail(PA_ERR_UNSUPPORTED, "head_size %d unsupported (only %d)", head_size, pa::kHeadDim);
@@ -166,18 +168,24 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
     return fail(PA_ERR_UNSUPPORTED, "group size %d exceeds %d query heads per kv head", G,
                 pa::kMaxGroup);
   if (!isfinite(scale)) return fail(PA_ERR_SHAPE, "scale is not finite");
-  if (S == 0) return PA_OK;
+  const bool mq = cu_seqlens_q != nullptr;
+  if (mq && (num_q_rows < 0 || max_seqlen_q < 0))
+    return fail(PA_ERR_SHAPE, "negative num_q_tokens or max_seqlen_q");
+  if (S == 0 || (mq && num_q_rows == 0)) return PA_OK;
+  if (mq && max_seqlen_q == 0)
+    return fail(PA_ERR_SHAPE, "max_seqlen_q must be positive when there are query tokens");
   if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !k_scale || !v_scale || !out)
     return fail(PA_ERR_NULL, "a required pointer is NULL");
   if (W == 0 || NB == 0)
     return fail(PA_ERR_SHAPE, "max_blocks_per_seq and num_blocks must be positive when num_seqs > 0");
 
-  const size_t q_bytes = (size_t)S * Hq * pa::kHeadDim * 2;
+  const size_t q_bytes = (size_t)(mq ? num_q_rows : S) * Hq * pa::kHeadDim * 2;
   const size_t cache_bytes = (size_t)NB * Hkv * pa::kPageBytes;
   if (overlaps(out, q_bytes, q, q_bytes) || overlaps(out, q_bytes, k_cache, cache_bytes) ||
       overlaps(out, q_bytes, v_cache, cache_bytes) ||
       overlaps(out, q_bytes, block_tables, (size_t)S * W * 4) ||
       overlaps(out, q_bytes, seq_lens, (size_t)S * 4) || overlaps(out, q_bytes, k_scale, 4) ||
+      (mq && overlaps(out, q_bytes, cu_seqlens_q, (size_t)(S + 1) * 4)) ||
       overlaps(out, q_bytes, v_scale, 4))
     return fail(PA_ERR_ALIAS, "out overlaps an input");
   if (slot_scales && (overlaps(out, q_bytes, k_scale, (size_t)NB * Hkv * 64) ||
@@ -192,9 +200,19 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   // --- past this point HIP is called
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice failed");
+  // query tokens per work item: as many as the 16 MFMA columns hold with the group
+  const int32_t q_tile = mq ? (pa::kMaxGroup / G > 0 ? pa::kMaxGroup / G : 1) : 1;
+  const int32_t q_tiles = mq ? (max_seqlen_q + q_tile - 1) / q_tile : 1;
   Plan plan;
-  int rc = make_plan(S, Hq, Hkv, W, device_cus(dev), ppp_req, &plan);
+  int rc = make_plan(S, Hq, Hkv, W, device_cus(dev), ppp_req, &plan, q_tiles, mq ? num_q_rows : S);
   if (rc) return rc;
+  // one 64-lane block per work item, 256 lanes per merged row: keep both grids
+  // within 2^32 lanes
+  const int64_t items = (int64_t)S * Hkv * plan.num_parts * q_tiles;
+  const int64_t merge_rows = (int64_t)(mq ? num_q_rows : S) * Hq;
+  if (items > (int64_t(1) << 26) || merge_rows > (int64_t(1) << 24))
+    return fail(PA_ERR_UNSUPPORTED, "launch too large: %lld work items, %lld merged rows",
+                (long long)items, (long long)merge_rows);
   hipStream_t stream = (hipStream_t)stream_ptr;
 
   pa::DecodeParams p;
@@ -218,12 +236,16 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   p.num_parts = plan.num_parts;
   p.pages_per_part = plan.pages_per_part;
   p.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  p.cu_seqlens_q = cu_seqlens_q;
+  p.num_q_rows = mq ? num_q_rows : S;
+  p.q_tile = q_tile;
+  p.num_q_tiles = q_tiles;
   if (plan.workspace_bytes) {
     void* ws = nullptr;
     rc = ensure_workspace(dev, plan.workspace_bytes, stream, true, &ws);
     if (rc) return rc;
     p.part_acc = (float*)ws;
-    p.part_ml = (float*)ws + (size_t)S * Hq * plan.num_parts * pa::kHeadDim;
+    p.part_ml = (float*)ws + (size_t)p.num_q_rows * Hq * plan.num_parts * pa::kHeadDim;
   }
   const hipError_t err = pa::launch_decode(p, stream);
   if (err != hipSuccess) return fail(PA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
@@ -255,6 +277,22 @@ int paged_decode_attention_split(const void* q, const void* k_cache, const void*
   return decode(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads, num_kv_heads,
                 head_size, block_size, max_blocks_per_seq, num_blocks, scale, k_scale, v_scale, out,
                 stream, pages_per_partition);
+}
+
+int paged_multi_query_attention(const void* q, const int32_t* cu_seqlens_q, int32_t num_q_tokens,
+                                int32_t max_seqlen_q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, const int32_t* seq_lens,
+                                int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
+                                int64_t num_blocks, float scale, const float* k_scale,
+                                const float* v_scale, void* out, void* stream) {
+  if (!cu_seqlens_q && num_seqs > 0) return fail(PA_ERR_NULL, "cu_seqlens_q is NULL");
+  if (num_seqs > 0 && num_q_tokens > 0 && ((uintptr_t)cu_seqlens_q & 3))
+    return fail(PA_ERR_SHAPE, "misaligned cu_seqlens_q (4 B)");
+  return decode(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads, num_kv_heads,
+                head_size, block_size, max_blocks_per_seq, num_blocks, scale, k_scale, v_scale, out,
+                stream, 0, false, cu_seqlens_q, num_q_tokens,
+                max_seqlen_q);
 }
 
 int paged_decode_attention_slot_scales(const void* q, const void* k_cache, const void* v_cache,

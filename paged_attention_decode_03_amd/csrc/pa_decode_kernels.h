@@ -34,6 +34,11 @@ struct DecodeParams {
   int32_t num_parts;         // P, partitions per sequence
   int32_t pages_per_part;    // blocks per partition
   float scale_log2e;         // softmax scale * log2(e)
+  // several query tokens per sequence (null cu_seqlens_q: one per sequence)
+  const int32_t* cu_seqlens_q;  // [S + 1] query row offsets
+  int32_t num_q_rows;        // cu_seqlens_q[S]: rows of q and out
+  int32_t q_tile;            // query tokens per work item (columns = q_tile * group <= 16)
+  int32_t num_q_tiles;       // query tiles per sequence (from the host's max_seqlen_q)
 };
 
 // Enqueue the decode (and, when num_parts > 1, the merge) on `stream`.

@@ -124,7 +124,12 @@ struct Stage {
 // exact power of two, 2^-e with e the exponent of the item's first V scale,
 // and the epilogue divides it out exactly.  (Scales more than 2^14 above the
 // first one would saturate the fp16 weights.)
-template <int PPS, int NB, bool SS>
+// MQ: several query tokens per sequence (rows cu_seqlens_q[s] ..), causal.  The
+// 16 MFMA columns then hold (query token, head) pairs: q_tile tokens of the
+// tile times the group's heads.  Query i of a sequence with L tokens and q_len
+// queries sees tokens 0 .. L - q_len + i, so a tile's context ends at its last
+// query's position and the tokens past each column's own position are masked.
+template <int PPS, int NB, bool SS, bool MQ>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU))) void pa_decode_kernel(const DecodeParams p) {
   const int lane = threadIdx.x;
   const int col = lane & 15;  // MFMA column (query head in group); K load row (token)
@@ -132,15 +137,31 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
 
   const int item = blockIdx.x;
   const int part = item % p.num_parts;
-  const int sk = item / p.num_parts;
-  const int kvh = sk % p.num_kv_heads;
-  const int s = sk / p.num_kv_heads;
+  int rest = item / p.num_parts;
+  int qt = 0;  // query tile
+  if constexpr (MQ) {
+    qt = rest % p.num_q_tiles;
+    rest /= p.num_q_tiles;
+  }
+  const int kvh = rest % p.num_kv_heads;
+  const int s = rest / p.num_kv_heads;
   const int ppp = p.pages_per_part;
   const int pbeg = part * ppp;  // < max_blocks: the planner never makes an empty partition range
 
-  const int h = kvh * p.group + col;
-  const bool hvalid = col < p.group;
-  const size_t orow = ((size_t)s * p.num_heads + h) * kHeadDim;
+  // column -> (query token of the tile, head of the group)
+  int qi = 0, g = col, q0 = s, q_len = 1;
+  if constexpr (MQ) {
+    qi = col / p.group;
+    g = col - qi * p.group;
+    q0 = scalar_load(p.cu_seqlens_q + s);
+    q_len = scalar_load(p.cu_seqlens_q + s + 1) - q0;
+    if (qt * p.q_tile >= q_len) return;  // no query of this sequence in this tile
+  }
+  const int h = kvh * p.group + g;
+  const int qrow = q0 + qt * p.q_tile + qi;  // row of q and out
+  const bool hvalid = MQ ? (col < p.q_tile * p.group && qt * p.q_tile + qi < q_len && qrow >= 0 && qrow < p.num_q_rows)
+                          : col < p.group;
+  const size_t orow = ((size_t)qrow * p.num_heads + h) * kHeadDim;
 
   // Start the three independent reads of the prologue together: this
   // partition's slice of the block-table row (its length is not known yet, so
@@ -171,7 +192,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
         qop[h2][c] = bf16x8{};
   }
 
-  const int L = clamp_len(scalar_load(p.seq_lens + s), p.max_blocks);
+  const int Lseq = clamp_len(scalar_load(p.seq_lens + s), p.max_blocks);
+  // tokens this item's queries can see: all of them for one query per sequence;
+  // up to the tile's last query's position otherwise
+  int L = Lseq, pos_first = Lseq - 1, pos_col = Lseq - 1;
+  if constexpr (MQ) {
+    const int base = Lseq - q_len;  // position of query 0 minus 0
+    L = max(0, min(Lseq, base + min(qt * p.q_tile + p.q_tile, q_len)));
+    pos_first = base + qt * p.q_tile;
+    pos_col = hvalid ? base + qt * p.q_tile + qi : L - 1;
+  }
   const int npages = (L + kBlockTokens - 1) / kBlockTokens;
   const int nused = (npages + ppp - 1) / ppp;  // partitions holding tokens
   if (part > 0 && part >= nused) return;
@@ -188,6 +218,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
 
   const int pend = min(pbeg + ppp, npages);
   const int tend = min(L, pend * kBlockTokens);  // first token this item must not use
+  // several queries: first token this column must not use (its own causal end)
+  const int tlim = MQ ? min(tend, pos_col + 1) : tend;
 
   // logits in log2 units: z * scale * k_scale * log2(e) (k_scale per slot when SS)
   const float c_log2 = SS ? p.scale_log2e : p.scale_log2e * scalar_load(p.k_scale);
@@ -276,6 +308,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
 
   auto compute = [&](const Stage<PPS>& st, int stage, bool last) {
     const int j0 = pbeg + stage * PPS;
+    // columns with their own causal end: the stages reaching past the tile's first position
+    const bool causal = MQ && (j0 + PPS) * kBlockTokens > pos_first + 1;
     f32x4 z[PPS];
 #pragma unroll
     for (int pp = 0; pp < PPS; ++pp) {
@@ -296,9 +330,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
       for (int i = 0; i < 4; ++i) {
         float v = z[pp][i] * c_log2;
         if constexpr (SS) v *= __uint_as_float(st.ks[pp][i]);
-        if (last) {
+        if (last || causal) {
           const int t = (j0 + pp) * kBlockTokens + rq * 4 + i;
-          v = (t < tend) ? v : -INFINITY;
+          v = (t < tlim) ? v : -INFINITY;
         }
         z[pp][i] = v;
         mx = fmaxf(mx, v);
@@ -348,7 +382,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
       } else {
         f16x4 pb;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pb[i] = (_Float16)__builtin_amdgcn_exp2f(z[pp][i] - m_run);
+        for (int i = 0; i < 4; ++i) {
+          // a column that has seen no token yet has m_run = -inf: its weights are 0
+          float e = __builtin_amdgcn_exp2f(z[pp][i] - m_run);
+          if constexpr (MQ) e = (z[pp][i] == -INFINITY) ? 0.0f : e;
+          pb[i] = (_Float16)e;
+        }
 #pragma unroll
         for (int jd = 0; jd < 8; ++jd)
           acc[jd] = __builtin_amdgcn_mfma_f32_16x16x16f16(fp8x4_to_f16(st.v[pp][jd] & vmask), pb, acc[jd], 0, 0, 0);
@@ -374,7 +413,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
   if (!hvalid) return;
   const float lsum = accl[0];
   if (direct) {
-    const float inv = (SS ? vnorm_inv : scalar_load(p.v_scale)) / lsum;
+    // several queries: lsum is 0 for a query that sees no token (more queries than context)
+    const float inv = (!MQ || lsum > 0.0f) ? (SS ? vnorm_inv : scalar_load(p.v_scale)) / lsum : 0.0f;
     uint16_t* o = p.out + orow + rq * 4;
 #pragma unroll
     for (int jd = 0; jd < 8; ++jd) {
@@ -382,7 +422,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
       *(uint2*)(o + jd * 16) = make_uint2(pack_bf16x2(a[0] * inv, a[1] * inv), pack_bf16x2(a[2] * inv, a[3] * inv));
     }
   } else {
-    const size_t prow = ((size_t)s * p.num_heads + h) * p.num_parts + part;
+    const size_t prow = ((size_t)qrow * p.num_heads + h) * p.num_parts + part;
     float* a = p.part_acc + prow * kHeadDim + rq * 4;
 #pragma unroll
     for (int jd = 0; jd < 8; ++jd) *(f32x4*)(a + jd * 16) = acc[jd] * vnorm_inv;
@@ -406,9 +446,26 @@ __device__ __forceinline__ float wave_max(float x) {
 
 __global__ __launch_bounds__(kMergeThreads) void pa_merge_kernel(const DecodeParams p) {
   const int t = threadIdx.x;
-  const int sh = blockIdx.x;
-  const int s = sh / p.num_heads;
-  const int L = clamp_len(scalar_load(p.seq_lens + s), p.max_blocks);
+  const int sh = blockIdx.x;  // (query row, head)
+  const int r = sh / p.num_heads;
+  int s = r, L = 0;
+  if (p.cu_seqlens_q) {
+    // the row's sequence: last s with cu_seqlens_q[s] <= r
+    int lo = 0, hi = p.num_seqs;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (scalar_load(p.cu_seqlens_q + mid) <= r) lo = mid; else hi = mid;
+    }
+    s = lo;
+    const int q0 = scalar_load(p.cu_seqlens_q + s);
+    const int q_len = scalar_load(p.cu_seqlens_q + s + 1) - q0;
+    const int Lseq = clamp_len(scalar_load(p.seq_lens + s), p.max_blocks);
+    const int qt = (r - q0) / p.q_tile;
+    if (qt >= p.num_q_tiles) return;  // past max_seqlen_q: not computed
+    L = max(0, min(Lseq, Lseq - q_len + min(qt * p.q_tile + p.q_tile, q_len)));
+  } else {
+    L = clamp_len(scalar_load(p.seq_lens + s), p.max_blocks);
+  }
   const int npages = (L + kBlockTokens - 1) / kBlockTokens;
   const int nused = (npages + p.pages_per_part - 1) / p.pages_per_part;
   if (nused <= 1) return;  // uniform over the block
@@ -434,8 +491,8 @@ __global__ __launch_bounds__(kMergeThreads) void pa_merge_kernel(const DecodePar
   float den = 0.f;
 #pragma unroll 4
   for (int i = pl; i < nused; i += 8) {
-    const float2 m_l = ml[i];  // every partition in use holds >= 1 token: m is finite
-    const float w = __builtin_amdgcn_exp2f(m_l.x - M);
+    const float2 m_l = ml[i];  // m = -inf (l = 0) for a causal query that saw none of it
+    const float w = m_l.x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_l.x - M);
     const float4 a = acc[(size_t)i * (kHeadDim / 4)];
     den += w * m_l.y;
     num.x += w * a.x;
@@ -458,7 +515,7 @@ __global__ __launch_bounds__(kMergeThreads) void pa_merge_kernel(const DecodePar
       n.w += a.w;
       dsum += red_den[k];
     }
-    const float inv = (p.v_slot_scales ? 1.0f : scalar_load(p.v_scale)) / dsum;
+    const float inv = dsum > 0.0f ? (p.v_slot_scales ? 1.0f : scalar_load(p.v_scale)) / dsum : 0.0f;
     *(uint2*)(p.out + (size_t)sh * kHeadDim + 4 * t) =
         make_uint2(pack_bf16x2(n.x * inv, n.y * inv), pack_bf16x2(n.z * inv, n.w * inv));
   }
@@ -467,16 +524,20 @@ __global__ __launch_bounds__(kMergeThreads) void pa_merge_kernel(const DecodePar
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
-  const size_t items = (size_t)p.num_seqs * p.num_kv_heads * p.num_parts;
-  if (p.k_slot_scales)
-    hipLaunchKernelGGL((pa_decode_kernel<kSlotScalePagesPerStage, kRingDepth, true>), dim3((unsigned)items),
+  const size_t items = (size_t)p.num_seqs * p.num_kv_heads * p.num_parts * (p.cu_seqlens_q ? p.num_q_tiles : 1);
+  if (p.cu_seqlens_q)
+    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, true>), dim3((unsigned)items),
                        dim3(64), 0, stream, p);
+  else if (p.k_slot_scales)
+    hipLaunchKernelGGL((pa_decode_kernel<kSlotScalePagesPerStage, kRingDepth, true, false>),
+                       dim3((unsigned)items), dim3(64), 0, stream, p);
   else
-    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false>), dim3((unsigned)items), dim3(64),
-                       0, stream, p);
-  if (p.num_parts > 1)
-    hipLaunchKernelGGL(pa_merge_kernel, dim3((unsigned)((size_t)p.num_seqs * p.num_heads)),
-                       dim3(kMergeThreads), 0, stream, p);
+    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false>), dim3((unsigned)items),
+                       dim3(64), 0, stream, p);
+  const size_t rows = p.cu_seqlens_q ? (size_t)p.num_q_rows : (size_t)p.num_seqs;
+  if (p.num_parts > 1 && rows > 0)
+    hipLaunchKernelGGL(pa_merge_kernel, dim3((unsigned)(rows * p.num_heads)), dim3(kMergeThreads), 0, stream,
+                       p);
   return hipGetLastError();
 }
 

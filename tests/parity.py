@@ -9,7 +9,8 @@ import torch
 
 import oracle
 
-# Bound for bf16 output against the fp64 oracle: max abs 1e-2, mean abs 5e-4.
+# Bound for bf16 output against the fp64 oracle: max abs 1e-2, mean abs 5e-4
+# (how it is applied where bf16 rounding alone exceeds it: see compare).
 MAX_ABS = 1e-2
 MEAN_ABS = 5e-4
 
@@ -45,14 +46,25 @@ def run_oracle(case, seqs=None):
                          h.scale, h.k_scale, h.v_scale)
 
 
+def bf16_ulp(x):
+    """Spacing of bf16 values at |x| (8 significant bits; subnormals at 2^-133)."""
+    a = np.maximum(np.abs(x), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - 7)
+
+
 def compare(gpu_out, ref, label, seqs=None, max_abs=MAX_ABS, mean_abs=MEAN_ABS, relative=False):
     """Check bf16 GPU output against the fp64 oracle.
 
-    The bound (max abs <= 1e-2, mean abs <= 5e-4) is applied to |gpu - oracle|
-    wherever a bf16 output can meet it at all, i.e. wherever the correctly
-    rounded oracle output does; it is always applied to |gpu - bf16(oracle)|,
-    the distance from the best bf16 answer.  (Short contexts with |out| near 1,
-    such as a one-token sequence, have a bf16 rounding floor above 5e-4 mean.)
+    Max bound, element by element: |gpu - oracle| <= 1e-2 wherever a bf16
+    value can meet it at all (wherever the correctly rounded oracle does);
+    where none can (|out| >= 4, half a bf16 step is above 1e-2) the output
+    must be one of the two bf16 neighbours of the exact value, i.e. less than
+    one bf16 step away from it.
+    Mean bound: mean |gpu - bf16(oracle)| <= 5e-4 always (error beyond the
+    correctly rounded answer), and mean |gpu - oracle| <= 5e-4 where bf16
+    rounding itself takes at most half of that budget (short contexts with
+    |out| near 1, such as one-token sequences or the first queries of a new
+    sequence, have a rounding floor near or above 5e-4 mean).
 
     relative=True (workloads whose outputs are far larger than N(0,1) data's,
     e.g. per-token magnitudes spread over 2^8): every error is divided by
@@ -67,18 +79,23 @@ def compare(gpu_out, ref, label, seqs=None, max_abs=MAX_ABS, mean_abs=MEAN_ABS, 
     rne = oracle.bf16_bits_to_f64(oracle.bf16_rne(ref))
     floor = np.abs(rne - ref)
     err_rne = np.abs(g - rne)
-    if relative:
-        denom = np.maximum(1.0, np.abs(ref))
-        err, floor, err_rne = err / denom, floor / denom, err_rne / denom
-    log(f"[{label}]{' (relative)' if relative else ''} vs fp64: max={err.max():.3e} mean={err.mean():.3e} | "
-        f"vs bf16(oracle): max={err_rne.max():.3e} mean={err_rne.mean():.3e} | "
-        f"bf16 floor: max={floor.max():.3e} mean={floor.mean():.3e} | n={err.size}")
-    assert err_rne.max() <= max_abs, f"{label}: max error vs bf16(oracle) {err_rne.max():.3e} > {max_abs}"
-    assert err_rne.mean() <= mean_abs, f"{label}: mean error vs bf16(oracle) {err_rne.mean():.3e} > {mean_abs}"
-    if floor.max() <= max_abs:
-        assert err.max() <= max_abs, f"{label}: max abs error {err.max():.3e} > {max_abs}"
-    if floor.mean() <= mean_abs:
-        assert err.mean() <= mean_abs, f"{label}: mean abs error {err.mean():.3e} > {mean_abs}"
+    ulp = bf16_ulp(ref)
+    denom = np.maximum(1.0, np.abs(ref)) if relative else np.ones_like(ref)
+    err_s, floor_s, err_rne_s = err / denom, floor / denom, err_rne / denom
+    reach = floor_s <= max_abs
+    log(f"[{label}]{' (relative)' if relative else ''} vs fp64: max={err_s.max():.3e} mean={err_s.mean():.3e} | "
+        f"vs bf16(oracle): max={err_rne_s.max():.3e} mean={err_rne_s.mean():.3e} | "
+        f"bf16 floor: max={floor_s.max():.3e} mean={floor_s.mean():.3e} | "
+        f"beyond reach of 1e-2: {int((~reach).sum())} | n={err.size}")
+    over = reach & (err_s > max_abs)
+    assert not over.any(), \
+        f"{label}: {int(over.sum())} errors above {max_abs} (worst {err_s[reach].max():.3e})"
+    far = ~reach & (err >= ulp)
+    assert not far.any(), f"{label}: {int(far.sum())} outputs not a bf16 neighbour of the exact value"
+    assert err_rne_s.mean() <= mean_abs, \
+        f"{label}: mean error vs bf16(oracle) {err_rne_s.mean():.3e} > {mean_abs}"
+    if floor_s.mean() <= mean_abs / 2:
+        assert err_s.mean() <= mean_abs, f"{label}: mean abs error {err_s.mean():.3e} > {mean_abs}"
     return err
 
 

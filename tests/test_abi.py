@@ -29,7 +29,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("paged_decode_attention", "paged_decode_attention_split", "pa_decode_plan",
               "pa_decode_reserve_workspace", "paged_kv_cache_write",
-              "paged_decode_attention_slot_scales", "pa_last_error"):
+              "paged_decode_attention_slot_scales", "paged_multi_query_attention",
+              "pa_last_error"):
         assert n in names
 
 
@@ -137,3 +138,21 @@ def test_slot_scale_decode_checks_its_tables(lib):
     assert lib.paged_decode_attention_slot_scales(*args(0, FAKE * 80)) == -1
     assert lib.paged_decode_attention_slot_scales(*args(FAKE * 80 + 4, FAKE * 90)) == -2
     assert lib.paged_decode_attention_slot_scales(*args(FAKE * 64 + 256, FAKE * 90)) == -4
+
+
+def mq(lib, cu=FAKE * 70, T=6, maxq=4, S=2, out=FAKE * 64):
+    vp = ctypes.c_void_p
+    return lib.paged_multi_query_attention(vp(FAKE), vp(cu), T, maxq, vp(FAKE * 16), vp(FAKE * 32),
+                                           vp(FAKE * 48), vp(FAKE * 50), S, 8, 2, 128, 16, 4, 16,
+                                           ctypes.c_float(0.088), vp(FAKE * 52), vp(FAKE * 53),
+                                           vp(out), None)
+
+
+def test_multi_query_argument_checks(lib):
+    assert mq(lib, cu=0) == -1
+    assert mq(lib, cu=FAKE * 70 + 2) == -2
+    assert mq(lib, T=-1) == -2
+    assert mq(lib, maxq=0) == -2
+    assert mq(lib, out=FAKE * 70) == -4          # out over cu_seqlens_q
+    assert mq(lib, T=0) == 0
+    assert mq(lib, S=0, cu=0) == 0

@@ -54,7 +54,7 @@ class Case:
 
     @property
     def num_seqs(self) -> int:
-        return self.q.shape[0]
+        return self.seq_lens.shape[0]
 
     @property
     def num_heads(self) -> int:
@@ -89,12 +89,16 @@ class Case:
         return int(self.seq_lens.to(torch.int64).sum().item()) * self.num_kv_heads * HEAD_DIM * 2
 
     def algorithmic_bytes(self) -> int:
-        """Bytes the method must move: K+V fp8 of every cached token, q in and
-        out as bf16, the block-table entries in use, seq_lens and the scales."""
+        """Bytes the method must move: K+V fp8 of every cached token (once), q in
+        and out as bf16 for every query row, the block-table entries in use,
+        seq_lens, the query row offsets when there are several queries per
+        sequence, and the scales."""
         lens = self.seq_lens.to(torch.int64)
         table = int(((lens + BLOCK - 1) // BLOCK).sum().item()) * 4
-        qo = 2 * self.num_seqs * self.num_heads * HEAD_DIM * 2
-        return self.kv_bytes() + qo + table + 4 * self.num_seqs + 8
+        rows = self.q.shape[0]
+        qo = 2 * rows * self.num_heads * HEAD_DIM * 2
+        cu = 0 if self.cu_seqlens_q is None else 4 * (self.num_seqs + 1)
+        return self.kv_bytes() + qo + table + 4 * self.num_seqs + cu + 8
 
 
 def _quantise(x: torch.Tensor, scale_mode: str):
