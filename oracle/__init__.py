@@ -58,6 +58,10 @@ def _load():
     lib.pa_oracle_decode_partitioned.restype = i32
     lib.pa_oracle_decode_slot_scales.argtypes = [P, P, P, P, P, i32, i32, i32, i32, f32, P, P, P, i32]
     lib.pa_oracle_decode_slot_scales.restype = i32
+    lib.pa_oracle_decode_strided.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_int64,
+                                             ctypes.c_int64, P, P, i32, i32, i32, i32, f32, f32,
+                                             f32, P, i32]
+    lib.pa_oracle_decode_strided.restype = i32
     lib.pa_oracle_attend_multi.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, f32, f32, f32, P, i32]
     lib.pa_oracle_attend_multi.restype = i32
     lib.pa_oracle_fp8_e4m3fn_encode.argtypes = [ctypes.c_float]
@@ -142,6 +146,48 @@ def decode(q_bits, k_cache, v_cache, block_tables, seq_lens, scale, k_scale,
         q_bits.ctypes.data, k_cache.ctypes.data, v_cache.ctypes.data, bt.ctypes.data,
         sl.ctypes.data, S, Hq, Hkv, W, float(scale), float(k_scale), float(v_scale),
         out.ctypes.data, int(nt))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return out
+
+
+def decode_strided(q_bits, k_buf, v_buf, block_stride, token_stride, head_stride, num_kv_heads,
+                   block_tables, seq_lens, scale, k_scale, v_scale,
+                   num_threads: int | None = None) -> np.ndarray:
+    """fp64 paged decode attention over a token-row cache layout.
+
+    k_buf / v_buf: uint8 buffers starting at the K / V base; token t of kv head
+    k in physical block p has its 128 fp8 dims at byte
+    p * block_stride + (t % 16) * token_stride + k * head_stride.
+    Returns float64 [S, Hq, 128]."""
+    q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    k_buf = np.ascontiguousarray(np.asarray(k_buf).reshape(-1), dtype=np.uint8)
+    v_buf = np.ascontiguousarray(np.asarray(v_buf).reshape(-1), dtype=np.uint8)
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    if q_bits.ndim != 3 or q_bits.shape[2] != 128 or bt.ndim != 2 or sl.shape != (q_bits.shape[0],):
+        raise ValueError("q [S, Hq, 128], block_tables [S, W], seq_lens [S] expected")
+    S, Hq, _ = q_bits.shape
+    W = bt.shape[1]
+    Hkv = int(num_kv_heads)
+    need = 0
+    for s in range(S):
+        n = int(sl[s])
+        if n < 0 or n > 16 * W:
+            raise ValueError("seq_lens out of range")
+        if n:
+            pmax = int(bt[s, :(n + 15) // 16].max())
+            if int(bt[s, :(n + 15) // 16].min()) < 0:
+                raise ValueError("negative block id in use")
+            need = max(need, pmax * block_stride + 15 * token_stride + (Hkv - 1) * head_stride + 128)
+    if need > min(k_buf.size, v_buf.size):
+        raise ValueError("a block in use lies past the end of a cache buffer")
+    out = np.zeros((S, Hq, 128), dtype=np.float64)
+    nt = num_threads if num_threads else (os.cpu_count() or 1)
+    rc = _load().pa_oracle_decode_strided(
+        q_bits.ctypes.data, k_buf.ctypes.data, v_buf.ctypes.data, int(block_stride),
+        int(token_stride), int(head_stride), bt.ctypes.data, sl.ctypes.data, S, Hq, Hkv, W,
+        float(scale), float(k_scale), float(v_scale), out.ctypes.data, int(nt))
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (code {rc})")
     return out

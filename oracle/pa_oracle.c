@@ -56,6 +56,16 @@
  * with n = seq_lens[s] tokens sits at position n - q_len + i and sees tokens
  * 0 .. n - q_len + i.  q_len > n is a caller error (return -5).
  *
+ * Token-row cache layouts (pa_oracle_decode_strided): the same quantity with
+ * each token's 128 dims stored contiguously, as the flash-style caches of the
+ * API page's unified backend keep them (the forward docstring's
+ * [num_blocks, 2, block_size, num_kv_heads, head_size]; _split_kv_cache's
+ * views of the packed (blocks, heads, tokens, 2 * head_size) and of the
+ * shuffled (2, blocks, tokens, heads, head_size) caches).  With byte strides
+ * for block, token and kv head (dims contiguous):
+ *   K_t[e] = fp8(k_cache[p_t * block_stride + j * token_stride + k * head_stride + e]) * k_scale
+ *   V_t[e] = fp8(v_cache[p_t * block_stride + j * token_stride + k * head_stride + e]) * v_scale
+ *
  * Cache write (pa_oracle_cache_write): the step that fills the cache the
  * decode reads (API page, do_kv_cache_update: new tokens' key and value, the
  * two caches, slot_mapping and the per-tensor k/v scales go to the cache
@@ -143,11 +153,15 @@ uint16_t pa_oracle_bf16_rne(double x) {
 }
 
 /* Dequantisation scales: one per tensor, or (when the tables are not NULL) one
- * per (block, kv head, slot) from tables [num_blocks][num_kv_heads][16]. */
+ * per (block, kv head, slot) from tables [num_blocks][num_kv_heads][16].
+ * token_rows != 0 selects the token-row layout with the three byte strides
+ * instead of the page layout. */
 typedef struct {
   double k_scale, v_scale;
   const float* k_slot;
   const float* v_slot;
+  int token_rows;
+  int64_t block_stride, token_stride, head_stride;
 } scales_t;
 
 /* Gather + dequantise token t of sequence s for kv head k (one row of K and V). */
@@ -160,6 +174,14 @@ static void load_token(const uint8_t* k_cache, const uint8_t* v_cache,
   if (sc->k_slot) {
     k_scale = sc->k_slot[(p * num_kv_heads + k) * PA_BLOCK + j];
     v_scale = sc->v_slot[(p * num_kv_heads + k) * PA_BLOCK + j];
+  }
+  if (sc->token_rows) {
+    const int64_t row = p * sc->block_stride + j * sc->token_stride + k * sc->head_stride;
+    for (int e = 0; e < PA_HEAD_DIM; ++e) {
+      K[e] = pa_oracle_fp8_e4m3fn(k_cache[row + e]) * k_scale;
+      V[e] = pa_oracle_fp8_e4m3fn(v_cache[row + e]) * v_scale;
+    }
+    return;
   }
   const uint8_t* kpage = k_cache + (p * num_kv_heads + k) * (int64_t)(PA_HEAD_DIM * PA_BLOCK);
   const uint8_t* vpage = v_cache + (p * num_kv_heads + k) * (int64_t)(PA_HEAD_DIM * PA_BLOCK);
@@ -236,6 +258,18 @@ int pa_oracle_decode(const uint16_t* q_bits, const uint8_t* k_cache,
                      float scale, float k_scale, float v_scale, double* out,
                      int num_threads) {
   const scales_t sc = {k_scale, v_scale, NULL, NULL};
+  return decode_impl(q_bits, k_cache, v_cache, block_tables, seq_lens, S, Hq, Hkv, W, scale, &sc,
+                     out, num_threads);
+}
+
+/* pa_oracle_decode over a token-row cache layout (byte strides; dims contiguous). */
+int pa_oracle_decode_strided(const uint16_t* q_bits, const uint8_t* k_cache,
+                             const uint8_t* v_cache, int64_t block_stride, int64_t token_stride,
+                             int64_t head_stride, const int32_t* block_tables,
+                             const int32_t* seq_lens, int S, int Hq, int Hkv, int W, float scale,
+                             float k_scale, float v_scale, double* out, int num_threads) {
+  if (block_stride <= 0 || token_stride <= 0 || head_stride <= 0) return -4;
+  const scales_t sc = {k_scale, v_scale, NULL, NULL, 1, block_stride, token_stride, head_stride};
   return decode_impl(q_bits, k_cache, v_cache, block_tables, seq_lens, S, Hq, Hkv, W, scale, &sc,
                      out, num_threads);
 }

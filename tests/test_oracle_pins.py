@@ -431,3 +431,75 @@ def test_multi_rejects_more_queries_than_context(oracle_lib):
         oracle.attend_multi(case.q_bits(), case.cu_seqlens_q.numpy(), case.k_cache.numpy(),
                             case.v_cache.numpy(), case.block_tables.numpy(), bad.numpy(),
                             case.scale, case.k_scale, case.v_scale)
+
+
+# --------------------------------------------------------------------------
+# Token-row cache layouts (each token's 128 dims contiguous, byte strides for
+# block, token and kv head): the flash-style caches of the unified backend.
+
+def run_strided(case, layout):
+    kv, vv = workloads.token_row_views(case, layout)
+    kb, ks = workloads.strided_buffer(kv)
+    vb, vs = workloads.strided_buffer(vv)
+    assert ks == vs
+    return oracle.decode_strided(case.q_bits(), kb, vb, *ks, case.num_kv_heads,
+                                 case.block_tables.numpy(), case.seq_lens.numpy(), case.scale,
+                                 case.k_scale, case.v_scale)
+
+
+@pytest.mark.parametrize("layout", workloads.TOKEN_ROW_LAYOUTS)
+@pytest.mark.parametrize("case", list(small_cases())[:5], ids=lambda c: c.name)
+def test_token_row_layouts_reproduce_page_layout(oracle_lib, case, layout):
+    """The same cache bytes re-laid by torch permutes give the page-layout
+    oracle's result bit for bit (same loads, same order of operations)."""
+    assert np.array_equal(run_strided(case, layout), run_oracle(case))
+
+
+@pytest.mark.parametrize("hq,hkv,lens", [(8, 2, [1, 17, 33, 64]), (12, 4, [100, 3, 257, 0])])
+def test_token_row_layout_matches_sdpa_on_nhd_gather(oracle_lib, hq, hkv, lens):
+    """K/V gathered straight from the [blocks, 16, kv_heads, 128] tensor by
+    numpy indexing, decoded by torch, fp64 SDPA: an independent route."""
+    case = workloads.make_case(hq, hkv, lens, seed=hq + hkv, extra_blocks=3)
+    kv, vv = workloads.token_row_views(case, "nhd")
+    ours = run_strided(case, "nhd")
+    G = hq // hkv
+    q = case.q.to(torch.float64)
+    for s, L in enumerate(lens):
+        if L == 0:
+            assert not ours[s].any()
+            continue
+        t = np.arange(L)
+        blocks = case.block_tables.numpy()[s, t // 16]
+        kb = kv.numpy()[blocks, t % 16]          # [L, Hkv, 128]
+        vb = vv.numpy()[blocks, t % 16]
+        K = torch.from_numpy(np.ascontiguousarray(kb)).view(torch.float8_e4m3fn).double() * case.k_scale
+        V = torch.from_numpy(np.ascontiguousarray(vb)).view(torch.float8_e4m3fn).double() * case.v_scale
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q[s][:, None, :].contiguous(), K.permute(1, 0, 2).repeat_interleave(G, 0).contiguous(),
+            V.permute(1, 0, 2).repeat_interleave(G, 0).contiguous(), scale=case.scale)[:, 0]
+        np.testing.assert_allclose(ours[s], ref.numpy(), rtol=0, atol=1e-12)
+
+
+def test_token_row_strides_select_the_right_bytes(oracle_lib):
+    """Exchanging the token and kv-head strides of an NHD view reads other
+    tokens' bytes: the result must change (the strides are really used)."""
+    case = workloads.make_case(8, 2, [40, 33], seed=91)
+    kv, vv = workloads.token_row_views(case, "nhd")
+    kb, (bs, ts, hs) = workloads.strided_buffer(kv)
+    vb, _ = workloads.strided_buffer(vv)
+    assert (ts, hs) == (256, 128)
+    args = (case.block_tables.numpy(), case.seq_lens.numpy(), case.scale, case.k_scale, case.v_scale)
+    good = oracle.decode_strided(case.q_bits(), kb, vb, bs, ts, hs, 2, *args)
+    assert np.array_equal(good, run_oracle(case))
+    wrong = oracle.decode_strided(case.q_bits(), kb, vb, bs, hs, ts, 2, *args)
+    assert not np.allclose(wrong, good)
+
+
+def test_token_row_buffer_too_small_is_rejected(oracle_lib):
+    case = workloads.make_case(8, 2, [40], seed=92)
+    kv, vv = workloads.token_row_views(case, "nhd")
+    kb, st = workloads.strided_buffer(kv)
+    vb, _ = workloads.strided_buffer(vv)
+    with pytest.raises(ValueError):
+        oracle.decode_strided(case.q_bits(), kb[:100], vb, *st, 2, case.block_tables.numpy(),
+                              case.seq_lens.numpy(), case.scale, case.k_scale, case.v_scale)

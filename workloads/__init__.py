@@ -241,6 +241,42 @@ def make_multi_case(num_heads: int, num_kv_heads: int, seq_lens, q_lens, seed: i
 
 
 # ----------------------------------------------------------------------------
+# The same cache bytes in token-row layouts (each token's 128 dims contiguous),
+# as the flash-style caches of the unified backend keep them.
+
+TOKEN_ROW_LAYOUTS = ("nhd", "combined", "packed")
+
+
+def token_row_views(case, layout: str = "nhd"):
+    """(k_view, v_view), each [num_blocks, 16, num_kv_heads, 128] uint8 with a
+    contiguous last dim, holding exactly the bytes of case.k_cache / v_cache:
+      nhd       two tensors [NB, 16, Hkv, 128];
+      combined  one tensor [NB, 2, 16, Hkv, 128], K at [:, 0], V at [:, 1];
+      packed    one tensor [NB, Hkv, 16, 256] (K then V per token), viewed
+                through transpose(1, 2) and a split of the last dim."""
+    NB, Hkv = case.k_cache.shape[:2]
+    k_nhd = case.k_cache.permute(0, 3, 1, 2, 4).reshape(NB, BLOCK, Hkv, HEAD_DIM).contiguous()
+    v_nhd = case.v_cache.reshape(NB, Hkv, HEAD_DIM, BLOCK).permute(0, 3, 1, 2).contiguous()
+    if layout == "nhd":
+        return k_nhd, v_nhd
+    if layout == "combined":
+        kv = torch.stack([k_nhd, v_nhd], dim=1).contiguous()
+        return kv[:, 0], kv[:, 1]
+    if layout == "packed":
+        kv = torch.cat([k_nhd.permute(0, 2, 1, 3), v_nhd.permute(0, 2, 1, 3)], dim=-1).contiguous()
+        t = kv.transpose(1, 2)
+        return t[..., :HEAD_DIM], t[..., HEAD_DIM:]
+    raise ValueError(layout)
+
+
+def strided_buffer(view: torch.Tensor):
+    """(uint8 numpy array of the storage from the view's first byte,
+    (block_stride, token_stride, head_stride) in bytes) of a CPU token-row view."""
+    flat = torch.empty(0, dtype=torch.uint8).set_(view.untyped_storage())
+    return flat[view.storage_offset():].numpy(), tuple(int(x) for x in view.stride()[:3])
+
+
+# ----------------------------------------------------------------------------
 # The named workloads (token counts, head layouts, batch sizes).
 
 def tiny(seed: int = 0, device="cpu") -> Case:
