@@ -73,6 +73,13 @@ def make_workload(name, device):
         hq, hkv, ctx, s = map(int, m.groups())
         return workloads.make_case(hq, hkv, [ctx] * s, seed=0, device=device, scale_mode="per_slot",
                                    name=name)
+    m = re.fullmatch(r"tokenrows_(nhd|combined|packed)_(\d+)x(\d+)_ctx(\d+)_s(\d+)", name)
+    if m:
+        layout = m.group(1)
+        hq, hkv, ctx, s = map(int, m.groups()[1:])
+        case = workloads.dense(hq, hkv, s, ctx, seed=0, device=device)
+        case.token_rows = workloads.token_row_views(case, layout)
+        return case
     m = re.fullmatch(r"specdec_(\d+)x(\d+)_ctx(\d+)_s(\d+)_q(\d+)", name)
     if m:
         hq, hkv, ctx, s, ql = map(int, m.groups())
@@ -91,6 +98,7 @@ def suite_names():
     names += ["target", "dense_20x4_ctx4096_s256"]
     names += ["slotscales_40x8_ctx4096_s256"]
     names += [f"specdec_40x8_ctx4096_s256_q{q}" for q in (2, 3, 4, 8)]
+    names += [f"tokenrows_{lay}_40x8_ctx4096_s256" for lay in ("nhd", "packed")]
     names += [f"ragged_{a}x{b}_seed0" for (a, b) in workloads.RAGGED_LAYOUTS]
     names += [f"dense_{a}x{b}_ctx{c}_s{s}" for (a, b, s, c) in workloads.LOW_BATCH]
     return names
@@ -108,6 +116,11 @@ def make_call(case, out, stream=None):
         return lambda: pa.paged_decode_attention_slot_scales(
             case.q, case.k_cache, case.v_cache, case.block_tables, case.seq_lens, case.scale,
             case.k_slot_scales, case.v_slot_scales, out=out, stream=stream)
+    if getattr(case, "token_rows", None) is not None:
+        kv, vv = case.token_rows
+        return lambda: pa.paged_decode_attention_nhd(case.q, kv, vv, case.block_tables,
+                                                     case.seq_lens, case.scale, ks, vs, out=out,
+                                                     stream=stream)
     if case.cu_seqlens_q is not None:
         max_q = int((case.cu_seqlens_q[1:] - case.cu_seqlens_q[:-1]).max().item())
         return lambda: pa.paged_multi_query_attention(

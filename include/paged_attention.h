@@ -138,6 +138,31 @@ int paged_multi_query_attention(const void* q, const int32_t* cu_seqlens_q, int3
                                 const float* v_scale, void* out, void* stream);
 
 /*
+ * paged_decode_attention over a token-row cache layout: each token's 128 fp8
+ * dims are contiguous, and blocks, tokens and kv heads are reached by byte
+ * strides (the flash-style caches of the API page
+ * vllm.v1.attention.backends.rocm_aiter_unified_attn: the forward docstring's
+ * [num_blocks, 2, block_size, num_kv_heads, head_size], and the
+ * [blocks, tokens, kv_heads, head_size] views _split_kv_cache takes of the
+ * packed and shuffled caches).  Token j of kv head k in physical block p:
+ *   K bytes at k_cache + p * block_stride + j * token_stride + k * head_stride,
+ *   V bytes at v_cache + the same offset.
+ *   k_cache, v_cache   device, 16-byte aligned (K and V may share one allocation)
+ *   block_stride, token_stride, head_stride
+ *                      bytes, positive multiples of 16, token_stride <= 2^26
+ * Same result as paged_decode_attention on the same bytes in the page layout
+ * (bit for bit: the same arithmetic in the same order).  Other arguments, plan,
+ * scratch and errors as for paged_decode_attention.
+ */
+int paged_decode_attention_nhd(const void* q, const void* k_cache, const void* v_cache,
+                               int64_t block_stride, int64_t token_stride, int64_t head_stride,
+                               const int32_t* block_tables, const int32_t* seq_lens,
+                               int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                               int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
+                               int64_t num_blocks, float scale, const float* k_scale,
+                               const float* v_scale, void* out, void* stream);
+
+/*
  * paged_decode_attention with per-slot dequantisation scales: one fp32 K scale
  * and one V scale per (block, kv head, slot) instead of one per tensor (the
  * tables the asm decode of the vLLM pull request lishuoshuo-amd/vllm #3 reads,

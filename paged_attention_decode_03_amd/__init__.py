@@ -27,7 +27,7 @@ import torch
 __all__ = [
     "paged_decode_attention", "paged_decode_attention_split", "pa_decode_plan",
     "pa_decode_reserve_workspace", "paged_kv_cache_write", "paged_decode_attention_slot_scales",
-    "pa_last_error",
+    "paged_multi_query_attention", "paged_decode_attention_nhd", "pa_last_error",
     "PagedAttentionError", "library_path",
     "load_library",
 ]
@@ -70,6 +70,9 @@ def load_library():
     lib.paged_multi_query_attention.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, i32,
                                                 i32, i32, i64, f32, vp, vp, vp, vp]
     lib.paged_multi_query_attention.restype = ctypes.c_int
+    lib.paged_decode_attention_nhd.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i32, i32, i32,
+                                               i32, i32, i32, i64, f32, vp, vp, vp, vp]
+    lib.paged_decode_attention_nhd.restype = ctypes.c_int
     lib.pa_decode_plan.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(i32),
                                    ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_size_t)]
     lib.pa_decode_plan.restype = ctypes.c_int
@@ -106,7 +109,7 @@ def _scale_tensor(x, device):
 
 
 def _args(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale, v_scale, out, stream,
-          q_rows_free=False):
+          q_rows_free=False, cache_contiguous=True):
     """Validate and marshal the shared arguments.  With q_rows_free, q's first
     dimension counts query tokens and need not equal num_seqs."""
     if q.dtype != torch.bfloat16 or q.dim() != 3:
@@ -117,7 +120,7 @@ def _args(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale, v_scale, 
     for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
         if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
             raise TypeError(f"{name} must be uint8 or float8_e4m3fn")
-        if t.device != dev or not t.is_contiguous():
+        if t.device != dev or (cache_contiguous and not t.is_contiguous()):
             raise ValueError(f"{name} must be contiguous and on {dev}")
     if k_cache.dim() != 5:
         raise ValueError("k_cache must be [num_blocks, num_kv_heads, head_size/16, 16, 16]")
@@ -222,6 +225,41 @@ def paged_multi_query_attention(q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache,
         _check(lib.paged_multi_query_attention(
             _ptr(q), _ptr(cu_seqlens_q), q.shape[0], int(max_seqlen_q), kc, vc, bt, sl, S, Hq,
             Hkv, D, bs, W, NB, sc, ks, vs, _ptr(out), handle))
+    return out
+
+
+def paged_decode_attention_nhd(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale,
+                               v_scale, out=None, stream=None):
+    """paged_decode_attention over token-row caches.
+
+    k_cache, v_cache: uint8 or float8_e4m3fn views [num_blocks, 16, num_kv_heads,
+    128] with a contiguous last dim and the same strides (e.g. the two halves
+    of a [num_blocks, 2, 16, num_kv_heads, 128] tensor, or of a packed
+    [num_blocks, num_kv_heads, 16, 256] tensor seen through transpose(1, 2)).
+    """
+    lib = load_library()
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn) or t.dim() != 4 or t.stride(3) != 1:
+            raise TypeError(f"{name} must be a uint8/float8_e4m3fn [blocks, 16, kv_heads, 128] "
+                            "view with a contiguous last dim")
+        if t.device != q.device:
+            raise ValueError(f"{name} must be on {q.device}")
+    if k_cache.shape != v_cache.shape or k_cache.stride() != v_cache.stride():
+        raise ValueError("k_cache and v_cache must have the same shape and strides")
+    NB, bs, Hkv, D = k_cache.shape
+    # marshal the shared arguments through page-shaped stand-ins of the same sizes
+    kstand = torch.empty((1,), dtype=torch.uint8, device=q.device).as_strided(
+        (NB, Hkv, D // 16, bs, 16), (0, 0, 0, 0, 0))
+    vstand = torch.empty((1,), dtype=torch.uint8, device=q.device).as_strided(
+        (NB, Hkv, D, bs), (0, 0, 0, 0))
+    dev, out, c_args, keep = _args(q, kstand, vstand, block_tables, seq_lens, scale, k_scale,
+                                   v_scale, out, stream, cache_contiguous=False)
+    (qp, _, _, bt, sl, S, Hq, Hkv_, D_, bs_, W, NB_, sc, ks, vs, op, handle) = c_args
+    st = k_cache.stride()
+    with torch.cuda.device(dev):
+        _check(lib.paged_decode_attention_nhd(
+            qp, _ptr(k_cache), _ptr(v_cache), st[0], st[1], st[2], bt, sl, S, Hq, Hkv_, D_, bs_, W,
+            NB_, sc, ks, vs, op, handle))
     return out
 
 

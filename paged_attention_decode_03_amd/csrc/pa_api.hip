@@ -144,12 +144,25 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return na && nb && a0 < b0 + nb && b0 < a0 + na;
 }
 
+// What a call reads beyond the plain decode's arguments.
+struct Variant {
+  bool slot_scales = false;                // k_scale / v_scale are [NB][Hkv][16] tables
+  const int32_t* cu_seqlens_q = nullptr;   // several queries per sequence
+  int32_t num_q_rows = 0;
+  int32_t max_seqlen_q = 1;
+  bool token_rows = false;                 // token-row cache layout with byte strides
+  int64_t block_stride = 0, token_stride = 0, head_stride = 0;
+};
+
 int decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
            const int32_t* seq_lens, int32_t S, int32_t Hq, int32_t Hkv, int32_t head_size,
            int32_t block_size, int32_t W, int64_t NB, float scale, const float* k_scale,
            const float* v_scale, void* out, void* stream_ptr, int32_t ppp_req,
-           bool slot_scales = false, const int32_t* cu_seqlens_q = nullptr, int32_t num_q_rows = 0,
-           int32_t max_seqlen_q = 1) {
+           const Variant& var = Variant()) {
+  const bool slot_scales = var.slot_scales;
+  const int32_t* cu_seqlens_q = var.cu_seqlens_q;
+  const int32_t num_q_rows = var.num_q_rows;
+  const int32_t max_seqlen_q = var.max_seqlen_q;
   g_last_error[0] = '\0';
   if (head_size != pa::kHeadDim)
     return fail(PA_ERR_UNSUPPORTED, "head_size %d unsupported (only %d)", head_size, pa::kHeadDim);
@@ -180,7 +193,18 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
     return fail(PA_ERR_SHAPE, "max_blocks_per_seq and num_blocks must be positive when num_seqs > 0");
 
   const size_t q_bytes = (size_t)(mq ? num_q_rows : S) * Hq * pa::kHeadDim * 2;
-  const size_t cache_bytes = (size_t)NB * Hkv * pa::kPageBytes;
+  size_t cache_bytes = (size_t)NB * Hkv * pa::kPageBytes;
+  if (var.token_rows) {
+    const int64_t bs = var.block_stride, ts = var.token_stride, hs = var.head_stride;
+    if (bs <= 0 || ts <= 0 || hs <= 0 || (bs | ts | hs) & 15)
+      return fail(PA_ERR_SHAPE, "token-row strides must be positive multiples of 16 bytes "
+                                "(block %lld, token %lld, head %lld)",
+                  (long long)bs, (long long)ts, (long long)hs);
+    if (ts > (int64_t(1) << 26))
+      return fail(PA_ERR_UNSUPPORTED, "token stride %lld exceeds 2^26 bytes", (long long)ts);
+    // bytes from the cache base to the end of the last block's last row
+    cache_bytes = (size_t)((NB - 1) * bs + (pa::kBlockTokens - 1) * ts + (Hkv - 1) * hs + pa::kHeadDim);
+  }
   if (overlaps(out, q_bytes, q, q_bytes) || overlaps(out, q_bytes, k_cache, cache_bytes) ||
       overlaps(out, q_bytes, v_cache, cache_bytes) ||
       overlaps(out, q_bytes, block_tables, (size_t)S * W * 4) ||
@@ -191,6 +215,8 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   if (slot_scales && (overlaps(out, q_bytes, k_scale, (size_t)NB * Hkv * 64) ||
                       overlaps(out, q_bytes, v_scale, (size_t)NB * Hkv * 64)))
     return fail(PA_ERR_ALIAS, "out overlaps a scale table");
+  if (var.token_rows && ((uintptr_t)v_cache & 15))
+    return fail(PA_ERR_SHAPE, "misaligned v_cache (token rows: 16 B)");
   if (((uintptr_t)q & 15) || ((uintptr_t)k_cache & 15) || ((uintptr_t)v_cache & 3) ||
       ((uintptr_t)out & 7) || ((uintptr_t)block_tables & 3) || ((uintptr_t)seq_lens & 3))
     return fail(PA_ERR_SHAPE, "misaligned pointer (q, k_cache: 16 B; out: 8 B; others: 4 B)");
@@ -208,7 +234,8 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   if (rc) return rc;
   // one 64-lane block per work item, 256 lanes per merged row: keep both grids
   // within 2^32 lanes
-  const int64_t items = (int64_t)S * Hkv * plan.num_parts * q_tiles;
+  const int64_t units = (int64_t)S * Hkv * plan.num_parts;
+  const int64_t items = mq ? (units + 7) / 8 * 8 * q_tiles : units;
   const int64_t merge_rows = (int64_t)(mq ? num_q_rows : S) * Hq;
   if (items > (int64_t(1) << 26) || merge_rows > (int64_t(1) << 24))
     return fail(PA_ERR_UNSUPPORTED, "launch too large: %lld work items, %lld merged rows",
@@ -240,6 +267,10 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   p.num_q_rows = mq ? num_q_rows : S;
   p.q_tile = q_tile;
   p.num_q_tiles = q_tiles;
+  p.token_rows = var.token_rows ? 1 : 0;
+  p.block_stride = var.block_stride;
+  p.token_stride = var.token_stride;
+  p.head_stride = var.head_stride;
   if (plan.workspace_bytes) {
     void* ws = nullptr;
     rc = ensure_workspace(dev, plan.workspace_bytes, stream, true, &ws);
@@ -289,10 +320,13 @@ int paged_multi_query_attention(const void* q, const int32_t* cu_seqlens_q, int3
   if (!cu_seqlens_q && num_seqs > 0) return fail(PA_ERR_NULL, "cu_seqlens_q is NULL");
   if (num_seqs > 0 && num_q_tokens > 0 && ((uintptr_t)cu_seqlens_q & 3))
     return fail(PA_ERR_SHAPE, "misaligned cu_seqlens_q (4 B)");
+  Variant mq;
+  mq.cu_seqlens_q = cu_seqlens_q;
+  mq.num_q_rows = num_q_tokens;
+  mq.max_seqlen_q = max_seqlen_q;
   return decode(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads, num_kv_heads,
                 head_size, block_size, max_blocks_per_seq, num_blocks, scale, k_scale, v_scale, out,
-                stream, 0, false, cu_seqlens_q, num_q_tokens,
-                max_seqlen_q);
+                stream, 0, mq);
 }
 
 int paged_decode_attention_slot_scales(const void* q, const void* k_cache, const void* v_cache,
@@ -302,9 +336,28 @@ int paged_decode_attention_slot_scales(const void* q, const void* k_cache, const
                                        int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
                                        const float* k_slot_scales, const float* v_slot_scales,
                                        void* out, void* stream) {
+  Variant ss;
+  ss.slot_scales = true;
   return decode(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads, num_kv_heads,
                 head_size, block_size, max_blocks_per_seq, num_blocks, scale, k_slot_scales,
-                v_slot_scales, out, stream, 0, true);
+                v_slot_scales, out, stream, 0, ss);
+}
+
+int paged_decode_attention_nhd(const void* q, const void* k_cache, const void* v_cache,
+                               int64_t block_stride, int64_t token_stride, int64_t head_stride,
+                               const int32_t* block_tables, const int32_t* seq_lens,
+                               int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                               int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
+                               int64_t num_blocks, float scale, const float* k_scale,
+                               const float* v_scale, void* out, void* stream) {
+  Variant tr;
+  tr.token_rows = true;
+  tr.block_stride = block_stride;
+  tr.token_stride = token_stride;
+  tr.head_stride = head_stride;
+  return decode(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads, num_kv_heads,
+                head_size, block_size, max_blocks_per_seq, num_blocks, scale, k_scale, v_scale, out,
+                stream, 0, tr);
 }
 
 int pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,

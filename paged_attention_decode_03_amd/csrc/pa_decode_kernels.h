@@ -39,6 +39,13 @@ struct DecodeParams {
   int32_t num_q_rows;        // cu_seqlens_q[S]: rows of q and out
   int32_t q_tile;            // query tokens per work item (columns = q_tile * group <= 16)
   int32_t num_q_tiles;       // query tiles per sequence (from the host's max_seqlen_q)
+  // token-row cache layout (token_rows != 0): token j of kv head k in block p
+  // has its 128 dims at p * block_stride + j * token_stride + k * head_stride
+  // bytes from k_cache / v_cache
+  int32_t token_rows;
+  int64_t block_stride;
+  int64_t token_stride;
+  int64_t head_stride;
 };
 
 // Enqueue the decode (and, when num_parts > 1, the merge) on `stream`.

@@ -28,6 +28,10 @@
 //   K: two fully coalesced 1 KiB dwordx4 loads per page (lane l: token l & 15,
 //      16-dim chunks l >> 4 and 4 + (l >> 4)),
 //   V: eight dword loads per page, each a contiguous 256 B (16 dims x 16 slots).
+// Token-row caches (TR: each token's 128 dims contiguous, the flash-style
+// layouts of the API page's unified backend) load K the same way (lane l:
+// 16 B chunks of token l & 15's row) and V as 32 B per lane of token rows;
+// a V page then passes through LDS, transposed into the dims x tokens operand.
 // Pages are software-pipelined PPS at a time, one stage ahead.
 #include <math.h>
 
@@ -47,6 +51,8 @@ typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 // of stages (depth - 1 stages are in flight while one is computed), waves per
 // SIMD the register budget is sized for, and the cache-policy bits of the K/V
 // loads (gfx950 buffer-load aux: 2 = nt, i.e. streamed once, not kept).
+// Several query tiles of one sequence read the same pages: their loads use the
+// default policy instead, so the pages stay in L2 for the other tiles.
 #ifndef PA_PAGES_PER_STAGE
 #define PA_PAGES_PER_STAGE 4
 #endif
@@ -129,20 +135,27 @@ struct Stage {
 // tile times the group's heads.  Query i of a sequence with L tokens and q_len
 // queries sees tokens 0 .. L - q_len + i, so a tile's context ends at its last
 // query's position and the tokens past each column's own position are masked.
-template <int PPS, int NB, bool SS, bool MQ>
+template <int PPS, int NB, bool SS, bool MQ, int AUX = PA_LOAD_AUX, bool TR = false>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU))) void pa_decode_kernel(const DecodeParams p) {
   const int lane = threadIdx.x;
   const int col = lane & 15;  // MFMA column (query head in group); K load row (token)
   const int rq = lane >> 4;   // row quad: rows 4*rq .. 4*rq+3 of the 16x16 tiles
 
-  const int item = blockIdx.x;
-  const int part = item % p.num_parts;
-  int rest = item / p.num_parts;
+  int item = blockIdx.x;
   int qt = 0;  // query tile
   if constexpr (MQ) {
-    qt = rest % p.num_q_tiles;
-    rest /= p.num_q_tiles;
+    // The query tiles of one (sequence, kv head, partition) read the same
+    // pages: place them 8 blocks apart, which puts them on one XCD (blocks go
+    // to the 8 XCDs round robin) at about the same time, so one tile's page
+    // reads are served by that XCD's L2 for the others.
+    const int xcd = item & 7;
+    const int r = item >> 3;
+    qt = r % p.num_q_tiles;
+    item = (r / p.num_q_tiles) * 8 + xcd;
+    if (item >= p.num_seqs * p.num_kv_heads * p.num_parts) return;  // grid padding
   }
+  const int part = item % p.num_parts;
+  int rest = item / p.num_parts;
   const int kvh = rest % p.num_kv_heads;
   const int s = rest / p.num_kv_heads;
   const int ppp = p.pages_per_part;
@@ -224,11 +237,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
   // logits in log2 units: z * scale * k_scale * log2(e) (k_scale per slot when SS)
   const float c_log2 = SS ? p.scale_log2e : p.scale_log2e * scalar_load(p.k_scale);
 
-  const size_t page_stride = (size_t)p.num_kv_heads * kPageBytes;
-  const uint8_t* kpage0 = p.k_cache + (size_t)kvh * kPageBytes;
-  const uint8_t* vpage0 = p.v_cache + (size_t)kvh * kPageBytes;
-  const int koff = lane * 16;            // K: token lane & 15, chunks lane >> 4 and 4 + (lane >> 4)
-  const int voff = col * 16 + rq * 4;    // V: dim col (+16 jd), slots 4 rq .. 4 rq + 3
+  const size_t page_stride = TR ? (size_t)p.block_stride : (size_t)p.num_kv_heads * kPageBytes;
+  const size_t head_off = TR ? (size_t)kvh * p.head_stride : (size_t)kvh * kPageBytes;
+  const uint8_t* kpage0 = p.k_cache + head_off;
+  const uint8_t* vpage0 = p.v_cache + head_off;
+  // K: token lane & 15, chunks lane >> 4 (koff) and 4 + (lane >> 4) (koff + khi)
+  const int tstride = TR ? (int)p.token_stride : 0;
+  const int koff = TR ? col * tstride + rq * 16 : lane * 16;
+  constexpr int khi = TR ? 64 : 1024;
+  // V: page layout: dim col (+16 jd), slots 4 rq .. 4 rq + 3 (one dword per jd);
+  // token rows: token lane >> 2, bytes 32 (lane & 3) .. +31 of its row
+  const int voff = TR ? (lane >> 2) * tstride + (lane & 3) * 32 : col * 16 + rq * 4;
+  // bytes a page's descriptor covers
+  const int page_bytes = TR ? (kBlockTokens - 1) * tstride + kHeadDim : kPageBytes;
 
   f32x4 acc[8];  // O^T tiles: dims 16*jd + 4*rq + i for head `col`
 #pragma unroll
@@ -255,6 +276,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
   }
   __syncthreads();
 
+  constexpr int kAux = AUX;
+  // Token rows: the stage's V pages pass through LDS, row j of page pp at
+  // vt + (pp * 16 + j) * kVRow.  Rows are 128 + 8 bytes apart so that the
+  // 4-byte column gathers below (4 rows x 16 columns x 4 row groups) hit
+  // distinct banks.
+  constexpr int kVRow = kHeadDim + 8;
+  __shared__ __attribute__((aligned(16))) uint8_t vt[TR ? PPS * kBlockTokens * kVRow : 16];
   auto load = [&](Stage<PPS>& st, int stage) {
     const int i0 = stage * PPS;
     int32_t pid[PPS];
@@ -280,7 +308,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
     }
 #pragma unroll
     for (int pp = 0; pp < PPS; ++pp) {
-      const int bytes = (i0 + pp < npg) ? kPageBytes : 0;
+      const int bytes = (i0 + pp < npg) ? page_bytes : 0;
       const size_t off = (size_t)__builtin_amdgcn_readfirstlane(pid[pp]) * page_stride;
       const __amdgpu_buffer_rsrc_t rk =
           __builtin_amdgcn_make_buffer_rsrc((void*)(kpage0 + off), (short)0, bytes, kRsrcWord3);
@@ -296,18 +324,48 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
         st.ks[pp] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rks, rq * 16, 0, 0));
         st.vs[pp] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rvs, rq * 16, 0, 0));
       }
-      st.k[pp][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, 0, PA_LOAD_AUX));
-      st.k[pp][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff + 1024, 0, PA_LOAD_AUX));
+      st.k[pp][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, 0, kAux));
+      st.k[pp][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff + khi, 0, kAux));
+      if constexpr (TR) {
 #pragma unroll
-      for (int jd = 0; jd < 8; ++jd)
-        st.v[pp][jd] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff + jd * 256, 0, PA_LOAD_AUX);
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff + 16 * h, 0, kAux));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) st.v[pp][4 * h + e] = w[e];
+        }
+      } else {
+#pragma unroll
+        for (int jd = 0; jd < 8; ++jd)
+          st.v[pp][jd] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff + jd * 256, 0, kAux);
+      }
     }
     // keep the scheduler from hoisting compute above these loads
     __builtin_amdgcn_sched_barrier(0);
   };
 
+  // PV operand: dims 16 jd + col, tokens 4 rq .. 4 rq + 3 of page pp (byte i = token 4 rq + i)
+  auto vword = [&](const Stage<PPS>& st, int pp, int jd) -> uint32_t {
+    if constexpr (TR) {
+      const uint8_t* b = vt + (pp * kBlockTokens + 4 * rq) * kVRow + 16 * jd + col;
+      return (uint32_t)b[0] | ((uint32_t)b[kVRow] << 8) | ((uint32_t)b[2 * kVRow] << 16) |
+             ((uint32_t)b[3 * kVRow] << 24);
+    } else {
+      return st.v[pp][jd];
+    }
+  };
+
   auto compute = [&](const Stage<PPS>& st, int stage, bool last) {
     const int j0 = pbeg + stage * PPS;
+    if constexpr (TR) {
+      __syncthreads();  // the previous stage's gathers from vt are done
+#pragma unroll
+      for (int pp = 0; pp < PPS; ++pp) {
+        uint8_t* dst = vt + (pp * kBlockTokens + (lane >> 2)) * kVRow + (lane & 3) * 32;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) *(uint2*)(dst + 8 * e) = make_uint2(st.v[pp][2 * e], st.v[pp][2 * e + 1]);
+      }
+      __syncthreads();
+    }
     // columns with their own causal end: the stages reaching past the tile's first position
     const bool causal = MQ && (j0 + PPS) * kBlockTokens > pos_first + 1;
     f32x4 z[PPS];
@@ -377,7 +435,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
         }
 #pragma unroll
         for (int jd = 0; jd < 8; ++jd)
-          acc[jd] = __builtin_amdgcn_mfma_f32_16x16x16f16(fp8x4_to_f16(st.v[pp][jd] & vmask), pv, acc[jd], 0, 0, 0);
+          acc[jd] = __builtin_amdgcn_mfma_f32_16x16x16f16(fp8x4_to_f16(vword(st, pp, jd) & vmask), pv, acc[jd], 0, 0, 0);
         accl = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pb, accl, 0, 0, 0);
       } else {
         f16x4 pb;
@@ -390,7 +448,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
         }
 #pragma unroll
         for (int jd = 0; jd < 8; ++jd)
-          acc[jd] = __builtin_amdgcn_mfma_f32_16x16x16f16(fp8x4_to_f16(st.v[pp][jd] & vmask), pb, acc[jd], 0, 0, 0);
+          acc[jd] = __builtin_amdgcn_mfma_f32_16x16x16f16(fp8x4_to_f16(vword(st, pp, jd) & vmask), pb, acc[jd], 0, 0, 0);
         accl = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pb, accl, 0, 0, 0);
       }
     }
@@ -524,8 +582,16 @@ __global__ __launch_bounds__(kMergeThreads) void pa_merge_kernel(const DecodePar
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
-  const size_t items = (size_t)p.num_seqs * p.num_kv_heads * p.num_parts * (p.cu_seqlens_q ? p.num_q_tiles : 1);
-  if (p.cu_seqlens_q)
+  const size_t units = (size_t)p.num_seqs * p.num_kv_heads * p.num_parts;
+  // several queries: units padded to a multiple of 8, times the query tiles
+  const size_t items = p.cu_seqlens_q ? (units + 7) / 8 * 8 * p.num_q_tiles : units;
+  if (p.token_rows)
+    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false, PA_LOAD_AUX, true>),
+                       dim3((unsigned)items), dim3(64), 0, stream, p);
+  else if (p.cu_seqlens_q && p.num_q_tiles > 1)
+    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, true, 0>), dim3((unsigned)items),
+                       dim3(64), 0, stream, p);
+  else if (p.cu_seqlens_q)
     hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, true>), dim3((unsigned)items),
                        dim3(64), 0, stream, p);
   else if (p.k_slot_scales)

@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     for n in ("paged_decode_attention", "paged_decode_attention_split", "pa_decode_plan",
               "pa_decode_reserve_workspace", "paged_kv_cache_write",
               "paged_decode_attention_slot_scales", "paged_multi_query_attention",
-              "pa_last_error"):
+              "paged_decode_attention_nhd", "pa_last_error"):
         assert n in names
 
 
@@ -156,3 +156,26 @@ def test_multi_query_argument_checks(lib):
     assert mq(lib, out=FAKE * 70) == -4          # out over cu_seqlens_q
     assert mq(lib, T=0) == 0
     assert mq(lib, S=0, cu=0) == 0
+
+
+def nhd(lib, k=FAKE * 16, v=FAKE * 32, bs=4096, ts=256, hs=128, out=FAKE * 64, NB=16, S=2):
+    vp = ctypes.c_void_p
+    return lib.paged_decode_attention_nhd(vp(FAKE), vp(k), vp(v), bs, ts, hs, vp(FAKE * 48),
+                                          vp(FAKE * 50), S, 8, 2, 128, 16, 4, NB,
+                                          ctypes.c_float(0.088), vp(FAKE * 52), vp(FAKE * 53),
+                                          vp(out), None)
+
+
+def test_token_row_decode_argument_checks(lib):
+    assert nhd(lib, bs=0) == -2
+    assert nhd(lib, ts=-256) == -2
+    assert nhd(lib, hs=136) == -2                      # not a multiple of 16
+    assert nhd(lib, ts=(1 << 26) + 16) == -3          # descriptor range
+    assert nhd(lib, v=FAKE * 32 + 8) == -2             # V rows need 16-byte alignment
+    assert nhd(lib, k=FAKE * 16 + 8) == -2
+    # out inside the K extent: 15 blocks * 4096 + 15 * 256 + 128 + 128 bytes from k
+    assert nhd(lib, out=FAKE * 16 + 15 * 4096 + 15 * 256) == -4
+    assert nhd(lib, S=0) == 0
+    # the page-layout extent would be 16 * 2 * 2048 = 64 KiB; a 1 MiB block stride
+    # reaches further, so an out 100 KiB past k overlaps only under token rows
+    assert nhd(lib, bs=1 << 20, out=FAKE * 16 + 100 * 1024) == -4
