@@ -34,7 +34,10 @@ int fail(int code, const char* fmt, ...) {
 }
 
 // Planner constants.
-constexpr int kWavesPerCU = 8;        // the decode kernel runs 2 waves per SIMD
+#ifndef PA_ITEMS_PER_CU
+#define PA_ITEMS_PER_CU 2
+#endif
+constexpr int kItemsPerCU = PA_ITEMS_PER_CU;  // work items the plan aims for, per CU
 constexpr int kDefaultCUs = 256;      // MI355X
 constexpr int kMinPagesPerPart = 8;   // shorter partitions cost more in start-up and merge than they gain
 constexpr int kStagePages = 4;        // the decode kernel loads 4 blocks per pipeline stage
@@ -66,7 +69,7 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t W, int32_t num_cus, in
     ppp = ppp_req < Wc ? ppp_req : Wc;
   } else {
     const int64_t items = (int64_t)(S > 0 ? S : 1) * Hkv * (q_tiles > 0 ? q_tiles : 1);
-    const int64_t target = (int64_t)(num_cus > 0 ? num_cus : kDefaultCUs) * kWavesPerCU / 4;
+    const int64_t target = (int64_t)(num_cus > 0 ? num_cus : kDefaultCUs) * kItemsPerCU;
     int64_t parts = ceil_div(target, items);
     if (parts > Wc) parts = Wc;
     ppp = ceil_div(Wc, parts < 1 ? 1 : parts);

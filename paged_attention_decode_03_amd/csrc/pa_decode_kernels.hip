@@ -491,16 +491,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
 // Log-sum-exp merge of the partitions of one (sequence, query head):
 //   M = max_p m_p,  w_p = 2^(m_p - M),  out = v_scale * sum_p w_p a_p / sum_p w_p l_p.
 // Sequences whose context fits one partition were finished by the decode kernel.
-// 256 threads: thread t owns dims 4*(t & 31) .. +3 of partitions p = t >> 5 (mod 8);
-// the eight partial sums are combined in LDS.
+// 256 threads: thread t owns dims 4*(t & 31) .. +3 of partitions p = t >> 5 (mod 8),
+// merged on the fly against a running max; the eight partial results are then
+// combined in LDS with the same formula.
 constexpr int kMergeThreads = 256;
-
-__device__ __forceinline__ float wave_max(float x) {
-  x = max_over_rows(x);  // lanes l, l^16, l^32, l^48
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
 
 __global__ __launch_bounds__(kMergeThreads) void pa_merge_kernel(const DecodeParams p) {
   const int t = threadIdx.x;
@@ -528,50 +522,66 @@ __global__ __launch_bounds__(kMergeThreads) void pa_merge_kernel(const DecodePar
   const int nused = (npages + p.pages_per_part - 1) / p.pages_per_part;
   if (nused <= 1) return;  // uniform over the block
 
-  __shared__ float red_max[kMergeThreads / 64];
+  __shared__ float red_max[8];
   __shared__ float4 red_acc[8][32];
   __shared__ float red_den[8];
 
-  const float2* ml = (const float2*)(p.part_ml + (size_t)sh * p.num_parts * 2);
-  float mx = -INFINITY;
-  for (int i = t; i < nused; i += kMergeThreads) mx = fmaxf(mx, ml[i].x);
-  mx = wave_max(mx);
-  if ((t & 63) == 0) red_max[t >> 6] = mx;
-  __syncthreads();
-  float M = red_max[0];
-#pragma unroll
-  for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, red_max[w]);
-
+  // Thread (pl, d4) folds partitions pl, pl + 8, ... into a running
+  // (max, numerator, denominator) as it goes, so all of its loads are
+  // independent of any reduction and issue together (one memory round trip).
   const int d4 = t & 31;
   const int pl = t >> 5;
+  const float2* ml = (const float2*)(p.part_ml + (size_t)sh * p.num_parts * 2);
   const float4* acc = (const float4*)(p.part_acc + (size_t)sh * p.num_parts * kHeadDim) + d4;
+  float m = -INFINITY;
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
   float den = 0.f;
-#pragma unroll 4
-  for (int i = pl; i < nused; i += 8) {
-    const float2 m_l = ml[i];  // m = -inf (l = 0) for a causal query that saw none of it
-    const float w = m_l.x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_l.x - M);
-    const float4 a = acc[(size_t)i * (kHeadDim / 4)];
-    den += w * m_l.y;
-    num.x += w * a.x;
-    num.y += w * a.y;
-    num.z += w * a.z;
-    num.w += w * a.w;
+  constexpr int kChunk = 8;  // partitions per thread loaded before any is folded
+  for (int i0 = pl; i0 < nused; i0 += 8 * kChunk) {
+    float2 mlv[kChunk];
+    float4 av[kChunk];
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const int i = i0 + 8 * u;
+      mlv[u] = i < nused ? ml[i] : make_float2(-INFINITY, 0.f);
+      av[u] = i < nused ? acc[(size_t)i * (kHeadDim / 4)] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      // m = -inf (l = 0): a partition a causal query saw none of, or past nused
+      if (mlv[u].x == -INFINITY) continue;
+      const float mn = fmaxf(m, mlv[u].x);
+      const float so = __builtin_amdgcn_exp2f(m - mn);  // 0 while m = -inf
+      const float sn = __builtin_amdgcn_exp2f(mlv[u].x - mn);
+      den = den * so + mlv[u].y * sn;
+      num.x = num.x * so + av[u].x * sn;
+      num.y = num.y * so + av[u].y * sn;
+      num.z = num.z * so + av[u].z * sn;
+      num.w = num.w * so + av[u].w * sn;
+      m = mn;
+    }
   }
   red_acc[pl][d4] = num;
-  if (d4 == 0) red_den[pl] = den;
+  if (d4 == 0) {
+    red_max[pl] = m;
+    red_den[pl] = den;
+  }
   __syncthreads();
   if (t < 32) {
-    float4 n = red_acc[0][t];
-    float dsum = red_den[0];
+    float M = red_max[0];
 #pragma unroll
-    for (int k = 1; k < 8; ++k) {
+    for (int k = 1; k < 8; ++k) M = fmaxf(M, red_max[k]);
+    float4 n = make_float4(0.f, 0.f, 0.f, 0.f);
+    float dsum = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float w = red_max[k] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(red_max[k] - M);
       const float4 a = red_acc[k][t];
-      n.x += a.x;
-      n.y += a.y;
-      n.z += a.z;
-      n.w += a.w;
-      dsum += red_den[k];
+      n.x += w * a.x;
+      n.y += w * a.y;
+      n.z += w * a.z;
+      n.w += w * a.w;
+      dsum += w * red_den[k];
     }
     const float inv = dsum > 0.0f ? (p.v_slot_scales ? 1.0f : scalar_load(p.v_scale)) / dsum : 0.0f;
     *(uint2*)(p.out + (size_t)sh * kHeadDim + 4 * t) =
