@@ -98,7 +98,7 @@ def suite_names():
     names += ["target", "dense_20x4_ctx4096_s256"]
     names += ["slotscales_40x8_ctx4096_s256"]
     names += [f"specdec_40x8_ctx4096_s256_q{q}" for q in (2, 3, 4, 8)]
-    names += [f"tokenrows_{lay}_40x8_ctx4096_s256" for lay in ("nhd", "packed")]
+    names += [f"tokenrows_{lay}_40x8_ctx4096_s256" for lay in ("nhd", "combined", "packed")]
     names += [f"ragged_{a}x{b}_seed0" for (a, b) in workloads.RAGGED_LAYOUTS]
     names += [f"dense_{a}x{b}_ctx{c}_s{s}" for (a, b, s, c) in workloads.LOW_BATCH]
     return names

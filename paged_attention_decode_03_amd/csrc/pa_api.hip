@@ -271,6 +271,18 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   p.q_tile = q_tile;
   p.num_q_tiles = q_tiles;
   p.token_rows = var.token_rows ? 1 : 0;
+  // token rows: where the kv heads' rows interleave within a token's row
+  // (head stride below token stride, as in [blocks, 16, kv_heads, 128]), the
+  // largest divisor of Hkv up to 8 kv heads share a workgroup and read each
+  // block together; a layout that keeps a (block, kv head) together gains
+  // nothing from it
+  p.kv_group = 1;
+  if (var.token_rows && var.head_stride < var.token_stride)
+    for (int g = 8; g >= 1; --g)
+      if (Hkv % g == 0) {
+        p.kv_group = g;
+        break;
+      }
   p.block_stride = var.block_stride;
   p.token_stride = var.token_stride;
   p.head_stride = var.head_stride;

@@ -43,6 +43,7 @@ struct DecodeParams {
   // has its 128 dims at p * block_stride + j * token_stride + k * head_stride
   // bytes from k_cache / v_cache
   int32_t token_rows;
+  int32_t kv_group;          // token rows: kv heads per workgroup (divides num_kv_heads, <= 8)
   int64_t block_stride;
   int64_t token_stride;
   int64_t head_stride;

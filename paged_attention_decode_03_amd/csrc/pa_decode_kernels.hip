@@ -72,6 +72,12 @@ constexpr int kRingDepth = PA_RING_DEPTH;
 constexpr int kSlotScalePagesPerStage = 2;
 // Word 3 of a raw buffer resource (no format conversion, no swizzle).
 constexpr int kRsrcWord3 = 0x00020000;
+// Token rows: kv heads per workgroup (waves walking a sequence's blocks together),
+// and each wave's LDS for one stage of V pages (16 rows of 128 + 8 bytes per page).
+constexpr int kMaxKvPerGroup = 8;
+constexpr int kVRow = kHeadDim + 8;
+template <int PPS>
+constexpr int kVtBytes = PPS * kBlockTokens * kVRow;
 
 // Wave-uniform load through the scalar data cache (read-only data).
 template <typename T>
@@ -136,8 +142,12 @@ struct Stage {
 // queries sees tokens 0 .. L - q_len + i, so a tile's context ends at its last
 // query's position and the tokens past each column's own position are masked.
 template <int PPS, int NB, bool SS, bool MQ, int AUX = PA_LOAD_AUX, bool TR = false>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU))) void pa_decode_kernel(const DecodeParams p) {
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU))) void pa_decode_kernel(const DecodeParams p) {
+  const int lane = threadIdx.x & 63;
+  // Token rows: a workgroup holds kv_group kv heads of one sequence (one wave
+  // each), which walk the sequence's blocks together (the barriers of each
+  // stage keep them in step), so the token rows they share are read at once.
+  const int wave = TR ? (int)(threadIdx.x >> 6) : 0;
   const int col = lane & 15;  // MFMA column (query head in group); K load row (token)
   const int rq = lane >> 4;   // row quad: rows 4*rq .. 4*rq+3 of the 16x16 tiles
 
@@ -156,8 +166,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
   }
   const int part = item % p.num_parts;
   int rest = item / p.num_parts;
-  const int kvh = rest % p.num_kv_heads;
-  const int s = rest / p.num_kv_heads;
+  const int kv_units = TR ? p.num_kv_heads / p.kv_group : p.num_kv_heads;  // work items per (sequence, partition)
+  const int kvh = TR ? (rest % kv_units) * p.kv_group + wave : rest % kv_units;
+  const int s = rest / kv_units;
   const int ppp = p.pages_per_part;
   const int pbeg = part * ppp;  // < max_blocks: the planner never makes an empty partition range
 
@@ -272,17 +283,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
   for (int k = 0; k < (kIdsCap + 63) / 64; ++k) {
     const int i = k * 64 + lane;
     const int32_t v = (k < kMaxPagesPerPart / 64) ? idv[k < kMaxPagesPerPart / 64 ? k : 0] : 0;
-    if (k * 64 < ids_fill && i < ids_fill) ids[i] = (i < npg) ? v : 0;
+    if (wave == 0 && k * 64 < ids_fill && i < ids_fill) ids[i] = (i < npg) ? v : 0;
   }
   __syncthreads();
 
   constexpr int kAux = AUX;
   // Token rows: the stage's V pages pass through LDS, row j of page pp at
-  // vt + (pp * 16 + j) * kVRow.  Rows are 128 + 8 bytes apart so that the
-  // 4-byte column gathers below (4 rows x 16 columns x 4 row groups) hit
-  // distinct banks.
-  constexpr int kVRow = kHeadDim + 8;
-  __shared__ __attribute__((aligned(16))) uint8_t vt[TR ? PPS * kBlockTokens * kVRow : 16];
+  // vtb + (pp * 16 + j) * kVRow, in one of two buffers per wave (stage parity)
+  // so that one barrier per stage orders both the writes before the gathers
+  // and the gathers before the next writes into the same buffer.  Rows are
+  // 128 + 8 bytes apart so that the 4-byte column gathers below (4 rows x 16
+  // columns x 4 row groups) hit distinct banks.
+  // (dynamic LDS, kv_group * 2 * kVtBytes<PPS> bytes, sized at launch)
+  extern __shared__ __attribute__((aligned(16))) uint8_t pa_dyn_lds[];
+  uint8_t* const vt = pa_dyn_lds + wave * 2 * kVtBytes<PPS>;
   auto load = [&](Stage<PPS>& st, int stage) {
     const int i0 = stage * PPS;
     int32_t pid[PPS];
@@ -344,9 +358,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
   };
 
   // PV operand: dims 16 jd + col, tokens 4 rq .. 4 rq + 3 of page pp (byte i = token 4 rq + i)
-  auto vword = [&](const Stage<PPS>& st, int pp, int jd) -> uint32_t {
+  auto vword = [&](const Stage<PPS>& st, const uint8_t* vtb, int pp, int jd) -> uint32_t {
     if constexpr (TR) {
-      const uint8_t* b = vt + (pp * kBlockTokens + 4 * rq) * kVRow + 16 * jd + col;
+      const uint8_t* b = vtb + (pp * kBlockTokens + 4 * rq) * kVRow + 16 * jd + col;
       return (uint32_t)b[0] | ((uint32_t)b[kVRow] << 8) | ((uint32_t)b[2 * kVRow] << 16) |
              ((uint32_t)b[3 * kVRow] << 24);
     } else {
@@ -356,11 +370,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
 
   auto compute = [&](const Stage<PPS>& st, int stage, bool last) {
     const int j0 = pbeg + stage * PPS;
+    uint8_t* const vtb = vt + (stage & 1) * kVtBytes<PPS>;
     if constexpr (TR) {
-      __syncthreads();  // the previous stage's gathers from vt are done
 #pragma unroll
       for (int pp = 0; pp < PPS; ++pp) {
-        uint8_t* dst = vt + (pp * kBlockTokens + (lane >> 2)) * kVRow + (lane & 3) * 32;
+        uint8_t* dst = vtb + (pp * kBlockTokens + (lane >> 2)) * kVRow + (lane & 3) * 32;
 #pragma unroll
         for (int e = 0; e < 4; ++e) *(uint2*)(dst + 8 * e) = make_uint2(st.v[pp][2 * e], st.v[pp][2 * e + 1]);
       }
@@ -435,7 +449,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
         }
 #pragma unroll
         for (int jd = 0; jd < 8; ++jd)
-          acc[jd] = __builtin_amdgcn_mfma_f32_16x16x16f16(fp8x4_to_f16(vword(st, pp, jd) & vmask), pv, acc[jd], 0, 0, 0);
+          acc[jd] = __builtin_amdgcn_mfma_f32_16x16x16f16(fp8x4_to_f16(vword(st, vtb, pp, jd) & vmask), pv, acc[jd], 0, 0, 0);
         accl = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pb, accl, 0, 0, 0);
       } else {
         f16x4 pb;
@@ -448,7 +462,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER
         }
 #pragma unroll
         for (int jd = 0; jd < 8; ++jd)
-          acc[jd] = __builtin_amdgcn_mfma_f32_16x16x16f16(fp8x4_to_f16(vword(st, pp, jd) & vmask), pb, acc[jd], 0, 0, 0);
+          acc[jd] = __builtin_amdgcn_mfma_f32_16x16x16f16(fp8x4_to_f16(vword(st, vtb, pp, jd) & vmask), pb, acc[jd], 0, 0, 0);
         accl = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pb, accl, 0, 0, 0);
       }
     }
@@ -597,7 +611,8 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const size_t items = p.cu_seqlens_q ? (units + 7) / 8 * 8 * p.num_q_tiles : units;
   if (p.token_rows)
     hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false, PA_LOAD_AUX, true>),
-                       dim3((unsigned)items), dim3(64), 0, stream, p);
+                       dim3((unsigned)(items / p.kv_group)), dim3(64 * p.kv_group),
+                       (unsigned)(p.kv_group * 2 * kVtBytes<kPagesPerStage>), stream, p);
   else if (p.cu_seqlens_q && p.num_q_tiles > 1)
     hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, true, 0>), dim3((unsigned)items),
                        dim3(64), 0, stream, p);
