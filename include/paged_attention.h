@@ -138,6 +138,40 @@ int paged_multi_query_attention(const void* q, const int32_t* cu_seqlens_q, int3
                                 const float* v_scale, void* out, void* stream);
 
 /*
+ * Options of the unified attention call (API page
+ * vllm.v1.attention.backends.rocm_aiter_unified_attn:
+ * RocmAiterUnifiedAttentionImpl.__init__ takes sliding_window, logits_soft_cap,
+ * alibi_slopes and sinks, and forward passes them as window_size, softcap,
+ * alibi_slopes and sinks).  For the query at position p of head h:
+ *   sliding_window   0: off; w > 0: it sees tokens max(0, p - w + 1) .. p
+ *   logits_soft_cap  0: off; c > 0: the logit z = scale * q.K becomes c * tanh(z / c)
+ *   alibi_slopes     NULL: off; else device fp32 [num_heads]: the logit gains
+ *                    slopes[h] * (t - p), after the softcap
+ *   sinks            NULL: off; else device fp32 [num_heads]: one more softmax
+ *                    term exp(sinks[h]) that carries no value
+ */
+typedef struct pa_attention_options {
+  int32_t sliding_window;
+  float logits_soft_cap;
+  const float* alibi_slopes;
+  const float* sinks;
+} pa_attention_options;
+
+/*
+ * paged_multi_query_attention with the options above (NULL options: none).
+ * Errors: PA_ERR_SHAPE for a negative window, a negative or non-finite cap,
+ * misaligned option arrays; otherwise as paged_multi_query_attention.  With a
+ * window, pages wholly before every query's window are not read.
+ */
+int paged_attention_unified(const void* q, const int32_t* cu_seqlens_q, int32_t num_q_tokens,
+                            int32_t max_seqlen_q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                            int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                            int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                            float scale, const float* k_scale, const float* v_scale,
+                            const pa_attention_options* options, void* out, void* stream);
+
+/*
  * paged_decode_attention over a token-row cache layout: each token's 128 fp8
  * dims are contiguous, and blocks, tokens and kv heads are reached by byte
  * strides (the flash-style caches of the API page

@@ -62,6 +62,9 @@ def _load():
                                              ctypes.c_int64, P, P, i32, i32, i32, i32, f32, f32,
                                              f32, P, i32]
     lib.pa_oracle_decode_strided.restype = i32
+    lib.pa_oracle_attend_ext.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, f32, f32, f32,
+                                         i32, f32, P, P, P, i32]
+    lib.pa_oracle_attend_ext.restype = i32
     lib.pa_oracle_attend_multi.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, f32, f32, f32, P, i32]
     lib.pa_oracle_attend_multi.restype = i32
     lib.pa_oracle_fp8_e4m3fn_encode.argtypes = [ctypes.c_float]
@@ -234,6 +237,42 @@ def attend_multi(q_bits, cu_seqlens_q, k_cache, v_cache, block_tables, seq_lens,
         q_bits.ctypes.data, cu.ctypes.data, k_cache.ctypes.data, v_cache.ctypes.data,
         bt.ctypes.data, sl.ctypes.data, S, Hq, Hkv, W, float(scale), float(k_scale),
         float(v_scale), out.ctypes.data, int(num_threads if num_threads else (os.cpu_count() or 1)))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (code {rc})")
+    return out
+
+
+def attend_ext(q_bits, cu_seqlens_q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale,
+               v_scale, sliding_window: int = 0, softcap: float = 0.0, alibi_slopes=None,
+               sinks=None, num_threads: int | None = None) -> np.ndarray:
+    """attend_multi with the unified backend's options: a sliding window of
+    `sliding_window` tokens ending at each query (0 = none), logit softcap
+    (0 = none), per-head ALiBi slopes and per-head sink logits (float32 [Hq],
+    or None).  Returns float64 [T, Hq, 128]."""
+    q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+    cu = np.ascontiguousarray(cu_seqlens_q, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    S = sl.shape[0]
+    if cu.shape != (S + 1,) or q_bits.ndim != 3 or q_bits.shape[0] != int(cu[-1]):
+        raise ValueError("cu_seqlens_q must be [S+1] with cu[S] = number of query rows")
+    _, Hq, _ = q_bits.shape
+    fake_q = np.zeros((S, Hq, 128), np.uint16)
+    _, k_cache, v_cache, bt, sl, S, Hq, Hkv, W = _check(fake_q, k_cache, v_cache, block_tables, sl)
+    def vec(x):
+        if x is None:
+            return None
+        a = np.ascontiguousarray(x, dtype=np.float32)
+        if a.shape != (Hq,):
+            raise ValueError("per-head options must have num_heads entries")
+        return a
+    sl_a, sk_a = vec(alibi_slopes), vec(sinks)
+    out = np.zeros((q_bits.shape[0], Hq, 128), dtype=np.float64)
+    rc = _load().pa_oracle_attend_ext(
+        q_bits.ctypes.data, cu.ctypes.data, k_cache.ctypes.data, v_cache.ctypes.data,
+        bt.ctypes.data, sl.ctypes.data, S, Hq, Hkv, W, float(scale), float(k_scale),
+        float(v_scale), int(sliding_window), float(softcap),
+        None if sl_a is None else sl_a.ctypes.data, None if sk_a is None else sk_a.ctypes.data,
+        out.ctypes.data, int(num_threads if num_threads else (os.cpu_count() or 1)))
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (code {rc})")
     return out

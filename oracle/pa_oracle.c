@@ -56,6 +56,19 @@
  * with n = seq_lens[s] tokens sits at position n - q_len + i and sees tokens
  * 0 .. n - q_len + i.  q_len > n is a caller error (return -5).
  *
+ * Attention options of the unified backend (pa_oracle_attend_ext; API page,
+ * RocmAiterUnifiedAttentionImpl.__init__ / forward: sliding_window as
+ * window_size, logits_soft_cap as softcap, alibi_slopes, sinks), on top of the
+ * several-queries form above.  Readings, for the query at position p of head h:
+ *   - window w > 0: it sees tokens max(0, p - w + 1) .. p (w tokens ending at
+ *     its own position); w = 0: no window;
+ *   - softcap c > 0: the scaled logit z = scale * q.K becomes c * tanh(z / c);
+ *   - ALiBi slope a_h: the logit gains a_h * (t - p) (after the softcap); a
+ *     per-query constant would not change the result;
+ *   - sink s_h: one more softmax term exp(s_h) with no value, so
+ *     out = sum_t exp(z_t - M) V_t / (sum_t exp(z_t - M) + exp(s_h - M)),
+ *     M = max(max_t z_t, s_h); a query that sees no token gets zeros.
+ *
  * Token-row cache layouts (pa_oracle_decode_strided): the same quantity with
  * each token's 128 dims stored contiguously, as the flash-style caches of the
  * API page's unified backend keep them (the forward docstring's
@@ -222,6 +235,50 @@ static void attend_row(const uint16_t* q_row, const uint8_t* k_cache, const uint
   /* softmax-weighted sum of V */
   double den = 0.0;
   for (int t = 0; t < n; ++t) {
+    load_token(k_cache, v_cache, bt_row, Hkv, k, t, sc, K, V);
+    const double w = exp(z[t] - zmax);
+    den += w;
+    for (int d = 0; d < PA_HEAD_DIM; ++d) o[d] += w * V[d];
+  }
+  for (int d = 0; d < PA_HEAD_DIM; ++d) o[d] /= den;
+  free(z);
+}
+
+/* attend_row with the unified backend's options (window, softcap, ALiBi
+ * slope, sink) for the query at position p = n - 1. */
+typedef struct {
+  int window;
+  double softcap;
+  double slope;
+  int has_sink;
+  double sink;
+} row_options_t;
+
+static void attend_row_ext(const uint16_t* q_row, const uint8_t* k_cache, const uint8_t* v_cache,
+                           const int32_t* bt_row, int Hkv, int k, int n, float scale,
+                           const scales_t* sc, const row_options_t* op, double* o) {
+  double q[PA_HEAD_DIM], K[PA_HEAD_DIM], V[PA_HEAD_DIM];
+  for (int e = 0; e < PA_HEAD_DIM; ++e) q[e] = pa_oracle_bf16(q_row[e]);
+  for (int d = 0; d < PA_HEAD_DIM; ++d) o[d] = 0.0;
+  const int p = n - 1;
+  const int lo = (op->window > 0 && p - op->window + 1 > 0) ? p - op->window + 1 : 0;
+  if (n <= 0) return;
+  double* z = (double*)malloc(sizeof(double) * (size_t)n);
+  /* logits of the visible tokens lo .. p */
+  double zmax = op->has_sink ? op->sink : -INFINITY;
+  for (int t = lo; t < n; ++t) {
+    load_token(k_cache, v_cache, bt_row, Hkv, k, t, sc, K, V);
+    double dot = 0.0;
+    for (int e = 0; e < PA_HEAD_DIM; ++e) dot += q[e] * K[e];
+    double zt = (double)scale * dot;
+    if (op->softcap > 0.0) zt = op->softcap * tanh(zt / op->softcap);
+    zt += op->slope * (double)(t - p);
+    z[t] = zt;
+    if (zt > zmax) zmax = zt;
+  }
+  /* softmax-weighted sum of V, the sink only in the denominator */
+  double den = op->has_sink ? exp(op->sink - zmax) : 0.0;
+  for (int t = lo; t < n; ++t) {
     load_token(k_cache, v_cache, bt_row, Hkv, k, t, sc, K, V);
     const double w = exp(z[t] - zmax);
     den += w;
@@ -416,6 +473,48 @@ int pa_oracle_attend_multi(const uint16_t* q_bits, const int32_t* cu_seqlens_q,
         attend_row(q_bits + ((int64_t)(q0 + i) * Hq + h) * PA_HEAD_DIM, k_cache, v_cache,
                    block_tables + (int64_t)s * W, Hkv, h / G, visible, scale, &sc,
                    out + ((int64_t)(q0 + i) * Hq + h) * PA_HEAD_DIM);
+    }
+  }
+  return 0;
+}
+
+/*
+ * pa_oracle_attend_multi with the unified backend's options: sliding_window
+ * (0 = none), softcap (0 = none), alibi_slopes [Hq] or NULL, sinks [Hq] or NULL.
+ */
+int pa_oracle_attend_ext(const uint16_t* q_bits, const int32_t* cu_seqlens_q,
+                         const uint8_t* k_cache, const uint8_t* v_cache,
+                         const int32_t* block_tables, const int32_t* seq_lens, int S, int Hq,
+                         int Hkv, int W, float scale, float k_scale, float v_scale,
+                         int sliding_window, float softcap, const float* alibi_slopes,
+                         const float* sinks, double* out, int num_threads) {
+  int rc = check_args(S, Hq, Hkv, W, seq_lens);
+  if (rc) return rc;
+  if (cu_seqlens_q[0] != 0 || sliding_window < 0 || !(softcap >= 0.0f)) return -5;
+  for (int s = 0; s < S; ++s) {
+    const int q_len = cu_seqlens_q[s + 1] - cu_seqlens_q[s];
+    if (q_len < 0 || q_len > seq_lens[s]) return -5;
+  }
+  const int G = Hq / Hkv;
+  const scales_t sc = {k_scale, v_scale, NULL, NULL};
+  (void)num_threads;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(num_threads > 0 ? num_threads : 1)
+  for (int s = 0; s < S; ++s) {
+    const int q0 = cu_seqlens_q[s];
+    const int q_len = cu_seqlens_q[s + 1] - q0;
+    for (int i = 0; i < q_len; ++i) {
+      const int visible = seq_lens[s] - q_len + i + 1;
+      for (int h = 0; h < Hq; ++h) {
+        row_options_t op;
+        op.window = sliding_window;
+        op.softcap = softcap;
+        op.slope = alibi_slopes ? (double)alibi_slopes[h] : 0.0;
+        op.has_sink = sinks != NULL;
+        op.sink = sinks ? (double)sinks[h] : 0.0;
+        attend_row_ext(q_bits + ((int64_t)(q0 + i) * Hq + h) * PA_HEAD_DIM, k_cache, v_cache,
+                       block_tables + (int64_t)s * W, Hkv, h / G, visible, scale, &sc, &op,
+                       out + ((int64_t)(q0 + i) * Hq + h) * PA_HEAD_DIM);
+      }
     }
   }
   return 0;

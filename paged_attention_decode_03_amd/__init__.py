@@ -27,7 +27,8 @@ import torch
 __all__ = [
     "paged_decode_attention", "paged_decode_attention_split", "pa_decode_plan",
     "pa_decode_reserve_workspace", "paged_kv_cache_write", "paged_decode_attention_slot_scales",
-    "paged_multi_query_attention", "paged_decode_attention_nhd", "pa_last_error",
+    "paged_multi_query_attention", "paged_attention_unified", "paged_decode_attention_nhd",
+    "pa_last_error",
     "PagedAttentionError", "library_path",
     "load_library",
 ]
@@ -47,6 +48,12 @@ class PagedAttentionError(RuntimeError):
     def __init__(self, code: int, message: str):
         super().__init__(f"{STATUS_NAMES.get(code, code)}: {message}")
         self.code = code
+
+
+class AttentionOptions(ctypes.Structure):
+    """pa_attention_options: sliding window, logit softcap, ALiBi slopes, sinks."""
+    _fields_ = [("sliding_window", ctypes.c_int32), ("logits_soft_cap", ctypes.c_float),
+                ("alibi_slopes", ctypes.c_void_p), ("sinks", ctypes.c_void_p)]
 
 
 def load_library():
@@ -70,6 +77,10 @@ def load_library():
     lib.paged_multi_query_attention.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, i32,
                                                 i32, i32, i64, f32, vp, vp, vp, vp]
     lib.paged_multi_query_attention.restype = ctypes.c_int
+    lib.paged_attention_unified.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, i32,
+                                            i32, i32, i64, f32, vp, vp,
+                                            ctypes.POINTER(AttentionOptions), vp, vp]
+    lib.paged_attention_unified.restype = ctypes.c_int
     lib.paged_decode_attention_nhd.argtypes = [vp, vp, vp, i64, i64, i64, vp, vp, i32, i32, i32,
                                                i32, i32, i32, i64, f32, vp, vp, vp, vp]
     lib.paged_decode_attention_nhd.restype = ctypes.c_int
@@ -225,6 +236,32 @@ def paged_multi_query_attention(q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache,
         _check(lib.paged_multi_query_attention(
             _ptr(q), _ptr(cu_seqlens_q), q.shape[0], int(max_seqlen_q), kc, vc, bt, sl, S, Hq,
             Hkv, D, bs, W, NB, sc, ks, vs, _ptr(out), handle))
+    return out
+
+
+def paged_attention_unified(q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache, block_tables,
+                            seq_lens, scale, k_scale, v_scale, sliding_window=0, softcap=0.0,
+                            alibi_slopes=None, sinks=None, out=None, stream=None):
+    """paged_multi_query_attention with the unified backend's options:
+    sliding_window (tokens ending at each query, 0 = off), softcap (0 = off),
+    alibi_slopes / sinks (float32 [num_heads] tensors on the q device, or None)."""
+    lib = load_library()
+    dev, out, c_args, keep = _args(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale,
+                                   v_scale, out, stream, q_rows_free=True)
+    S = c_args[5]
+    if (cu_seqlens_q.dtype != torch.int32 or tuple(cu_seqlens_q.shape) != (S + 1,)
+            or cu_seqlens_q.device != dev or not cu_seqlens_q.is_contiguous()):
+        raise TypeError("cu_seqlens_q must be a contiguous int32 [num_seqs + 1] tensor on the q device")
+    for name, t in (("alibi_slopes", alibi_slopes), ("sinks", sinks)):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (q.shape[1],)
+                              or t.device != dev or not t.is_contiguous()):
+            raise TypeError(f"{name} must be a contiguous float32 [num_heads] tensor on the q device")
+    opts = AttentionOptions(int(sliding_window), float(softcap), _ptr(alibi_slopes), _ptr(sinks))
+    (_, kc, vc, bt, sl, _, Hq, Hkv, D, bs, W, NB, sc, ks, vs, _, handle) = c_args
+    with torch.cuda.device(dev):
+        _check(lib.paged_attention_unified(
+            _ptr(q), _ptr(cu_seqlens_q), q.shape[0], int(max_seqlen_q), kc, vc, bt, sl, S, Hq,
+            Hkv, D, bs, W, NB, sc, ks, vs, ctypes.byref(opts), _ptr(out), handle))
     return out
 
 

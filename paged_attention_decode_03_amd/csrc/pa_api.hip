@@ -155,6 +155,7 @@ struct Variant {
   int32_t max_seqlen_q = 1;
   bool token_rows = false;                 // token-row cache layout with byte strides
   int64_t block_stride = 0, token_stride = 0, head_stride = 0;
+  pa_attention_options options = {0, 0.0f, nullptr, nullptr};  // several queries only
 };
 
 int decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
@@ -190,6 +191,13 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   if (S == 0 || (mq && num_q_rows == 0)) return PA_OK;
   if (mq && max_seqlen_q == 0)
     return fail(PA_ERR_SHAPE, "max_seqlen_q must be positive when there are query tokens");
+  const pa_attention_options& opt = var.options;
+  if (opt.sliding_window < 0)
+    return fail(PA_ERR_SHAPE, "sliding_window %d is negative", opt.sliding_window);
+  if (!(opt.logits_soft_cap >= 0.0f) || !isfinite(opt.logits_soft_cap))
+    return fail(PA_ERR_SHAPE, "logits_soft_cap must be finite and >= 0");
+  if (((uintptr_t)opt.alibi_slopes & 3) || ((uintptr_t)opt.sinks & 3))
+    return fail(PA_ERR_SHAPE, "misaligned alibi_slopes / sinks (4 B)");
   if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !k_scale || !v_scale || !out)
     return fail(PA_ERR_NULL, "a required pointer is NULL");
   if (W == 0 || NB == 0)
@@ -213,6 +221,8 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
       overlaps(out, q_bytes, block_tables, (size_t)S * W * 4) ||
       overlaps(out, q_bytes, seq_lens, (size_t)S * 4) || overlaps(out, q_bytes, k_scale, 4) ||
       (mq && overlaps(out, q_bytes, cu_seqlens_q, (size_t)(S + 1) * 4)) ||
+      overlaps(out, q_bytes, opt.alibi_slopes, opt.alibi_slopes ? (size_t)Hq * 4 : 0) ||
+      overlaps(out, q_bytes, opt.sinks, opt.sinks ? (size_t)Hq * 4 : 0) ||
       overlaps(out, q_bytes, v_scale, 4))
     return fail(PA_ERR_ALIAS, "out overlaps an input");
   if (slot_scales && (overlaps(out, q_bytes, k_scale, (size_t)NB * Hkv * 64) ||
@@ -270,6 +280,11 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   p.num_q_rows = mq ? num_q_rows : S;
   p.q_tile = q_tile;
   p.num_q_tiles = q_tiles;
+  p.window = opt.sliding_window;
+  p.softcap = opt.logits_soft_cap;
+  p.scale = scale;
+  p.alibi_slopes = opt.alibi_slopes;
+  p.sinks = opt.sinks;
   p.token_rows = var.token_rows ? 1 : 0;
   // token rows: where the kv heads' rows interleave within a token's row
   // (head stride below token stride, as in [blocks, 16, kv_heads, 128]), the
@@ -339,6 +354,26 @@ int paged_multi_query_attention(const void* q, const int32_t* cu_seqlens_q, int3
   mq.cu_seqlens_q = cu_seqlens_q;
   mq.num_q_rows = num_q_tokens;
   mq.max_seqlen_q = max_seqlen_q;
+  return decode(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads, num_kv_heads,
+                head_size, block_size, max_blocks_per_seq, num_blocks, scale, k_scale, v_scale, out,
+                stream, 0, mq);
+}
+
+int paged_attention_unified(const void* q, const int32_t* cu_seqlens_q, int32_t num_q_tokens,
+                            int32_t max_seqlen_q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                            int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                            int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
+                            float scale, const float* k_scale, const float* v_scale,
+                            const pa_attention_options* options, void* out, void* stream) {
+  if (!cu_seqlens_q && num_seqs > 0) return fail(PA_ERR_NULL, "cu_seqlens_q is NULL");
+  if (num_seqs > 0 && num_q_tokens > 0 && ((uintptr_t)cu_seqlens_q & 3))
+    return fail(PA_ERR_SHAPE, "misaligned cu_seqlens_q (4 B)");
+  Variant mq;
+  mq.cu_seqlens_q = cu_seqlens_q;
+  mq.num_q_rows = num_q_tokens;
+  mq.max_seqlen_q = max_seqlen_q;
+  if (options) mq.options = *options;
   return decode(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads, num_kv_heads,
                 head_size, block_size, max_blocks_per_seq, num_blocks, scale, k_scale, v_scale, out,
                 stream, 0, mq);

@@ -39,6 +39,12 @@ struct DecodeParams {
   int32_t num_q_rows;        // cu_seqlens_q[S]: rows of q and out
   int32_t q_tile;            // query tokens per work item (columns = q_tile * group <= 16)
   int32_t num_q_tiles;       // query tiles per sequence (from the host's max_seqlen_q)
+  // options of the several-queries form (0 / null: off)
+  int32_t window;            // a query at position p sees tokens p - window + 1 .. p
+  float softcap;             // logit z -> softcap * tanh(z / softcap)
+  float scale;               // softmax scale (natural units, for the softcap)
+  const float* alibi_slopes;  // [Hq]: logit + slope * (t - p)
+  const float* sinks;         // [Hq]: extra softmax term exp(sink) with no value
   // token-row cache layout (token_rows != 0): token j of kv head k in block p
   // has its 128 dims at p * block_stride + j * token_stride + k * head_stride
   // bytes from k_cache / v_cache

@@ -33,6 +33,7 @@
 // 16 B chunks of token l & 15's row) and V as 32 B per lane of token rows;
 // a V page then passes through LDS, transposed into the dims x tokens operand.
 // Pages are software-pipelined PPS at a time, one stage ahead.
+#include <limits.h>
 #include <math.h>
 
 #include "pa_decode_kernels.h"
@@ -72,6 +73,7 @@ constexpr int kRingDepth = PA_RING_DEPTH;
 constexpr int kSlotScalePagesPerStage = 2;
 // Word 3 of a raw buffer resource (no format conversion, no swizzle).
 constexpr int kRsrcWord3 = 0x00020000;
+constexpr float kLog2e = 1.4426950408889634f;
 // Token rows: kv heads per workgroup (waves walking a sequence's blocks together),
 // and each wave's LDS for one stage of V pages (16 rows of 128 + 8 bytes per page).
 constexpr int kMaxKvPerGroup = 8;
@@ -245,8 +247,31 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
   // several queries: first token this column must not use (its own causal end)
   const int tlim = MQ ? min(tend, pos_col + 1) : tend;
 
+  // Options of the several-queries form (window, softcap, ALiBi, sinks).
+  // Window: this column uses tokens tlo .. pos_col; the item starts at the
+  // first whole stage holding a token any of its columns can see (pstart).
+  int tlo = 0, tlo_max = INT_MIN, pstart = pbeg;
+  float slope_l2 = 0.0f, sink_l2 = -INFINITY;
+  if constexpr (MQ) {
+    if (p.window > 0) {
+      tlo = pos_col - p.window + 1;
+      tlo_max = L - p.window;  // the latest window start among the tile's columns
+      const int lo_pg = max(0, pos_first - p.window + 1) / kBlockTokens;
+      if (lo_pg > pbeg) pstart = pbeg + min(lo_pg - pbeg, ppp) / PPS * PPS;  // whole stages
+    }
+    if (p.alibi_slopes && hvalid) slope_l2 = p.alibi_slopes[h] * kLog2e;
+    if (p.sinks && hvalid) sink_l2 = p.sinks[h] * kLog2e;
+  }
+  const int ioff = MQ ? pstart - pbeg : 0;  // first staged page this item loads
+
   // logits in log2 units: z * scale * k_scale * log2(e) (k_scale per slot when SS)
   const float c_log2 = SS ? p.scale_log2e : p.scale_log2e * scalar_load(p.k_scale);
+  // softcap: the natural-unit logit z * scale * k_scale, capped, then in log2 units
+  const bool capped = MQ && p.softcap > 0.0f;
+  const float c_nat = MQ ? p.scale * scalar_load(p.k_scale) : 0.0f;
+  const float cap_k = MQ && capped ? 2.0f * kLog2e / p.softcap : 0.0f;
+  const float cap_l2 = MQ ? p.softcap * kLog2e : 0.0f;
+  const bool biased = MQ && p.alibi_slopes != nullptr;
 
   const size_t page_stride = TR ? (size_t)p.block_stride : (size_t)p.num_kv_heads * kPageBytes;
   const size_t head_off = TR ? (size_t)kvh * p.head_stride : (size_t)kvh * kPageBytes;
@@ -267,6 +292,13 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
   for (int jd = 0; jd < 8; ++jd) acc[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
   f32x4 accl = {0.f, 0.f, 0.f, 0.f};  // softmax denominator (same value in every element)
   float m_run = -INFINITY;
+  if constexpr (MQ) {
+    // the sink: one more softmax term 2^sink with no value, counted once (partition 0)
+    if (part == 0 && sink_l2 > -INFINITY) {
+      m_run = sink_l2;
+      accl = f32x4{1.f, 1.f, 1.f, 1.f};
+    }
+  }
   const f16x4 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
   float vnorm = 1.0f, vnorm_inv = 1.0f;  // per-slot variant: power-of-two weight factor
 
@@ -274,16 +306,16 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
   // the partition gets a buffer descriptor of zero bytes: it is still issued
   // (so the pipeline's wait counts do not depend on the data) but it returns
   // zeros without touching memory.  Those ids are therefore never used.
-  const int npg = pend - pbeg;
+  const int npg = MQ ? max(0, pend - pstart) : pend - pbeg;
   const int nsteps = (npg + PPS - 1) / PPS;
   constexpr int kIdsCap = kMaxPagesPerPart + NB * PPS;
   __shared__ __attribute__((aligned(16))) int32_t ids[kIdsCap];
-  const int ids_fill = (nsteps + NB - 1) * PPS;  // every index a load can reach
+  const int ids_fill = ioff + (nsteps + NB - 1) * PPS;  // every index a load can reach
 #pragma unroll
   for (int k = 0; k < (kIdsCap + 63) / 64; ++k) {
     const int i = k * 64 + lane;
     const int32_t v = (k < kMaxPagesPerPart / 64) ? idv[k < kMaxPagesPerPart / 64 ? k : 0] : 0;
-    if (wave == 0 && k * 64 < ids_fill && i < ids_fill) ids[i] = (i < npg) ? v : 0;
+    if (wave == 0 && k * 64 < ids_fill && i < ids_fill) ids[i] = (i < ioff + npg) ? v : 0;
   }
   __syncthreads();
 
@@ -298,12 +330,13 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
   extern __shared__ __attribute__((aligned(16))) uint8_t pa_dyn_lds[];
   uint8_t* const vt = pa_dyn_lds + wave * 2 * kVtBytes<PPS>;
   auto load = [&](Stage<PPS>& st, int stage) {
-    const int i0 = stage * PPS;
+    const int i0 = stage * PPS;           // page of the item (pages past npg are empty)
+    const int32_t* idp = ids + ioff + i0;  // their staged block ids
     int32_t pid[PPS];
     if constexpr (PPS % 4 == 0) {
 #pragma unroll
       for (int c = 0; c < PPS / 4; ++c) {
-        const int4 v = *(const int4*)(ids + i0 + 4 * c);
+        const int4 v = *(const int4*)(idp + 4 * c);
         pid[4 * c] = v.x;
         pid[4 * c + 1] = v.y;
         pid[4 * c + 2] = v.z;
@@ -312,13 +345,13 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
     } else if constexpr (PPS % 2 == 0) {
 #pragma unroll
       for (int c = 0; c < PPS / 2; ++c) {
-        const int2 v = *(const int2*)(ids + i0 + 2 * c);
+        const int2 v = *(const int2*)(idp + 2 * c);
         pid[2 * c] = v.x;
         pid[2 * c + 1] = v.y;
       }
     } else {
 #pragma unroll
-      for (int pp = 0; pp < PPS; ++pp) pid[pp] = ids[i0 + pp];
+      for (int pp = 0; pp < PPS; ++pp) pid[pp] = idp[pp];
     }
 #pragma unroll
     for (int pp = 0; pp < PPS; ++pp) {
@@ -369,7 +402,7 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
   };
 
   auto compute = [&](const Stage<PPS>& st, int stage, bool last) {
-    const int j0 = pbeg + stage * PPS;
+    const int j0 = pstart + stage * PPS;
     uint8_t* const vtb = vt + (stage & 1) * kVtBytes<PPS>;
     if constexpr (TR) {
 #pragma unroll
@@ -380,8 +413,9 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
       }
       __syncthreads();
     }
-    // columns with their own causal end: the stages reaching past the tile's first position
-    const bool causal = MQ && (j0 + PPS) * kBlockTokens > pos_first + 1;
+    // columns with their own causal end: the stages reaching past the tile's first
+    // position; with a window, also the stages before the latest window start
+    const bool causal = MQ && ((j0 + PPS) * kBlockTokens > pos_first + 1 || j0 * kBlockTokens < tlo_max);
     f32x4 z[PPS];
 #pragma unroll
     for (int pp = 0; pp < PPS; ++pp) {
@@ -402,7 +436,16 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
       for (int i = 0; i < 4; ++i) {
         float v = z[pp][i] * c_log2;
         if constexpr (SS) v *= __uint_as_float(st.ks[pp][i]);
-        if (last || causal) {
+        if constexpr (MQ) {
+          const int t = (j0 + pp) * kBlockTokens + rq * 4 + i;
+          if (capped) {
+            // c tanh(z / c) = c (1 - 2 / (e^(2 z / c) + 1)), then in log2 units
+            const float e2 = __builtin_amdgcn_exp2f(z[pp][i] * c_nat * cap_k);
+            v = cap_l2 * (1.0f - 2.0f * __builtin_amdgcn_rcpf(e2 + 1.0f));
+          }
+          if (biased) v += slope_l2 * (float)(t - pos_col);
+          if (last || causal) v = (t < tlim && t >= tlo) ? v : -INFINITY;
+        } else if (last) {
           const int t = (j0 + pp) * kBlockTokens + rq * 4 + i;
           v = (t < tlim) ? v : -INFINITY;
         }

@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     for n in ("paged_decode_attention", "paged_decode_attention_split", "pa_decode_plan",
               "pa_decode_reserve_workspace", "paged_kv_cache_write",
               "paged_decode_attention_slot_scales", "paged_multi_query_attention",
-              "paged_decode_attention_nhd", "pa_last_error"):
+              "paged_decode_attention_nhd", "paged_attention_unified", "pa_last_error"):
         assert n in names
 
 
@@ -179,3 +179,23 @@ def test_token_row_decode_argument_checks(lib):
     # the page-layout extent would be 16 * 2 * 2048 = 64 KiB; a 1 MiB block stride
     # reaches further, so an out 100 KiB past k overlaps only under token rows
     assert nhd(lib, bs=1 << 20, out=FAKE * 16 + 100 * 1024) == -4
+
+
+def unified(lib, window=0, cap=0.0, slopes=None, sinks=None, opts=True):
+    import paged_attention_decode_03_amd as pa
+    vp = ctypes.c_void_p
+    o = pa.AttentionOptions(window, cap, slopes, sinks)
+    return lib.paged_attention_unified(vp(FAKE), vp(FAKE * 70), 6, 4, vp(FAKE * 16), vp(FAKE * 32),
+                                       vp(FAKE * 48), vp(FAKE * 50), 2, 8, 2, 128, 16, 4, 16,
+                                       ctypes.c_float(0.088), vp(FAKE * 52), vp(FAKE * 53),
+                                       ctypes.byref(o) if opts else None, vp(FAKE * 64), None)
+
+
+def test_unified_option_checks(lib):
+    assert unified(lib, window=-1) == -2
+    assert unified(lib, cap=-1.0) == -2
+    assert unified(lib, cap=float("nan")) == -2
+    assert unified(lib, cap=float("inf")) == -2
+    assert unified(lib, slopes=FAKE * 80 + 2) == -2
+    assert unified(lib, sinks=FAKE * 80 + 1) == -2
+    assert unified(lib, sinks=FAKE * 64 + 64) == -4       # inside out

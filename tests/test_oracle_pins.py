@@ -503,3 +503,155 @@ def test_token_row_buffer_too_small_is_rejected(oracle_lib):
     with pytest.raises(ValueError):
         oracle.decode_strided(case.q_bits(), kb[:100], vb, *st, 2, case.block_tables.numpy(),
                               case.seq_lens.numpy(), case.scale, case.k_scale, case.v_scale)
+
+
+# --------------------------------------------------------------------------
+# The unified backend's options on top of several queries per sequence:
+# sliding window, logit softcap, ALiBi slopes, attention sinks.
+
+def run_ext(case, **kw):
+    return oracle.attend_ext(case.q_bits(), case.cu_seqlens_q.numpy(), case.k_cache.numpy(),
+                             case.v_cache.numpy(), case.block_tables.numpy(), case.seq_lens.numpy(),
+                             case.scale, case.k_scale, case.v_scale, **kw)
+
+
+def ext_case(seed=81, hq=8, hkv=2, lens=(40, 70, 5, 129), qlens=(3, 8, 5, 1)):
+    return workloads.make_multi_case(hq, hkv, list(lens), list(qlens), seed)
+
+
+def equal_keys(case):
+    """Every cached token of every kv head gets the same K codes (those of
+    physical block 0, slot 0), so all logits of a query are equal."""
+    k = case.k_cache.clone()
+    codes = k[0, :, :, 0:1, :].clone()            # [Hkv, 8, 1, 16]
+    k[:] = codes.unsqueeze(0)
+    case.k_cache = k
+    return case
+
+
+def positions(case):
+    """(row, sequence, position) of every query row."""
+    cu = case.cu_seqlens_q.numpy()
+    out = []
+    for s in range(case.num_seqs):
+        L = int(case.seq_lens[s]); ql = int(cu[s + 1] - cu[s])
+        for i in range(ql):
+            out.append((int(cu[s]) + i, s, L - ql + i))
+    return out
+
+
+def v_rows(case, s, kvh, ts):
+    """fp64 V rows (dequantised by torch) of tokens ts of sequence s."""
+    bt = case.block_tables.numpy()[s]
+    vb = np.stack([case.v_cache.numpy()[bt[t // 16], kvh, :, t % 16] for t in ts])
+    return torch.from_numpy(vb).view(torch.float8_e4m3fn).double().numpy() * case.v_scale
+
+
+def test_ext_defaults_reproduce_multi_query(oracle_lib):
+    case = ext_case()
+    assert np.array_equal(run_ext(case), run_multi(case))
+    big = run_ext(case, sliding_window=10_000, alibi_slopes=np.zeros(8, np.float32),
+                  sinks=np.full(8, -1e30, np.float32))
+    assert np.array_equal(big, run_multi(case))
+
+
+def test_window_of_one_returns_own_value(oracle_lib):
+    case = ext_case(seed=82)
+    out = run_ext(case, sliding_window=1)
+    G = case.num_heads // case.num_kv_heads
+    for row, s, p in positions(case):
+        for h in range(case.num_heads):
+            assert np.array_equal(out[row, h], v_rows(case, s, h // G, [p])[0])
+
+
+@pytest.mark.parametrize("window", [2, 7, 16, 33])
+def test_window_matches_masked_sdpa(oracle_lib, window):
+    case = ext_case(seed=83)
+    ours = run_ext(case, sliding_window=window)
+    G = case.num_heads // case.num_kv_heads
+    q = case.q.double()
+    for s in range(case.num_seqs):
+        L = int(case.seq_lens[s])
+        K, V = gather_dense(case, s)                       # [L, Hkv, 128]
+        rows = [(r, p) for r, s2, p in positions(case) if s2 == s]
+        if not rows:
+            continue
+        pos = torch.tensor([p for _, p in rows])
+        t = torch.arange(L)
+        allowed = (t[None, :] <= pos[:, None]) & (t[None, :] > pos[:, None] - window)
+        for h in range(case.num_heads):
+            qh = q[[r for r, _ in rows], h]                # [n_q, 128]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                qh[None], K[:, h // G][None].contiguous(), V[:, h // G][None].contiguous(),
+                attn_mask=allowed[None], scale=case.scale)[0]
+            np.testing.assert_allclose(ours[[r for r, _ in rows], h], ref.numpy(), rtol=0, atol=1e-12)
+
+
+def test_softcap_limits(oracle_lib):
+    case = ext_case(seed=84)
+    plain = run_multi(case)
+    np.testing.assert_allclose(run_ext(case, softcap=1e12), plain, rtol=0, atol=1e-12)
+    # a vanishing cap flattens every logit to ~0: uniform weights, the mean of the visible V
+    flat = run_ext(case, softcap=1e-12)
+    G = case.num_heads // case.num_kv_heads
+    for row, s, p in positions(case):
+        for h in range(case.num_heads):
+            mean = v_rows(case, s, h // G, range(p + 1)).mean(axis=0)
+            np.testing.assert_allclose(flat[row, h], mean, rtol=0, atol=1e-9)
+
+
+def test_softcap_bounds_the_logit_spread(oracle_lib):
+    """With cap c every logit lies in (-c, c), so no weight ratio exceeds
+    e^(2c): with c = 0.5 and one dominant key the output stays near the mean."""
+    case = ext_case(seed=85)
+    capped = run_ext(case, softcap=0.5)
+    G = case.num_heads // case.num_kv_heads
+    for row, s, p in positions(case):
+        for h in range(case.num_heads):
+            Vv = v_rows(case, s, h // G, range(p + 1))
+            # a convex combination with weights within a factor e of each other
+            lo = Vv.min(axis=0); hi = Vv.max(axis=0)
+            assert np.all(capped[row, h] >= lo - 1e-12) and np.all(capped[row, h] <= hi + 1e-12)
+            w_min = 1.0 / (1 + (p) * np.e)                  # smallest possible weight
+            assert np.all(np.abs(capped[row, h] - Vv.mean(axis=0)) <= (1 - (p + 1) * w_min) * (hi - lo) + 1e-12)
+
+
+def test_alibi_on_equal_keys_gives_geometric_weights(oracle_lib):
+    case = equal_keys(ext_case(seed=86))
+    slopes = np.array([0.5, 0.25, 0.125, 0.0625, 1.0, 2.0, 0.03125, 0.0], np.float32)
+    out = run_ext(case, alibi_slopes=slopes)
+    G = case.num_heads // case.num_kv_heads
+    for row, s, p in positions(case):
+        for h in range(case.num_heads):
+            ts = np.arange(p + 1)
+            w = np.exp(np.float64(slopes[h]) * (ts - p))
+            ref = (w[:, None] * v_rows(case, s, h // G, ts)).sum(0) / w.sum()
+            np.testing.assert_allclose(out[row, h], ref, rtol=0, atol=1e-12)
+
+
+def test_sink_on_equal_keys_scales_the_mean(oracle_lib):
+    case = equal_keys(ext_case(seed=87))
+    sinks = np.linspace(-3, 3, 8).astype(np.float32)
+    out = run_ext(case, sinks=sinks)
+    G = case.num_heads // case.num_kv_heads
+    q = case.q.double().numpy()
+    for row, s, p in positions(case):
+        for h in range(case.num_heads):
+            kvh = h // G
+            K0 = torch.from_numpy(np.ascontiguousarray(case.k_cache.numpy()[0, kvh, :, 0, :].reshape(128))) \
+                .view(torch.float8_e4m3fn).double().numpy() * case.k_scale
+            z = case.scale * float(q[row, h] @ K0)
+            n = p + 1
+            frac = n * np.exp(z) / (n * np.exp(z) + np.exp(np.float64(sinks[h])))
+            ref = v_rows(case, s, kvh, range(n)).mean(axis=0) * frac
+            np.testing.assert_allclose(out[row, h], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_ext_rejects_bad_options(oracle_lib):
+    case = ext_case(seed=88)
+    with pytest.raises(ValueError):
+        run_ext(case, sliding_window=-1)
+    with pytest.raises(ValueError):
+        run_ext(case, softcap=-1.0)
+    with pytest.raises(ValueError):
+        run_ext(case, sinks=np.zeros(3, np.float32))
