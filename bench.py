@@ -320,6 +320,17 @@ def main():
                   file=sys.stderr, flush=True)
         args.workload = "target"
 
+    m = re.fullmatch(r"cache_write_(prefill|decode)_(\d+)x(\d+)", args.workload)
+    if m:   # one workload of the cache write, for profiling runs
+        T, hkv = int(m.group(2)), int(m.group(3))
+        us = time_cache_write(T, args.steps, args.warmup, num_kv_heads=hkv,
+                              prefill=m.group(1) == "prefill")
+        b = cache_write_bytes(T, hkv)
+        print(json.dumps({"workload": args.workload, "us_per_call": round(us, 2),
+                          "GBps": round(b / us / 1e3, 1), "frac_of_peak": round(b / us / 1e3 / PEAK_GBS, 4),
+                          "bytes": b}), flush=True)
+        return
+
     case = make_workload(args.workload, "cuda")
     us = time_calls(case, args.steps, args.warmup)
     B = case.algorithmic_bytes()

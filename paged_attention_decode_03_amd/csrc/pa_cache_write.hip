@@ -52,15 +52,14 @@ __device__ __forceinline__ uint32_t fp8x4_saturate(float a, float b, float c, fl
 constexpr int kWavesPerBlock = 4;
 constexpr int kGroup = kBlockTokens;  // tokens per wave
 
-// One token, two dims per lane (any slot pattern).
-__device__ __forceinline__ void write_token(const CacheWriteParams& p, int t, int kvh, int64_t slot,
-                                            int lane, float ks, float vs) {
+// One token, two dims per lane (any slot pattern); kw / vw hold the lane's two
+// bf16 key and value dims of the token.
+__device__ __forceinline__ void write_token(const CacheWriteParams& p, int kvh, int64_t slot, int lane,
+                                            uint32_t kw, uint32_t vw, float ks, float vs) {
   if (slot < 0 || slot >= p.num_blocks * kBlockTokens) return;
   const int64_t block = slot / kBlockTokens;
   const int j = (int)(slot % kBlockTokens);
   const int d = 2 * lane;
-  const uint32_t kw = *(const uint32_t*)(p.key + t * p.key_stride + kvh * kHeadDim + d);
-  const uint32_t vw = *(const uint32_t*)(p.value + t * p.value_stride + kvh * kHeadDim + d);
   const uint32_t kc = fp8x2_saturate(bf16_lo(kw) / ks, bf16_hi(kw) / ks);
   const uint32_t vc = fp8x2_saturate(bf16_lo(vw) / vs, bf16_hi(vw) / vs);
   const size_t page = ((size_t)block * p.num_kv_heads + kvh) * kPageBytes;
@@ -140,10 +139,22 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void pa_cache_write_kernel(con
     write_block(p, t0, kvh, s0 / kBlockTokens, lane, ks, vs);
     return;
   }
-  for (int i = 0; i < n; ++i) {
+  // Any slot pattern: read every token's two dims first (the cache stores may
+  // alias the inputs as far as the compiler knows, so loads interleaved with
+  // them would wait for each store), then convert and store token by token.
+  uint32_t kw[kGroup], vw[kGroup];
+#pragma unroll
+  for (int i = 0; i < kGroup; ++i) {
+    const int t = t0 + min(i, n - 1);
+    kw[i] = *(const uint32_t*)(p.key + t * p.key_stride + kvh * kHeadDim + 2 * lane);
+    vw[i] = *(const uint32_t*)(p.value + t * p.value_stride + kvh * kHeadDim + 2 * lane);
+  }
+#pragma unroll
+  for (int i = 0; i < kGroup; ++i) {
+    if (i >= n) break;
     const int64_t slot = (int64_t)(uint32_t)__builtin_amdgcn_readlane((int)(my_slot & 0xFFFFFFFF), i) |
                          ((int64_t)__builtin_amdgcn_readlane((int)(my_slot >> 32), i) << 32);
-    write_token(p, t0 + i, kvh, slot, lane, ks, vs);
+    write_token(p, kvh, slot, lane, kw[i], vw[i], ks, vs);
   }
 }
 
