@@ -243,12 +243,14 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   const int32_t q_tile = mq ? (pa::kMaxGroup / G > 0 ? pa::kMaxGroup / G : 1) : 1;
   const int32_t q_tiles = mq ? (max_seqlen_q + q_tile - 1) / q_tile : 1;
   Plan plan;
-  int rc = make_plan(S, Hq, Hkv, W, device_cus(dev), ppp_req, &plan, q_tiles, mq ? num_q_rows : S);
+  // work items per (sequence, kv head, partition): one per pair of query tiles
+  const int32_t q_items = q_tiles > 1 ? (q_tiles + 1) / 2 : 1;
+  int rc = make_plan(S, Hq, Hkv, W, device_cus(dev), ppp_req, &plan, q_items, mq ? num_q_rows : S);
   if (rc) return rc;
   // one 64-lane block per work item, 256 lanes per merged row: keep both grids
   // within 2^32 lanes
   const int64_t units = (int64_t)S * Hkv * plan.num_parts;
-  const int64_t items = mq ? (units + 7) / 8 * 8 * q_tiles : units;
+  const int64_t items = mq ? (units + 7) / 8 * 8 * q_items : units;
   const int64_t merge_rows = (int64_t)(mq ? num_q_rows : S) * Hq;
   if (items > (int64_t(1) << 26) || merge_rows > (int64_t(1) << 24))
     return fail(PA_ERR_UNSUPPORTED, "launch too large: %lld work items, %lld merged rows",
@@ -280,6 +282,8 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   p.num_q_rows = mq ? num_q_rows : S;
   p.q_tile = q_tile;
   p.num_q_tiles = q_tiles;
+  // more than one tile of queries: two tiles per item share the page reads
+  p.tiles_per_item = q_tiles > 1 ? 2 : 1;
   p.window = opt.sliding_window;
   p.softcap = opt.logits_soft_cap;
   p.scale = scale;

@@ -71,6 +71,9 @@ constexpr int kRingDepth = PA_RING_DEPTH;
 // The per-slot-scale variant keeps 8 more VGPRs per page in flight; 2 pages per
 // stage keep it at 2 waves per SIMD.
 constexpr int kSlotScalePagesPerStage = 2;
+// Two query tiles per item hold a second set of accumulators: 2 pages per stage
+// keep that variant at 2 waves per SIMD too.
+constexpr int kTwoTilePagesPerStage = 2;
 // Word 3 of a raw buffer resource (no format conversion, no swizzle).
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -143,7 +146,11 @@ struct Stage {
 // tile times the group's heads.  Query i of a sequence with L tokens and q_len
 // queries sees tokens 0 .. L - q_len + i, so a tile's context ends at its last
 // query's position and the tokens past each column's own position are masked.
-template <int PPS, int NB, bool SS, bool MQ, int AUX = PA_LOAD_AUX, bool TR = false>
+//
+// NT (several queries): query tiles per item.  With NT = 2 one wave holds two
+// tiles' columns (two sets of accumulators against the same K/V registers), so
+// up to 2 * q_tile queries of a sequence cost one read of its pages.
+template <int PPS, int NB, bool SS, bool MQ, int AUX = PA_LOAD_AUX, bool TR = false, int NT = 1>
 __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU))) void pa_decode_kernel(const DecodeParams p) {
   const int lane = threadIdx.x & 63;
   // Token rows: a workgroup holds kv_group kv heads of one sequence (one wave
@@ -154,16 +161,17 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
   const int rq = lane >> 4;   // row quad: rows 4*rq .. 4*rq+3 of the 16x16 tiles
 
   int item = blockIdx.x;
-  int qt = 0;  // query tile
+  int qt0 = 0;  // first query tile of the item (it holds NT)
   if constexpr (MQ) {
-    // The query tiles of one (sequence, kv head, partition) read the same
-    // pages: place them 8 blocks apart, which puts them on one XCD (blocks go
-    // to the 8 XCDs round robin) at about the same time, so one tile's page
-    // reads are served by that XCD's L2 for the others.
+    // The items of one (sequence, kv head, partition) read the same pages:
+    // place them 8 blocks apart, which puts them on one XCD (blocks go to the
+    // 8 XCDs round robin) at about the same time, so one item's page reads are
+    // served by that XCD's L2 for the others.
+    const int ngroups = (p.num_q_tiles + NT - 1) / NT;
     const int xcd = item & 7;
     const int r = item >> 3;
-    qt = r % p.num_q_tiles;
-    item = (r / p.num_q_tiles) * 8 + xcd;
+    qt0 = (r % ngroups) * NT;
+    item = (r / ngroups) * 8 + xcd;
     if (item >= p.num_seqs * p.num_kv_heads * p.num_parts) return;  // grid padding
   }
   const int part = item % p.num_parts;
@@ -181,13 +189,21 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
     g = col - qi * p.group;
     q0 = scalar_load(p.cu_seqlens_q + s);
     q_len = scalar_load(p.cu_seqlens_q + s + 1) - q0;
-    if (qt * p.q_tile >= q_len) return;  // no query of this sequence in this tile
+    if (qt0 * p.q_tile >= q_len) return;  // no query of this sequence in the item's tiles
   }
   const int h = kvh * p.group + g;
-  const int qrow = q0 + qt * p.q_tile + qi;  // row of q and out
-  const bool hvalid = MQ ? (col < p.q_tile * p.group && qt * p.q_tile + qi < q_len && qrow >= 0 && qrow < p.num_q_rows)
-                          : col < p.group;
-  const size_t orow = ((size_t)qrow * p.num_heads + h) * kHeadDim;
+  int qrow[NT];      // row of q and out
+  bool hvalid[NT];   // the column holds a query of this sequence
+  size_t orow[NT];
+#pragma unroll
+  for (int u = 0; u < NT; ++u) {
+    const int qt = qt0 + u;
+    qrow[u] = q0 + qt * p.q_tile + qi;
+    hvalid[u] = MQ ? (col < p.q_tile * p.group && qt < p.num_q_tiles && qt * p.q_tile + qi < q_len &&
+                      qrow[u] >= 0 && qrow[u] < p.num_q_rows)
+                   : col < p.group;
+    orow[u] = ((size_t)qrow[u] * p.num_heads + h) * kHeadDim;
+  }
 
   // Start the three independent reads of the prologue together: this
   // partition's slice of the block-table row (its length is not known yet, so
@@ -202,31 +218,38 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
 
   // B operand of QK^T: q^T, 8 dims per MFMA.  Element e of qop[h2][c] is dim
   // 16 * (4 * h2 + rq) + 8 * c + e, matching the K bytes this lane loads.
-  bf16x8 qop[2][2];
-  if (hvalid) {
-    const uint16_t* qrow = p.q + orow;
+  bf16x8 qop[NT][2][2];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
+  for (int u = 0; u < NT; ++u) {
+    if (hvalid[u]) {
+      const uint16_t* qp = p.q + orow[u];
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-        qop[h2][c] = *(const bf16x8*)(qrow + 16 * (4 * h2 + rq) + 8 * c);
-  } else {
+      for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2)
+        for (int c = 0; c < 2; ++c)
+          qop[u][h2][c] = *(const bf16x8*)(qp + 16 * (4 * h2 + rq) + 8 * c);
+    } else {
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-        qop[h2][c] = bf16x8{};
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          qop[u][h2][c] = bf16x8{};
+    }
   }
 
   const int Lseq = clamp_len(scalar_load(p.seq_lens + s), p.max_blocks);
   // tokens this item's queries can see: all of them for one query per sequence;
   // up to the tile's last query's position otherwise
-  int L = Lseq, pos_first = Lseq - 1, pos_col = Lseq - 1;
+  int L = Lseq, pos_first = Lseq - 1;
+  int pos_col[NT];  // the column's query position (its causal end)
+#pragma unroll
+  for (int u = 0; u < NT; ++u) pos_col[u] = Lseq - 1;
   if constexpr (MQ) {
-    const int base = Lseq - q_len;  // position of query 0 minus 0
-    L = max(0, min(Lseq, base + min(qt * p.q_tile + p.q_tile, q_len)));
-    pos_first = base + qt * p.q_tile;
-    pos_col = hvalid ? base + qt * p.q_tile + qi : L - 1;
+    const int base = Lseq - q_len;  // position of query 0
+    L = max(0, min(Lseq, base + min((qt0 + NT) * p.q_tile, q_len)));
+    pos_first = base + qt0 * p.q_tile;
+#pragma unroll
+    for (int u = 0; u < NT; ++u) pos_col[u] = hvalid[u] ? base + (qt0 + u) * p.q_tile + qi : L - 1;
   }
   const int npages = (L + kBlockTokens - 1) / kBlockTokens;
   const int nused = (npages + ppp - 1) / ppp;  // partitions holding tokens
@@ -234,10 +257,13 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
   const bool direct = nused <= 1;  // one partition: write the final output here
 
   if (L == 0) {  // empty context: an all-zero row
-    if (hvalid) {
 #pragma unroll
-      for (int jd = 0; jd < 8; ++jd)
-        *(uint2*)(p.out + orow + jd * 16 + rq * 4) = make_uint2(0u, 0u);
+    for (int u = 0; u < NT; ++u) {
+      if (hvalid[u]) {
+#pragma unroll
+        for (int jd = 0; jd < 8; ++jd)
+          *(uint2*)(p.out + orow[u] + jd * 16 + rq * 4) = make_uint2(0u, 0u);
+      }
     }
     return;
   }
@@ -245,22 +271,27 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
   const int pend = min(pbeg + ppp, npages);
   const int tend = min(L, pend * kBlockTokens);  // first token this item must not use
   // several queries: first token this column must not use (its own causal end)
-  const int tlim = MQ ? min(tend, pos_col + 1) : tend;
+  int tlim[NT];
+#pragma unroll
+  for (int u = 0; u < NT; ++u) tlim[u] = MQ ? min(tend, pos_col[u] + 1) : tend;
 
   // Options of the several-queries form (window, softcap, ALiBi, sinks).
   // Window: this column uses tokens tlo .. pos_col; the item starts at the
   // first whole stage holding a token any of its columns can see (pstart).
-  int tlo = 0, tlo_max = INT_MIN, pstart = pbeg;
+  int tlo[NT], tlo_max = INT_MIN, pstart = pbeg;
+#pragma unroll
+  for (int u = 0; u < NT; ++u) tlo[u] = 0;
   float slope_l2 = 0.0f, sink_l2 = -INFINITY;
   if constexpr (MQ) {
     if (p.window > 0) {
-      tlo = pos_col - p.window + 1;
-      tlo_max = L - p.window;  // the latest window start among the tile's columns
+#pragma unroll
+      for (int u = 0; u < NT; ++u) tlo[u] = pos_col[u] - p.window + 1;
+      tlo_max = L - p.window;  // the latest window start among the item's columns
       const int lo_pg = max(0, pos_first - p.window + 1) / kBlockTokens;
       if (lo_pg > pbeg) pstart = pbeg + min(lo_pg - pbeg, ppp) / PPS * PPS;  // whole stages
     }
-    if (p.alibi_slopes && hvalid) slope_l2 = p.alibi_slopes[h] * kLog2e;
-    if (p.sinks && hvalid) sink_l2 = p.sinks[h] * kLog2e;
+    if (p.alibi_slopes) slope_l2 = p.alibi_slopes[h] * kLog2e;  // h < num_heads in every lane
+    if (p.sinks) sink_l2 = p.sinks[h] * kLog2e;
   }
   const int ioff = MQ ? pstart - pbeg : 0;  // first staged page this item loads
 
@@ -287,16 +318,21 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
   // bytes a page's descriptor covers
   const int page_bytes = TR ? (kBlockTokens - 1) * tstride + kHeadDim : kPageBytes;
 
-  f32x4 acc[8];  // O^T tiles: dims 16*jd + 4*rq + i for head `col`
+  f32x4 acc[NT][8];  // O^T tiles: dims 16*jd + 4*rq + i for column `col`
+  f32x4 accl[NT];    // softmax denominator (same value in every element)
+  float m_run[NT];
 #pragma unroll
-  for (int jd = 0; jd < 8; ++jd) acc[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 accl = {0.f, 0.f, 0.f, 0.f};  // softmax denominator (same value in every element)
-  float m_run = -INFINITY;
-  if constexpr (MQ) {
-    // the sink: one more softmax term 2^sink with no value, counted once (partition 0)
-    if (part == 0 && sink_l2 > -INFINITY) {
-      m_run = sink_l2;
-      accl = f32x4{1.f, 1.f, 1.f, 1.f};
+  for (int u = 0; u < NT; ++u) {
+#pragma unroll
+    for (int jd = 0; jd < 8; ++jd) acc[u][jd] = f32x4{0.f, 0.f, 0.f, 0.f};
+    accl[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[u] = -INFINITY;
+    if constexpr (MQ) {
+      // the sink: one more softmax term 2^sink with no value, counted once (partition 0)
+      if (part == 0 && hvalid[u] && sink_l2 > -INFINITY) {
+        m_run[u] = sink_l2;
+        accl[u] = f32x4{1.f, 1.f, 1.f, 1.f};
+      }
     }
   }
   const f16x4 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
@@ -416,51 +452,63 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
     // columns with their own causal end: the stages reaching past the tile's first
     // position; with a window, also the stages before the latest window start
     const bool causal = MQ && ((j0 + PPS) * kBlockTokens > pos_first + 1 || j0 * kBlockTokens < tlo_max);
-    f32x4 z[PPS];
+    f32x4 z[NT][PPS];
 #pragma unroll
     for (int pp = 0; pp < PPS; ++pp) {
-      f32x4 t = {0.f, 0.f, 0.f, 0.f};
+      bf16x8 kb[2][2];  // the page's K operand, shared by the item's tiles
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const u32x4 kk = st.k[pp][h2];
-        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(kk[0], kk[1]), qop[h2][0], t, 0, 0, 0);
-        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(kk[2], kk[3]), qop[h2][1], t, 0, 0, 0);
+        kb[h2][0] = fp8x8_to_bf16(kk[0], kk[1]);
+        kb[h2][1] = fp8x8_to_bf16(kk[2], kk[3]);
       }
-      z[pp] = t;
+#pragma unroll
+      for (int u = 0; u < NT; ++u) {
+        f32x4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[h2][0], qop[u][h2][0], t, 0, 0, 0);
+          t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[h2][1], qop[u][h2][1], t, 0, 0, 0);
+        }
+        z[u][pp] = t;
+      }
     }
     // scale, mask, running max
-    float mx = -INFINITY;
 #pragma unroll
-    for (int pp = 0; pp < PPS; ++pp) {
+    for (int u = 0; u < NT; ++u) {
+      float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = z[pp][i] * c_log2;
-        if constexpr (SS) v *= __uint_as_float(st.ks[pp][i]);
-        if constexpr (MQ) {
-          const int t = (j0 + pp) * kBlockTokens + rq * 4 + i;
-          if (capped) {
-            // c tanh(z / c) = c (1 - 2 / (e^(2 z / c) + 1)), then in log2 units
-            const float e2 = __builtin_amdgcn_exp2f(z[pp][i] * c_nat * cap_k);
-            v = cap_l2 * (1.0f - 2.0f * __builtin_amdgcn_rcpf(e2 + 1.0f));
+      for (int pp = 0; pp < PPS; ++pp) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = z[u][pp][i] * c_log2;
+          if constexpr (SS) v *= __uint_as_float(st.ks[pp][i]);
+          if constexpr (MQ) {
+            const int t = (j0 + pp) * kBlockTokens + rq * 4 + i;
+            if (capped) {
+              // c tanh(z / c) = c (1 - 2 / (e^(2 z / c) + 1)), then in log2 units
+              const float e2 = __builtin_amdgcn_exp2f(z[u][pp][i] * c_nat * cap_k);
+              v = cap_l2 * (1.0f - 2.0f * __builtin_amdgcn_rcpf(e2 + 1.0f));
+            }
+            if (biased) v += slope_l2 * (float)(t - pos_col[u]);
+            if (last || causal) v = (t < tlim[u] && t >= tlo[u]) ? v : -INFINITY;
+          } else if (last) {
+            const int t = (j0 + pp) * kBlockTokens + rq * 4 + i;
+            v = (t < tlim[u]) ? v : -INFINITY;
           }
-          if (biased) v += slope_l2 * (float)(t - pos_col);
-          if (last || causal) v = (t < tlim && t >= tlo) ? v : -INFINITY;
-        } else if (last) {
-          const int t = (j0 + pp) * kBlockTokens + rq * 4 + i;
-          v = (t < tlim) ? v : -INFINITY;
+          z[u][pp][i] = v;
+          mx = fmaxf(mx, v);
         }
-        z[pp][i] = v;
-        mx = fmaxf(mx, v);
       }
-    }
-    mx = max_over_rows(mx);
-    const float m_new = fmaxf(m_run, mx);
-    if (__builtin_amdgcn_ballot_w64(m_new > m_run)) {
-      const float alpha = (m_new == m_run) ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      mx = max_over_rows(mx);
+      const float m_new = fmaxf(m_run[u], mx);
+      if (__builtin_amdgcn_ballot_w64(m_new > m_run[u])) {
+        const float alpha = (m_new == m_run[u]) ? 1.0f : __builtin_amdgcn_exp2f(m_run[u] - m_new);
 #pragma unroll
-      for (int jd = 0; jd < 8; ++jd) acc[jd] *= alpha;
-      accl *= alpha;
-      m_run = m_new;
+        for (int jd = 0; jd < 8; ++jd) acc[u][jd] *= alpha;
+        accl[u] *= alpha;
+        m_run[u] = m_new;
+      }
     }
     // P = 2^(z - m) in fp16, then PV
     if constexpr (SS) {
@@ -484,7 +532,7 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
         f16x4 pb, pv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float e = __builtin_amdgcn_exp2f(z[pp][i] - m_run);
+          const float e = __builtin_amdgcn_exp2f(z[0][pp][i] - m_run[0]);
           pb[i] = (_Float16)e;
           // masked tokens have e == 0; their scale may be NaN and must not reach PV
           const float w = e == 0.0f ? 0.0f : fminf(e * __uint_as_float(st.vs[pp][i]) * vnorm, 65504.0f);
@@ -492,21 +540,28 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
         }
 #pragma unroll
         for (int jd = 0; jd < 8; ++jd)
-          acc[jd] = __builtin_amdgcn_mfma_f32_16x16x16f16(fp8x4_to_f16(vword(st, vtb, pp, jd) & vmask), pv, acc[jd], 0, 0, 0);
-        accl = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pb, accl, 0, 0, 0);
+          acc[0][jd] = __builtin_amdgcn_mfma_f32_16x16x16f16(fp8x4_to_f16(vword(st, vtb, pp, jd) & vmask), pv, acc[0][jd], 0, 0, 0);
+        accl[0] = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pb, accl[0], 0, 0, 0);
       } else {
-        f16x4 pb;
+        f16x4 pb[NT];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // a column that has seen no token yet has m_run = -inf: its weights are 0
-          float e = __builtin_amdgcn_exp2f(z[pp][i] - m_run);
-          if constexpr (MQ) e = (z[pp][i] == -INFINITY) ? 0.0f : e;
-          pb[i] = (_Float16)e;
+        for (int u = 0; u < NT; ++u) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            // a column that has seen no token yet has m_run = -inf: its weights are 0
+            float e = __builtin_amdgcn_exp2f(z[u][pp][i] - m_run[u]);
+            if constexpr (MQ) e = (z[u][pp][i] == -INFINITY) ? 0.0f : e;
+            pb[u][i] = (_Float16)e;
+          }
         }
 #pragma unroll
-        for (int jd = 0; jd < 8; ++jd)
-          acc[jd] = __builtin_amdgcn_mfma_f32_16x16x16f16(fp8x4_to_f16(vword(st, vtb, pp, jd) & vmask), pb, acc[jd], 0, 0, 0);
-        accl = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pb, accl, 0, 0, 0);
+        for (int jd = 0; jd < 8; ++jd) {
+          const f16x4 va = fp8x4_to_f16(vword(st, vtb, pp, jd) & vmask);  // shared by the tiles
+#pragma unroll
+          for (int u = 0; u < NT; ++u) acc[u][jd] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb[u], acc[u][jd], 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < NT; ++u) accl[u] = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pb[u], accl[u], 0, 0, 0);
       }
     }
   };
@@ -525,23 +580,26 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
     }
   }
 
-  if (!hvalid) return;
-  const float lsum = accl[0];
-  if (direct) {
-    // several queries: lsum is 0 for a query that sees no token (more queries than context)
-    const float inv = (!MQ || lsum > 0.0f) ? (SS ? vnorm_inv : scalar_load(p.v_scale)) / lsum : 0.0f;
-    uint16_t* o = p.out + orow + rq * 4;
 #pragma unroll
-    for (int jd = 0; jd < 8; ++jd) {
-      const f32x4 a = acc[jd];
-      *(uint2*)(o + jd * 16) = make_uint2(pack_bf16x2(a[0] * inv, a[1] * inv), pack_bf16x2(a[2] * inv, a[3] * inv));
+  for (int u = 0; u < NT; ++u) {
+    if (!hvalid[u]) continue;
+    const float lsum = accl[u][0];
+    if (direct) {
+      // several queries: lsum is 0 for a query that sees no token (more queries than context)
+      const float inv = (!MQ || lsum > 0.0f) ? (SS ? vnorm_inv : scalar_load(p.v_scale)) / lsum : 0.0f;
+      uint16_t* o = p.out + orow[u] + rq * 4;
+#pragma unroll
+      for (int jd = 0; jd < 8; ++jd) {
+        const f32x4 a = acc[u][jd];
+        *(uint2*)(o + jd * 16) = make_uint2(pack_bf16x2(a[0] * inv, a[1] * inv), pack_bf16x2(a[2] * inv, a[3] * inv));
+      }
+    } else {
+      const size_t prow = ((size_t)qrow[u] * p.num_heads + h) * p.num_parts + part;
+      float* a = p.part_acc + prow * kHeadDim + rq * 4;
+#pragma unroll
+      for (int jd = 0; jd < 8; ++jd) *(f32x4*)(a + jd * 16) = acc[u][jd] * vnorm_inv;
+      if (rq == 0) *(float2*)(p.part_ml + prow * 2) = make_float2(m_run[u], lsum);
     }
-  } else {
-    const size_t prow = ((size_t)qrow * p.num_heads + h) * p.num_parts + part;
-    float* a = p.part_acc + prow * kHeadDim + rq * 4;
-#pragma unroll
-    for (int jd = 0; jd < 8; ++jd) *(f32x4*)(a + jd * 16) = acc[jd] * vnorm_inv;
-    if (rq == 0) *(float2*)(p.part_ml + prow * 2) = make_float2(m_run, lsum);
   }
 }
 
@@ -571,7 +629,9 @@ __global__ __launch_bounds__(kMergeThreads) void pa_merge_kernel(const DecodePar
     const int Lseq = clamp_len(scalar_load(p.seq_lens + s), p.max_blocks);
     const int qt = (r - q0) / p.q_tile;
     if (qt >= p.num_q_tiles) return;  // past max_seqlen_q: not computed
-    L = max(0, min(Lseq, Lseq - q_len + min(qt * p.q_tile + p.q_tile, q_len)));
+    // the decode item holding this row covered tiles up to the end of its group
+    const int tiles_end = (qt / p.tiles_per_item + 1) * p.tiles_per_item;
+    L = max(0, min(Lseq, Lseq - q_len + min(tiles_end * p.q_tile, q_len)));
   } else {
     L = clamp_len(scalar_load(p.seq_lens + s), p.max_blocks);
   }
@@ -650,15 +710,20 @@ __global__ __launch_bounds__(kMergeThreads) void pa_merge_kernel(const DecodePar
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const size_t units = (size_t)p.num_seqs * p.num_kv_heads * p.num_parts;
-  // several queries: units padded to a multiple of 8, times the query tiles
-  const size_t items = p.cu_seqlens_q ? (units + 7) / 8 * 8 * p.num_q_tiles : units;
+  // several queries: units padded to a multiple of 8, times the groups of tiles
+  const size_t items = p.cu_seqlens_q
+                           ? (units + 7) / 8 * 8 * (size_t)((p.num_q_tiles + p.tiles_per_item - 1) / p.tiles_per_item)
+                           : units;
   if (p.token_rows)
     hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false, PA_LOAD_AUX, true>),
                        dim3((unsigned)(items / p.kv_group)), dim3(64 * p.kv_group),
                        (unsigned)(p.kv_group * 2 * kVtBytes<kPagesPerStage>), stream, p);
-  else if (p.cu_seqlens_q && p.num_q_tiles > 1)
-    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, true, 0>), dim3((unsigned)items),
-                       dim3(64), 0, stream, p);
+  else if (p.cu_seqlens_q && p.tiles_per_item == 2 && p.num_q_tiles > 2)
+    hipLaunchKernelGGL((pa_decode_kernel<kTwoTilePagesPerStage, kRingDepth, false, true, 0, false, 2>),
+                       dim3((unsigned)items), dim3(64), 0, stream, p);
+  else if (p.cu_seqlens_q && p.tiles_per_item == 2)
+    hipLaunchKernelGGL((pa_decode_kernel<kTwoTilePagesPerStage, kRingDepth, false, true, PA_LOAD_AUX, false, 2>),
+                       dim3((unsigned)items), dim3(64), 0, stream, p);
   else if (p.cu_seqlens_q)
     hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, true>), dim3((unsigned)items),
                        dim3(64), 0, stream, p);
