@@ -294,7 +294,7 @@ def main():
     if args.workload == "all":
         for name in suite_names():
             case = make_workload(name, "cuda")
-            us = time_calls(case, max(10, args.steps // 4), 5)
+            us = time_calls(case, args.steps, args.warmup)
             us_graph = time_graph(case)
             P, ppp, _ = pa.pa_decode_plan(case.num_seqs, case.num_heads, case.num_kv_heads,
                                           case.max_blocks, 256)
@@ -312,7 +312,7 @@ def main():
             torch.cuda.empty_cache()
         for name, T, pre in (("cache_write_decode_256x8", 256, False),
                              ("cache_write_prefill_32768x8", 32768, True)):
-            us = time_cache_write(T, max(10, args.steps // 4), 5, prefill=pre)
+            us = time_cache_write(T, args.steps, args.warmup, prefill=pre)
             b = cache_write_bytes(T)
             print(json.dumps({"workload": name, "us_per_call": round(us, 2),
                               "GBps": round(b / us / 1e3, 1),
