@@ -42,8 +42,15 @@ KERNEL_SRC = os.path.join(ROOT, "paged_attention_decode_03_amd", "csrc", "pa_dec
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256 (16 hex digits) of the decode kernel's source with // comments
+    and blank lines removed, so that comment edits keep counter data valid."""
+    code = []
+    with open(KERNEL_SRC, encoding="utf-8") as f:
+        for line in f:
+            line = line.split("//", 1)[0].rstrip()
+            if line:
+                code.append(line)
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()[:16]
 
 
 def counter_traffic():

@@ -32,6 +32,8 @@
 // layouts of the API page's unified backend) load K the same way (lane l:
 // 16 B chunks of token l & 15's row) and V as 32 B per lane of token rows;
 // a V page then passes through LDS, transposed into the dims x tokens operand.
+// Several queries per sequence (MQ): the 16 columns hold (query token, head)
+// pairs, and an item holds one or two such tiles against the same K/V.
 // Pages are software-pipelined PPS at a time, one stage ahead.
 #include <limits.h>
 #include <math.h>
@@ -52,8 +54,9 @@ typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 // of stages (depth - 1 stages are in flight while one is computed), waves per
 // SIMD the register budget is sized for, and the cache-policy bits of the K/V
 // loads (gfx950 buffer-load aux: 2 = nt, i.e. streamed once, not kept).
-// Several query tiles of one sequence read the same pages: their loads use the
-// default policy instead, so the pages stay in L2 for the other tiles.
+// When a sequence's query tiles are spread over several items, those items
+// read the same pages: their loads use the default policy instead, so the
+// pages stay in L2 for the other items.
 #ifndef PA_PAGES_PER_STAGE
 #define PA_PAGES_PER_STAGE 4
 #endif
