@@ -30,9 +30,10 @@
  * Errors: every check runs before any launch.  A failing call returns a
  * negative pa_status, launches nothing, and leaves a message for
  * pa_last_error() (thread-local).  No exception crosses the ABI; nothing aborts.
- * Conditions that only device memory could reveal are not checked: seq_lens
- * above 16 * max_blocks_per_seq are clamped to that, and block ids are trusted
- * (an id outside [0, num_blocks) reads outside the caches).
+ * Conditions that only device memory could reveal are not reported: seq_lens
+ * above 16 * max_blocks_per_seq are clamped to that, and a used block id
+ * outside [0, num_blocks) reads as an all-zero page (zero K, V and slot
+ * scales) without touching memory, so the result is defined but meaningless.
  */
 #ifndef PAGED_ATTENTION_H_
 #define PAGED_ATTENTION_H_

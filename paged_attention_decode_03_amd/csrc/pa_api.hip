@@ -9,6 +9,7 @@
 // and precision: the kernel choice is made on the host from shapes so one
 // captured graph uses one kernel).
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -275,6 +276,7 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   p.num_kv_heads = Hkv;
   p.group = G;
   p.max_blocks = W;
+  p.num_blocks_u32 = (uint32_t)(NB < INT32_MAX ? NB : INT32_MAX);
   p.num_parts = plan.num_parts;
   p.pages_per_part = plan.pages_per_part;
   p.scale_log2e = (float)((double)scale * 1.4426950408889634);

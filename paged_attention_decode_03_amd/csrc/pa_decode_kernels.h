@@ -31,6 +31,7 @@ struct DecodeParams {
   int32_t num_kv_heads;
   int32_t group;             // num_heads / num_kv_heads, 1..16
   int32_t max_blocks;        // W, block-table row length
+  uint32_t num_blocks_u32;   // physical blocks in the caches (capped at 2^31 - 1)
   int32_t num_parts;         // P, partitions per sequence
   int32_t pages_per_part;    // blocks per partition
   float scale_log2e;         // softmax scale * log2(e)

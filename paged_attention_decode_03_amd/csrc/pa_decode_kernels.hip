@@ -394,7 +394,10 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
     }
 #pragma unroll
     for (int pp = 0; pp < PPS; ++pp) {
-      const int bytes = (i0 + pp < npg) ? page_bytes : 0;
+      // a block id outside the caches (a caller error the host cannot see) reads
+      // as an all-zero page instead of touching memory
+      const bool used = i0 + pp < npg && (uint32_t)pid[pp] < p.num_blocks_u32;
+      const int bytes = used ? page_bytes : 0;
       const size_t off = (size_t)__builtin_amdgcn_readfirstlane(pid[pp]) * page_stride;
       const __amdgpu_buffer_rsrc_t rk =
           __builtin_amdgcn_make_buffer_rsrc((void*)(kpage0 + off), (short)0, bytes, kRsrcWord3);
@@ -402,7 +405,7 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
           __builtin_amdgcn_make_buffer_rsrc((void*)(vpage0 + off), (short)0, bytes, kRsrcWord3);
       if constexpr (SS) {
         const size_t srow = ((size_t)__builtin_amdgcn_readfirstlane(pid[pp]) * p.num_kv_heads + kvh) * kBlockTokens;
-        const int sbytes = (i0 + pp < npg) ? kBlockTokens * 4 : 0;
+        const int sbytes = used ? kBlockTokens * 4 : 0;
         const __amdgpu_buffer_rsrc_t rks =
             __builtin_amdgcn_make_buffer_rsrc((void*)(p.k_slot_scales + srow), (short)0, sbytes, kRsrcWord3);
         const __amdgpu_buffer_rsrc_t rvs =
@@ -517,8 +520,10 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
     if constexpr (SS) {
       if (stage == 0) {
         // 2^-e for the exponent e of the item's first V scale (token 0 is always
-        // in the context); clamped so that the factor and its inverse are normal
-        const uint32_t eb = min(max((__builtin_amdgcn_readfirstlane(st.vs[0][0]) >> 23) & 0xFFu, 1u), 253u);
+        // in the context); clamped so that the factor and its inverse are normal,
+        // and 1 when that scale is zero or subnormal (e.g. a page read as zeros)
+        const uint32_t e0 = (__builtin_amdgcn_readfirstlane(st.vs[0][0]) >> 23) & 0xFFu;
+        const uint32_t eb = e0 == 0u ? 127u : min(e0, 253u);
         vnorm = __uint_as_float((254u - eb) << 23);
         vnorm_inv = __uint_as_float(eb << 23);
       }

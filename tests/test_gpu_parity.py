@@ -290,3 +290,57 @@ def test_slot_scales_ragged_with_poison():
     out = run_gpu_slot(case)
     seqs = sample_seqs(case, 8)
     compare(out, oracle_slot(case, seqs), "slot scales ragged", seqs, relative=True)
+
+
+# ---------------------------------------------------------------- caller errors on the device
+
+def test_block_ids_outside_the_caches_read_as_zero_pages():
+    """A block id outside [0, num_blocks) in a used table entry is a caller
+    error the host cannot see: every entry point must read such a page as
+    zeros (no memory access), i.e. give bit for bit the result of the same
+    table pointing at an all-zero block."""
+    import paged_attention_decode_03_amd as pa
+    case = workloads.make_case(8, 2, [40, 70, 33], seed=97, extra_blocks=4, scale_mode="per_slot")
+    NB = case.k_cache.shape[0]
+    used = set(case.block_tables.flatten().tolist())
+    zero_blk = next(b for b in range(NB) if b not in used)
+    case.k_cache[zero_blk] = 0
+    case.v_cache[zero_blk] = 0
+    case.k_slot_scales[zero_blk] = 1.0
+    case.v_slot_scales[zero_blk] = 1.0
+    bad_ids = [NB, NB + 7, -1, 2**31 - 1]
+    spots = [(0, 1), (1, 0), (1, 3), (2, 2)]    # (sequence, table entry) inside each context
+    zero_tab = case.block_tables.clone()
+    bad_tab = case.block_tables.clone()
+    for (s, j), b in zip(spots, bad_ids):
+        zero_tab[s, j] = zero_blk
+        bad_tab[s, j] = b
+    c = case.to("cuda")
+    ks = torch.tensor([case.k_scale], device="cuda")
+    vs = torch.tensor([case.v_scale], device="cuda")
+    cu = torch.tensor([0, 2, 5, 6], dtype=torch.int32, device="cuda")
+    q_multi = torch.randn(6, 8, 128, device="cuda").to(torch.bfloat16)
+    kv, vv = workloads.token_row_views(c, "nhd")
+
+    def calls(tab):
+        tab = tab.to("cuda")
+        outs = [pa.paged_decode_attention(c.q, c.k_cache, c.v_cache, tab, c.seq_lens, c.scale, ks, vs),
+                pa.paged_decode_attention_split(c.q, c.k_cache, c.v_cache, tab, c.seq_lens, c.scale,
+                                                ks, vs, 1),
+                pa.paged_decode_attention_slot_scales(c.q, c.k_cache, c.v_cache, tab, c.seq_lens,
+                                                      c.scale, c.k_slot_scales, c.v_slot_scales),
+                pa.paged_multi_query_attention(q_multi, cu, 3, c.k_cache, c.v_cache, tab, c.seq_lens,
+                                               c.scale, ks, vs),
+                pa.paged_decode_attention_nhd(c.q, kv, vv, tab, c.seq_lens, c.scale, ks, vs)]
+        torch.cuda.synchronize()
+        return outs
+
+    for name, a, b in zip(("decode", "split", "slot scales", "multi-query", "token rows"),
+                          calls(zero_tab), calls(bad_tab)):
+        log(f"invalid block ids, {name}")
+        assert torch.isfinite(b.float()).all(), name
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), name
+    # the zero-block table is ordinary input: the decode meets the bound on it
+    # (per-tensor scales of 1 over codes up to 448: errors relative to |out|)
+    case.block_tables = zero_tab
+    compare(calls(zero_tab)[0], run_oracle(case), "zero-block table", relative=True)
