@@ -92,10 +92,13 @@ def make_workload(name, device):
         hq, hkv, ctx, s, ql = map(int, m.groups())
         return workloads.make_multi_case(hq, hkv, [ctx] * s, [ql] * s, seed=0, device=device,
                                          name=name)
-    m = re.fullmatch(r"ragged_(\d+)x(\d+)_seed(\d+)", name)
+    m = re.fullmatch(r"ragged_(\d+)x(\d+)_seed(\d+)(_lpt)?", name)
     if m:
-        hq, hkv, seed = map(int, m.groups())
-        return workloads.ragged(hq, hkv, seed, device=device)
+        hq, hkv, seed = map(int, m.groups()[:3])
+        case = workloads.ragged(hq, hkv, seed, device=device)
+        case.longest_first = m.group(4) is not None
+        case.name = name
+        return case
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -107,13 +110,15 @@ def suite_names():
     names += [f"specdec_40x8_ctx4096_s256_q{q}" for q in (2, 3, 4, 8)]
     names += [f"tokenrows_{lay}_40x8_ctx4096_s256" for lay in ("nhd", "combined", "packed")]
     names += [f"ragged_{a}x{b}_seed0" for (a, b) in workloads.RAGGED_LAYOUTS]
+    names += [f"ragged_{a}x{b}_seed0_lpt" for (a, b) in workloads.RAGGED_LAYOUTS]
     names += [f"dense_{a}x{b}_ctx{c}_s{s}" for (a, b, s, c) in workloads.LOW_BATCH]
     return names
 
 
 def make_call(case, out, stream=None):
     """One call of the entry point that serves `case` (per-tensor scales, per-slot
-    scales, or several queries per sequence), writing `out`."""
+    scales, token rows, longest-first dispatch, or several queries per
+    sequence), writing `out`."""
     import torch
     import paged_attention_decode_03_amd as pa
     dev = case.q.device
@@ -128,6 +133,10 @@ def make_call(case, out, stream=None):
         return lambda: pa.paged_decode_attention_nhd(case.q, kv, vv, case.block_tables,
                                                      case.seq_lens, case.scale, ks, vs, out=out,
                                                      stream=stream)
+    if getattr(case, "longest_first", False):
+        return lambda: pa.paged_attention_unified(case.q, None, 1, case.k_cache, case.v_cache,
+                                                  case.block_tables, case.seq_lens, case.scale, ks,
+                                                  vs, longest_first=True, out=out, stream=stream)
     if case.cu_seqlens_q is not None:
         max_q = int((case.cu_seqlens_q[1:] - case.cu_seqlens_q[:-1]).max().item())
         return lambda: pa.paged_multi_query_attention(

@@ -150,19 +150,33 @@ int paged_multi_query_attention(const void* q, const int32_t* cu_seqlens_q, int3
  *                    slopes[h] * (t - p), after the softcap
  *   sinks            NULL: off; else device fp32 [num_heads]: one more softmax
  *                    term exp(sinks[h]) that carries no value
+ * and, for any call:
+ *   longest_first    0: off; 1: work items are dispatched longest sequence first
+ *                    (a small kernel orders the sequences by length on the device
+ *                    before the attention; up to 8192 sequences).  Same results,
+ *                    bit for bit; pays off for ragged contexts (256 sequences of
+ *                    1..4000 tokens at 40/8 heads on MI355X: 226 -> 205 us) and
+ *                    costs the extra launch (about 4 us) when contexts are alike.
+ *                    Its scratch (4 bytes per sequence, after the split-KV scratch
+ *                    rounded up to 256 bytes) is not in pa_decode_plan's figure.
  */
 typedef struct pa_attention_options {
   int32_t sliding_window;
   float logits_soft_cap;
   const float* alibi_slopes;
   const float* sinks;
+  int32_t longest_first;
 } pa_attention_options;
 
 /*
  * paged_multi_query_attention with the options above (NULL options: none).
+ * cu_seqlens_q may be NULL: one query per sequence (the decode; num_q_tokens
+ * must equal num_seqs, max_seqlen_q is ignored), computed by the decode kernel
+ * when no logit option is set.
  * Errors: PA_ERR_SHAPE for a negative window, a negative or non-finite cap,
- * misaligned option arrays; otherwise as paged_multi_query_attention.  With a
- * window, pages wholly before every query's window are not read.
+ * misaligned option arrays, num_q_tokens != num_seqs without cu_seqlens_q;
+ * otherwise as paged_multi_query_attention.  With a window, pages wholly
+ * before every query's window are not read.
  */
 int paged_attention_unified(const void* q, const int32_t* cu_seqlens_q, int32_t num_q_tokens,
                             int32_t max_seqlen_q, const void* k_cache, const void* v_cache,

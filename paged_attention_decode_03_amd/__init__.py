@@ -53,7 +53,8 @@ class PagedAttentionError(RuntimeError):
 class AttentionOptions(ctypes.Structure):
     """pa_attention_options: sliding window, logit softcap, ALiBi slopes, sinks."""
     _fields_ = [("sliding_window", ctypes.c_int32), ("logits_soft_cap", ctypes.c_float),
-                ("alibi_slopes", ctypes.c_void_p), ("sinks", ctypes.c_void_p)]
+                ("alibi_slopes", ctypes.c_void_p), ("sinks", ctypes.c_void_p),
+                ("longest_first", ctypes.c_int32)]
 
 
 def load_library():
@@ -241,22 +242,28 @@ def paged_multi_query_attention(q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache,
 
 def paged_attention_unified(q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache, block_tables,
                             seq_lens, scale, k_scale, v_scale, sliding_window=0, softcap=0.0,
-                            alibi_slopes=None, sinks=None, out=None, stream=None):
+                            alibi_slopes=None, sinks=None, longest_first=False, out=None,
+                            stream=None):
     """paged_multi_query_attention with the unified backend's options:
     sliding_window (tokens ending at each query, 0 = off), softcap (0 = off),
-    alibi_slopes / sinks (float32 [num_heads] tensors on the q device, or None)."""
+    alibi_slopes / sinks (float32 [num_heads] tensors on the q device, or None),
+    and longest_first dispatch.  cu_seqlens_q=None: one query per sequence."""
     lib = load_library()
     dev, out, c_args, keep = _args(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale,
                                    v_scale, out, stream, q_rows_free=True)
     S = c_args[5]
-    if (cu_seqlens_q.dtype != torch.int32 or tuple(cu_seqlens_q.shape) != (S + 1,)
+    if cu_seqlens_q is not None and (
+            cu_seqlens_q.dtype != torch.int32 or tuple(cu_seqlens_q.shape) != (S + 1,)
             or cu_seqlens_q.device != dev or not cu_seqlens_q.is_contiguous()):
         raise TypeError("cu_seqlens_q must be a contiguous int32 [num_seqs + 1] tensor on the q device")
+    if cu_seqlens_q is None and q.shape[0] != S:
+        raise ValueError("without cu_seqlens_q, q must hold one row per sequence")
     for name, t in (("alibi_slopes", alibi_slopes), ("sinks", sinks)):
         if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (q.shape[1],)
                               or t.device != dev or not t.is_contiguous()):
             raise TypeError(f"{name} must be a contiguous float32 [num_heads] tensor on the q device")
-    opts = AttentionOptions(int(sliding_window), float(softcap), _ptr(alibi_slopes), _ptr(sinks))
+    opts = AttentionOptions(int(sliding_window), float(softcap), _ptr(alibi_slopes), _ptr(sinks),
+                            1 if longest_first else 0)
     (_, kc, vc, bt, sl, _, Hq, Hkv, D, bs, W, NB, sc, ks, vs, _, handle) = c_args
     with torch.cuda.device(dev):
         _check(lib.paged_attention_unified(

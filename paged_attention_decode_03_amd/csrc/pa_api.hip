@@ -46,8 +46,18 @@ constexpr int kStagePages = 4;        // the decode kernel loads 4 blocks per pi
 struct Plan {
   int32_t num_parts;
   int32_t pages_per_part;
+  bool longest_first;   // dispatch sequences longest first (order computed on the device)
+  size_t order_offset;  // bytes into the scratch where that order lives
   size_t workspace_bytes;
 };
+
+// Longest-first dispatch (an option): with ragged contexts, work items run
+// about as long as their sequences, and items dispatched last set the end of
+// the call.  A small kernel orders the sequences by length on the device (no
+// host read) and the decode kernel takes its items in that order.  Measured on
+// MI355X, 256 sequences of 1..4000 tokens at 40/8 heads: 226 -> 205 us; the
+// extra launch costs about 4 us, a loss when the contexts are all alike.
+constexpr int kLongestFirstMaxSeqs = 8192;  // what the one-workgroup order kernel holds
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -60,7 +70,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // with partitions of at least kMinPagesPerPart blocks, whole pipeline stages,
 // and never more than pa::kMaxPagesPerPart blocks.
 int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t W, int32_t num_cus, int32_t ppp_req,
-              Plan* plan, int32_t q_tiles = 1, int64_t q_rows = -1) {
+              Plan* plan, int32_t q_tiles = 1, int64_t q_rows = -1, bool longest_first = false) {
   if (S < 0 || Hq <= 0 || Hkv <= 0 || W < 0 || ppp_req < 0)
     return fail(PA_ERR_SHAPE, "plan: negative or zero size (S=%d Hq=%d Hkv=%d W=%d ppp=%d)", S, Hq,
                 Hkv, W, ppp_req);
@@ -85,8 +95,12 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t W, int32_t num_cus, in
   plan->num_parts = (int32_t)parts;
   plan->pages_per_part = (int32_t)ppp;
   const int64_t rows = q_rows >= 0 ? q_rows : S;
-  plan->workspace_bytes =
+  const size_t partial_bytes =
       parts > 1 ? (size_t)rows * Hq * parts * (pa::kHeadDim + 2) * sizeof(float) : 0;
+  plan->longest_first = longest_first && S >= 2 && S <= kLongestFirstMaxSeqs;
+  plan->order_offset = (partial_bytes + 255) & ~size_t(255);
+  plan->workspace_bytes =
+      plan->longest_first ? plan->order_offset + (size_t)S * sizeof(int32_t) : partial_bytes;
   return PA_OK;
 }
 
@@ -156,7 +170,7 @@ struct Variant {
   int32_t max_seqlen_q = 1;
   bool token_rows = false;                 // token-row cache layout with byte strides
   int64_t block_stride = 0, token_stride = 0, head_stride = 0;
-  pa_attention_options options = {0, 0.0f, nullptr, nullptr};  // several queries only
+  pa_attention_options options = {0, 0.0f, nullptr, nullptr, 0};
 };
 
 int decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
@@ -186,13 +200,16 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
     return fail(PA_ERR_UNSUPPORTED, "group size %d exceeds %d query heads per kv head", G,
                 pa::kMaxGroup);
   if (!isfinite(scale)) return fail(PA_ERR_SHAPE, "scale is not finite");
-  const bool mq = cu_seqlens_q != nullptr;
+  const pa_attention_options& opt = var.options;
+  // the several-queries kernel serves several queries and every logit option
+  const bool any_option = opt.sliding_window != 0 || opt.logits_soft_cap != 0.0f ||
+                          opt.alibi_slopes != nullptr || opt.sinks != nullptr;
+  const bool mq = cu_seqlens_q != nullptr || any_option;
   if (mq && (num_q_rows < 0 || max_seqlen_q < 0))
     return fail(PA_ERR_SHAPE, "negative num_q_tokens or max_seqlen_q");
   if (S == 0 || (mq && num_q_rows == 0)) return PA_OK;
   if (mq && max_seqlen_q == 0)
     return fail(PA_ERR_SHAPE, "max_seqlen_q must be positive when there are query tokens");
-  const pa_attention_options& opt = var.options;
   if (opt.sliding_window < 0)
     return fail(PA_ERR_SHAPE, "sliding_window %d is negative", opt.sliding_window);
   if (!(opt.logits_soft_cap >= 0.0f) || !isfinite(opt.logits_soft_cap))
@@ -246,7 +263,8 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   Plan plan;
   // work items per (sequence, kv head, partition): one per pair of query tiles
   const int32_t q_items = q_tiles > 1 ? (q_tiles + 1) / 2 : 1;
-  int rc = make_plan(S, Hq, Hkv, W, device_cus(dev), ppp_req, &plan, q_items, mq ? num_q_rows : S);
+  int rc = make_plan(S, Hq, Hkv, W, device_cus(dev), ppp_req, &plan, q_items, mq ? num_q_rows : S,
+                     opt.longest_first != 0);
   if (rc) return rc;
   // one 64-lane block per work item, 256 lanes per merged row: keep both grids
   // within 2^32 lanes
@@ -280,6 +298,7 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   p.num_parts = plan.num_parts;
   p.pages_per_part = plan.pages_per_part;
   p.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  p.multi_query = mq ? 1 : 0;
   p.cu_seqlens_q = cu_seqlens_q;
   p.num_q_rows = mq ? num_q_rows : S;
   p.q_tile = q_tile;
@@ -307,12 +326,16 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   p.block_stride = var.block_stride;
   p.token_stride = var.token_stride;
   p.head_stride = var.head_stride;
+  p.seq_order = nullptr;
   if (plan.workspace_bytes) {
     void* ws = nullptr;
     rc = ensure_workspace(dev, plan.workspace_bytes, stream, true, &ws);
     if (rc) return rc;
-    p.part_acc = (float*)ws;
-    p.part_ml = (float*)ws + (size_t)p.num_q_rows * Hq * plan.num_parts * pa::kHeadDim;
+    if (plan.num_parts > 1) {
+      p.part_acc = (float*)ws;
+      p.part_ml = (float*)ws + (size_t)p.num_q_rows * Hq * plan.num_parts * pa::kHeadDim;
+    }
+    if (plan.longest_first) p.seq_order = (int32_t*)((char*)ws + plan.order_offset);
   }
   const hipError_t err = pa::launch_decode(p, stream);
   if (err != hipSuccess) return fail(PA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
@@ -372,14 +395,22 @@ int paged_attention_unified(const void* q, const int32_t* cu_seqlens_q, int32_t 
                             int32_t block_size, int32_t max_blocks_per_seq, int64_t num_blocks,
                             float scale, const float* k_scale, const float* v_scale,
                             const pa_attention_options* options, void* out, void* stream) {
-  if (!cu_seqlens_q && num_seqs > 0) return fail(PA_ERR_NULL, "cu_seqlens_q is NULL");
-  if (num_seqs > 0 && num_q_tokens > 0 && ((uintptr_t)cu_seqlens_q & 3))
-    return fail(PA_ERR_SHAPE, "misaligned cu_seqlens_q (4 B)");
+  g_last_error[0] = '\0';
   Variant mq;
-  mq.cu_seqlens_q = cu_seqlens_q;
-  mq.num_q_rows = num_q_tokens;
-  mq.max_seqlen_q = max_seqlen_q;
   if (options) mq.options = *options;
+  if (cu_seqlens_q) {
+    if (num_seqs > 0 && num_q_tokens > 0 && ((uintptr_t)cu_seqlens_q & 3))
+      return fail(PA_ERR_SHAPE, "misaligned cu_seqlens_q (4 B)");
+    mq.cu_seqlens_q = cu_seqlens_q;
+    mq.num_q_rows = num_q_tokens;
+    mq.max_seqlen_q = max_seqlen_q;
+  } else {
+    // one query per sequence
+    if (num_q_tokens != num_seqs)
+      return fail(PA_ERR_SHAPE, "without cu_seqlens_q, num_q_tokens (%d) must equal num_seqs (%d)",
+                  num_q_tokens, num_seqs);
+    mq.num_q_rows = num_seqs;
+  }
   return decode(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads, num_kv_heads,
                 head_size, block_size, max_blocks_per_seq, num_blocks, scale, k_scale, v_scale, out,
                 stream, 0, mq);

@@ -35,7 +35,9 @@ struct DecodeParams {
   int32_t num_parts;         // P, partitions per sequence
   int32_t pages_per_part;    // blocks per partition
   float scale_log2e;         // softmax scale * log2(e)
-  // several query tokens per sequence (null cu_seqlens_q: one per sequence)
+  // the several-queries kernel (its options included); cu_seqlens_q null: one
+  // query per sequence
+  int32_t multi_query;
   const int32_t* cu_seqlens_q;  // [S + 1] query row offsets
   int32_t num_q_rows;        // cu_seqlens_q[S]: rows of q and out
   int32_t q_tile;            // query tokens per work item (columns = q_tile * group <= 16)
@@ -55,6 +57,9 @@ struct DecodeParams {
   int64_t block_stride;
   int64_t token_stride;
   int64_t head_stride;
+  // longest-first dispatch: work items take sequence seq_order[i] for the i-th
+  // sequence slot (written by the order kernel before the decode); null: in order
+  int32_t* seq_order;
 };
 
 // Enqueue the decode (and, when num_parts > 1, the merge) on `stream`.

@@ -181,7 +181,7 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
   int rest = item / p.num_parts;
   const int kv_units = TR ? p.num_kv_heads / p.kv_group : p.num_kv_heads;  // work items per (sequence, partition)
   const int kvh = TR ? (rest % kv_units) * p.kv_group + wave : rest % kv_units;
-  const int s = rest / kv_units;
+  const int s = p.seq_order ? scalar_load(p.seq_order + rest / kv_units) : rest / kv_units;
   const int ppp = p.pages_per_part;
   const int pbeg = part * ppp;  // < max_blocks: the planner never makes an empty partition range
 
@@ -190,8 +190,9 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
   if constexpr (MQ) {
     qi = col / p.group;
     g = col - qi * p.group;
-    q0 = scalar_load(p.cu_seqlens_q + s);
-    q_len = scalar_load(p.cu_seqlens_q + s + 1) - q0;
+    // no row offsets: one query per sequence (the options without several queries)
+    q0 = p.cu_seqlens_q ? scalar_load(p.cu_seqlens_q + s) : s;
+    q_len = p.cu_seqlens_q ? scalar_load(p.cu_seqlens_q + s + 1) - q0 : 1;
     if (qt0 * p.q_tile >= q_len) return;  // no query of this sequence in the item's tiles
   }
   const int h = kvh * p.group + g;
@@ -624,7 +625,7 @@ __global__ __launch_bounds__(kMergeThreads) void pa_merge_kernel(const DecodePar
   const int sh = blockIdx.x;  // (query row, head)
   const int r = sh / p.num_heads;
   int s = r, L = 0;
-  if (p.cu_seqlens_q) {
+  if (p.multi_query && p.cu_seqlens_q) {
     // the row's sequence: last s with cu_seqlens_q[s] <= r
     int lo = 0, hi = p.num_seqs;
     while (hi - lo > 1) {
@@ -716,23 +717,81 @@ __global__ __launch_bounds__(kMergeThreads) void pa_merge_kernel(const DecodePar
 
 }  // namespace
 
+// Sequences ordered by length, longest first (by context pages, in kOrderBins
+// buckets; order within a bucket is arbitrary, which no result depends on:
+// every work item computes the same thing in any order).  One workgroup: each
+// thread reads the lengths of up to kOrderPer sequences once and keeps their
+// buckets, a bucket histogram in LDS, an exclusive scan from the longest bucket
+// down, then each sequence takes the next slot of its bucket.  More sequences
+// than the workgroup holds keep the plain order (the host does not order them).
+constexpr int kOrderThreads = 256;
+constexpr int kOrderPer = 32;
+constexpr int kOrderBins = 256;
+
+__global__ __launch_bounds__(kOrderThreads) void pa_order_kernel(const DecodeParams p) {
+  __shared__ int cnt[kOrderBins];
+  __shared__ int wave_sum[kOrderThreads / 64];
+  const int t = threadIdx.x;
+  const int S = p.num_seqs;
+  const int wmax = p.max_blocks > 0 ? p.max_blocks : 1;  // pages of the longest possible context
+  int bin[kOrderPer];
+#pragma unroll
+  for (int k = 0; k < kOrderPer; ++k) {
+    const int s = t + k * kOrderThreads;
+    int b = -1;
+    if (s < S) {
+      const int pages = (clamp_len(p.seq_lens[s], p.max_blocks) + kBlockTokens - 1) / kBlockTokens;
+      b = kOrderBins - 1 - (int)((int64_t)pages * (kOrderBins - 1) / wmax);  // 0 = longest
+    }
+    bin[k] = b;
+  }
+  if (t < kOrderBins) cnt[t] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kOrderPer; ++k)
+    if (bin[k] >= 0) atomicAdd(&cnt[bin[k]], 1);
+  __syncthreads();
+  // exclusive scan of the bins (one bin per thread)
+  static_assert(kOrderBins == kOrderThreads, "one bin per thread");
+  const int own = t < kOrderBins ? cnt[t] : 0;
+  const int lane = t & 63;
+  int incl = own;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wave_sum[t >> 6] = incl;
+  __syncthreads();
+  int base = incl - own;
+  for (int w = 0; w < (t >> 6); ++w) base += wave_sum[w];
+  __syncthreads();
+  if (t < kOrderBins) cnt[t] = base;  // first slot of the bin
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kOrderPer; ++k)
+    if (bin[k] >= 0) p.seq_order[atomicAdd(&cnt[bin[k]], 1)] = t + k * kOrderThreads;
+}
+
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
+  if (p.seq_order)
+    hipLaunchKernelGGL(pa_order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, p);
   const size_t units = (size_t)p.num_seqs * p.num_kv_heads * p.num_parts;
   // several queries: units padded to a multiple of 8, times the groups of tiles
-  const size_t items = p.cu_seqlens_q
+  const size_t items = p.multi_query
                            ? (units + 7) / 8 * 8 * (size_t)((p.num_q_tiles + p.tiles_per_item - 1) / p.tiles_per_item)
                            : units;
   if (p.token_rows)
     hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false, PA_LOAD_AUX, true>),
                        dim3((unsigned)(items / p.kv_group)), dim3(64 * p.kv_group),
                        (unsigned)(p.kv_group * 2 * kVtBytes<kPagesPerStage>), stream, p);
-  else if (p.cu_seqlens_q && p.tiles_per_item == 2 && p.num_q_tiles > 2)
+  else if (p.multi_query && p.tiles_per_item == 2 && p.num_q_tiles > 2)
     hipLaunchKernelGGL((pa_decode_kernel<kTwoTilePagesPerStage, kRingDepth, false, true, 0, false, 2>),
                        dim3((unsigned)items), dim3(64), 0, stream, p);
-  else if (p.cu_seqlens_q && p.tiles_per_item == 2)
+  else if (p.multi_query && p.tiles_per_item == 2)
     hipLaunchKernelGGL((pa_decode_kernel<kTwoTilePagesPerStage, kRingDepth, false, true, PA_LOAD_AUX, false, 2>),
                        dim3((unsigned)items), dim3(64), 0, stream, p);
-  else if (p.cu_seqlens_q)
+  else if (p.multi_query)
     hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, true>), dim3((unsigned)items),
                        dim3(64), 0, stream, p);
   else if (p.k_slot_scales)
@@ -741,7 +800,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   else
     hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false>), dim3((unsigned)items),
                        dim3(64), 0, stream, p);
-  const size_t rows = p.cu_seqlens_q ? (size_t)p.num_q_rows : (size_t)p.num_seqs;
+  const size_t rows = p.multi_query ? (size_t)p.num_q_rows : (size_t)p.num_seqs;
   if (p.num_parts > 1 && rows > 0)
     hipLaunchKernelGGL(pa_merge_kernel, dim3((unsigned)(rows * p.num_heads)), dim3(kMergeThreads), 0, stream,
                        p);

@@ -181,11 +181,11 @@ def test_token_row_decode_argument_checks(lib):
     assert nhd(lib, bs=1 << 20, out=FAKE * 16 + 100 * 1024) == -4
 
 
-def unified(lib, window=0, cap=0.0, slopes=None, sinks=None, opts=True):
+def unified(lib, window=0, cap=0.0, slopes=None, sinks=None, opts=True, cu=FAKE * 70, T=6):
     import paged_attention_decode_03_amd as pa
     vp = ctypes.c_void_p
-    o = pa.AttentionOptions(window, cap, slopes, sinks)
-    return lib.paged_attention_unified(vp(FAKE), vp(FAKE * 70), 6, 4, vp(FAKE * 16), vp(FAKE * 32),
+    o = pa.AttentionOptions(window, cap, slopes, sinks, 0)
+    return lib.paged_attention_unified(vp(FAKE), vp(cu), T, 4, vp(FAKE * 16), vp(FAKE * 32),
                                        vp(FAKE * 48), vp(FAKE * 50), 2, 8, 2, 128, 16, 4, 16,
                                        ctypes.c_float(0.088), vp(FAKE * 52), vp(FAKE * 53),
                                        ctypes.byref(o) if opts else None, vp(FAKE * 64), None)
@@ -199,3 +199,4 @@ def test_unified_option_checks(lib):
     assert unified(lib, slopes=FAKE * 80 + 2) == -2
     assert unified(lib, sinks=FAKE * 80 + 1) == -2
     assert unified(lib, sinks=FAKE * 64 + 64) == -4       # inside out
+    assert unified(lib, cu=0, T=3) == -2                  # one query per sequence: T must be 2

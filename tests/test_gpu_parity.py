@@ -344,3 +344,36 @@ def test_block_ids_outside_the_caches_read_as_zero_pages():
     # (per-tensor scales of 1 over codes up to 448: errors relative to |out|)
     case.block_tables = zero_tab
     compare(calls(zero_tab)[0], run_oracle(case), "zero-block table", relative=True)
+
+
+def test_longest_first_order_covers_every_sequence():
+    """Longest-first dispatch (an order computed on the device) must compute
+    every sequence exactly once with the same arithmetic: the unified call with
+    no row offsets and longest_first must equal the plain decode bit for bit,
+    for ragged contexts that split and for ones that do not, and so must a
+    graph replay of it."""
+    import paged_attention_decode_03_amd as pa
+    for S, seed in ((48, 5), (300, 6), (3, 7)):
+        lens = workloads.ragged_lens(S, seed=seed)
+        case = workloads.make_case(40, 8, lens, seed=98 + S, max_blocks=250).to("cuda")
+        ks = torch.tensor([case.k_scale], device="cuda")
+        vs = torch.tensor([case.v_scale], device="cuda")
+        args = (case.k_cache, case.v_cache, case.block_tables, case.seq_lens, case.scale, ks, vs)
+        plain = pa.paged_decode_attention(case.q, *args)
+        ordered = pa.paged_attention_unified(case.q, None, 1, *args, longest_first=True)
+        torch.cuda.synchronize()
+        log(f"longest first S={S}")
+        assert torch.equal(ordered.view(torch.int16), plain.view(torch.int16)), f"S={S}"
+    out = torch.empty_like(case.q)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            pa.paged_attention_unified(case.q, None, 1, *args, longest_first=True, out=out)
+    for r in range(3):
+        out.fill_(7.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), plain.view(torch.int16)), f"replay {r}"

@@ -179,6 +179,28 @@ def test_graph_capture_replays_match_eager():
     compare(out, ref, "options graph replay", seqs=rows)
 
 
+def test_one_query_per_sequence_without_row_offsets():
+    """cu_seqlens_q=None means one query per sequence: with options it must
+    equal the call with row offsets 0, 1, .., S bit for bit, and with
+    longest-first dispatch too."""
+    import paged_attention_decode_03_amd as pa
+    lens = [1, 100, 1000, 17, 4, 2500, 33, 2]
+    case = workloads.make_multi_case(40, 8, lens, [1] * len(lens), seed=97).to("cuda")
+    ks = torch.tensor([case.k_scale], device="cuda")
+    vs = torch.tensor([case.v_scale], device="cuda")
+    sinks = torch.linspace(-1, 2, 40, device="cuda")
+    args = (case.k_cache, case.v_cache, case.block_tables, case.seq_lens, case.scale, ks, vs)
+    opt = dict(sliding_window=64, softcap=20.0, sinks=sinks)
+    a = pa.paged_attention_unified(case.q, case.cu_seqlens_q, 1, *args, **opt)
+    b = pa.paged_attention_unified(case.q, None, 1, *args, **opt)
+    c = pa.paged_attention_unified(case.q, None, 1, *args, longest_first=True, **opt)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+    ref, rows = run_ext_oracle(case, sliding_window=64, softcap=20.0, sinks=sinks.cpu().numpy())
+    compare(b, ref, "one query per sequence, options", seqs=rows)
+
+
 def test_speculative_decode_with_window_and_sinks_sampled():
     """40/8 heads, 256 sequences of 4096 tokens, 4 queries each, a 128-token
     window and per-head sinks: only the last pages of each sequence are read."""
