@@ -38,7 +38,18 @@ int fail(int code, const char* fmt, ...) {
 #ifndef PA_ITEMS_PER_CU
 #define PA_ITEMS_PER_CU 2
 #endif
-constexpr int kItemsPerCU = PA_ITEMS_PER_CU;  // work items the plan aims for, per CU
+#ifndef PA_SPLIT_ITEMS_PER_CU
+#define PA_SPLIT_ITEMS_PER_CU 4
+#endif
+#ifndef PA_CACHED_LOAD_MAX_MIB
+#define PA_CACHED_LOAD_MAX_MIB 320
+#endif
+constexpr int kItemsPerCU = PA_ITEMS_PER_CU;  // from this many items per CU, no split
+constexpr int kSplitItemsPerCU = PA_SPLIT_ITEMS_PER_CU;  // what a split aims for, per CU
+// K/V working sets up to this size (about the 256 MB Infinity Cache and a
+// little more) are read with the default cache policy, which lets repeated
+// calls find the pages in that cache; larger ones stream past it (nt).
+constexpr size_t kCachedLoadMaxBytes = (size_t)PA_CACHED_LOAD_MAX_MIB << 20;
 constexpr int kDefaultCUs = 256;      // MI355X
 constexpr int kMinPagesPerPart = 8;   // shorter partitions cost more in start-up and merge than they gain
 constexpr int kStagePages = 4;        // the decode kernel loads 4 blocks per pipeline stage
@@ -62,12 +73,14 @@ constexpr int kLongestFirstMaxSeqs = 8192;  // what the one-workgroup order kern
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Shape-only plan (no device data: it must not depend on seq_lens).  One
-// partition per (sequence, kv head) when that already gives a quarter of the
-// device's wave slots (2 waves per CU) a work item: measured on MI355X, a wave
-// streaming one long partition sustains ~12 GB/s, so 512 of them already
-// saturate HBM, and every extra partition costs a start-up and a merge.
-// Otherwise split each sequence's blocks so that about that many items exist,
-// with partitions of at least kMinPagesPerPart blocks, whole pipeline stages,
+// partition per (sequence, kv head) when that already gives every CU two work
+// items: every extra partition costs a start-up and a merge.  Fewer units:
+// split each sequence's blocks into the largest power of two of partitions
+// that keeps the items within four per CU.  Measured on MI355X (graph replay,
+// 16..64 sequences at ctx 1024..4096 and 1..4 at 4096..32768): a CU streams
+// at most ~25 GB/s, so every CU needs work, and items that divide evenly over
+// the CUs with even partitions beat the same bytes in uneven pieces by 10-25%.
+// Partitions hold at least kMinPagesPerPart blocks, whole pipeline stages,
 // and never more than pa::kMaxPagesPerPart blocks.
 int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t W, int32_t num_cus, int32_t ppp_req,
               Plan* plan, int32_t q_tiles = 1, int64_t q_rows = -1, bool longest_first = false) {
@@ -80,8 +93,12 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t W, int32_t num_cus, in
     ppp = ppp_req < Wc ? ppp_req : Wc;
   } else {
     const int64_t items = (int64_t)(S > 0 ? S : 1) * Hkv * (q_tiles > 0 ? q_tiles : 1);
-    const int64_t target = (int64_t)(num_cus > 0 ? num_cus : kDefaultCUs) * kItemsPerCU;
-    int64_t parts = ceil_div(target, items);
+    const int64_t cus = num_cus > 0 ? num_cus : kDefaultCUs;
+    // a power of two of partitions, so that (table widths being powers of
+    // two in practice) partitions are even and items divide over the CUs
+    int64_t parts = 1;
+    if (items < cus * kItemsPerCU)
+      while (parts * 2 * items <= cus * kSplitItemsPerCU) parts *= 2;
     if (parts > Wc) parts = Wc;
     ppp = ceil_div(Wc, parts < 1 ? 1 : parts);
     if (ppp < Wc) {
@@ -298,6 +315,11 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   p.num_parts = plan.num_parts;
   p.pages_per_part = plan.pages_per_part;
   p.scale_log2e = (float)((double)scale * 1.4426950408889634);
+  // the plain decode reads a working set that fits the Infinity Cache with the
+  // default policy (K and V of every table entry: an upper bound)
+  p.cached_loads = (!mq && !slot_scales && !var.token_rows &&
+                    (size_t)S * W * Hkv * 2 * pa::kPageBytes <= kCachedLoadMaxBytes)
+                       ? 1 : 0;
   p.multi_query = mq ? 1 : 0;
   p.cu_seqlens_q = cu_seqlens_q;
   p.num_q_rows = mq ? num_q_rows : S;

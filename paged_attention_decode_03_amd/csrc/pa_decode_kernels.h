@@ -35,6 +35,7 @@ struct DecodeParams {
   int32_t num_parts;         // P, partitions per sequence
   int32_t pages_per_part;    // blocks per partition
   float scale_log2e;         // softmax scale * log2(e)
+  int32_t cached_loads;      // plain decode: K/V loads with the default cache policy (else nt)
   // the several-queries kernel (its options included); cu_seqlens_q null: one
   // query per sequence
   int32_t multi_query;

@@ -159,7 +159,8 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
   // Token rows: a workgroup holds kv_group kv heads of one sequence (one wave
   // each), which walk the sequence's blocks together (the barriers of each
   // stage keep them in step), so the token rows they share are read at once.
-  const int wave = TR ? (int)(threadIdx.x >> 6) : 0;
+  // (wave-uniform, and known to be: buffer descriptors built from it stay scalar)
+  const int wave = TR ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) : 0;
   const int col = lane & 15;  // MFMA column (query head in group); K load row (token)
   const int rq = lane >> 4;   // row quad: rows 4*rq .. 4*rq+3 of the 16x16 tiles
 
@@ -177,8 +178,15 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
     item = (r / ngroups) * 8 + xcd;
     if (item >= p.num_seqs * p.num_kv_heads * p.num_parts) return;  // grid padding
   }
-  const int part = item % p.num_parts;
   int rest = item / p.num_parts;
+  // partition: rotated by the unit, so that the first partition of every unit
+  // (the one each context has) does not land on the same XCD (blocks go to the
+  // 8 XCDs round robin) whenever the partition count is a multiple of 8
+  int part = item % p.num_parts;
+  if (p.num_parts > 1) {
+    part += rest % p.num_parts;
+    if (part >= p.num_parts) part -= p.num_parts;
+  }
   const int kv_units = TR ? p.num_kv_heads / p.kv_group : p.num_kv_heads;  // work items per (sequence, partition)
   const int kvh = TR ? (rest % kv_units) * p.kv_group + wave : rest % kv_units;
   const int s = p.seq_order ? scalar_load(p.seq_order + rest / kv_units) : rest / kv_units;
@@ -397,9 +405,11 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
     for (int pp = 0; pp < PPS; ++pp) {
       // a block id outside the caches (a caller error the host cannot see) reads
       // as an all-zero page instead of touching memory
-      const bool used = i0 + pp < npg && (uint32_t)pid[pp] < p.num_blocks_u32;
+      // (the same in every lane; read as such, so that the descriptors stay scalar)
+      const int32_t pu = __builtin_amdgcn_readfirstlane(pid[pp]);
+      const bool used = i0 + pp < npg && (uint32_t)pu < p.num_blocks_u32;
       const int bytes = used ? page_bytes : 0;
-      const size_t off = (size_t)__builtin_amdgcn_readfirstlane(pid[pp]) * page_stride;
+      const size_t off = (size_t)pu * page_stride;
       const __amdgpu_buffer_rsrc_t rk =
           __builtin_amdgcn_make_buffer_rsrc((void*)(kpage0 + off), (short)0, bytes, kRsrcWord3);
       const __amdgpu_buffer_rsrc_t rv =
@@ -797,6 +807,9 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   else if (p.k_slot_scales)
     hipLaunchKernelGGL((pa_decode_kernel<kSlotScalePagesPerStage, kRingDepth, true, false>),
                        dim3((unsigned)items), dim3(64), 0, stream, p);
+  else if (p.cached_loads)
+    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false, 0>), dim3((unsigned)items),
+                       dim3(64), 0, stream, p);
   else
     hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false>), dim3((unsigned)items),
                        dim3(64), 0, stream, p);

@@ -52,10 +52,24 @@ def test_plan_large_batch_is_unsplit(lib):
 
 def test_plan_small_batch_splits_long_context(lib):
     rc, P, n, ws = plan(lib, 1, 40, 8, 2048)        # one sequence of 32768 tokens
-    assert rc == 0 and P * n >= 2048 and (P, n) == (64, 32)
+    assert rc == 0 and P * n >= 2048 and (P, n) == (128, 16)   # 1024 items: 4 per CU
     assert ws == 1 * 40 * P * 130 * 4
     rc, P, n, ws = plan(lib, 1, 40, 8, 256)         # one sequence of 4096 tokens
     assert rc == 0 and (P, n) == (32, 8)            # never below 8 blocks per partition
+
+
+def test_plan_split_is_a_power_of_two_within_four_items_per_cu(lib):
+    # 40/8 ctx 1024 x 16: 128 units -> 8 partitions of 8 blocks (1024 items)
+    assert plan(lib, 16, 40, 8, 64)[:3] == (0, 8, 8)
+    # 32/8 ctx 4096 x 24: 192 units -> 4 partitions of 64 blocks (768 items)
+    assert plan(lib, 24, 32, 8, 256)[:3] == (0, 4, 64)
+    # 4 x ctx 32768: 32 units -> 32 partitions of 64 blocks
+    assert plan(lib, 4, 40, 8, 2048)[:3] == (0, 32, 64)
+    # 300 units -> 2 partitions; 512 units (two per CU) -> unsplit
+    assert plan(lib, 300, 8, 1, 256)[:3] == (0, 2, 128)
+    assert plan(lib, 64, 40, 8, 64)[:3] == (0, 1, 64)
+    # a width that is no power of two: partitions of whole stages, the last shorter
+    assert plan(lib, 256, 8, 1, 250)[:3] == (0, 4, 64)
 
 
 def test_plan_partitions_are_whole_stages(lib):
