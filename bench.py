@@ -104,7 +104,8 @@ def make_workload(name, device):
 
 def suite_names():
     import workloads
-    names = [f"dense_{a}x{b}_ctx{c}_s{s}" for (a, b, s, c) in workloads.DENSE_1K + workloads.DENSE_4K]
+    names = [f"dense_{a}x{b}_ctx{c}_s{s}"
+             for (a, b, s, c) in workloads.DENSE_1K + workloads.DENSE_4K + workloads.PAGES_TABLE_EXTRA]
     names += ["target", "dense_20x4_ctx4096_s256"]
     names += ["slotscales_40x8_ctx4096_s256"]
     names += [f"specdec_40x8_ctx4096_s256_q{q}" for q in (2, 3, 4, 8)]

@@ -308,5 +308,7 @@ def ragged(num_heads: int, num_kv_heads: int, seed: int, num_seqs: int = 256,
 RAGGED_LAYOUTS = [(32, 8), (40, 8), (32, 4), (8, 1)]
 DENSE_1K = [(40, 8, s, 1024) for s in (16, 64, 256)]
 DENSE_4K = [(32, 8, s, 4096) for s in (24, 64, 256)]
+# the other rows of the pages' latency table (40/8 at ctx 4096, 32/8 at ctx 1024)
+PAGES_TABLE_EXTRA = [(40, 8, s, 4096) for s in (16, 64)] + [(32, 8, s, 1024) for s in (24, 64, 256)]
 LOW_BATCH = [(40, 8, s, L) for s in (1, 2, 3, 4) for L in (4096, 8192, 16384, 32768)]
 TARGET = (40, 8, 256, 4096)
