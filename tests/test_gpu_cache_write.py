@@ -168,3 +168,28 @@ def test_whole_block_runs(pattern):
     kc, vc, ok, ov = run_both(key, value, slots, NB, 0.015, 0.021)
     assert_same(kc, ok, "k_cache")
     assert_same(vc, ov, "v_cache")
+
+
+# scales taking the short correctly rounded quotient, and ones outside its
+# range (tiny, huge, subnormal, negative) that take the division
+QUOTIENT_SCALES = [0.0173, 1.0 / 3.0, 3.0, 0.99999994, 7.3e-3, 1.1e2, 2.0 ** -60, 2.0 ** 60,
+                   -0.021, 1.0e-20, 3.0e19, 1.0e-39]
+
+
+@pytest.mark.parametrize("scale", QUOTIENT_SCALES)
+def test_every_bf16_value_bit_exact(scale):
+    """All 65536 bf16 bit patterns (zeros, subnormals, infinities and NaNs of
+    both signs included) through both write paths, in-order whole blocks and
+    scattered tokens, against the oracle's fp32 division and rounding."""
+    pats = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    key = torch.from_numpy(pats.view(np.int16).copy()).view(torch.bfloat16).view(512, 1, 128)
+    value = torch.from_numpy(pats[::-1].view(np.int16).copy()).view(torch.bfloat16).view(512, 1, 128)
+    ks = float(np.float32(scale))
+    vs = float(np.float32(scale * 1.37))
+    in_order = torch.arange(512, dtype=torch.int64)
+    scattered = torch.randperm(512, generator=torch.Generator().manual_seed(7)).to(torch.int64)
+    for name, slots in (("whole blocks", in_order), ("scattered", scattered)):
+        log(f"every bf16 value, scale {ks:g} / {vs:g}, {name}")
+        kc, vc, ok, ov = run_both(key, value, slots, 32, ks, vs)
+        assert_same(kc, ok, f"k_cache ({name})")
+        assert_same(vc, ov, f"v_cache ({name})")
