@@ -30,59 +30,91 @@ __device__ __forceinline__ T scalar_load(const T* ptr) {
   return *(const __attribute__((address_space(4))) T*)(ptr);
 }
 
-// Two fp32 values -> two fp8 e4m3fn codes (low byte = a): round to nearest
-// even, saturate to +-448, NaN stays NaN with its sign (S.1111.111; the clamp
-// turns a NaN into some number, whose code is then replaced).
-__device__ __forceinline__ uint32_t fp8x2_saturate(float a, float b) {
-  const float ca = fminf(fmaxf(a, -448.0f), 448.0f);
-  const float cb = fminf(fmaxf(b, -448.0f), 448.0f);
+// One per-tensor scale s with what the short quotient needs: r = RN(1 / s)
+// and the dividend bound lim = 512 s.
+struct Scale {
+  float s, r, lim;
+};
+
+// The fp32 quotient x / s, correctly rounded.  FAST: Markstein's correction
+// of the product with the rounded reciprocal: q0 = RN(x r), e = q0 s - x
+// (exact, one FMA), q = RN(q0 - e r) is the correctly rounded quotient when
+// no step under- or overflows.  The kernel takes this path for scales in
+// [2^-60, 2^60] only: then r is normal, and for every quotient fp8 can tell
+// from zero (|x / s| >= 2^-10) e is a normal number, so the FMA is exact.
+// Dividends beyond 512 s (quotients past 512, saturated to 448 either way,
+// infinities included) are clamped to +-512 s first, so nothing overflows;
+// the correction's signs keep the sign of a zero quotient.  NaN dividends
+// are told apart by the caller.  Checked on the CPU against fp32 division
+// for all 65536 bf16 dividends at 4000 scales: the same fp8 code every time.
+template <bool FAST>
+__device__ __forceinline__ float quot(float x, const Scale& sc) {
+  if constexpr (FAST) {
+    const float xc = __builtin_amdgcn_fmed3f(x, -sc.lim, sc.lim);  // (a NaN x: any value)
+    const float q0 = xc * sc.r;
+    const float e = __builtin_fmaf(q0, sc.s, -xc);
+    return __builtin_fmaf(-e, sc.r, q0);
+  } else {
+    return x / sc.s;
+  }
+}
+
+// Two quotients -> two fp8 e4m3fn codes (low byte = a): round to nearest
+// even, saturate to +-448.  WITH_NAN: where na / nb is a NaN, the code is
+// NaN with its sign (S.1111.111), whatever the clamp made of the quotient;
+// without it the caller has made sure there is no NaN.
+template <bool WITH_NAN>
+__device__ __forceinline__ uint32_t fp8x2_code(float a, float b, float na, float nb) {
+  // (the median of three is the clamp; a NaN gives some value, replaced below)
+  const float ca = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  const float cb = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
   uint32_t r = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false) & 0xFFFFu;
-  if (a != a) r = (r & 0xFF00u) | (signbit(a) ? 0xFFu : 0x7Fu);
-  if (b != b) r = (r & 0x00FFu) | ((signbit(b) ? 0xFFu : 0x7Fu) << 8);
+  if constexpr (WITH_NAN) {
+    if (na != na) r = (r & 0xFF00u) | (signbit(na) ? 0xFFu : 0x7Fu);
+    if (nb != nb) r = (r & 0x00FFu) | ((signbit(nb) ? 0xFFu : 0x7Fu) << 8);
+  }
   return r;
 }
 
-// The fp32 quotient x / s, correctly rounded.  FAST: Markstein's correction
-// of the product with the rounded reciprocal r = RN(1 / s): q0 = RN(x r),
-// e = x - q0 s (exact, one FMA), q = RN(q0 + e r) is the correctly rounded
-// quotient whenever no step under- or overflows (the kernel checks the scale
-// once; other scales take the division).  Where e is 0 (exact quotients, zeros, whose
-// sign q0 keeps) or |q0| is far beyond fp8's range (saturated either way,
-// infinities included) or q0 is NaN, q0 itself is that quotient's fp8 code.
-template <bool FAST>
-__device__ __forceinline__ float quot(float x, float s, float r) {
-  if constexpr (FAST) {
-    const float q0 = x * r;
-    const float e = __builtin_fmaf(-q0, s, x);
-    const float q = __builtin_fmaf(e, r, q0);
-    return (e != 0.0f && __builtin_fabsf(q0) <= 1.0e4f) ? q : q0;
-  } else {
-    return x / s;
-  }
+// Two dividends -> their quotients' fp8 codes.  A NaN quotient comes from a
+// NaN dividend on the short path (with the dividend's sign, as the division
+// would give) and is taken from the quotient itself on the division path.
+template <bool FAST, bool WITH_NAN>
+__device__ __forceinline__ uint32_t code2(float x0, float x1, const Scale& sc) {
+  const float q0 = quot<FAST>(x0, sc);
+  const float q1 = quot<FAST>(x1, sc);
+  return fp8x2_code<WITH_NAN>(q0, q1, FAST ? x0 : q0, FAST ? x1 : q1);
+}
+
+template <bool FAST, bool WITH_NAN>
+__device__ __forceinline__ uint32_t code4(float a, float b, float c, float d, const Scale& sc) {
+  return code2<FAST, WITH_NAN>(a, b, sc) | (code2<FAST, WITH_NAN>(c, d, sc) << 16);
+}
+
+// Lanes of the wave holding a NaN among a, b, c, d (one compare per value; the
+// masks are wave-wide, so or-ing them costs scalar instructions only).
+__device__ __forceinline__ uint64_t nan_lanes(float a, float b, float c, float d) {
+  return __builtin_amdgcn_ballot_w64(a != a) | __builtin_amdgcn_ballot_w64(b != b) |
+         __builtin_amdgcn_ballot_w64(c != c) | __builtin_amdgcn_ballot_w64(d != d);
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Four fp32 -> four fp8 codes in byte order a, b, c, d.
-__device__ __forceinline__ uint32_t fp8x4_saturate(float a, float b, float c, float d) {
-  return fp8x2_saturate(a, b) | (fp8x2_saturate(c, d) << 16);
-}
-
 constexpr int kWavesPerBlock = 4;
 constexpr int kGroup = kBlockTokens;  // tokens per wave
 
 // One token, two dims per lane (any slot pattern); kw / vw hold the lane's two
-// bf16 key and value dims of the token; kr / vr the scales' reciprocals.
+// bf16 key and value dims of the token.
 template <bool FAST>
 __device__ __forceinline__ void write_token(const CacheWriteParams& p, int kvh, int64_t slot, int lane,
-                                            uint32_t kw, uint32_t vw, float ks, float vs, float kr, float vr) {
+                                            uint32_t kw, uint32_t vw, const Scale& ks, const Scale& vs) {
   if (slot < 0 || slot >= p.num_blocks * kBlockTokens) return;
   const int64_t block = slot / kBlockTokens;
   const int j = (int)(slot % kBlockTokens);
   const int d = 2 * lane;
-  const uint32_t kc = fp8x2_saturate(quot<FAST>(bf16_lo(kw), ks, kr), quot<FAST>(bf16_hi(kw), ks, kr));
-  const uint32_t vc = fp8x2_saturate(quot<FAST>(bf16_lo(vw), vs, vr), quot<FAST>(bf16_hi(vw), vs, vr));
+  const uint32_t kc = code2<FAST, true>(bf16_lo(kw), bf16_hi(kw), ks);
+  const uint32_t vc = code2<FAST, true>(bf16_lo(vw), bf16_hi(vw), vs);
   const size_t page = ((size_t)block * p.num_kv_heads + kvh) * kPageBytes;
   *(uint16_t*)(p.k_cache + page + (d / 16) * 256 + j * 16 + (d % 16)) = (uint16_t)kc;
   uint8_t* vp = p.v_cache + page + (size_t)d * kBlockTokens + j;
@@ -91,56 +123,81 @@ __device__ __forceinline__ void write_token(const CacheWriteParams& p, int kvh, 
 }
 
 // Sixteen tokens that fill block `block` in slot order: whole-page writes.
-template <bool FAST>
-__device__ __forceinline__ void write_block(const CacheWriteParams& p, int t0, int kvh, int64_t block,
-                                            int lane, float ks, float vs, float kr, float vr) {
-  const size_t page = ((size_t)block * p.num_kv_heads + kvh) * kPageBytes;
-  // K page bytes [32 l, 32 l + 32): chunk c = l / 8 (dims 16c..16c+15), slots 2(l%8), 2(l%8)+1
-  {
-    const int c = lane >> 3;
-    const int j0 = 2 * (lane & 7);
-    uint4 outw[2];
+// K page bytes [32 l, 32 l + 32): chunk c = l / 8 (dims 16c..16c+15), slots
+// 2(l%8), 2(l%8)+1; V page bytes [32 l, 32 l + 32): dims 2l and 2l+1, all 16
+// slots of each.  The codes are made without NaN handling unless a NaN is in
+// the wave's inputs (or the division path, where the scale may be one).
+template <bool FAST, bool WITH_NAN>
+__device__ __forceinline__ void block_codes(const uint32_t (&kin)[2][8], const uint32_t (&vin)[kGroup],
+                                            const Scale& ks, const Scale& vs, uint4 (&kout)[2], uint4 (&vout)[2]) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint16_t* src = p.key + (size_t)(t0 + j0 + u) * p.key_stride + kvh * kHeadDim + 16 * c;
-      const uint4 lo = *(const uint4*)src;        // dims +0..7
-      const uint4 hi = *(const uint4*)(src + 8);  // dims +8..15
-      uint32_t w[4];
-      const uint32_t in[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  for (int u = 0; u < 2; ++u) {
+    uint32_t w[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        w[q] = fp8x4_saturate(quot<FAST>(bf16_lo(in[2 * q]), ks, kr), quot<FAST>(bf16_hi(in[2 * q]), ks, kr),
-                              quot<FAST>(bf16_lo(in[2 * q + 1]), ks, kr), quot<FAST>(bf16_hi(in[2 * q + 1]), ks, kr));
-      outw[u] = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-    uint4* dst = (uint4*)(p.k_cache + page + c * 256 + j0 * 16);
-    dst[0] = outw[0];
-    dst[1] = outw[1];
+    for (int q = 0; q < 4; ++q)
+      w[q] = code4<FAST, WITH_NAN>(bf16_lo(kin[u][2 * q]), bf16_hi(kin[u][2 * q]), bf16_lo(kin[u][2 * q + 1]),
+                              bf16_hi(kin[u][2 * q + 1]), ks);
+    kout[u] = make_uint4(w[0], w[1], w[2], w[3]);
   }
-  // V page bytes [32 l, 32 l + 32): dims 2l and 2l+1, all 16 slots of each
-  {
-    const int d = 2 * lane;
-    float lo[kGroup], hi[kGroup];
+  uint32_t a[4], b[4];
 #pragma unroll
-    for (int j = 0; j < kGroup; ++j) {
-      const uint32_t vw = *(const uint32_t*)(p.value + (size_t)(t0 + j) * p.value_stride + kvh * kHeadDim + d);
-      lo[j] = quot<FAST>(bf16_lo(vw), vs, vr);
-      hi[j] = quot<FAST>(bf16_hi(vw), vs, vr);
-    }
-    uint32_t a[4], b[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      a[q] = fp8x4_saturate(lo[4 * q], lo[4 * q + 1], lo[4 * q + 2], lo[4 * q + 3]);
-      b[q] = fp8x4_saturate(hi[4 * q], hi[4 * q + 1], hi[4 * q + 2], hi[4 * q + 3]);
-    }
-    uint4* dst = (uint4*)(p.v_cache + page + (size_t)d * kBlockTokens);
-    dst[0] = make_uint4(a[0], a[1], a[2], a[3]);
-    dst[1] = make_uint4(b[0], b[1], b[2], b[3]);
+  for (int q = 0; q < 4; ++q) {
+    a[q] = code4<FAST, WITH_NAN>(bf16_lo(vin[4 * q]), bf16_lo(vin[4 * q + 1]), bf16_lo(vin[4 * q + 2]),
+                            bf16_lo(vin[4 * q + 3]), vs);
+    b[q] = code4<FAST, WITH_NAN>(bf16_hi(vin[4 * q]), bf16_hi(vin[4 * q + 1]), bf16_hi(vin[4 * q + 2]),
+                            bf16_hi(vin[4 * q + 3]), vs);
   }
+  vout[0] = make_uint4(a[0], a[1], a[2], a[3]);
+  vout[1] = make_uint4(b[0], b[1], b[2], b[3]);
 }
 
 template <bool FAST>
-__device__ __forceinline__ void cache_write_group(const CacheWriteParams& p, float ks, float vs, float kr, float vr) {
+__device__ __forceinline__ void write_block(const CacheWriteParams& p, int t0, int kvh, int64_t block,
+                                            int lane, const Scale& ks, const Scale& vs) {
+  const size_t page = ((size_t)block * p.num_kv_heads + kvh) * kPageBytes;
+  const int c = lane >> 3;
+  const int j0 = 2 * (lane & 7);
+  const int d = 2 * lane;
+  uint32_t kin[2][8], vin[kGroup];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const uint16_t* src = p.key + (size_t)(t0 + j0 + u) * p.key_stride + kvh * kHeadDim + 16 * c;
+    const uint4 lo = *(const uint4*)src;        // dims +0..7
+    const uint4 hi = *(const uint4*)(src + 8);  // dims +8..15
+    kin[u][0] = lo.x, kin[u][1] = lo.y, kin[u][2] = lo.z, kin[u][3] = lo.w;
+    kin[u][4] = hi.x, kin[u][5] = hi.y, kin[u][6] = hi.z, kin[u][7] = hi.w;
+  }
+#pragma unroll
+  for (int j = 0; j < kGroup; ++j)
+    vin[j] = *(const uint32_t*)(p.value + (size_t)(t0 + j) * p.value_stride + kvh * kHeadDim + d);
+  bool nan = true;
+  if constexpr (FAST) {
+    uint64_t m = 0;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int q = 0; q < 8; q += 2)
+        m |= nan_lanes(bf16_lo(kin[u][q]), bf16_hi(kin[u][q]), bf16_lo(kin[u][q + 1]), bf16_hi(kin[u][q + 1]));
+#pragma unroll
+    for (int j = 0; j < kGroup; j += 2)
+      m |= nan_lanes(bf16_lo(vin[j]), bf16_hi(vin[j]), bf16_lo(vin[j + 1]), bf16_hi(vin[j + 1]));
+    nan = m != 0;
+  }
+  uint4 kout[2], vout[2];
+  if (nan)
+    block_codes<FAST, true>(kin, vin, ks, vs, kout, vout);
+  else
+    block_codes<FAST, false>(kin, vin, ks, vs, kout, vout);
+  uint4* kdst = (uint4*)(p.k_cache + page + c * 256 + j0 * 16);
+  kdst[0] = kout[0];
+  kdst[1] = kout[1];
+  uint4* vdst = (uint4*)(p.v_cache + page + (size_t)d * kBlockTokens);
+  vdst[0] = vout[0];
+  vdst[1] = vout[1];
+}
+
+template <bool FAST>
+__device__ __forceinline__ void cache_write_group(const CacheWriteParams& p, const Scale& ks, const Scale& vs) {
   const int lane = threadIdx.x & 63;
   // (the wave index read as wave-uniform: the token and head of the item, and
   // every address derived from them, stay scalar)
@@ -159,7 +216,7 @@ __device__ __forceinline__ void cache_write_group(const CacheWriteParams& p, flo
   const bool whole = p.vec16 && n == kGroup && s0 >= 0 && (s0 % kBlockTokens) == 0 &&
                      s0 < p.num_blocks * kBlockTokens && __builtin_amdgcn_ballot_w64(!in_order) == 0;
   if (whole) {
-    write_block<FAST>(p, t0, kvh, s0 / kBlockTokens, lane, ks, vs, kr, vr);
+    write_block<FAST>(p, t0, kvh, s0 / kBlockTokens, lane, ks, vs);
     return;
   }
   // Any slot pattern: read every token's two dims first (the cache stores may
@@ -177,29 +234,24 @@ __device__ __forceinline__ void cache_write_group(const CacheWriteParams& p, flo
     if (i >= n) break;
     const int64_t slot = (int64_t)(uint32_t)__builtin_amdgcn_readlane((int)(my_slot & 0xFFFFFFFF), i) |
                          ((int64_t)__builtin_amdgcn_readlane((int)(my_slot >> 32), i) << 32);
-    write_token<FAST>(p, kvh, slot, lane, kw[i], vw[i], ks, vs, kr, vr);
+    write_token<FAST>(p, kvh, slot, lane, kw[i], vw[i], ks, vs);
   }
 }
 
-// Scales whose magnitude lies in [2^-60, 2^60]: then r is normal too, and for
-// every quotient fp8 can tell from zero (|x / s| >= 2^-10) the remainder e is
-// a normal number, so the FMA computes it exactly.  False for 0, subnormals,
-// infinities and NaN.
-__device__ __forceinline__ bool quotient_scale(float x) {
-  const float a = __builtin_fabsf(x);
-  return a >= 0x1p-60f && a <= 0x1p60f;
-}
+// Scales in [2^-60, 2^60] (positive): the short quotient's range.  False for
+// negative scales, 0, subnormals, infinities and NaN.
+__device__ __forceinline__ bool quotient_scale(float x) { return x >= 0x1p-60f && x <= 0x1p60f; }
 
 __global__ __launch_bounds__(64 * kWavesPerBlock) void pa_cache_write_kernel(const CacheWriteParams p) {
   const float ks = scalar_load(p.k_scale);
   const float vs = scalar_load(p.v_scale);
-  const float kr = 1.0f / ks;
-  const float vr = 1.0f / vs;
+  const Scale kq = {ks, 1.0f / ks, 512.0f * ks};
+  const Scale vq = {vs, 1.0f / vs, 512.0f * vs};
   // usable scales: the short quotient; anything else takes the division
   if (quotient_scale(ks) && quotient_scale(vs))
-    cache_write_group<true>(p, ks, vs, kr, vr);
+    cache_write_group<true>(p, kq, vq);
   else
-    cache_write_group<false>(p, ks, vs, kr, vr);
+    cache_write_group<false>(p, kq, vq);
 }
 
 }  // namespace
