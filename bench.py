@@ -92,6 +92,32 @@ def make_workload(name, device):
         hq, hkv, ctx, s, ql = map(int, m.groups())
         return workloads.make_multi_case(hq, hkv, [ctx] * s, [ql] * s, seed=0, device=device,
                                          name=name)
+    m = re.fullmatch(r"unified_(\d+)x(\d+)_ctx(\d+)_s(\d+)(?:_q(\d+))?_([a-z0-9+]+)", name)
+    if m:
+        # the unified call's options: window<N>, softcap<C>, alibi, sinks, joined by '+'
+        hq, hkv, ctx, s = map(int, m.groups()[:4])
+        ql = int(m.group(5) or 0)
+        if ql:
+            case = workloads.make_multi_case(hq, hkv, [ctx] * s, [ql] * s, seed=0, device=device,
+                                             name=name)
+        else:
+            case = workloads.dense(hq, hkv, s, ctx, seed=0, device=device)
+        import torch
+        opts = {}
+        for part in m.group(6).split("+"):
+            if part.startswith("window"):
+                opts["sliding_window"] = int(part[6:])
+            elif part.startswith("softcap"):
+                opts["softcap"] = float(part[7:])
+            elif part == "alibi":
+                opts["alibi_slopes"] = (2.0 ** (-8.0 * (torch.arange(hq, device=device) + 1) / hq)).float()
+            elif part == "sinks":
+                opts["sinks"] = torch.linspace(-1.0, 2.0, hq, device=device)
+            else:
+                raise SystemExit(f"unknown option {part} in {name}")
+        case.meta["options"] = opts
+        case.name = name
+        return case
     m = re.fullmatch(r"ragged_(\d+)x(\d+)_seed(\d+)(_lpt)?", name)
     if m:
         hq, hkv, seed = map(int, m.groups()[:3])
@@ -110,10 +136,36 @@ def suite_names():
     names += ["slotscales_40x8_ctx4096_s256"]
     names += [f"specdec_40x8_ctx4096_s256_q{q}" for q in (2, 3, 4, 8)]
     names += [f"tokenrows_{lay}_40x8_ctx4096_s256" for lay in ("nhd", "combined", "packed")]
+    names += ["unified_40x8_ctx4096_s256_" + o for o in ("window1024", "softcap30", "alibi", "sinks")]
+    names += ["unified_40x8_ctx4096_s256_q4_window128+sinks"]
     names += [f"ragged_{a}x{b}_seed0" for (a, b) in workloads.RAGGED_LAYOUTS]
     names += [f"ragged_{a}x{b}_seed0_lpt" for (a, b) in workloads.RAGGED_LAYOUTS]
     names += [f"dense_{a}x{b}_ctx{c}_s{s}" for (a, b, s, c) in workloads.LOW_BATCH]
     return names
+
+
+def workload_bytes(case):
+    """Algorithmic bytes of one call; with a sliding window, only the K/V of
+    the tokens some query's window holds (and their table entries), plus the
+    option arrays."""
+    b = case.algorithmic_bytes()
+    opts = case.meta.get("options")
+    if not opts:
+        return b
+    import torch
+    lens = case.seq_lens.to(torch.int64).cpu()
+    win = opts.get("sliding_window", 0)
+    if win > 0:
+        cu = case.cu_seqlens_q
+        ql = torch.ones_like(lens) if cu is None else (cu[1:] - cu[:-1]).to(torch.int64).cpu()
+        seen = torch.minimum(lens, win + ql - 1)           # tokens the union of the windows covers
+        b -= case.kv_bytes()
+        b += int(seen.sum().item()) * case.num_kv_heads * 128 * 2
+        pages_all = (lens + 15) // 16
+        pages_seen = pages_all - (lens - seen) // 16
+        b -= int((pages_all - pages_seen).sum().item()) * 4
+    b += 4 * case.num_heads * sum(1 for k in ("alibi_slopes", "sinks") if opts.get(k) is not None)
+    return b
 
 
 def make_call(case, out, stream=None):
@@ -134,6 +186,13 @@ def make_call(case, out, stream=None):
         return lambda: pa.paged_decode_attention_nhd(case.q, kv, vv, case.block_tables,
                                                      case.seq_lens, case.scale, ks, vs, out=out,
                                                      stream=stream)
+    opts = case.meta.get("options")
+    if opts is not None:
+        cu = case.cu_seqlens_q
+        max_q = 1 if cu is None else int((cu[1:] - cu[:-1]).max().item())
+        return lambda: pa.paged_attention_unified(case.q, cu, max_q, case.k_cache, case.v_cache,
+                                                  case.block_tables, case.seq_lens, case.scale, ks,
+                                                  vs, out=out, stream=stream, **opts)
     if getattr(case, "longest_first", False):
         return lambda: pa.paged_attention_unified(case.q, None, 1, case.k_cache, case.v_cache,
                                                   case.block_tables, case.seq_lens, case.scale, ks,
@@ -315,7 +374,7 @@ def main():
             us_graph = time_graph(case)
             P, ppp, _ = pa.pa_decode_plan(case.num_seqs, case.num_heads, case.num_kv_heads,
                                           case.max_blocks, 256)
-            b = case.algorithmic_bytes()
+            b = workload_bytes(case)
             if case.k_slot_scales is not None:
                 b += case.kv_bytes() // 128 * 4   # one fp32 K or V scale per cached token and kv head
             row = {"workload": name, "us_per_call": round(us, 2),
@@ -350,7 +409,7 @@ def main():
 
     case = make_workload(args.workload, "cuda")
     us = time_calls(case, args.steps, args.warmup)
-    B = case.algorithmic_bytes()
+    B = workload_bytes(case)
     gbs = B / us / 1e3
     P, ppp, _ = pa.pa_decode_plan(case.num_seqs, case.num_heads, case.num_kv_heads, case.max_blocks, 256)
     traffic = counter_traffic() if args.workload == "target" else None
