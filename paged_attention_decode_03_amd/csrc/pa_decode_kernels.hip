@@ -73,7 +73,10 @@ constexpr int kPagesPerStage = PA_PAGES_PER_STAGE;
 constexpr int kRingDepth = PA_RING_DEPTH;
 // The per-slot-scale variant keeps 8 more VGPRs per page in flight; 2 pages per
 // stage keep it at 2 waves per SIMD.
-constexpr int kSlotScalePagesPerStage = 2;
+#ifndef PA_SLOT_SCALE_PAGES_PER_STAGE
+#define PA_SLOT_SCALE_PAGES_PER_STAGE 2
+#endif
+constexpr int kSlotScalePagesPerStage = PA_SLOT_SCALE_PAGES_PER_STAGE;
 // Two query tiles per item hold a second set of accumulators: 2 pages per stage
 // keep that variant at 2 waves per SIMD too.
 constexpr int kTwoTilePagesPerStage = 2;
@@ -119,6 +122,18 @@ __device__ __forceinline__ float max_over_rows(float x) {
   return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
 }
 
+// The value lane I of this lane's quad (lanes 4k .. 4k + 3) holds (DPP quad
+// broadcast).
+template <int I>
+__device__ __forceinline__ uint32_t quad_lane(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x55 * I, 0xF, 0xF, false);
+}
+
+// The four values lanes 0..3 of this lane's quad hold.
+__device__ __forceinline__ u32x4 quad_gather(uint32_t v) {
+  return u32x4{quad_lane<0>(v), quad_lane<1>(v), quad_lane<2>(v), quad_lane<3>(v)};
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   const __bf16 x = (__bf16)a;
   const __bf16 y = (__bf16)b;
@@ -133,8 +148,8 @@ template <int PPS>
 struct Stage {
   u32x4 k[PPS][2];     // per page: 16 bytes of chunk (l >> 4) and of chunk 4 + (l >> 4)
   uint32_t v[PPS][8];  // per page: 4 slots of one dim in each of the 8 16-dim blocks
-  u32x4 ks[PPS];       // per-slot scales of slots 4 rq .. 4 rq + 3 (per-slot variant only)
-  u32x4 vs[PPS];
+  uint32_t ks[PPS];    // per-slot scale of slot 4 rq + (lane & 3) (per-slot variant only)
+  uint32_t vs[PPS];
 };
 
 // SS: per-slot scale tables instead of per-tensor scales.  K scales multiply
@@ -421,8 +436,10 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
             __builtin_amdgcn_make_buffer_rsrc((void*)(p.k_slot_scales + srow), (short)0, sbytes, kRsrcWord3);
         const __amdgpu_buffer_rsrc_t rvs =
             __builtin_amdgcn_make_buffer_rsrc((void*)(p.v_slot_scales + srow), (short)0, sbytes, kRsrcWord3);
-        st.ks[pp] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rks, rq * 16, 0, 0));
-        st.vs[pp] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rvs, rq * 16, 0, 0));
+        // one dword a lane: the scale of slot 4 rq + (lane & 3); the lane's
+        // four slots 4 rq .. 4 rq + 3 are gathered from its quad at use
+        st.ks[pp] = __builtin_amdgcn_raw_buffer_load_b32(rks, (rq * 4 + (lane & 3)) * 4, 0, 0);
+        st.vs[pp] = __builtin_amdgcn_raw_buffer_load_b32(rvs, (rq * 4 + (lane & 3)) * 4, 0, 0);
       }
       st.k[pp][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff, 0, kAux));
       st.k[pp][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, koff + khi, 0, kAux));
@@ -490,6 +507,12 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
         z[u][pp] = t;
       }
     }
+    // per-slot K scales of the lane's four slots of each page
+    u32x4 ksq[PPS];
+    if constexpr (SS) {
+#pragma unroll
+      for (int pp = 0; pp < PPS; ++pp) ksq[pp] = quad_gather(st.ks[pp]);
+    }
     // scale, mask, running max
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
@@ -499,7 +522,7 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float v = z[u][pp][i] * c_log2;
-          if constexpr (SS) v *= __uint_as_float(st.ks[pp][i]);
+          if constexpr (SS) v *= __uint_as_float(ksq[pp][i]);
           if constexpr (MQ) {
             const int t = (j0 + pp) * kBlockTokens + rq * 4 + i;
             if (capped) {
@@ -533,7 +556,7 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
         // 2^-e for the exponent e of the item's first V scale (token 0 is always
         // in the context); clamped so that the factor and its inverse are normal,
         // and 1 when that scale is zero or subnormal (e.g. a page read as zeros)
-        const uint32_t e0 = (__builtin_amdgcn_readfirstlane(st.vs[0][0]) >> 23) & 0xFFu;
+        const uint32_t e0 = (__builtin_amdgcn_readfirstlane(st.vs[0]) >> 23) & 0xFFu;  // lane 0: slot 0
         const uint32_t eb = e0 == 0u ? 127u : min(e0, 253u);
         vnorm = __uint_as_float((254u - eb) << 23);
         vnorm_inv = __uint_as_float(eb << 23);
@@ -548,13 +571,14 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
         vmask = nv >= 4 ? 0xFFFFFFFFu : (nv <= 0 ? 0u : ((1u << (8 * nv)) - 1u));
       }
       if constexpr (SS) {
+        const u32x4 vsq = quad_gather(st.vs[pp]);  // the lane's four slots' V scales
         f16x4 pb, pv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float e = __builtin_amdgcn_exp2f(z[0][pp][i] - m_run[0]);
           pb[i] = (_Float16)e;
           // masked tokens have e == 0; their scale may be NaN and must not reach PV
-          const float w = e == 0.0f ? 0.0f : fminf(e * __uint_as_float(st.vs[pp][i]) * vnorm, 65504.0f);
+          const float w = e == 0.0f ? 0.0f : fminf(e * __uint_as_float(vsq[i]) * vnorm, 65504.0f);
           pv[i] = (_Float16)w;
         }
 #pragma unroll
