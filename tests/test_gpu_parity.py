@@ -377,3 +377,23 @@ def test_longest_first_order_covers_every_sequence():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), plain.view(torch.int16)), f"replay {r}"
+
+
+def test_cache_policy_does_not_change_results():
+    """Working sets within the Infinity Cache are read with the default cache
+    policy, larger ones with the streaming hint: two instantiations of the
+    same arithmetic.  The same sequences with a table padded to 2048 blocks
+    (K/V bound 8 x 2048 x 8 x 4 KiB = 512 MiB: streaming) and with a 256-block
+    table (64 MiB: cached), at one explicit partition size, must agree bit for
+    bit, and meet the bound against the oracle."""
+    lens = [4096, 1, 3000, 17, 2048, 4095, 100, 777]
+    case = workloads.make_case(40, 8, lens, seed=41, max_blocks=256).to("cuda")
+    wide = torch.zeros(len(lens), 2048, dtype=torch.int32, device="cuda")
+    wide[:, :256] = case.block_tables
+    padded = workloads.Case("padded", case.q, case.k_cache, case.v_cache, wide, case.seq_lens,
+                            case.scale, case.k_scale, case.v_scale)
+    log("cache policy: 256- vs 2048-block tables, 32 blocks per partition")
+    a = run_gpu(case, 32)
+    b = run_gpu(padded, 32)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    compare(a, run_oracle(case), "cache policy")
