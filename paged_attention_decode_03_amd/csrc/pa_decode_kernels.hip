@@ -340,8 +340,9 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
   const int koff = TR ? col * tstride + rq * 16 : lane * 16;
   constexpr int khi = TR ? 64 : 1024;
   // V: page layout: dim col (+16 jd), slots 4 rq .. 4 rq + 3 (one dword per jd);
-  // token rows: token lane >> 2, bytes 32 (lane & 3) .. +31 of its row
-  const int voff = TR ? (lane >> 2) * tstride + (lane & 3) * 32 : col * 16 + rq * 4;
+  // token rows: bytes 16 (lane & 7) .. +15 of tokens lane >> 3 and 8 + (lane >> 3)
+  // (each load reads eight whole 128-byte rows)
+  const int voff = TR ? (lane >> 3) * tstride + (lane & 7) * 16 : col * 16 + rq * 4;
   // bytes a page's descriptor covers
   const int page_bytes = TR ? (kBlockTokens - 1) * tstride + kHeadDim : kPageBytes;
 
@@ -446,7 +447,8 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
       if constexpr (TR) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const u32x4 w = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff + 16 * h, 0, kAux));
+          const u32x4 w =
+              __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff + 8 * h * tstride, 0, kAux));
 #pragma unroll
           for (int e = 0; e < 4; ++e) st.v[pp][4 * h + e] = w[e];
         }
@@ -477,9 +479,12 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
     if constexpr (TR) {
 #pragma unroll
       for (int pp = 0; pp < PPS; ++pp) {
-        uint8_t* dst = vtb + (pp * kBlockTokens + (lane >> 2)) * kVRow + (lane & 3) * 32;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) *(uint2*)(dst + 8 * e) = make_uint2(st.v[pp][2 * e], st.v[pp][2 * e + 1]);
+        for (int h = 0; h < 2; ++h) {
+          uint8_t* dst = vtb + (pp * kBlockTokens + 8 * h + (lane >> 3)) * kVRow + (lane & 7) * 16;
+          *(uint2*)dst = make_uint2(st.v[pp][4 * h], st.v[pp][4 * h + 1]);
+          *(uint2*)(dst + 8) = make_uint2(st.v[pp][4 * h + 2], st.v[pp][4 * h + 3]);
+        }
       }
       __syncthreads();
     }
