@@ -44,6 +44,10 @@ int fail(int code, const char* fmt, ...) {
 #ifndef PA_CACHED_LOAD_MAX_MIB
 #define PA_CACHED_LOAD_MAX_MIB 320
 #endif
+#ifndef PA_TR_MAX_KV_GROUP
+#define PA_TR_MAX_KV_GROUP 8
+#endif
+constexpr int kTokenRowMaxKvGroup = PA_TR_MAX_KV_GROUP;  // kv heads walking a sequence together
 constexpr int kItemsPerCU = PA_ITEMS_PER_CU;  // from this many items per CU, no split
 constexpr int kSplitItemsPerCU = PA_SPLIT_ITEMS_PER_CU;  // what a split aims for, per CU
 // K/V working sets up to this size (about the 256 MB Infinity Cache and a
@@ -340,7 +344,7 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   // nothing from it
   p.kv_group = 1;
   if (var.token_rows && var.head_stride < var.token_stride)
-    for (int g = 8; g >= 1; --g)
+    for (int g = kTokenRowMaxKvGroup; g >= 1; --g)
       if (Hkv % g == 0) {
         p.kv_group = g;
         break;
