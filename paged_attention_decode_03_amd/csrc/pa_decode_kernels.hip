@@ -195,12 +195,15 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
     if (item >= p.num_seqs * p.num_kv_heads * p.num_parts) return;  // grid padding
   }
   int rest = item / p.num_parts;
-  // partition: rotated by the unit, so that the first partition of every unit
-  // (the one each context has) does not land on the same XCD (blocks go to the
-  // 8 XCDs round robin) whenever the partition count is a multiple of 8
+  // partition: rotated across units, so that the first partition of every
+  // unit (the one each context has) does not always land on the same XCDs.
+  // Blocks go to the 8 XCDs round robin, so with P partitions a block's XCD
+  // depends on the unit only through rest mod 8 / gcd(P, 8): rotating by
+  // rest / (8 / gcd(P, 8)) gives every XCD every partition index in turn.
   int part = item % p.num_parts;
   if (p.num_parts > 1) {
-    part += rest % p.num_parts;
+    const int g = min(p.num_parts & -p.num_parts, 8);  // gcd(P, 8)
+    part += (rest >> (3 - __builtin_ctz(g))) % p.num_parts;
     if (part >= p.num_parts) part -= p.num_parts;
   }
   const int kv_units = TR ? p.num_kv_heads / p.kv_group : p.num_kv_heads;  // work items per (sequence, partition)
