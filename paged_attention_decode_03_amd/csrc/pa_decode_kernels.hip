@@ -87,6 +87,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 // and each wave's LDS for one stage of V pages (16 rows of 128 + 8 bytes per page).
 constexpr int kMaxKvPerGroup = 8;
 
+
 constexpr int kVRow = kHeadDim + 8;
 template <int PPS>
 constexpr int kVtBytes = PPS * kBlockTokens * kVRow;
@@ -169,7 +170,12 @@ struct Stage {
 // NT (several queries): query tiles per item.  With NT = 2 one wave holds two
 // tiles' columns (two sets of accumulators against the same K/V registers), so
 // up to 2 * q_tile queries of a sequence cost one read of its pages.
-template <int PPS, int NB, bool SS, bool MQ, int AUX = PA_LOAD_AUX, bool TR = false, int NT = 1>
+//
+// VL (page layout): V pages are loaded as two 16-byte pieces a lane (dims lane
+// and 64 + lane, all 16 slots: two load instructions a page instead of eight)
+// and copied to LDS, where each PV operand is one dword of the page.
+template <int PPS, int NB, bool SS, bool MQ, int AUX = PA_LOAD_AUX, bool TR = false, int NT = 1,
+          bool VL = false>
 __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU))) void pa_decode_kernel(const DecodeParams p) {
   const int lane = threadIdx.x & 63;
   // Token rows: a workgroup holds kv_group kv heads of one sequence (one wave
@@ -457,6 +463,14 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
 #pragma unroll
           for (int e = 0; e < 4; ++e) st.v[pp][4 * h + e] = w[e];
         }
+      } else if constexpr (VL) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 w =
+              __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, lane * 16 + 1024 * h, 0, kAux));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) st.v[pp][4 * h + e] = w[e];
+        }
       } else {
 #pragma unroll
         for (int jd = 0; jd < 8; ++jd)
@@ -473,6 +487,8 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
       const uint8_t* b = vtb + (pp * kBlockTokens + 4 * rq) * kVRow + 16 * jd + col;
       return (uint32_t)b[0] | ((uint32_t)b[kVRow] << 8) | ((uint32_t)b[2 * kVRow] << 16) |
              ((uint32_t)b[3 * kVRow] << 24);
+    } else if constexpr (VL) {
+      return *(const uint32_t*)(vtb + pp * kPageBytes + (col + 16 * jd) * 16 + 4 * rq);
     } else {
       return st.v[pp][jd];
     }
@@ -480,7 +496,19 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
 
   auto compute = [&](const Stage<PPS>& st, int stage, bool last) {
     const int j0 = pstart + stage * PPS;
-    uint8_t* const vtb = vt + (stage & 1) * kVtBytes<PPS>;
+    uint8_t* const vtb = vt + (TR ? (stage & 1) * kVtBytes<PPS> : 0);
+    if constexpr (VL) {
+      // the stage's V pages, copied as they are (one buffer: the wave's LDS
+      // operations run in order, so these writes follow the last stage's reads)
+#pragma unroll
+      for (int pp = 0; pp < PPS; ++pp) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          *(u32x4*)(vtb + pp * kPageBytes + 1024 * h + lane * 16) =
+              u32x4{st.v[pp][4 * h], st.v[pp][4 * h + 1], st.v[pp][4 * h + 2], st.v[pp][4 * h + 3]};
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    }
     if constexpr (TR) {
 #pragma unroll
       for (int pp = 0; pp < PPS; ++pp) {
@@ -847,9 +875,11 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   else if (p.cached_loads)
     hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false, 0>), dim3((unsigned)items),
                        dim3(64), 0, stream, p);
-  else
-    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false>), dim3((unsigned)items),
-                       dim3(64), 0, stream, p);
+  else  // streamed working sets: V through LDS (fewer load instructions; measured on MI355X,
+        // 40/8 ctx 4096: 256 sequences 327.6 -> 326.9 us, ragged 1..4000 216.7 -> 202.5 us,
+        // while a 24-sequence set that stays in the Infinity Cache lost 4% with it)
+    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false, PA_LOAD_AUX, false, 1, true>),
+                       dim3((unsigned)items), dim3(64), kPagesPerStage * kPageBytes, stream, p);
   const size_t rows = p.multi_query ? (size_t)p.num_q_rows : (size_t)p.num_seqs;
   if (p.num_parts > 1 && rows > 0)
     hipLaunchKernelGGL(pa_merge_kernel, dim3((unsigned)(rows * p.num_heads)), dim3(kMergeThreads), 0, stream,
