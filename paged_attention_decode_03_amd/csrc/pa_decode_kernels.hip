@@ -88,6 +88,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxKvPerGroup = 8;
 
 
+
 constexpr int kVRow = kHeadDim + 8;
 template <int PPS>
 constexpr int kVtBytes = PPS * kBlockTokens * kVRow;
@@ -860,18 +861,21 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false, PA_LOAD_AUX, true>),
                        dim3((unsigned)(items / p.kv_group)), dim3(64 * p.kv_group),
                        (unsigned)(p.kv_group * 2 * kVtBytes<kPagesPerStage>), stream, p);
+  // V through LDS where it measured faster on MI355X (40/8 ctx 4096 x 256):
+  // two query tiles per item (4 queries: 372.9 -> 369.4 us) and per-slot
+  // scales (339.8 -> 335.6 us); one tile per item was 0.5% slower with it
   else if (p.multi_query && p.tiles_per_item == 2 && p.num_q_tiles > 2)
-    hipLaunchKernelGGL((pa_decode_kernel<kTwoTilePagesPerStage, kRingDepth, false, true, 0, false, 2>),
-                       dim3((unsigned)items), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((pa_decode_kernel<kTwoTilePagesPerStage, kRingDepth, false, true, 0, false, 2, true>),
+                       dim3((unsigned)items), dim3(64), kTwoTilePagesPerStage * kPageBytes, stream, p);
   else if (p.multi_query && p.tiles_per_item == 2)
-    hipLaunchKernelGGL((pa_decode_kernel<kTwoTilePagesPerStage, kRingDepth, false, true, PA_LOAD_AUX, false, 2>),
-                       dim3((unsigned)items), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((pa_decode_kernel<kTwoTilePagesPerStage, kRingDepth, false, true, PA_LOAD_AUX, false, 2, true>),
+                       dim3((unsigned)items), dim3(64), kTwoTilePagesPerStage * kPageBytes, stream, p);
   else if (p.multi_query)
     hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, true>), dim3((unsigned)items),
                        dim3(64), 0, stream, p);
   else if (p.k_slot_scales)
-    hipLaunchKernelGGL((pa_decode_kernel<kSlotScalePagesPerStage, kRingDepth, true, false>),
-                       dim3((unsigned)items), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((pa_decode_kernel<kSlotScalePagesPerStage, kRingDepth, true, false, PA_LOAD_AUX, false, 1, true>),
+                       dim3((unsigned)items), dim3(64), kSlotScalePagesPerStage * kPageBytes, stream, p);
   else if (p.cached_loads)
     hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false, 0>), dim3((unsigned)items),
                        dim3(64), 0, stream, p);
