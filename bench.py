@@ -306,23 +306,32 @@ def time_cache_write(num_tokens, steps, warmup, num_kv_heads=8, prefill=True):
     return start.elapsed_time(end) * 1e3 / steps
 
 
-def cpu_baseline(sample_seqs=16):
-    """The fp64 oracle on a bounded sample of the same workload (host cores)."""
-    import numpy as np
+def cpu_baseline(target_seconds=12.0, max_seqs=256):
+    """The fp64 oracle on a bounded sample of the same workload (host cores):
+    16 sequences first, then as many as about target_seconds of oracle work
+    allow (a multiple of 16, up to the workload's 256), timed on their own."""
     import oracle
     import workloads
     hq, hkv, _, ctx = workloads.TARGET
-    case = workloads.dense(hq, hkv, sample_seqs, ctx, seed=1, device="cpu")
     cores = os.cpu_count() or 1
-    args = (case.q_bits(), case.k_cache.numpy(), case.v_cache.numpy(), case.block_tables.numpy(),
-            case.seq_lens.numpy(), case.scale, case.k_scale, case.v_scale)
-    t0 = time.perf_counter()
-    oracle.decode(*args, num_threads=cores)
-    dt = time.perf_counter() - t0
-    return {"value": round(case.algorithmic_bytes() / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"{sample_seqs} of 256 sequences of the same shape (40/8 heads, ctx {ctx}), "
-                      f"all heads; {dt:.2f} s wall on {cores} threads"}
+
+    def run(n):
+        case = workloads.dense(hq, hkv, n, ctx, seed=1, device="cpu")
+        args = (case.q_bits(), case.k_cache.numpy(), case.v_cache.numpy(), case.block_tables.numpy(),
+                case.seq_lens.numpy(), case.scale, case.k_scale, case.v_scale)
+        t0 = time.perf_counter()
+        oracle.decode(*args, num_threads=cores)
+        return case.algorithmic_bytes(), time.perf_counter() - t0
+
+    n = 16
+    b, dt = run(n)
+    m = int(min(max_seqs, n * target_seconds / max(dt, 1e-3))) // 16 * 16
+    if m > n:
+        n = m
+        b, dt = run(n)
+    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} of 256 sequences of the same shape (40/8 heads, ctx {ctx}), all heads; "
+                      f"{dt:.2f} s wall on {cores} threads"}
 
 
 def copy_calibration(steps):
