@@ -24,14 +24,18 @@
 // per-head softmax quantity (running max, rescale factor) is lane-local; the
 // only cross-lane step is a max over the four 16-lane rows (permlane swaps).
 //
-// Loads go straight from HBM into VGPRs, in the layouts the MFMAs want:
-//   K: two fully coalesced 1 KiB dwordx4 loads per page (lane l: token l & 15,
-//      16-dim chunks l >> 4 and 4 + (l >> 4)),
-//   V: eight dword loads per page, each a contiguous 256 B (16 dims x 16 slots).
+// Loads go from HBM into VGPRs:
+//   K: two fully coalesced 1 KiB dwordx4 loads per page, in the layout the
+//      MFMA wants (lane l: token l & 15, 16-dim chunks l >> 4 and 4 + (l >> 4)),
+//   V: either eight dword loads per page in the operand layout (each a
+//      contiguous 256 B: 16 dims x 16 slots), or (VL) two 1 KiB dwordx4 loads
+//      whose page is copied to LDS and read back one operand dword at a time;
+//      fewer load instructions per page measured faster on streamed sets.
 // Token-row caches (TR: each token's 128 dims contiguous, the flash-style
 // layouts of the API page's unified backend) load K the same way (lane l:
-// 16 B chunks of token l & 15's row) and V as 32 B per lane of token rows;
-// a V page then passes through LDS, transposed into the dims x tokens operand.
+// 16 B chunks of token l & 15's row) and V as whole 128 B token rows (eight
+// per load); a V page then passes through LDS, transposed into the dims x
+// tokens operand.
 // Several queries per sequence (MQ): the 16 columns hold (query token, head)
 // pairs, and an item holds one or two such tiles against the same K/V.
 // Pages are software-pipelined PPS at a time, one stage ahead.
