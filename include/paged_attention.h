@@ -155,8 +155,8 @@ int paged_multi_query_attention(const void* q, const int32_t* cu_seqlens_q, int3
  *                    (a small kernel orders the sequences by length on the device
  *                    before the attention; up to 8192 sequences).  Same results,
  *                    bit for bit; pays off for ragged contexts (256 sequences of
- *                    1..4000 tokens at 40/8 heads on MI355X: 226 -> 205 us) and
- *                    costs the extra launch (about 4 us) when contexts are alike.
+ *                    1..4000 tokens at 40/8 heads on MI355X: 207 -> 193 us) and
+ *                    costs the extra launch (about 4.6 us) when contexts are alike.
  *                    Its scratch (4 bytes per sequence, after the split-KV scratch
  *                    rounded up to 256 bytes) is not in pa_decode_plan's figure.
  */

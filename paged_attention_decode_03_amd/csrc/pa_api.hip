@@ -70,7 +70,7 @@ struct Plan {
 // about as long as their sequences, and items dispatched last set the end of
 // the call.  A small kernel orders the sequences by length on the device (no
 // host read) and the decode kernel takes its items in that order.  Measured on
-// MI355X, 256 sequences of 1..4000 tokens at 40/8 heads: 226 -> 205 us; the
+// MI355X, 256 sequences of 1..4000 tokens at 40/8 heads: 207 -> 193 us; the
 // extra launch costs about 4 us, a loss when the contexts are all alike.
 constexpr int kLongestFirstMaxSeqs = 8192;  // what the one-workgroup order kernel holds
 
