@@ -397,3 +397,19 @@ def test_cache_policy_does_not_change_results():
     b = run_gpu(padded, 32)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     compare(a, run_oracle(case), "cache policy")
+
+
+def test_streamed_path_poison_empty_and_splits():
+    """The streamed-set instantiation (V pages through LDS) at its edges: tail
+    slots and unused blocks poisoned with NaN, empty and one-token sequences,
+    partial last pages, with and without split contexts.  A 2048-block table
+    (K/V bound 512 MiB) selects it; the poisoned case must equal the clean
+    one bit for bit and meet the bound."""
+    lens = [0, 1, 17, 4095, 33, 2000, 0, 256, 3001, 15]
+    cases = [workloads.make_case(40, 8, lens, seed=43, max_blocks=2048, poison=p) for p in (True, False)]
+    for ppp in (None, 64, 24):
+        log(f"streamed path, poison vs clean, pages per partition {ppp}")
+        a, b = run_gpu(cases[0], ppp).cpu(), run_gpu(cases[1], ppp).cpu()
+        assert torch.isfinite(a.float()).all()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+        compare(a, run_oracle(cases[1]), f"streamed path ppp={ppp}")
