@@ -361,9 +361,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; the kernel works on one GPU's share of "
-              "heads/sequences and has no cross-GPU path (see the sharding notes in DESIGN.md).",
-              file=sys.stderr)
+        print("bench.py: runs on one GPU only: the kernel works on one GPU's share of "
+              "heads/sequences (tensor or data parallel shards need no exchange inside attention) "
+              "and there is no cross-GPU path.", file=sys.stderr)
         sys.exit(2)
 
     import torch
