@@ -283,7 +283,10 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   const int32_t q_tiles = mq ? (max_seqlen_q + q_tile - 1) / q_tile : 1;
   Plan plan;
   // work items per (sequence, kv head, partition): one per pair of query tiles
-  const int32_t q_items = q_tiles > 1 ? (q_tiles + 1) / 2 : 1;
+  // query tiles per work item: up to three (one wave holds their accumulators
+  // against the same K/V); four tiles go as two items of two
+  const int32_t tiles_per_item = q_tiles <= 2 ? q_tiles : (q_tiles == 4 ? 2 : 3);
+  const int32_t q_items = (q_tiles + tiles_per_item - 1) / tiles_per_item;
   int rc = make_plan(S, Hq, Hkv, W, device_cus(dev), ppp_req, &plan, q_items, mq ? num_q_rows : S,
                      opt.longest_first != 0);
   if (rc) return rc;
@@ -330,7 +333,7 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   p.q_tile = q_tile;
   p.num_q_tiles = q_tiles;
   // more than one tile of queries: two tiles per item share the page reads
-  p.tiles_per_item = q_tiles > 1 ? 2 : 1;
+  p.tiles_per_item = tiles_per_item;
   p.window = opt.sliding_window;
   p.softcap = opt.logits_soft_cap;
   p.scale = scale;

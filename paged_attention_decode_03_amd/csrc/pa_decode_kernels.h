@@ -43,7 +43,7 @@ struct DecodeParams {
   int32_t num_q_rows;        // cu_seqlens_q[S]: rows of q and out
   int32_t q_tile;            // query tokens per work item (columns = q_tile * group <= 16)
   int32_t num_q_tiles;       // query tiles per sequence (from the host's max_seqlen_q)
-  int32_t tiles_per_item;    // query tiles one work item holds (1 or 2)
+  int32_t tiles_per_item;    // query tiles one work item holds (1 to 3)
   // options of the several-queries form (0 / null: off)
   int32_t window;            // a query at position p sees tokens p - window + 1 .. p
   float softcap;             // logit z -> softcap * tanh(z / softcap)

@@ -84,6 +84,10 @@ constexpr int kSlotScalePagesPerStage = PA_SLOT_SCALE_PAGES_PER_STAGE;
 // Two query tiles per item hold a second set of accumulators: 2 pages per stage
 // keep that variant at 2 waves per SIMD too.
 constexpr int kTwoTilePagesPerStage = 2;
+// Three tiles per item: a third set of accumulators; one page per stage keeps
+// it within 256 VGPRs (2 waves per SIMD).
+constexpr int kThreeTilePagesPerStage = 1;
+
 // Word 3 of a raw buffer resource (no format conversion, no swizzle).
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -172,9 +176,10 @@ struct Stage {
 // queries sees tokens 0 .. L - q_len + i, so a tile's context ends at its last
 // query's position and the tokens past each column's own position are masked.
 //
-// NT (several queries): query tiles per item.  With NT = 2 one wave holds two
-// tiles' columns (two sets of accumulators against the same K/V registers), so
-// up to 2 * q_tile queries of a sequence cost one read of its pages.
+// NT (several queries): query tiles per item.  With NT = 2 or 3 one wave holds
+// that many tiles' columns (sets of accumulators against the same K/V
+// registers), so up to NT * q_tile queries of a sequence cost one read of its
+// pages.
 //
 // VL (page layout): V pages are loaded as two 16-byte pieces a lane (dims lane
 // and 64 + lane, all 16 slots: two load instructions a page instead of eight)
@@ -868,6 +873,9 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   // V through LDS where it measured faster on MI355X (40/8 ctx 4096 x 256):
   // two query tiles per item (4 queries: 372.9 -> 369.4 us) and per-slot
   // scales (339.8 -> 335.6 us); one tile per item was 0.5% slower with it
+  else if (p.multi_query && p.tiles_per_item == 3)
+    hipLaunchKernelGGL((pa_decode_kernel<kThreeTilePagesPerStage, kRingDepth, false, true, PA_LOAD_AUX, false, 3, true>),
+                       dim3((unsigned)items), dim3(64), kThreeTilePagesPerStage * kPageBytes, stream, p);
   else if (p.multi_query && p.tiles_per_item == 2 && p.num_q_tiles > 2)
     hipLaunchKernelGGL((pa_decode_kernel<kTwoTilePagesPerStage, kRingDepth, false, true, 0, false, 2, true>),
                        dim3((unsigned)items), dim3(64), kTwoTilePagesPerStage * kPageBytes, stream, p);
