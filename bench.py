@@ -68,6 +68,12 @@ def counter_traffic():
 
 def make_workload(name, device):
     import workloads
+    if name.endswith("_lpt") and not name.startswith("ragged_"):
+        # any one-query workload with longest-first dispatch
+        case = make_workload(name[:-4], device)
+        case.longest_first = True
+        case.name = name
+        return case
     if name == "target":
         hq, hkv, s, ctx = workloads.TARGET
         return workloads.dense(hq, hkv, s, ctx, seed=0, device=device)

@@ -151,14 +151,17 @@ int paged_multi_query_attention(const void* q, const int32_t* cu_seqlens_q, int3
  *   sinks            NULL: off; else device fp32 [num_heads]: one more softmax
  *                    term exp(sinks[h]) that carries no value
  * and, for any call:
- *   longest_first    0: off; 1: work items are dispatched longest sequence first
- *                    (a small kernel orders the sequences by length on the device
- *                    before the attention; up to 8192 sequences).  Same results,
- *                    bit for bit; pays off for ragged contexts (256 sequences of
- *                    1..4000 tokens at 40/8 heads on MI355X: 207 -> 193 us) and
- *                    costs the extra launch (about 4.6 us) when contexts are alike.
- *                    Its scratch (4 bytes per sequence, after the split-KV scratch
- *                    rounded up to 256 bytes) is not in pa_decode_plan's figure.
+ *   longest_first    0: off; 1: work items are dispatched longest sequence first.
+ *                    Up to 512 sequences (block-table caches) each work item
+ *                    finds its own sequence by a counting sort of the lengths;
+ *                    otherwise, up to 8192 sequences, a small kernel orders them
+ *                    first (about 4.6 us more); above that the order stays plain.
+ *                    Same results, bit for bit; pays off for ragged contexts
+ *                    (256 sequences of 1..4000 tokens at 40/8 heads on MI355X:
+ *                    202 -> 185 us) and costs about 3 us when contexts are alike.
+ *                    The order kernel's scratch (4 bytes per sequence, after the
+ *                    split-KV scratch rounded up to 256 bytes) is not in
+ *                    pa_decode_plan's figure.
  */
 typedef struct pa_attention_options {
   int32_t sliding_window;

@@ -70,9 +70,15 @@ struct Plan {
 // about as long as their sequences, and items dispatched last set the end of
 // the call.  A small kernel orders the sequences by length on the device (no
 // host read) and the decode kernel takes its items in that order.  Measured on
-// MI355X, 256 sequences of 1..4000 tokens at 40/8 heads: 207 -> 193 us; the
-// extra launch costs about 4 us, a loss when the contexts are all alike.
+// MI355X, 256 sequences of 1..4000 tokens at 40/8 heads: 202 -> 185 us with
+// the order computed inside the work items (the order kernel instead: 188 us,
+// its extra launch costing about 4.6 us); a loss of about 3 us when the
+// contexts are all alike.
 constexpr int kLongestFirstMaxSeqs = 8192;  // what the one-workgroup order kernel holds
+constexpr int kInKernelOrderMaxSeqs = 512;  // what a work item orders by itself (8 per lane)
+#ifndef PA_LPT_IN_KERNEL
+#define PA_LPT_IN_KERNEL 1
+#endif
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -287,8 +293,12 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   // against the same K/V); four tiles go as two items of two
   const int32_t tiles_per_item = q_tiles <= 2 ? q_tiles : (q_tiles == 4 ? 2 : 3);
   const int32_t q_items = (q_tiles + tiles_per_item - 1) / tiles_per_item;
+  // longest-first: computed by each work item where its workgroup is one wave
+  // and the sequences few enough, else by the order kernel
+  const bool lpt_in_kernel =
+      PA_LPT_IN_KERNEL && opt.longest_first != 0 && !var.token_rows && S >= 2 && S <= kInKernelOrderMaxSeqs;
   int rc = make_plan(S, Hq, Hkv, W, device_cus(dev), ppp_req, &plan, q_items, mq ? num_q_rows : S,
-                     opt.longest_first != 0);
+                     opt.longest_first != 0 && !lpt_in_kernel);
   if (rc) return rc;
   // one 64-lane block per work item, 256 lanes per merged row: keep both grids
   // within 2^32 lanes
@@ -356,6 +366,7 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   p.token_stride = var.token_stride;
   p.head_stride = var.head_stride;
   p.seq_order = nullptr;
+  p.order_in_kernel = lpt_in_kernel ? 1 : 0;
   if (plan.workspace_bytes) {
     void* ws = nullptr;
     rc = ensure_workspace(dev, plan.workspace_bytes, stream, true, &ws);

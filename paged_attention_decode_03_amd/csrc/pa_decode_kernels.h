@@ -61,6 +61,9 @@ struct DecodeParams {
   // longest-first dispatch: work items take sequence seq_order[i] for the i-th
   // sequence slot (written by the order kernel before the decode); null: in order
   int32_t* seq_order;
+  // longest-first computed by each work item itself (one-wave workgroups,
+  // num_seqs <= 512); excludes seq_order
+  int32_t order_in_kernel;
 };
 
 // Enqueue the decode (and, when num_parts > 1, the merge) on `stream`.

@@ -155,6 +155,84 @@ __device__ __forceinline__ int clamp_len(int len, int max_blocks) {
   return min(max(len, 0), max_blocks * kBlockTokens);
 }
 
+// Longest-first order: sequences bucketed by context pages into kOrderBins
+// bins (bin 0 longest).  The order kernel takes up to kOrderThreads *
+// kOrderPer sequences; a one-wave work item computes its own sequence for up
+// to 64 * kInKernelOrderPer.
+constexpr int kOrderThreads = 256;
+constexpr int kOrderPer = 32;
+constexpr int kOrderBins = 256;
+constexpr int kInKernelOrderPer = 8;
+
+// The sequence of longest-first slot `slot`, computed by one wave alone: the
+// sequences in bin order and, within a bin, in index order (a stable counting
+// sort, so every wave of the grid computes the same permutation).  The bin
+// histogram lives in this wave's LDS; a wave's LDS operations run in order.
+__device__ __forceinline__ int lpt_sequence(const DecodeParams& p, int slot, int lane) {
+  __shared__ int cnt[kOrderBins];
+  const int S = p.num_seqs;
+  const int wmax = p.max_blocks > 0 ? p.max_blocks : 1;
+#pragma unroll
+  for (int b = 0; b < kOrderBins / 64; ++b) cnt[b * 64 + lane] = 0;
+  int bin[kInKernelOrderPer];
+#pragma unroll
+  for (int k = 0; k < kInKernelOrderPer; ++k) {
+    const int s = lane + 64 * k;
+    int b = -1;
+    if (s < S) {
+      const int len = min(max(p.seq_lens[s], 0), p.max_blocks * kBlockTokens);
+      const int pages = (len + kBlockTokens - 1) / kBlockTokens;
+      b = kOrderBins - 1 - (int)((int64_t)pages * (kOrderBins - 1) / wmax);
+    }
+    bin[k] = b;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+  for (int k = 0; k < kInKernelOrderPer; ++k)
+    if (bin[k] >= 0) atomicAdd(&cnt[bin[k]], 1);
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  // exclusive scan over the bins: lane l owns bins 4 l .. 4 l + 3
+  int c[4], st[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) c[k] = cnt[4 * lane + k];
+  const int own = c[0] + c[1] + c[2] + c[3];
+  int incl = own;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  st[0] = incl - own;
+#pragma unroll
+  for (int k = 1; k < 4; ++k) st[k] = st[k - 1] + c[k - 1];
+  // the bin holding the slot, and the slot's rank within it
+  int code = -1, rank = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    if (slot >= st[k] && slot < st[k] + c[k]) {
+      code = 4 * lane + k;
+      rank = slot - st[k];
+    }
+  const uint64_t hitm = __builtin_amdgcn_ballot_w64(code >= 0);
+  if (hitm == 0) return slot;  // (not reached: every slot < S lies in some bin)
+  const int hl = __builtin_ctzll(hitm);
+  const int B = __builtin_amdgcn_readlane(code, hl);
+  int j = __builtin_amdgcn_readlane(rank, hl);
+  // the j-th sequence of bin B in index order
+#pragma unroll
+  for (int k = 0; k < kInKernelOrderPer; ++k) {
+    const uint64_t m = __builtin_amdgcn_ballot_w64(bin[k] == B);
+    const int cntk = __builtin_popcountll(m);
+    if (j < cntk) {
+      const int r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+      const uint64_t pick = __builtin_amdgcn_ballot_w64(((m >> lane) & 1) && r == j);
+      return 64 * k + __builtin_ctzll(pick);
+    }
+    j -= cntk;
+  }
+  return slot;  // (not reached)
+}
+
 template <int PPS>
 struct Stage {
   u32x4 k[PPS][2];     // per page: 16 bytes of chunk (l >> 4) and of chunk 4 + (l >> 4)
@@ -224,7 +302,11 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
   }
   const int kv_units = TR ? p.num_kv_heads / p.kv_group : p.num_kv_heads;  // work items per (sequence, partition)
   const int kvh = TR ? (rest % kv_units) * p.kv_group + wave : rest % kv_units;
-  const int s = p.seq_order ? scalar_load(p.seq_order + rest / kv_units) : rest / kv_units;
+  // longest-first: the sequence of this slot, from the order kernel or computed
+  // here (one-wave workgroups only)
+  const int s = (!TR && p.order_in_kernel) ? __builtin_amdgcn_readfirstlane(lpt_sequence(p, rest / kv_units, lane))
+                : p.seq_order                ? scalar_load(p.seq_order + rest / kv_units)
+                                             : rest / kv_units;
   const int ppp = p.pages_per_part;
   const int pbeg = part * ppp;  // < max_blocks: the planner never makes an empty partition range
 
@@ -809,9 +891,6 @@ __global__ __launch_bounds__(kMergeThreads) void pa_merge_kernel(const DecodePar
 // buckets, a bucket histogram in LDS, an exclusive scan from the longest bucket
 // down, then each sequence takes the next slot of its bucket.  More sequences
 // than the workgroup holds keep the plain order (the host does not order them).
-constexpr int kOrderThreads = 256;
-constexpr int kOrderPer = 32;
-constexpr int kOrderBins = 256;
 
 __global__ __launch_bounds__(kOrderThreads) void pa_order_kernel(const DecodeParams p) {
   __shared__ int cnt[kOrderBins];

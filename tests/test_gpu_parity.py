@@ -350,10 +350,11 @@ def test_longest_first_order_covers_every_sequence():
     """Longest-first dispatch (an order computed on the device) must compute
     every sequence exactly once with the same arithmetic: the unified call with
     no row offsets and longest_first must equal the plain decode bit for bit,
-    for ragged contexts that split and for ones that do not, and so must a
-    graph replay of it."""
+    for ragged contexts that split and for ones that do not, with the order
+    sorted inside each work item (up to 512 sequences) and by the order kernel
+    (more), for several queries per sequence, and in a graph replay."""
     import paged_attention_decode_03_amd as pa
-    for S, seed in ((48, 5), (300, 6), (3, 7)):
+    for S, seed in ((48, 5), (300, 6), (3, 7), (512, 8), (700, 9)):
         lens = workloads.ragged_lens(S, seed=seed)
         case = workloads.make_case(40, 8, lens, seed=98 + S, max_blocks=250).to("cuda")
         ks = torch.tensor([case.k_scale], device="cuda")
@@ -364,6 +365,18 @@ def test_longest_first_order_covers_every_sequence():
         torch.cuda.synchronize()
         log(f"longest first S={S}")
         assert torch.equal(ordered.view(torch.int16), plain.view(torch.int16)), f"S={S}"
+    # several queries per sequence (one to six at 8 heads a group: one to three
+    # 16-row query tiles)
+    lens = workloads.ragged_lens(96, lo=8, hi=3000, seed=10)
+    ql = [1 + (i * 7) % 6 for i in range(96)]
+    mcase = workloads.make_multi_case(32, 4, lens, ql, seed=99).to("cuda")
+    margs = (mcase.k_cache, mcase.v_cache, mcase.block_tables, mcase.seq_lens, mcase.scale,
+             torch.tensor([mcase.k_scale], device="cuda"), torch.tensor([mcase.v_scale], device="cuda"))
+    a = pa.paged_attention_unified(mcase.q, mcase.cu_seqlens_q, 6, *margs)
+    b = pa.paged_attention_unified(mcase.q, mcase.cu_seqlens_q, 6, *margs, longest_first=True)
+    torch.cuda.synchronize()
+    log("longest first, several queries")
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     out = torch.empty_like(case.q)
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
