@@ -233,6 +233,59 @@ def time_calls(case, steps, warmup):
     return start.elapsed_time(end) * 1e3 / steps
 
 
+COLD_MIN_BYTES = 512 << 20   # twice the 256 MB Infinity Cache
+COLD_MAX_RESIDENT = 16 << 30
+
+
+def cold_copies(case):
+    """Copies of `case` in distinct device buffers, enough that the calls of one
+    round over them touch at least COLD_MIN_BYTES, so a call finds none of its
+    inputs left in the Infinity Cache by the previous ones.  [case] when the
+    workload already touches that much (or its layout is a view of a larger
+    tensor: token rows)."""
+    import copy
+    import torch
+    touched = workload_bytes(case)
+    if touched >= COLD_MIN_BYTES or getattr(case, "token_rows", None) is not None:
+        return [case]
+    resident = sum(t.numel() * t.element_size() for t in vars(case).values()
+                   if isinstance(t, torch.Tensor))
+    k = -(-COLD_MIN_BYTES // touched)
+    k = max(2, min(k, COLD_MAX_RESIDENT // max(resident, 1)))
+    out = [case]
+    for _ in range(k - 1):
+        c = copy.copy(case)
+        for name, t in vars(case).items():
+            if isinstance(t, torch.Tensor):
+                setattr(c, name, t.clone())
+        out.append(c)
+    return out
+
+
+def time_calls_cold(case, steps, warmup):
+    """Average µs per call over calls that rotate through cold_copies(case)
+    (each with its own output), HIP events on the launch stream: the
+    cold-cache figure of a workload smaller than twice the Infinity Cache."""
+    import torch
+    dev = case.q.device
+    cases = cold_copies(case)
+    stream = torch.cuda.Stream(dev)
+    calls = [make_call(c, torch.empty_like(c.q), stream) for c in cases]
+    for i in range(max(warmup, len(calls))):
+        calls[i % len(calls)]()
+    torch.cuda.synchronize(dev)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        calls[i % len(calls)]()
+    end.record(stream)
+    torch.cuda.synchronize(dev)
+    us = start.elapsed_time(end) * 1e3 / steps
+    del calls, cases
+    return us
+
+
 def time_graph(case, replays=50, calls_per_graph=10):
     """Average µs per call when `calls_per_graph` calls are captured in one HIP
     graph and the graph is replayed (the way the pages time impl.forward)."""
@@ -365,6 +418,10 @@ def main():
     ap.add_argument("--workload", default="target")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--cold", action="store_true",
+                    help="rotate the calls over copies of the inputs in distinct buffers "
+                         "(at least 512 MiB touched per round), so a small workload is "
+                         "timed from HBM rather than from the Infinity Cache")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: runs on one GPU only: the kernel works on one GPU's share of "
@@ -387,6 +444,8 @@ def main():
             case = make_workload(name, "cuda")
             us = time_calls(case, args.steps, args.warmup)
             us_graph = time_graph(case)
+            us_cold = time_calls_cold(case, args.steps, args.warmup) \
+                if workload_bytes(case) < COLD_MIN_BYTES else None
             P, ppp, _ = pa.pa_decode_plan(case.num_seqs, case.num_heads, case.num_kv_heads,
                                           case.max_blocks, 256)
             b = workload_bytes(case)
@@ -394,6 +453,7 @@ def main():
                 b += case.kv_bytes() // 128 * 4   # one fp32 K or V scale per cached token and kv head
             row = {"workload": name, "us_per_call": round(us, 2),
                    "us_per_call_graph": round(us_graph, 2),
+                   "us_per_call_cold": None if us_cold is None else round(us_cold, 2),
                    "GBps": round(b / us / 1e3, 1), "frac_of_peak": round(b / us / 1e3 / PEAK_GBS, 4),
                    "bytes": b}
             if case.cu_seqlens_q is None:   # the exported planner covers one query per sequence
@@ -423,7 +483,7 @@ def main():
         return
 
     case = make_workload(args.workload, "cuda")
-    us = time_calls(case, args.steps, args.warmup)
+    us = (time_calls_cold if args.cold else time_calls)(case, args.steps, args.warmup)
     B = workload_bytes(case)
     gbs = B / us / 1e3
     P, ppp, _ = pa.pa_decode_plan(case.num_seqs, case.num_heads, case.num_kv_heads, case.max_blocks, 256)
@@ -448,7 +508,8 @@ def main():
                    "40q/8kv heads, head_dim 128, 256 seqs x ctx 4096, fp8 e4m3fn KV, 16-token blocks",
                    "num_seqs": case.num_seqs, "num_heads": case.num_heads,
                    "num_kv_heads": case.num_kv_heads, "max_blocks_per_seq": case.max_blocks,
-                   "partitions": P, "pages_per_partition": ppp, "algorithmic_bytes": B},
+                   "partitions": P, "pages_per_partition": ppp, "algorithmic_bytes": B,
+                   "inputs": "rotated over copies (cold cache)" if args.cold else "one set"},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_GBS, 4), "traffic": traffic},
     }
