@@ -64,6 +64,10 @@ struct DecodeParams {
   // longest-first computed by each work item itself (one-wave workgroups,
   // num_seqs <= 512); excludes seq_order
   int32_t order_in_kernel;
+  // longest-first with one query per sequence: sequence slots per round of
+  // work items (one item per CU a round); every other round takes its slots in
+  // reverse order.  0: slots in plain longest-first order
+  int32_t lpt_round_slots;
 };
 
 // Enqueue the decode (and, when num_parts > 1, the merge) on `stream`.

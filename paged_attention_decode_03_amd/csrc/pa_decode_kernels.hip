@@ -233,6 +233,18 @@ __device__ __forceinline__ int lpt_sequence(const DecodeParams& p, int slot, int
   return slot;  // (not reached)
 }
 
+// Longest-first slots are dealt to the CUs in rounds of one work item per CU.
+// Taken in plain order, every round would give the same CUs its longest
+// sequences, and those CUs would get more than their share of the bytes; so
+// every other round runs in reverse (a CU that takes a round's longest
+// sequence takes the next round's shortest).  A bijection on [0, S).
+__device__ __forceinline__ int snake_slot(int slot, int per_round, int S) {
+  const int r = slot / per_round;
+  if (!(r & 1)) return slot;
+  const int end = min((r + 1) * per_round, S);
+  return r * per_round + (end - 1 - slot);
+}
+
 template <int PPS>
 struct Stage {
   u32x4 k[PPS][2];     // per page: 16 bytes of chunk (l >> 4) and of chunk 4 + (l >> 4)
@@ -304,9 +316,11 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
   const int kvh = TR ? (rest % kv_units) * p.kv_group + wave : rest % kv_units;
   // longest-first: the sequence of this slot, from the order kernel or computed
   // here (one-wave workgroups only)
-  const int s = (!TR && p.order_in_kernel) ? __builtin_amdgcn_readfirstlane(lpt_sequence(p, rest / kv_units, lane))
-                : p.seq_order                ? scalar_load(p.seq_order + rest / kv_units)
-                                             : rest / kv_units;
+  const int slot = p.lpt_round_slots > 0 ? snake_slot(rest / kv_units, p.lpt_round_slots, p.num_seqs)
+                                         : rest / kv_units;
+  const int s = (!TR && p.order_in_kernel) ? __builtin_amdgcn_readfirstlane(lpt_sequence(p, slot, lane))
+                : p.seq_order                ? scalar_load(p.seq_order + slot)
+                                             : slot;
   const int ppp = p.pages_per_part;
   const int pbeg = part * ppp;  // < max_blocks: the planner never makes an empty partition range
 
