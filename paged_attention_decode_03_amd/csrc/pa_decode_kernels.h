@@ -68,6 +68,9 @@ struct DecodeParams {
   // work items (one item per CU a round); every other round takes its slots in
   // reverse order.  0: slots in plain longest-first order
   int32_t lpt_round_slots;
+  // waves per work item: 1, or 2 (the page-layout decode with one query per
+  // sequence and per-tensor scales only)
+  int32_t waves_per_item;
 };
 
 // Enqueue the decode (and, when num_parts > 1, the merge) on `stream`.

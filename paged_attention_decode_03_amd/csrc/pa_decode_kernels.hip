@@ -274,15 +274,23 @@ struct Stage {
 // VL (page layout): V pages are loaded as two 16-byte pieces a lane (dims lane
 // and 64 + lane, all 16 slots: two load instructions a page instead of eight)
 // and copied to LDS, where each PV operand is one dword of the page.
+//
+// WPI (page layout, one query per sequence): waves per work item.  With 2,
+// wave w computes stages w, w + 2, ... of the item and wave 1 hands its
+// (max, denominator, accumulator) to wave 0 through LDS at the end, which
+// combines them by the log-sum-exp rule: twice the waves on a CU for the same
+// work items, no second kernel.
 template <int PPS, int NB, bool SS, bool MQ, int AUX = PA_LOAD_AUX, bool TR = false, int NT = 1,
-          bool VL = false>
-__global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU))) void pa_decode_kernel(const DecodeParams p) {
+          bool VL = false, int WPI = 1>
+__global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64 * WPI) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU))) void pa_decode_kernel(const DecodeParams p) {
   const int lane = threadIdx.x & 63;
   // Token rows: a workgroup holds kv_group kv heads of one sequence (one wave
   // each); on one CU at the same time, they walk the sequence's blocks at
   // about the same pace, so the token rows they share are read close together.
   // (wave-uniform, and known to be: buffer descriptors built from it stay scalar)
-  const int wave = TR ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) : 0;
+  // (two waves per item: the wave's share of the item's stages)
+  const int wave = (TR || WPI > 1) ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) : 0;
+  static_assert(WPI == 1 || (WPI == 2 && !TR && !MQ && !SS && NT == 1), "two waves: plain page-layout decode");
   const int col = lane & 15;  // MFMA column (query head in group); K load row (token)
   const int rq = lane >> 4;   // row quad: rows 4*rq .. 4*rq+3 of the 16x16 tiles
 
@@ -318,7 +326,22 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
   // here (one-wave workgroups only)
   const int slot = p.lpt_round_slots > 0 ? snake_slot(rest / kv_units, p.lpt_round_slots, p.num_seqs)
                                          : rest / kv_units;
-  const int s = (!TR && p.order_in_kernel) ? __builtin_amdgcn_readfirstlane(lpt_sequence(p, slot, lane))
+  int s_pick = 0;
+  if (!TR && p.order_in_kernel) {
+    if constexpr (WPI == 1) {
+      s_pick = __builtin_amdgcn_readfirstlane(lpt_sequence(p, slot, lane));
+    } else {
+      // one wave sorts (the histogram in LDS is its own); the other reads its pick
+      __shared__ int lpt_pick;
+      if (wave == 0) {
+        const int v = lpt_sequence(p, slot, lane);
+        if (lane == 0) lpt_pick = v;
+      }
+      __syncthreads();
+      s_pick = __builtin_amdgcn_readfirstlane(lpt_pick);
+    }
+  }
+  const int s = (!TR && p.order_in_kernel) ? s_pick
                 : p.seq_order                ? scalar_load(p.seq_order + slot)
                                              : slot;
   const int ppp = p.pages_per_part;
@@ -402,7 +425,7 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
   if (L == 0) {  // empty context: an all-zero row
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
-      if (hvalid[u]) {
+      if (hvalid[u] && (WPI == 1 || wave == 0)) {
 #pragma unroll
         for (int jd = 0; jd < 8; ++jd)
           *(uint2*)(p.out + orow[u] + jd * 16 + rq * 4) = make_uint2(0u, 0u);
@@ -488,9 +511,9 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
   // zeros without touching memory.  Those ids are therefore never used.
   const int npg = MQ ? max(0, pend - pstart) : pend - pbeg;
   const int nsteps = (npg + PPS - 1) / PPS;
-  constexpr int kIdsCap = kMaxPagesPerPart + NB * PPS;
+  constexpr int kIdsCap = kMaxPagesPerPart + (WPI * NB + 1) * PPS;
   __shared__ __attribute__((aligned(16))) int32_t ids[kIdsCap];
-  const int ids_fill = ioff + (nsteps + NB - 1) * PPS;  // every index a load can reach
+  const int ids_fill = ioff + (nsteps + WPI * NB) * PPS;  // every index a load can reach
 #pragma unroll
   for (int k = 0; k < (kIdsCap + 63) / 64; ++k) {
     const int i = k * 64 + lane;
@@ -509,7 +532,8 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
   // columns x 4 row groups) hit distinct banks.
   // (dynamic LDS, kv_group * 2 * kVtBytes<PPS> bytes, sized at launch)
   extern __shared__ __attribute__((aligned(16))) uint8_t pa_dyn_lds[];
-  uint8_t* const vt = pa_dyn_lds + wave * 2 * kVtBytes<PPS>;
+  // (VL: one stage of V pages per wave)
+  uint8_t* const vt = pa_dyn_lds + (TR ? wave * 2 * kVtBytes<PPS> : VL ? wave * PPS * kPageBytes : 0);
   auto load = [&](Stage<PPS>& st, int stage) {
     const int i0 = stage * PPS;           // page of the item (pages past npg are empty)
     const int32_t* idp = ids + ioff + i0;  // their staged block ids
@@ -757,16 +781,47 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64) __attribute__((amdgp
   };
 
   // Register ring of NB stages: NB - 1 stages are in flight while one is
-  // computed.  Loads past the last stage are empty (see above).
+  // computed.  Loads past the last stage are empty (see above).  With two
+  // waves per item, the wave's i-th stage is stage 2 i + wave of the item.
   Stage<PPS> ring[NB];
+  // (token rows: the waves of a workgroup are kv heads, each with every stage)
+  const int wsub = WPI > 1 ? wave : 0;
+  const int nloc = WPI == 1 ? nsteps : max(0, (nsteps - wsub + WPI - 1) / WPI);
 #pragma unroll
-  for (int k = 0; k < NB - 1; ++k) load(ring[k], k);
-  for (int st = 0; st < nsteps; st += NB) {
+  for (int k = 0; k < NB - 1; ++k) load(ring[k], WPI * k + wsub);
+  for (int st = 0; st < nloc; st += NB) {
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
-      if (st + k >= nsteps) break;
-      load(ring[(k + NB - 1) % NB], st + k + NB - 1);
-      compute(ring[k], st + k, st + k == nsteps - 1);
+      if (st + k >= nloc) break;
+      load(ring[(k + NB - 1) % NB], WPI * (st + k + NB - 1) + wsub);
+      const int g = WPI * (st + k) + wsub;
+      compute(ring[k], g, g == nsteps - 1);
+    }
+  }
+  if constexpr (WPI == 2) {
+    // Wave 1's (max, denominator, accumulator) to wave 0, lane by lane (both
+    // waves hold the same (head, dims) in a lane), combined as
+    // m = max(m0, m1), acc = acc0 2^(m0 - m) + acc1 2^(m1 - m), likewise l.
+    __shared__ f32x4 x_acc[8][64];
+    __shared__ float x_m[64], x_l[64];
+    if (wave == 1) {
+#pragma unroll
+      for (int jd = 0; jd < 8; ++jd) x_acc[jd][lane] = acc[0][jd];
+      x_m[lane] = m_run[0];
+      x_l[lane] = accl[0][0];
+    }
+    __syncthreads();
+    if (wave == 1) return;
+    const float m1 = x_m[lane];
+    const float m = fmaxf(m_run[0], m1);
+    if (m > -INFINITY) {  // (-inf in both: a column that holds no head)
+      const float f0 = __builtin_amdgcn_exp2f(m_run[0] - m);
+      const float f1 = __builtin_amdgcn_exp2f(m1 - m);
+#pragma unroll
+      for (int jd = 0; jd < 8; ++jd) acc[0][jd] = acc[0][jd] * f0 + x_acc[jd][lane] * f1;
+      const float l = accl[0][0] * f0 + x_l[lane] * f1;
+      accl[0] = f32x4{l, l, l, l};
+      m_run[0] = m;
     }
   }
 
@@ -981,6 +1036,12 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   else if (p.k_slot_scales)
     hipLaunchKernelGGL((pa_decode_kernel<kSlotScalePagesPerStage, kRingDepth, true, false, PA_LOAD_AUX, false, 1, true>),
                        dim3((unsigned)items), dim3(64), kSlotScalePagesPerStage * kPageBytes, stream, p);
+  else if (p.waves_per_item == 2 && p.cached_loads)
+    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false, 0, false, 1, false, 2>),
+                       dim3((unsigned)items), dim3(128), 0, stream, p);
+  else if (p.waves_per_item == 2)
+    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false, PA_LOAD_AUX, false, 1, true, 2>),
+                       dim3((unsigned)items), dim3(128), 2 * kPagesPerStage * kPageBytes, stream, p);
   else if (p.cached_loads)
     hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false, 0>), dim3((unsigned)items),
                        dim3(64), 0, stream, p);
