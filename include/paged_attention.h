@@ -25,7 +25,10 @@
  * library (one buffer per device, grown with hipMalloc outside capture only;
  * see pa_decode_reserve_workspace).  Two calls that run concurrently on one
  * device (different streams or threads) must not both need the split-KV
- * scratch: they would share it.
+ * scratch: they would share it, including the arrival counters at its front
+ * (one per (sequence, kv head), zeroed when the scratch is allocated and left
+ * at zero by every call), which overlapping calls could leave counting wrong
+ * for the calls that follow.
  *
  * Errors: every check runs before any launch.  A failing call returns a
  * negative pa_status, launches nothing, and leaves a message for

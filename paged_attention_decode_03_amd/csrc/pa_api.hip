@@ -67,6 +67,13 @@ struct Plan {
   size_t workspace_bytes;
 };
 
+// The front of the split-KV scratch holds the fused merge's arrival counters
+// (one int per (sequence, kv head), up to kCounterSlots of them): zeroed when
+// the scratch is allocated and left at zero by every call; partials and the
+// longest-first order follow it, so no call writes over the counters.
+constexpr size_t kCounterRegion = 4096;
+constexpr int64_t kCounterSlots = kCounterRegion / sizeof(int32_t);
+
 // Longest-first dispatch (an option): with ragged contexts, work items run
 // about as long as their sequences, and items dispatched last set the end of
 // the call.  A small kernel orders the sequences by length on the device (no
@@ -126,9 +133,10 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t W, int32_t num_cus, in
   const size_t partial_bytes =
       parts > 1 ? (size_t)rows * Hq * parts * (pa::kHeadDim + 2) * sizeof(float) : 0;
   plan->longest_first = longest_first && S >= 2 && S <= kLongestFirstMaxSeqs;
-  plan->order_offset = (partial_bytes + 255) & ~size_t(255);
-  plan->workspace_bytes =
-      plan->longest_first ? plan->order_offset + (size_t)S * sizeof(int32_t) : partial_bytes;
+  plan->order_offset = kCounterRegion + ((partial_bytes + 255) & ~size_t(255));
+  plan->workspace_bytes = plan->longest_first ? plan->order_offset + (size_t)S * sizeof(int32_t)
+                          : partial_bytes     ? kCounterRegion + partial_bytes
+                                              : 0;
   return PA_OK;
 }
 
@@ -179,6 +187,13 @@ int ensure_workspace(int dev, size_t bytes, hipStream_t stream, bool check_captu
   }
   void* p = nullptr;
   if (hipMalloc(&p, grow) != hipSuccess) return fail(PA_ERR_HIP, "hipMalloc(%zu) for scratch failed", grow);
+  // the arrival counters start at zero (outside capture: allocation never
+  // happens while `stream` captures)
+  if (hipMemsetAsync(p, 0, kCounterRegion, stream) != hipSuccess ||
+      (stream == nullptr && hipStreamSynchronize(nullptr) != hipSuccess)) {
+    hipFree(p);
+    return fail(PA_ERR_HIP, "clearing the scratch's counters failed");
+  }
   ws.ptr = p;
   ws.bytes = grow;
   *out = p;
@@ -381,6 +396,13 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   // split (measured on MI355X, 512 items: 40/8 ctx 4096 x 64 sequences 95.7 ->
   // 88.3 us, 20/4 ctx 4096 x 128 96.0 -> 87.8 us, ctx 1024 and 2048 within 1%;
   // at 3 to 4 items per CU, and with split contexts, it measured 3-10% slower)
+  // the last item of a split (sequence, kv head) merges its partitions where
+  // they are few (one query per sequence): no merge kernel and no kernel
+  // boundary before it
+  p.fused_merge = (!mq && plan.num_parts > 1 && plan.num_parts <= pa::kFusedMergeMaxParts &&
+                   (int64_t)G * plan.num_parts <= pa::kFusedMergeMaxLoads && (int64_t)S * Hkv <= kCounterSlots)
+                      ? 1 : 0;
+  p.unit_count = nullptr;
   const int64_t cus = device_cus(dev);
   p.waves_per_item = (!mq && !slot_scales && !var.token_rows && plan.num_parts == 1 &&
                       units > cus && units <= 2 * cus)
@@ -389,9 +411,10 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
     void* ws = nullptr;
     rc = ensure_workspace(dev, plan.workspace_bytes, stream, true, &ws);
     if (rc) return rc;
+    p.unit_count = (int32_t*)ws;
     if (plan.num_parts > 1) {
-      p.part_acc = (float*)ws;
-      p.part_ml = (float*)ws + (size_t)p.num_q_rows * Hq * plan.num_parts * pa::kHeadDim;
+      p.part_acc = (float*)((char*)ws + kCounterRegion);
+      p.part_ml = p.part_acc + (size_t)p.num_q_rows * Hq * plan.num_parts * pa::kHeadDim;
     }
     if (plan.longest_first) p.seq_order = (int32_t*)((char*)ws + plan.order_offset);
   }

@@ -71,7 +71,19 @@ struct DecodeParams {
   // waves per work item: 1, or 2 (the page-layout decode with one query per
   // sequence and per-tensor scales only)
   int32_t waves_per_item;
+  // split contexts with few partitions (one query per sequence): the last
+  // item of each (sequence, kv head) to finish merges the partitions itself
+  // (no merge kernel).  unit_count: one arrival counter per (sequence, kv
+  // head), zero before and after every call
+  int32_t fused_merge;
+  int32_t* unit_count;
 };
+// partitions a fused merge folds: measured on MI355X, 32/8 heads x 24
+// sequences (4 partitions): ctx 1024 15.2 -> 14.7 us, ctx 4096 34.7 -> 34.0 us;
+// at 8 partitions (40/8 x 16 sequences) the last item's loads made it slower
+// than the merge kernel (ctx 1024 12.9 -> 13.9 us)
+constexpr int kFusedMergeMaxParts = 4;
+constexpr int kFusedMergeMaxLoads = 40;   // group size x partitions
 
 // Enqueue the decode (and, when num_parts > 1, the merge) on `stream`.
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);

@@ -825,6 +825,11 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64 * WPI) __attribute__(
     }
   }
 
+  // fused merge: the partials through buffer descriptors (agent-coherent
+  // accesses need the sc1 bit, which the buffer forms take)
+  constexpr int kAuxSc1 = 16;
+  const auto part_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.part_acc, (short)0, 0x7FFFFFF0, kRsrcWord3);
+  const auto ml_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.part_ml, (short)0, 0x7FFFFFF0, kRsrcWord3);
 #pragma unroll
   for (int u = 0; u < NT; ++u) {
     if (!hvalid[u]) continue;
@@ -838,12 +843,89 @@ __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64 * WPI) __attribute__(
         const f32x4 a = acc[u][jd];
         *(uint2*)(o + jd * 16) = make_uint2(pack_bf16x2(a[0] * inv, a[1] * inv), pack_bf16x2(a[2] * inv, a[3] * inv));
       }
+    } else if (!MQ && p.fused_merge) {
+      // agent-coherent stores (sc1: written through the XCD's L2), so the
+      // item that merges, on any XCD, reads them with agent-coherent loads
+      const size_t prow = ((size_t)qrow[u] * p.num_heads + h) * p.num_parts + part;
+#pragma unroll
+      for (int jd = 0; jd < 8; ++jd)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[u][jd] * vnorm_inv), part_rsrc,
+                                               (int)((prow * kHeadDim + rq * 4 + jd * 16) * 4), 0, kAuxSc1);
+      if (rq == 0)
+        __builtin_amdgcn_raw_buffer_store_b64(
+            __builtin_bit_cast(__attribute__((__vector_size__(8))) uint32_t, make_float2(m_run[u], lsum)),
+            ml_rsrc, (int)(prow * 8), 0, kAuxSc1);
     } else {
       const size_t prow = ((size_t)qrow[u] * p.num_heads + h) * p.num_parts + part;
       float* a = p.part_acc + prow * kHeadDim + rq * 4;
 #pragma unroll
       for (int jd = 0; jd < 8; ++jd) *(f32x4*)(a + jd * 16) = acc[u][jd] * vnorm_inv;
       if (rq == 0) *(float2*)(p.part_ml + prow * 2) = make_float2(m_run[u], lsum);
+    }
+  }
+  if constexpr (!MQ) {
+    if (!direct && p.fused_merge) {
+      // Arrival: once this item's partial stores are performed, count it; the
+      // unit's last item (count nused - 1 before its own) merges, and leaves
+      // the counter at zero for the next call.
+      // (the signal fences keep the compiler from moving memory accesses
+      // across the wait and the count)
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0);
+      const int unit = s * p.num_kv_heads + kvh;
+      int before = 0;
+      if (lane == 0) before = __hip_atomic_fetch_add(p.unit_count + unit, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      before = __builtin_amdgcn_readlane(before, 0);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      if (before != nused - 1) return;
+      if (lane == 0) __hip_atomic_store(p.unit_count + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // The unit's G heads x nused partitions (nused <= 4, G * nused <= 40): lane (hs, d4)
+      // takes dims 4 d4 .. 4 d4 + 3 of heads 2 k + hs, three head pairs (all
+      // their partitions' loads in flight together) at a time.
+      const int hs = lane >> 5, d4 = lane & 31;
+      const float vsc = SS ? 1.0f : scalar_load(p.v_scale);
+      const size_t row0 = (size_t)s * p.num_heads + (size_t)kvh * p.group;  // (s, first head of the group)
+      constexpr int kPairs = 3;
+      for (int k0 = 0; 2 * k0 < p.group; k0 += kPairs) {
+        f32x4 av[kPairs][kFusedMergeMaxParts];
+        float2 mv[kPairs][kFusedMergeMaxParts];
+#pragma unroll
+        for (int kk = 0; kk < kPairs; ++kk) {
+          const int g2 = 2 * (k0 + kk) + hs;
+#pragma unroll
+          for (int j = 0; j < kFusedMergeMaxParts; ++j) {
+            av[kk][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            mv[kk][j] = make_float2(-INFINITY, 0.f);
+            if (g2 < p.group && j < nused) {
+              const size_t pr = (row0 + g2) * p.num_parts + j;
+              av[kk][j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        part_rsrc, (int)((pr * kHeadDim + 4 * d4) * 4), 0, kAuxSc1));
+              mv[kk][j] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(ml_rsrc, (int)(pr * 8), 0,
+                                                                                            kAuxSc1));
+            }
+          }
+        }
+#pragma unroll
+        for (int kk = 0; kk < kPairs; ++kk) {
+          const int g2 = 2 * (k0 + kk) + hs;
+          float M = -INFINITY;
+#pragma unroll
+          for (int j = 0; j < kFusedMergeMaxParts; ++j) M = fmaxf(M, mv[kk][j].x);
+          f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
+          float den = 0.f;
+#pragma unroll
+          for (int j = 0; j < kFusedMergeMaxParts; ++j) {
+            const float w = mv[kk][j].x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mv[kk][j].x - M);
+            num += av[kk][j] * w;
+            den += mv[kk][j].y * w;
+          }
+          if (g2 < p.group) {
+            const float inv = den > 0.0f ? vsc / den : 0.0f;
+            *(uint2*)(p.out + (row0 + g2) * kHeadDim + 4 * d4) =
+                make_uint2(pack_bf16x2(num[0] * inv, num[1] * inv), pack_bf16x2(num[2] * inv, num[3] * inv));
+          }
+        }
+      }
     }
   }
 }
@@ -1051,7 +1133,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false, PA_LOAD_AUX, false, 1, true>),
                        dim3((unsigned)items), dim3(64), kPagesPerStage * kPageBytes, stream, p);
   const size_t rows = p.multi_query ? (size_t)p.num_q_rows : (size_t)p.num_seqs;
-  if (p.num_parts > 1 && rows > 0)
+  if (p.num_parts > 1 && rows > 0 && !p.fused_merge)
     hipLaunchKernelGGL(pa_merge_kernel, dim3((unsigned)(rows * p.num_heads)), dim3(kMergeThreads), 0, stream,
                        p);
   return hipGetLastError();

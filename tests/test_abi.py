@@ -53,7 +53,7 @@ def test_plan_large_batch_is_unsplit(lib):
 def test_plan_small_batch_splits_long_context(lib):
     rc, P, n, ws = plan(lib, 1, 40, 8, 2048)        # one sequence of 32768 tokens
     assert rc == 0 and P * n >= 2048 and (P, n) == (128, 16)   # 1024 items: 4 per CU
-    assert ws == 1 * 40 * P * 130 * 4
+    assert ws == 4096 + 1 * 40 * P * 130 * 4   # arrival counters, then the partials
     rc, P, n, ws = plan(lib, 1, 40, 8, 256)         # one sequence of 4096 tokens
     assert rc == 0 and (P, n) == (32, 8)            # never below 8 blocks per partition
 

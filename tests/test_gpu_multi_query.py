@@ -95,7 +95,9 @@ def test_small_layouts(hq, hkv, lens, qlens):
 
 def test_one_query_per_sequence_equals_decode_bitwise():
     """With one query per sequence the multi-token entry point computes what
-    decode computes, in the same order: the outputs are bit-identical."""
+    decode computes, in the same order: the outputs are bit-identical.  (The
+    shape splits into 16 partitions, so both merge with the merge kernel; the
+    decode merges up to 4 partitions in its own last work item instead.)"""
     lens = [1, 15, 16, 17, 100, 1000, 4000, 333]
     case = workloads.make_multi_case(40, 8, lens, [1] * len(lens), seed=21)
     dec = workloads.make_case(40, 8, lens, seed=21)

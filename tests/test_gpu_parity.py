@@ -379,6 +379,54 @@ def test_two_waves_per_item():
         assert torch.equal(lpt.cpu().view(torch.int16), a.view(torch.int16))
 
 
+def test_fused_merge_counters_stay_consistent():
+    """Split contexts with few partitions (here 4 at 32/8 heads and 2 at 16/1)
+    are merged by the last work item of each (sequence, kv head) to finish,
+    counted by arrival counters in the scratch that every call leaves at zero;
+    more partitions (8 at 40/8) go to the merge kernel.  Calls of these shapes
+    in turn, a repeat (bit for bit), and a captured graph replayed three times
+    with eager calls of the other shapes in between must all meet the bound."""
+    import paged_attention_decode_03_amd as pa
+    lens_a = [0, 1, 15, 16, 17, 127, 128, 129, 1024, 1023, 513, 700, 64, 65, 900, 1000] + \
+             [1024 - 37 * i for i in range(8)]
+    a = workloads.make_case(32, 8, lens_a, seed=61, max_blocks=64)
+    b = workloads.make_case(40, 8, lens_a[:16], seed=62, max_blocks=64)
+    d = workloads.make_case(16, 1, [2048, 0, 1, 1025, 1024, 2047] * 50, seed=64, max_blocks=128)
+    assert pa.pa_decode_plan(24, 32, 8, 64, 256)[:2] == (4, 16)
+    assert pa.pa_decode_plan(16, 40, 8, 64, 256)[:2] == (8, 8)
+    assert pa.pa_decode_plan(300, 16, 1, 128, 256)[:2] == (2, 64)
+    first = run_gpu(a).cpu()
+    log("fused merge: shapes A (4 partitions), B (8: merge kernel), D (2), A")
+    compare(first, run_oracle(a), "fused merge A")
+    compare(run_gpu(b).cpu(), run_oracle(b), "merge kernel B")
+    compare(run_gpu(d).cpu(), run_oracle(d), "fused merge D")
+    big = workloads.make_case(40, 8, [300] * 64, seed=63)   # one partition: no counters
+    run_gpu(big)
+    again = run_gpu(a).cpu()
+    assert torch.equal(again.view(torch.int16), first.view(torch.int16))
+    c = a.to("cuda")
+    ks = torch.tensor([c.k_scale], device="cuda")
+    vs = torch.tensor([c.v_scale], device="cuda")
+    out = torch.empty_like(c.q)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(2):
+                pa.paged_decode_attention(c.q, c.k_cache, c.v_cache, c.block_tables, c.seq_lens,
+                                          c.scale, ks, vs, out=out)
+    for r in range(3):
+        out.fill_(7.0)
+        run_gpu(b)                      # eager work of other shapes between replays
+        run_gpu(d)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        log(f"fused merge: graph replay {r}")
+        assert torch.equal(out.cpu().view(torch.int16), first.view(torch.int16)), f"replay {r}"
+
+
 def test_longest_first_order_covers_every_sequence():
     """Longest-first dispatch (an order computed on the device) must compute
     every sequence exactly once with the same arithmetic: the unified call with
