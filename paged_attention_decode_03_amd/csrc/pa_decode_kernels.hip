@@ -87,6 +87,13 @@ constexpr int kTwoTilePagesPerStage = 2;
 // Three tiles per item: a third set of accumulators; one page per stage keeps
 // it within 256 VGPRs (2 waves per SIMD).
 constexpr int kThreeTilePagesPerStage = 1;
+// Two waves per item run where a launch holds two items per CU, i.e. one wave
+// per SIMD: their register budget is a whole SIMD's, spent on a ring of three
+// stages (two in flight while one is computed).  Measured on MI355X, 40/8 x 64
+// sequences: ctx 1024 26.5 -> 25.2 us, 2048 47.2 -> 43.3 us, 4096 91.8 -> 88.1
+// us; a ring of four was slower than three.
+constexpr int kTwoWaveRingDepth = 3;
+constexpr int kTwoWaveWavesPerEU = 1;
 
 // Word 3 of a raw buffer resource (no format conversion, no swizzle).
 constexpr int kRsrcWord3 = 0x00020000;
@@ -282,7 +289,8 @@ struct Stage {
 // work items, no second kernel.
 template <int PPS, int NB, bool SS, bool MQ, int AUX = PA_LOAD_AUX, bool TR = false, int NT = 1,
           bool VL = false, int WPI = 1>
-__global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64 * WPI) __attribute__((amdgpu_waves_per_eu(PA_WAVES_PER_EU))) void pa_decode_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64 * WPI)
+__attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_EU))) void pa_decode_kernel(const DecodeParams p) {
   const int lane = threadIdx.x & 63;
   // Token rows: a workgroup holds kv_group kv heads of one sequence (one wave
   // each); on one CU at the same time, they walk the sequence's blocks at
@@ -1131,10 +1139,10 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((pa_decode_kernel<kSlotScalePagesPerStage, kRingDepth, true, false, PA_LOAD_AUX, false, 1, true>),
                        dim3((unsigned)items), dim3(64), kSlotScalePagesPerStage * kPageBytes, stream, p);
   else if (p.waves_per_item == 2 && p.cached_loads)
-    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false, 0, false, 1, false, 2>),
+    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kTwoWaveRingDepth, false, false, 0, false, 1, false, 2>),
                        dim3((unsigned)items), dim3(128), 0, stream, p);
   else if (p.waves_per_item == 2)
-    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false, PA_LOAD_AUX, false, 1, true, 2>),
+    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kTwoWaveRingDepth, false, false, PA_LOAD_AUX, false, 1, true, 2>),
                        dim3((unsigned)items), dim3(128), 2 * kPagesPerStage * kPageBytes, stream, p);
   else if (p.cached_loads)
     hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false, 0>), dim3((unsigned)items),
