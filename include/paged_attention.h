@@ -23,7 +23,8 @@
  * return; they never read device memory on the host and never synchronise, so
  * they may be captured into a HIP graph.  Split-KV scratch is owned by the
  * library (one buffer per device, grown with hipMalloc outside capture only;
- * see pa_decode_reserve_workspace).  Two calls that run concurrently on one
+ * see pa_decode_reserve_workspace); the call that grows it also waits for
+ * `stream` once (the new buffer's counters are cleared before any use).  Two calls that run concurrently on one
  * device (different streams or threads) must not both need the split-KV
  * scratch: they would share it, including the arrival counters at its front
  * (one per (sequence, kv head), zeroed when the scratch is allocated and left

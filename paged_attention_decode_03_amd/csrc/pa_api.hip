@@ -187,10 +187,10 @@ int ensure_workspace(int dev, size_t bytes, hipStream_t stream, bool check_captu
   }
   void* p = nullptr;
   if (hipMalloc(&p, grow) != hipSuccess) return fail(PA_ERR_HIP, "hipMalloc(%zu) for scratch failed", grow);
-  // the arrival counters start at zero (outside capture: allocation never
-  // happens while `stream` captures)
-  if (hipMemsetAsync(p, 0, kCounterRegion, stream) != hipSuccess ||
-      (stream == nullptr && hipStreamSynchronize(nullptr) != hipSuccess)) {
+  // the arrival counters start at zero, for calls on any stream: cleared and
+  // waited for here (outside capture: allocation never happens while `stream`
+  // captures)
+  if (hipMemsetAsync(p, 0, kCounterRegion, stream) != hipSuccess || hipStreamSynchronize(stream) != hipSuccess) {
     hipFree(p);
     return fail(PA_ERR_HIP, "clearing the scratch's counters failed");
   }
