@@ -57,7 +57,7 @@ constexpr int kSplitItemsPerCU = PA_SPLIT_ITEMS_PER_CU;  // what a split aims fo
 constexpr size_t kCachedLoadMaxBytes = (size_t)PA_CACHED_LOAD_MAX_MIB << 20;
 constexpr int kDefaultCUs = 256;      // MI355X
 constexpr int kMinPagesPerPart = 8;   // shorter partitions cost more in start-up and merge than they gain
-constexpr int kStagePages = 4;        // the decode kernel loads 4 blocks per pipeline stage
+constexpr int kStagePages = 4;        // partitions are whole stages of every decode kernel (2 or 4 blocks)
 
 struct Plan {
   int32_t num_parts;

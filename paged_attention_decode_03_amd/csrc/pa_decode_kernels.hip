@@ -62,7 +62,7 @@ typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 // read the same pages: their loads use the default policy instead, so the
 // pages stay in L2 for the other items.
 #ifndef PA_PAGES_PER_STAGE
-#define PA_PAGES_PER_STAGE 4
+#define PA_PAGES_PER_STAGE 2
 #endif
 #ifndef PA_RING_DEPTH
 #define PA_RING_DEPTH 2
@@ -94,6 +94,14 @@ constexpr int kThreeTilePagesPerStage = 1;
 // us; a ring of four was slower than three.
 constexpr int kTwoWaveRingDepth = 3;
 constexpr int kTwoWaveWavesPerEU = 1;
+// Stages of two pages (one wave per item): on small batches an item's pages
+// land nearly at once, and smaller stages leave less compute after the last
+// one (measured on MI355X against four pages: 40/8 ctx 1024 x 16 12.5 -> 11.4
+// us, 32/8 ctx 1024 x 24 14.6 -> 13.4 us, 40/8 ctx 4096 x 16 26.7 -> 25.3 us;
+// the target, ragged, token-row and several-queries rows the same or up to 3%
+// faster).  Two waves per item keep four (with two: ctx 4096 x 64 88.7 -> 92.9
+// us).
+constexpr int kTwoWavePagesPerStage = 4;
 
 // Word 3 of a raw buffer resource (no format conversion, no swizzle).
 constexpr int kRsrcWord3 = 0x00020000;
@@ -1139,11 +1147,11 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((pa_decode_kernel<kSlotScalePagesPerStage, kRingDepth, true, false, PA_LOAD_AUX, false, 1, true>),
                        dim3((unsigned)items), dim3(64), kSlotScalePagesPerStage * kPageBytes, stream, p);
   else if (p.waves_per_item == 2 && p.cached_loads)
-    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kTwoWaveRingDepth, false, false, 0, false, 1, false, 2>),
+    hipLaunchKernelGGL((pa_decode_kernel<kTwoWavePagesPerStage, kTwoWaveRingDepth, false, false, 0, false, 1, false, 2>),
                        dim3((unsigned)items), dim3(128), 0, stream, p);
   else if (p.waves_per_item == 2)
-    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kTwoWaveRingDepth, false, false, PA_LOAD_AUX, false, 1, true, 2>),
-                       dim3((unsigned)items), dim3(128), 2 * kPagesPerStage * kPageBytes, stream, p);
+    hipLaunchKernelGGL((pa_decode_kernel<kTwoWavePagesPerStage, kTwoWaveRingDepth, false, false, PA_LOAD_AUX, false, 1, true, 2>),
+                       dim3((unsigned)items), dim3(128), 2 * kTwoWavePagesPerStage * kPageBytes, stream, p);
   else if (p.cached_loads)
     hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false, 0>), dim3((unsigned)items),
                        dim3(64), 0, stream, p);
