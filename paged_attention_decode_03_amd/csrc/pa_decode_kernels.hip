@@ -88,20 +88,20 @@ constexpr int kTwoTilePagesPerStage = 2;
 // it within 256 VGPRs (2 waves per SIMD).
 constexpr int kThreeTilePagesPerStage = 1;
 // Two waves per item run where a launch holds two items per CU, i.e. one wave
-// per SIMD: their register budget is a whole SIMD's, spent on a ring of three
-// stages (two in flight while one is computed).  Measured on MI355X, 40/8 x 64
-// sequences: ctx 1024 26.5 -> 25.2 us, 2048 47.2 -> 43.3 us, 4096 91.8 -> 88.1
-// us; a ring of four was slower than three.
-constexpr int kTwoWaveRingDepth = 3;
+// per SIMD: their register budget is a whole SIMD's, spent on a ring of four
+// two-page stages (three in flight while one is computed).  Measured on
+// MI355X, 40/8 x 64 sequences against a ring of two four-page stages: ctx 1024
+// 26.5 -> 24.4 us, 2048 47.2 -> 42.3 us, 4096 91.8 -> 87.9 us (three four-page
+// stages: 25.7, 43.2, 88.8 us; four of them: slower).
+constexpr int kTwoWaveRingDepth = 4;
 constexpr int kTwoWaveWavesPerEU = 1;
 // Stages of two pages (one wave per item): on small batches an item's pages
 // land nearly at once, and smaller stages leave less compute after the last
 // one (measured on MI355X against four pages: 40/8 ctx 1024 x 16 12.5 -> 11.4
 // us, 32/8 ctx 1024 x 24 14.6 -> 13.4 us, 40/8 ctx 4096 x 16 26.7 -> 25.3 us;
 // the target, ragged, token-row and several-queries rows the same or up to 3%
-// faster).  Two waves per item keep four (with two: ctx 4096 x 64 88.7 -> 92.9
-// us).
-constexpr int kTwoWavePagesPerStage = 4;
+// faster).  Two waves per item use two-page stages too, in a deeper ring.
+constexpr int kTwoWavePagesPerStage = 2;
 
 // Word 3 of a raw buffer resource (no format conversion, no swizzle).
 constexpr int kRsrcWord3 = 0x00020000;
