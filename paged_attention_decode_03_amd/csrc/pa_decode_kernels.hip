@@ -61,6 +61,12 @@ typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
 // When a sequence's query tiles are spread over several items, those items
 // read the same pages: their loads use the default policy instead, so the
 // pages stay in L2 for the other items.
+// Stages of two pages (one wave per item): on small batches an item's pages
+// land nearly at once, and smaller stages leave less compute after the last
+// one (measured on MI355X against four pages: 40/8 ctx 1024 x 16 12.5 -> 11.4
+// us, 32/8 ctx 1024 x 24 14.6 -> 13.4 us, 40/8 ctx 4096 x 16 26.7 -> 25.3 us;
+// the target, ragged, token-row and several-queries rows the same or up to 3%
+// faster).  Two waves per item use two-page stages too, in a deeper ring.
 #ifndef PA_PAGES_PER_STAGE
 #define PA_PAGES_PER_STAGE 2
 #endif
@@ -95,12 +101,6 @@ constexpr int kThreeTilePagesPerStage = 1;
 // stages: 25.7, 43.2, 88.8 us; four of them: slower).
 constexpr int kTwoWaveRingDepth = 4;
 constexpr int kTwoWaveWavesPerEU = 1;
-// Stages of two pages (one wave per item): on small batches an item's pages
-// land nearly at once, and smaller stages leave less compute after the last
-// one (measured on MI355X against four pages: 40/8 ctx 1024 x 16 12.5 -> 11.4
-// us, 32/8 ctx 1024 x 24 14.6 -> 13.4 us, 40/8 ctx 4096 x 16 26.7 -> 25.3 us;
-// the target, ragged, token-row and several-queries rows the same or up to 3%
-// faster).  Two waves per item use two-page stages too, in a deeper ring.
 constexpr int kTwoWavePagesPerStage = 2;
 
 // Word 3 of a raw buffer resource (no format conversion, no swizzle).
