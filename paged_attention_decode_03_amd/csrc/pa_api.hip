@@ -57,6 +57,7 @@ constexpr int kSplitItemsPerCU = PA_SPLIT_ITEMS_PER_CU;  // what a split aims fo
 constexpr size_t kCachedLoadMaxBytes = (size_t)PA_CACHED_LOAD_MAX_MIB << 20;
 constexpr int kDefaultCUs = 256;      // MI355X
 constexpr int kMinPagesPerPart = 8;   // shorter partitions cost more in start-up and merge than they gain
+constexpr int kMinPagesPerPartFewItems = 4;  // ... unless the items are at most one per CU
 constexpr int kStagePages = 4;        // partitions are whole stages of every decode kernel (2 or 4 blocks)
 
 struct Plan {
@@ -98,8 +99,9 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // 16..64 sequences at ctx 1024..4096 and 1..4 at 4096..32768): a CU streams
 // at most ~25 GB/s, so every CU needs work, and items that divide evenly over
 // the CUs with even partitions beat the same bytes in uneven pieces by 10-25%.
-// Partitions hold at least kMinPagesPerPart blocks, whole pipeline stages,
-// and never more than pa::kMaxPagesPerPart blocks.
+// Partitions hold at least kMinPagesPerPart blocks (kMinPagesPerPartFewItems
+// where that leaves at most one item per CU), whole pipeline stages, and never
+// more than pa::kMaxPagesPerPart blocks.
 int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t W, int32_t num_cus, int32_t ppp_req,
               Plan* plan, int32_t q_tiles = 1, int64_t q_rows = -1, bool longest_first = false) {
   if (S < 0 || Hq <= 0 || Hkv <= 0 || W < 0 || ppp_req < 0)
@@ -120,7 +122,15 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t W, int32_t num_cus, in
     if (parts > Wc) parts = Wc;
     ppp = ceil_div(Wc, parts < 1 ? 1 : parts);
     if (ppp < Wc) {
-      if (ppp < kMinPagesPerPart) ppp = kMinPagesPerPart;
+      if (ppp < kMinPagesPerPart) {
+        ppp = kMinPagesPerPart;
+        // where partitions of the minimum leave at most one item per CU,
+        // halving them pays (two items per CU): measured on MI355X, one
+        // sequence x 4096 at 40/8 heads 9.1 -> 8.4 us, 8/1 x 16 sequences x
+        // 2048 9.1 -> 8.4 us; with more items it measured slower (4 sequences
+        // x 4096: 11.7 -> 13.3 us)
+        if (items * ceil_div(Wc, ppp) <= cus) ppp = kMinPagesPerPartFewItems;
+      }
       ppp = ceil_div(ppp, kStagePages) * kStagePages;
       if (ppp > Wc) ppp = Wc;
     }

@@ -55,7 +55,12 @@ def test_plan_small_batch_splits_long_context(lib):
     assert rc == 0 and P * n >= 2048 and (P, n) == (128, 16)   # 1024 items: 4 per CU
     assert ws == 4096 + 1 * 40 * P * 130 * 4   # arrival counters, then the partials
     rc, P, n, ws = plan(lib, 1, 40, 8, 256)         # one sequence of 4096 tokens
-    assert rc == 0 and (P, n) == (32, 8)            # never below 8 blocks per partition
+    # 8-block partitions would leave one item per CU: 4-block ones, two per CU
+    assert rc == 0 and (P, n) == (64, 4)
+    rc, P, n, ws = plan(lib, 4, 40, 8, 256)         # four sequences of 4096 tokens
+    assert rc == 0 and (P, n) == (32, 8)            # 1024 items: not below 8 blocks
+    rc, P, n, ws = plan(lib, 1, 40, 8, 512)         # one sequence of 8192 tokens
+    assert rc == 0 and (P, n) == (64, 8)
 
 
 def test_plan_split_is_a_power_of_two_within_four_items_per_cu(lib):
@@ -76,7 +81,10 @@ def test_plan_partitions_are_whole_stages(lib):
     for S, W in [(3, 256), (24, 256), (5, 100), (2, 37)]:
         rc, P, n, ws = plan(lib, S, 40, 8, W)
         assert rc == 0 and P * n >= W
-        assert P == 1 or (n % 4 == 0 and n >= 8)
+        # whole 4-block stages of at least 8 blocks, or of 4 where 8-block
+        # partitions would leave at most one item per CU (256 CUs)
+        few = S * 8 * -(-W // 8) <= 256
+        assert P == 1 or (n % 4 == 0 and (n >= 8 or (few and n == 4)))
 
 
 def test_plan_caps_partition_length(lib):
