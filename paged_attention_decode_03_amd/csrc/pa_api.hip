@@ -585,6 +585,11 @@ int paged_kv_cache_write(const void* key, const void* value, int64_t key_token_s
                 "token strides (%lld, %lld) must be even and at least num_kv_heads * 128 = %lld",
                 (long long)key_token_stride, (long long)value_token_stride, (long long)row);
   if (num_blocks == 0) return fail(PA_ERR_SHAPE, "num_blocks must be positive");
+  // one workgroup per (16 tokens, kv head): keep the grid within 2^31 - 1
+  const int64_t cw_items = ((int64_t)num_tokens + pa::kBlockTokens - 1) / pa::kBlockTokens * num_kv_heads;
+  if (cw_items > INT32_MAX)
+    return fail(PA_ERR_UNSUPPORTED, "launch too large: %lld work items (16 tokens x kv head)",
+                (long long)cw_items);
   if (((uintptr_t)key & 3) || ((uintptr_t)value & 3) || ((uintptr_t)k_cache & 1) ||
       ((uintptr_t)slot_mapping & 7))
     return fail(PA_ERR_SHAPE, "misaligned pointer (key, value: 4 B; k_cache: 2 B; slot_mapping: 8 B)");

@@ -101,7 +101,11 @@ __device__ __forceinline__ uint64_t nan_lanes(float a, float b, float c, float d
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-constexpr int kWavesPerBlock = 4;
+// One wave per workgroup: the waves of a launch spread over every CU (measured
+// on MI355X, graph replay: 256 tokens x 8 kv heads at random slots 7.1 ->
+// 6.6 us, 32768 tokens x 8 kv heads in whole blocks 38.3 -> 35.0 us, against
+// four waves per workgroup; two: 7.4 / 35.5 us).
+constexpr int kWavesPerBlock = 1;
 constexpr int kGroup = kBlockTokens;  // tokens per wave
 
 // One token, two dims per lane (any slot pattern); kw / vw hold the lane's two

@@ -148,6 +148,12 @@ def test_cache_write_rejects_bad_arguments(lib, kw, code):
     assert lib.pa_last_error().decode() != ""
 
 
+def test_cache_write_rejects_a_grid_past_its_limit(lib):
+    # 2^31 - 1 tokens x 32 kv heads: 2^32 groups of 16 tokens x kv head
+    assert cw(lib, T=2**31 - 1, Hkv=32, ks_=4096, vs_=4096) == -3
+    assert "too large" in lib.pa_last_error().decode()
+
+
 def test_cache_write_empty_is_a_noop(lib):
     assert cw(lib, T=0, key=0, value=0, kc=0, vc=0, sm=0) == 0
 
