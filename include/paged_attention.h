@@ -283,7 +283,8 @@ int pa_decode_reserve_workspace(size_t bytes);
  *   num_tokens        0 is a no-op
  *   k_scale, v_scale  fp32 [1], device
  * Two tokens with the same slot race (one of them wins).  Asynchronous like
- * paged_decode_attention; errors as there.
+ * paged_decode_attention; errors as there, and PA_ERR_UNSUPPORTED when
+ * ceil(num_tokens / 16) * num_kv_heads exceeds 2^31 - 1 (one workgroup each).
  */
 int paged_kv_cache_write(const void* key, const void* value, int64_t key_token_stride,
                          int64_t value_token_stride, void* k_cache, void* v_cache,
