@@ -54,7 +54,7 @@ def _load():
                                      f32, f32, f32, P, i32]
     lib.pa_oracle_decode.restype = i32
     lib.pa_oracle_decode_partitioned.argtypes = [P, P, P, P, P, i32, i32, i32, i32,
-                                                 f32, f32, f32, i32, P]
+                                                 f32, f32, f32, i32, P, P]
     lib.pa_oracle_decode_partitioned.restype = i32
     lib.pa_oracle_decode_slot_scales.argtypes = [P, P, P, P, P, i32, i32, i32, i32, f32, P, P, P, i32]
     lib.pa_oracle_decode_slot_scales.restype = i32
@@ -279,18 +279,24 @@ def attend_ext(q_bits, cu_seqlens_q, k_cache, v_cache, block_tables, seq_lens, s
 
 
 def decode_partitioned(q_bits, k_cache, v_cache, block_tables, seq_lens, scale,
-                       k_scale, v_scale, tokens_per_part: int) -> np.ndarray:
-    """The same quantity via per-partition partials and a log-sum-exp merge."""
+                       k_scale, v_scale, tokens_per_part: int, return_empty: bool = False):
+    """The same quantity via per-partition partials and a log-sum-exp merge.
+
+    Partitions of `tokens_per_part` tokens cut the whole table row (16 * W
+    tokens), so contexts shorter than the row leave empty partitions, which
+    the merge skips.  Returns float64 [S, Hq, 128], and with return_empty also
+    the number of empty partitions formed over all (sequence, head) rows."""
     q_bits, k_cache, v_cache, bt, sl, S, Hq, Hkv, W = _check(
         q_bits, k_cache, v_cache, block_tables, seq_lens)
     out = np.zeros((S, Hq, 128), dtype=np.float64)
+    empty = ctypes.c_int64(0)
     rc = _load().pa_oracle_decode_partitioned(
         q_bits.ctypes.data, k_cache.ctypes.data, v_cache.ctypes.data, bt.ctypes.data,
         sl.ctypes.data, S, Hq, Hkv, W, float(scale), float(k_scale), float(v_scale),
-        int(tokens_per_part), out.ctypes.data)
+        int(tokens_per_part), out.ctypes.data, ctypes.byref(empty))
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (code {rc})")
-    return out
+    return (out, int(empty.value)) if return_empty else out
 
 
 def fp8_encode(values) -> np.ndarray:

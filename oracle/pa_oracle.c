@@ -343,41 +343,56 @@ int pa_oracle_decode_slot_scales(const uint16_t* q_bits, const uint8_t* k_cache,
 }
 
 /*
- * Same quantity, computed as independent partitions of `tokens_per_part`
- * consecutive tokens followed by a log-sum-exp merge:
- *   partition p keeps  m_p = max z,  l_p = sum exp(z - m_p),
- *                      a_p[d] = sum exp(z - m_p) V[d];
- *   merge:  M = max_p m_p,  w_p = exp(m_p - M)  (partitions with no tokens
- *           are skipped),  out = sum_p w_p a_p / sum_p w_p l_p.
+ * Same quantity, computed as independent partitions followed by a log-sum-exp
+ * merge.  The partitions cut the block-table row, as a launch plan made from
+ * shapes alone must (it cannot see seq_lens): partition p covers tokens
+ * p * tokens_per_part .. (p + 1) * tokens_per_part - 1 of the 16 * W a row can
+ * address, so a context shorter than the row leaves the trailing partitions
+ * without a token.
+ *   partition p with tokens: m_p = max z,  l_p = sum exp(z - m_p),
+ *                            a_p[d] = sum exp(z - m_p) V[d];
+ *   partition p without tokens: m_p = -inf, l_p = 0, a_p = 0 (empty);
+ *   merge:  M = max over the non-empty partitions of m_p,  w_p = exp(m_p - M),
+ *           out = sum_p w_p a_p / sum_p w_p l_p, over the non-empty partitions
+ *           only (an empty one would need exp(-inf - M), and -inf - (-inf) where
+ *           every partition is empty; a context of no tokens gives zeros).
+ * empty_parts (may be NULL) receives the number of empty partitions formed
+ * over all (sequence, head) rows.
  */
 int pa_oracle_decode_partitioned(const uint16_t* q_bits, const uint8_t* k_cache,
                                  const uint8_t* v_cache, const int32_t* block_tables,
                                  const int32_t* seq_lens, int S, int Hq, int Hkv, int W,
                                  float scale, float k_scale, float v_scale,
-                                 int tokens_per_part, double* out) {
+                                 int tokens_per_part, double* out, int64_t* empty_parts) {
   int rc = check_args(S, Hq, Hkv, W, seq_lens);
   if (rc) return rc;
   if (tokens_per_part <= 0) return -4;
   const int G = Hq / Hkv;
   const scales_t sc = {k_scale, v_scale, NULL, NULL};
+  const int nparts = (PA_BLOCK * W + tokens_per_part - 1) / tokens_per_part;
+  int64_t empty = 0;
   for (int s = 0; s < S; ++s) {
     for (int h = 0; h < Hq; ++h) {
       const int n = seq_lens[s];
       const int k = h / G;
-      const int nparts = (n + tokens_per_part - 1) / tokens_per_part;
       double* o = out + ((int64_t)s * Hq + h) * PA_HEAD_DIM;
       double q[PA_HEAD_DIM], K[PA_HEAD_DIM], V[PA_HEAD_DIM];
       for (int e = 0; e < PA_HEAD_DIM; ++e)
         q[e] = pa_oracle_bf16(q_bits[((int64_t)s * Hq + h) * PA_HEAD_DIM + e]);
       for (int d = 0; d < PA_HEAD_DIM; ++d) o[d] = 0.0;
-      if (n == 0) continue;
-      double* m = (double*)malloc(sizeof(double) * (size_t)nparts);
-      double* l = (double*)malloc(sizeof(double) * (size_t)nparts);
-      double* a = (double*)calloc((size_t)nparts * PA_HEAD_DIM, sizeof(double));
+      double* m = (double*)malloc(sizeof(double) * (size_t)(nparts > 0 ? nparts : 1));
+      double* l = (double*)malloc(sizeof(double) * (size_t)(nparts > 0 ? nparts : 1));
+      double* a = (double*)calloc((size_t)(nparts > 0 ? nparts : 1) * PA_HEAD_DIM, sizeof(double));
       const int32_t* bt_row = block_tables + (int64_t)s * W;
       for (int p = 0; p < nparts; ++p) {
         const int t0 = p * tokens_per_part;
         const int t1 = (t0 + tokens_per_part < n) ? t0 + tokens_per_part : n;
+        m[p] = -INFINITY;
+        l[p] = 0.0;
+        if (t0 >= t1) {
+          ++empty;
+          continue;
+        }
         double zmax = -INFINITY;
         for (int t = t0; t < t1; ++t) {
           load_token(k_cache, v_cache, bt_row, Hkv, k, t, &sc, K, V);
@@ -387,7 +402,6 @@ int pa_oracle_decode_partitioned(const uint16_t* q_bits, const uint8_t* k_cache,
           if (zt > zmax) zmax = zt;
         }
         m[p] = zmax;
-        l[p] = 0.0;
         for (int t = t0; t < t1; ++t) {
           load_token(k_cache, v_cache, bt_row, Hkv, k, t, &sc, K, V);
           double dot = 0.0;
@@ -399,19 +413,22 @@ int pa_oracle_decode_partitioned(const uint16_t* q_bits, const uint8_t* k_cache,
       }
       double M = -INFINITY;
       for (int p = 0; p < nparts; ++p)
-        if (m[p] > M) M = m[p];
+        if (l[p] > 0.0 && m[p] > M) M = m[p];
       double den = 0.0;
       for (int p = 0; p < nparts; ++p) {
+        if (l[p] == 0.0) continue; /* empty partition: skipped */
         const double w = exp(m[p] - M);
         den += w * l[p];
         for (int d = 0; d < PA_HEAD_DIM; ++d) o[d] += w * a[(int64_t)p * PA_HEAD_DIM + d];
       }
-      for (int d = 0; d < PA_HEAD_DIM; ++d) o[d] /= den;
+      if (den > 0.0)
+        for (int d = 0; d < PA_HEAD_DIM; ++d) o[d] /= den;
       free(m);
       free(l);
       free(a);
     }
   }
+  if (empty_parts) *empty_parts = empty;
   return 0;
 }
 

@@ -324,12 +324,34 @@ def test_empty_sequence_gives_zeros_and_overlong_is_rejected(oracle_lib):
 
 @pytest.mark.parametrize("tpp", [16, 48, 64, 1000])
 def test_partition_merge_equals_unsplit(oracle_lib, tpp):
+    """Partitions cut the 64-block table row (1024 tokens), so every context
+    shorter than the row leaves empty partitions; the merge must skip them
+    and still equal the unsplit definition."""
     case = workloads.make_case(10, 2, [1, 15, 16, 17, 100, 1024, 0, 333], 41, max_blocks=64)
     whole = run_oracle(case)
+    split, empty = oracle.decode_partitioned(case.q_bits(), case.k_cache.numpy(),
+                                             case.v_cache.numpy(), case.block_tables.numpy(),
+                                             case.seq_lens.numpy(), case.scale, case.k_scale,
+                                             case.v_scale, tpp, return_empty=True)
+    np.testing.assert_allclose(split, whole, rtol=0, atol=1e-12)
+    # empty partitions per head row: ceil(1024 / tpp) minus those holding a token
+    nparts = -(-1024 // tpp)
+    expect = sum(nparts - (-(-int(n) // tpp)) for n in case.seq_lens) * case.num_heads
+    assert empty == expect
+    if tpp < 1024:
+        assert empty > 0
+
+
+def test_partition_merge_of_an_empty_context_is_zero(oracle_lib):
+    """A row whose every partition is empty gives an all-zero output (no
+    -inf - (-inf) in the merge)."""
+    case = workloads.make_case(4, 1, [0, 0, 5], 42, max_blocks=8)
     split = oracle.decode_partitioned(case.q_bits(), case.k_cache.numpy(), case.v_cache.numpy(),
                                       case.block_tables.numpy(), case.seq_lens.numpy(),
-                                      case.scale, case.k_scale, case.v_scale, tpp)
-    np.testing.assert_allclose(split, whole, rtol=0, atol=1e-12)
+                                      case.scale, case.k_scale, case.v_scale, 16)
+    assert np.isfinite(split).all()
+    assert not split[:2].any()
+    np.testing.assert_allclose(split, run_oracle(case), rtol=0, atol=1e-12)
 
 
 # --------------------------------------------------------------------------
@@ -645,6 +667,100 @@ def test_sink_on_equal_keys_scales_the_mean(oracle_lib):
             frac = n * np.exp(z) / (n * np.exp(z) + np.exp(np.float64(sinks[h])))
             ref = v_rows(case, s, kvh, range(n)).mean(axis=0) * frac
             np.testing.assert_allclose(out[row, h], ref, rtol=1e-12, atol=1e-12)
+
+
+def dense_ext_reference(case, window=0, cap=0.0, slopes=None, sinks=None, cap_after_bias=False):
+    """The options composed on an independent route: K/V gathered by numpy
+    indexing and decoded by torch, logits in torch fp64, then (in this order)
+    the softcap c*tanh(z/c), the ALiBi bias slope*(t - p), the window mask, a
+    sink column with a zero value row, and torch's softmax.
+    cap_after_bias=True applies the bias before the cap instead (a plausible
+    mistake the pins must tell apart)."""
+    G = case.num_heads // case.num_kv_heads
+    q = case.q.double()
+    out = np.zeros((case.q.shape[0], case.num_heads, 128))
+    for s in range(case.num_seqs):
+        L = int(case.seq_lens[s])
+        rows = [(r, p) for r, s2, p in positions(case) if s2 == s]
+        if not rows:
+            continue
+        K, V = gather_dense(case, s)                                  # [L, Hkv, 128]
+        t = torch.arange(L, dtype=torch.float64)
+        for r, p in rows:
+            for h in range(case.num_heads):
+                kvh = h // G
+                z = case.scale * (K[:, kvh] @ q[r, h])                  # [L]
+                bias = (float(slopes[h]) * (t - p)) if slopes is not None else torch.zeros(L, dtype=torch.float64)
+                if cap_after_bias:
+                    z = z + bias
+                    if cap > 0:
+                        z = cap * torch.tanh(z / cap)
+                else:
+                    if cap > 0:
+                        z = cap * torch.tanh(z / cap)
+                    z = z + bias
+                seen = t <= p
+                if window > 0:
+                    seen &= t > p - window
+                zz = z[seen]
+                vv = V[:, kvh][seen]
+                if sinks is not None:
+                    zz = torch.cat([zz, torch.tensor([float(sinks[h])], dtype=torch.float64)])
+                    vv = torch.cat([vv, torch.zeros(1, 128, dtype=torch.float64)])
+                w = torch.softmax(zz, dim=0)
+                out[r, h] = (w @ vv).numpy()
+    return out
+
+
+COMPOSED = {
+    "cap+alibi": dict(cap=2.0),
+    "cap5+alibi": dict(cap=5.0),
+    "cap30+alibi": dict(cap=30.0),
+    "window+sinks": dict(window=9),
+    "all four": dict(window=13, cap=5.0),
+}
+
+
+@pytest.mark.parametrize("combo", list(COMPOSED))
+def test_options_composed_match_a_dense_torch_route(oracle_lib, combo):
+    """Finite softcaps with ALiBi, a window with sinks, and all four options
+    together, against the independent dense route (within 1e-12)."""
+    cfg = COMPOSED[combo]
+    case = ext_case(seed=89, lens=(40, 70, 5, 129, 200), qlens=(3, 8, 5, 1, 4))
+    slopes = np.array([0.5, 0.25, 0.125, 0.0625, 1.0, 2.0, 0.03125, 0.0], np.float32) \
+        if "alibi" in combo or combo == "all four" else None
+    sinks = np.linspace(-2, 4, 8).astype(np.float32) if "sinks" in combo or combo == "all four" else None
+    # scale the queries up so the softcap bites (logits of several units)
+    case.q = (case.q.float() * 4).to(torch.bfloat16)
+    ours = run_ext(case, sliding_window=cfg.get("window", 0), softcap=cfg.get("cap", 0.0),
+                   alibi_slopes=slopes, sinks=sinks)
+    ref = dense_ext_reference(case, window=cfg.get("window", 0), cap=cfg.get("cap", 0.0),
+                              slopes=slopes, sinks=sinks)
+    np.testing.assert_allclose(ours, ref, rtol=0, atol=1e-12)
+
+
+def test_cap_is_applied_before_the_bias(oracle_lib):
+    """Applying the ALiBi bias before the softcap gives a measurably different
+    result on this case, so the order is pinned by the composition test."""
+    case = ext_case(seed=90, lens=(40, 70, 129), qlens=(3, 8, 4))
+    case.q = (case.q.float() * 4).to(torch.bfloat16)
+    slopes = np.array([0.5, 0.25, 0.125, 0.0625, 1.0, 2.0, 0.03125, 0.0], np.float32)
+    ours = run_ext(case, softcap=2.0, alibi_slopes=slopes)
+    right = dense_ext_reference(case, cap=2.0, slopes=slopes)
+    swapped = dense_ext_reference(case, cap=2.0, slopes=slopes, cap_after_bias=True)
+    np.testing.assert_allclose(ours, right, rtol=0, atol=1e-12)
+    assert np.abs(ours - swapped).max() > 1e-6
+
+
+def test_sink_counts_once_with_a_window(oracle_lib):
+    """A window with a sink: the sink enlarges the denominator once per query
+    (not per window position); dropping it changes the result."""
+    case = ext_case(seed=91, lens=(40, 70, 129), qlens=(3, 8, 4))
+    sinks = np.linspace(-1, 3, 8).astype(np.float32)
+    with_sink = run_ext(case, sliding_window=7, sinks=sinks)
+    ref = dense_ext_reference(case, window=7, sinks=sinks)
+    np.testing.assert_allclose(with_sink, ref, rtol=0, atol=1e-12)
+    assert np.abs(with_sink - run_ext(case, sliding_window=7)).max() > 1e-3
 
 
 def test_ext_rejects_bad_options(oracle_lib):
