@@ -21,15 +21,24 @@
  * the caller and not retained after the call returns.  Calls are asynchronous:
  * they validate their arguments on the host, enqueue work on `stream` and
  * return; they never read device memory on the host and never synchronise, so
- * they may be captured into a HIP graph.  Split-KV scratch is owned by the
- * library (one buffer per device, grown with hipMalloc outside capture only;
- * see pa_decode_reserve_workspace); the call that grows it also waits for
- * `stream` once (the new buffer's counters are cleared before any use).  Two calls that run concurrently on one
- * device (different streams or threads) must not both need the split-KV
- * scratch: they would share it, including the arrival counters at its front
- * (one per (sequence, kv head), zeroed when the scratch is allocated and left
- * at zero by every call), which overlapping calls could leave counting wrong
- * for the calls that follow.
+ * they may be captured into a HIP graph (the pull request's Validation ran
+ * its decode under torch's host-sync check, and Details > Cut and precision
+ * makes the kernel choice from shapes so that one captured graph keeps one
+ * kernel).
+ *
+ * Split-KV scratch: calls whose plan splits contexts (pa_workspace_bytes > 0)
+ * keep partial results and arrival counters in a scratch buffer the library
+ * owns, one per (device, stream).  Calls on different streams therefore never
+ * share it and may run concurrently; calls on one stream run in order.  The
+ * buffer grows with hipMalloc when a call needs more, outside graph capture
+ * only (that call also waits for `stream` once while it clears the new
+ * buffer's counters); a capturing stream whose scratch is too small gets
+ * PA_ERR_WORKSPACE, so reserve it first (pa_workspace_reserve, or one eager
+ * call of the same shapes on that stream).  A graph uses the scratch of the
+ * stream it was captured on: replaying it concurrently with other work that
+ * uses that scratch (eager calls on that stream, other graphs captured there)
+ * races.  An outgrown buffer is never freed (graphs captured before the
+ * growth still use it); every buffer lives until the process ends.
  *
  * Errors: every check runs before any launch.  A failing call returns a
  * negative pa_status, launches nothing, and leaves a message for
@@ -56,8 +65,31 @@ typedef enum pa_status {
   PA_ERR_UNSUPPORTED = -3, /* head_size != 128, block_size != 16 or group > 16      */
   PA_ERR_ALIAS = -4,       /* out overlaps an input                                 */
   PA_ERR_WORKSPACE = -5,   /* split-KV scratch too small while `stream` captures    */
-  PA_ERR_HIP = -6          /* a HIP runtime call or a kernel launch failed          */
+  PA_ERR_HIP = -6,         /* a HIP runtime call or a kernel launch failed          */
+  PA_ERR_DTYPE = -7,       /* a tensor descriptor has the wrong element type        */
+  PA_ERR_LAYOUT = -8       /* a stride the kernels need dense (or aligned) is not   */
 } pa_status;
+
+/*
+ * Tensor descriptors (paged_decode_attention_desc).  Element types: */
+typedef enum pa_dtype {
+  PA_DTYPE_BF16 = 1,
+  PA_DTYPE_FP8_E4M3FN = 2, /* OCP e4m3fn bytes                                       */
+  PA_DTYPE_UINT8 = 3,      /* the same bytes seen as uint8 (accepted for the caches) */
+  PA_DTYPE_INT32 = 4,
+  PA_DTYPE_FP32 = 5
+} pa_dtype;
+
+#define PA_MAX_DIMS 5
+/* data: device address of element [0, .., 0]; sizes and strides in elements
+ * (strides >= 0); a dim of size 1 may have any stride. */
+typedef struct pa_tensor {
+  void* data;
+  int32_t dtype; /* pa_dtype */
+  int32_t ndim;  /* 0 .. PA_MAX_DIMS */
+  int64_t sizes[PA_MAX_DIMS];
+  int64_t strides[PA_MAX_DIMS];
+} pa_tensor;
 
 /*
  * Paged decode attention (see the top of this file for the operation).
@@ -94,6 +126,36 @@ int paged_decode_attention(const void* q, const void* k_cache, const void* v_cac
                            int32_t max_blocks_per_seq, int64_t num_blocks, float scale,
                            const float* k_scale, const float* v_scale, void* out,
                            void* stream);
+
+/*
+ * paged_decode_attention on tensor descriptors: the same operation, with the
+ * element types and layouts checked at this boundary and the strides the
+ * kernels can follow left free (the arguments of the API page's
+ * RocmAiterUnifiedAttentionImpl.forward: query, key_cache / value_cache,
+ * block_table, seqused_k, softmax_scale, k_descale / v_descale, output).
+ *
+ *   q             BF16  [num_seqs, num_heads, 128]: rows [num_heads, 128] dense,
+ *                       the sequence stride free (a multiple of 8, >= num_heads * 128)
+ *   k_cache       FP8_E4M3FN or UINT8 [num_blocks, num_kv_heads, 8, 16, 16]: each
+ *                       (block, kv head) page dense, block and kv-head strides free
+ *                       (multiples of 16)
+ *   v_cache       FP8_E4M3FN or UINT8 [num_blocks, num_kv_heads, 128, 16] or
+ *                       [num_blocks, num_kv_heads, 1, 128, 16]: pages dense, with
+ *                       k_cache's block and kv-head strides
+ *   block_tables  INT32 [num_seqs, max_blocks_per_seq]: rows dense, row stride free
+ *   seq_lens      INT32 [num_seqs], dense
+ *   k_scale, v_scale  FP32, one element each (device)
+ *   out           BF16  q's sizes, dense, must not overlap any input
+ *   scale, stream as for paged_decode_attention
+ * Errors: PA_ERR_NULL (a NULL descriptor), PA_ERR_DTYPE (an element type),
+ * PA_ERR_SHAPE (ranks and sizes), PA_ERR_UNSUPPORTED (head_size, block_size,
+ * group), PA_ERR_LAYOUT (a stride that must be dense or aligned is not, or K
+ * and V strides differ), then everything paged_decode_attention reports.
+ */
+int paged_decode_attention_desc(const pa_tensor* q, const pa_tensor* k_cache,
+                                const pa_tensor* v_cache, const pa_tensor* block_tables,
+                                const pa_tensor* seq_lens, float scale, const pa_tensor* k_scale,
+                                const pa_tensor* v_scale, const pa_tensor* out, void* stream);
 
 /*
  * The same operation with an explicit split-KV partition size: each sequence's
@@ -238,12 +300,15 @@ int paged_decode_attention_slot_scales(const void* q, const void* k_cache, const
                                        void* out, void* stream);
 
 /*
- * Launch plan for the given shapes (host arithmetic only; no device access).
+ * Launch plan of the one-query decode (paged_decode_attention,
+ * paged_decode_attention_split, _desc, _slot_scales, _nhd) for the given
+ * shapes: host arithmetic only, no device access.
  * num_compute_units: the device's CU count (256 on MI355X).
  * pages_per_partition: as in paged_decode_attention_split (0 = library's choice).
  * Outputs (any may be NULL): number of partitions per sequence, blocks per
  * partition, and the split-KV scratch bytes that plan needs (0 when it has one
- * partition).  Returns PA_OK or PA_ERR_SHAPE.
+ * partition).  Several queries per sequence and longest-first dispatch change
+ * the plan: pa_workspace_bytes covers them.  Returns PA_OK or PA_ERR_SHAPE.
  */
 int pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                    int32_t max_blocks_per_seq, int32_t num_compute_units,
@@ -251,13 +316,31 @@ int pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                    int32_t* pages_per_part, size_t* workspace_bytes);
 
 /*
- * Make the current device's split-KV scratch at least `bytes` large.
- * Growing it frees the old buffer (hipFree, which waits for the device) and
- * allocates a new one (hipMalloc), so do it outside graph capture: call it
- * before capturing a graph whose calls need scratch (pa_decode_plan gives the
- * size).  Returns PA_OK or PA_ERR_HIP (allocation failed).
+ * Split-KV scratch bytes a call needs (0: none), for every entry point that
+ * plans by itself (all but paged_decode_attention_split):
+ *   num_q_tokens, max_seqlen_q  as for paged_multi_query_attention /
+ *                               paged_attention_unified; 0, 0 for one query
+ *                               per sequence
+ *   longest_first               as in pa_attention_options
+ *   token_rows                  nonzero for paged_decode_attention_nhd
+ *   device                      the HIP device whose compute units the plan
+ *                               uses, or -1 for MI355X's 256 (no device access)
+ * *bytes receives the size.  Returns PA_OK, PA_ERR_NULL, PA_ERR_SHAPE,
+ * PA_ERR_UNSUPPORTED or PA_ERR_HIP (no such device).
  */
-int pa_decode_reserve_workspace(size_t bytes);
+int pa_workspace_bytes(int32_t num_seqs, int32_t num_q_tokens, int32_t max_seqlen_q,
+                       int32_t num_heads, int32_t num_kv_heads, int32_t max_blocks_per_seq,
+                       int32_t longest_first, int32_t token_rows, int device, size_t* bytes);
+
+/*
+ * Make the split-KV scratch that calls on (device, stream) use at least
+ * `bytes` large: hipMalloc, plus one wait for `stream` while the new buffer's
+ * counters are cleared, so call it outside graph capture, before capturing
+ * calls on that stream (pa_workspace_bytes gives the size).  An outgrown
+ * buffer stays allocated (see the top of this file).  Returns PA_OK,
+ * PA_ERR_WORKSPACE (the stream is capturing) or PA_ERR_HIP.
+ */
+int pa_workspace_reserve(int device, void* stream, size_t bytes);
 
 /*
  * Fill the paged fp8 cache with new tokens (the cache update that precedes the
@@ -284,7 +367,8 @@ int pa_decode_reserve_workspace(size_t bytes);
  *   k_scale, v_scale  fp32 [1], device
  * Two tokens with the same slot race (one of them wins).  Asynchronous like
  * paged_decode_attention; errors as there, and PA_ERR_UNSUPPORTED when
- * ceil(num_tokens / 16) * num_kv_heads exceeds 2^31 - 1 (one workgroup each).
+ * ceil(num_tokens / 16) * num_kv_heads exceeds 2^26 (one 64-lane workgroup
+ * each, within a 2^32-lane grid).
  */
 int paged_kv_cache_write(const void* key, const void* value, int64_t key_token_stride,
                          int64_t value_token_stride, void* k_cache, void* v_cache,

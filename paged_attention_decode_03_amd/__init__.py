@@ -25,12 +25,11 @@ import os
 import torch
 
 __all__ = [
-    "paged_decode_attention", "paged_decode_attention_split", "pa_decode_plan",
-    "pa_decode_reserve_workspace", "paged_kv_cache_write", "paged_decode_attention_slot_scales",
-    "paged_multi_query_attention", "paged_attention_unified", "paged_decode_attention_nhd",
-    "pa_last_error",
-    "PagedAttentionError", "library_path",
-    "load_library",
+    "paged_decode_attention", "paged_decode_attention_desc", "paged_decode_attention_split",
+    "pa_decode_plan", "pa_workspace_bytes", "pa_workspace_reserve", "paged_kv_cache_write",
+    "paged_decode_attention_slot_scales", "paged_multi_query_attention",
+    "paged_attention_unified", "paged_decode_attention_nhd", "pa_last_error",
+    "PagedAttentionError", "library_path", "load_library",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -38,8 +37,13 @@ library_path = os.path.join(_HERE, "libpagedattn.so")
 
 STATUS_NAMES = {
     0: "PA_OK", -1: "PA_ERR_NULL", -2: "PA_ERR_SHAPE", -3: "PA_ERR_UNSUPPORTED",
-    -4: "PA_ERR_ALIAS", -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_HIP",
+    -4: "PA_ERR_ALIAS", -5: "PA_ERR_WORKSPACE", -6: "PA_ERR_HIP", -7: "PA_ERR_DTYPE",
+    -8: "PA_ERR_LAYOUT",
 }
+
+# pa_dtype codes
+PA_DTYPE_BF16, PA_DTYPE_FP8_E4M3FN, PA_DTYPE_UINT8, PA_DTYPE_INT32, PA_DTYPE_FP32 = 1, 2, 3, 4, 5
+PA_MAX_DIMS = 5
 
 _lib = None
 
@@ -55,6 +59,32 @@ class AttentionOptions(ctypes.Structure):
     _fields_ = [("sliding_window", ctypes.c_int32), ("logits_soft_cap", ctypes.c_float),
                 ("alibi_slopes", ctypes.c_void_p), ("sinks", ctypes.c_void_p),
                 ("longest_first", ctypes.c_int32)]
+
+
+class Tensor(ctypes.Structure):
+    """pa_tensor: device address, element type, rank, sizes and strides (elements)."""
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("sizes", ctypes.c_int64 * PA_MAX_DIMS), ("strides", ctypes.c_int64 * PA_MAX_DIMS)]
+
+
+_TORCH_DTYPES = {torch.bfloat16: PA_DTYPE_BF16, torch.float8_e4m3fn: PA_DTYPE_FP8_E4M3FN,
+                 torch.uint8: PA_DTYPE_UINT8, torch.int32: PA_DTYPE_INT32,
+                 torch.float32: PA_DTYPE_FP32}
+
+
+def tensor_desc(t) -> Tensor:
+    """A pa_tensor describing torch tensor `t` as it is (no copy, no check
+    beyond what a descriptor can hold: the library checks the rest)."""
+    if t.dim() > PA_MAX_DIMS:
+        raise ValueError(f"at most {PA_MAX_DIMS} dims")
+    d = Tensor()
+    d.data = t.data_ptr()
+    d.dtype = _TORCH_DTYPES.get(t.dtype, 0)
+    d.ndim = t.dim()
+    for i in range(t.dim()):
+        d.sizes[i] = t.shape[i]
+        d.strides[i] = t.stride(i)
+    return d
 
 
 def load_library():
@@ -88,8 +118,14 @@ def load_library():
     lib.pa_decode_plan.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(i32),
                                    ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_size_t)]
     lib.pa_decode_plan.restype = ctypes.c_int
-    lib.pa_decode_reserve_workspace.argtypes = [ctypes.c_size_t]
-    lib.pa_decode_reserve_workspace.restype = ctypes.c_int
+    TP = ctypes.POINTER(Tensor)
+    lib.paged_decode_attention_desc.argtypes = [TP, TP, TP, TP, TP, f32, TP, TP, TP, vp]
+    lib.paged_decode_attention_desc.restype = ctypes.c_int
+    lib.pa_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, ctypes.c_int,
+                                       ctypes.POINTER(ctypes.c_size_t)]
+    lib.pa_workspace_bytes.restype = ctypes.c_int
+    lib.pa_workspace_reserve.argtypes = [ctypes.c_int, vp, ctypes.c_size_t]
+    lib.pa_workspace_reserve.restype = ctypes.c_int
     lib.paged_kv_cache_write.argtypes = [vp, vp, i64, i64, vp, vp, vp, i32, i32, i32, i32, i64,
                                          vp, vp, vp]
     lib.paged_kv_cache_write.restype = ctypes.c_int
@@ -113,11 +149,22 @@ def _ptr(t):
 
 
 def _scale_tensor(x, device):
-    if isinstance(x, torch.Tensor):
-        if x.dtype != torch.float32 or x.numel() != 1 or x.device != device:
-            raise TypeError("k_scale / v_scale must be one-element float32 tensors on the q device")
-        return x
-    return torch.tensor([float(x)], dtype=torch.float32, device=device)
+    """Scales are read by the kernels from device memory (as vLLM's layer
+    scales are tensors), so a graph replay sees their current values; a host
+    float would need a host-to-device copy on every call, which a captured
+    graph cannot repeat, so it is refused."""
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("k_scale / v_scale must be one-element float32 device tensors "
+                        "(a host float would be copied on every call, which graph capture cannot replay)")
+    if x.dtype != torch.float32 or x.numel() != 1 or x.device != device:
+        raise TypeError("k_scale / v_scale must be one-element float32 tensors on the q device")
+    return x
+
+
+def _stream_handle(stream, dev):
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
 def _args(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale, v_scale, out, stream,
@@ -162,9 +209,7 @@ def _args(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale, v_scale, 
         raise ValueError("out must be a contiguous bfloat16 tensor shaped like q")
     ks = _scale_tensor(k_scale, dev)
     vs = _scale_tensor(v_scale, dev)
-    if stream is None:
-        stream = torch.cuda.current_stream(dev)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    handle = _stream_handle(stream, dev)
     c_args = (_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens),
               S, Hq, Hkv, D, bs, block_tables.shape[1], NB, float(scale), _ptr(ks), _ptr(vs),
               _ptr(out), handle)
@@ -176,13 +221,35 @@ def paged_decode_attention(q, k_cache, v_cache, block_tables, seq_lens, scale, k
     """Enqueue paged decode attention on `stream` (default: torch's current stream).
 
     Returns ``out`` (allocated like q when not given).  k_scale / v_scale are
-    one-element float32 device tensors (a Python float is copied to the device).
+    one-element float32 device tensors.  Dense tensors only (the flat C ABI
+    takes pointers and sizes); see paged_decode_attention_desc for strided ones.
     """
     lib = load_library()
     dev, out, c_args, keep = _args(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale,
                                    v_scale, out, stream)
     with torch.cuda.device(dev):
         _check(lib.paged_decode_attention(*c_args))
+    return out
+
+
+def paged_decode_attention_desc(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale,
+                                v_scale, out=None, stream=None):
+    """paged_decode_attention through tensor descriptors: the library checks
+    element types, sizes and layouts itself and follows the free strides (q's
+    sequence stride, block-table rows, the caches' block and kv-head strides).
+    Returns ``out`` (a dense bf16 tensor like q when not given)."""
+    lib = load_library()
+    dev = q.device
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    descs = [tensor_desc(t) for t in (q, k_cache, v_cache, block_tables, seq_lens, k_scale, v_scale,
+                                      out)]
+    qd, kd, vd, bd, sd, ksd, vsd, od = descs
+    with torch.cuda.device(dev):
+        _check(lib.paged_decode_attention_desc(
+            ctypes.byref(qd), ctypes.byref(kd), ctypes.byref(vd), ctypes.byref(bd), ctypes.byref(sd),
+            float(scale), ctypes.byref(ksd), ctypes.byref(vsd), ctypes.byref(od),
+            _stream_handle(stream, dev)))
     return out
 
 
@@ -320,11 +387,24 @@ def pa_decode_plan(num_seqs, num_heads, num_kv_heads, max_blocks_per_seq, num_co
     return P.value, ppp.value, ws.value
 
 
-def pa_decode_reserve_workspace(nbytes: int, device=None):
-    """Grow the split-KV scratch of `device` (default: current) to at least nbytes."""
+def pa_workspace_bytes(num_seqs, num_heads, num_kv_heads, max_blocks_per_seq, num_q_tokens=0,
+                       max_seqlen_q=0, longest_first=False, token_rows=False, device=-1):
+    """Split-KV scratch bytes a call of these shapes needs (device -1: plan for
+    256 compute units without touching a device)."""
     lib = load_library()
-    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
-        _check(lib.pa_decode_reserve_workspace(int(nbytes)))
+    n = ctypes.c_size_t()
+    _check(lib.pa_workspace_bytes(num_seqs, num_q_tokens, max_seqlen_q, num_heads, num_kv_heads,
+                                  max_blocks_per_seq, 1 if longest_first else 0,
+                                  1 if token_rows else 0, int(device), ctypes.byref(n)))
+    return n.value
+
+
+def pa_workspace_reserve(nbytes: int, stream=None, device=None):
+    """Grow the split-KV scratch that calls on `stream` (default: the current
+    stream) of `device` (default: current) use to at least nbytes."""
+    lib = load_library()
+    dev = torch.device("cuda", device if device is not None else torch.cuda.current_device())
+    _check(lib.pa_workspace_reserve(dev.index, _stream_handle(stream, dev), int(nbytes)))
 
 
 def paged_kv_cache_write(key, value, k_cache, v_cache, slot_mapping, k_scale, v_scale,
@@ -356,9 +436,7 @@ def paged_kv_cache_write(key, value, k_cache, v_cache, slot_mapping, k_scale, v_
         raise TypeError("slot_mapping must be a contiguous int64 [num_tokens] tensor on the key device")
     ks = _scale_tensor(k_scale, dev)
     vs = _scale_tensor(v_scale, dev)
-    if stream is None:
-        stream = torch.cuda.current_stream(dev)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    handle = _stream_handle(stream, dev)
     with torch.cuda.device(dev):
         _check(lib.paged_kv_cache_write(
             _ptr(key), _ptr(value), key.stride(0) if T else Hkv * D, value.stride(0) if T else Hkv * D,

@@ -16,7 +16,9 @@
 #include <string.h>
 
 #include <algorithm>
+#include <map>
 #include <mutex>
+#include <utility>
 #include <vector>
 
 #include "paged_attention.h"
@@ -150,13 +152,18 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t W, int32_t num_cus, in
   return PA_OK;
 }
 
-// Per-device split-KV scratch.
+// Split-KV scratch: one buffer per (device, stream), so calls on different
+// streams never share partials or arrival counters, while calls on one stream
+// run in order.  A buffer that is outgrown is never freed: graphs captured
+// earlier hold its address and keep using it on replay, so it stays allocated
+// (and its counters at zero) until the process ends.
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
 };
 std::mutex g_ws_mutex;
-std::vector<Workspace> g_ws;
+std::map<std::pair<int, uintptr_t>, Workspace> g_ws;
+std::vector<void*> g_retired;  // outgrown buffers, still referenced by captured graphs
 std::vector<int> g_cus;
 
 int device_cus(int dev) {
@@ -171,39 +178,33 @@ int device_cus(int dev) {
   return g_cus[dev];
 }
 
-int ensure_workspace(int dev, size_t bytes, hipStream_t stream, bool check_capture, void** out) {
+// The scratch of (dev, stream), grown to at least `bytes` (outside capture
+// only: a capturing stream whose scratch is too small gets PA_ERR_WORKSPACE).
+int ensure_workspace(int dev, hipStream_t stream, size_t bytes, void** out) {
   std::lock_guard<std::mutex> lock(g_ws_mutex);
-  if ((int)g_ws.size() <= dev) g_ws.resize(dev + 1);
-  Workspace& ws = g_ws[dev];
+  Workspace& ws = g_ws[std::make_pair(dev, (uintptr_t)stream)];
   if (ws.bytes >= bytes) {
     *out = ws.ptr;
     return PA_OK;
   }
-  if (check_capture) {
-    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &st) != hipSuccess)
-      return fail(PA_ERR_HIP, "hipStreamIsCapturing failed");
-    if (st != hipStreamCaptureStatusNone)
-      return fail(PA_ERR_WORKSPACE,
-                  "split-KV scratch needs %zu bytes but %zu are reserved and the stream is "
-                  "capturing; call pa_decode_reserve_workspace before capture",
-                  bytes, ws.bytes);
-  }
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (stream != nullptr && hipStreamIsCapturing(stream, &st) != hipSuccess)
+    return fail(PA_ERR_HIP, "hipStreamIsCapturing failed");
+  if (st != hipStreamCaptureStatusNone)
+    return fail(PA_ERR_WORKSPACE,
+                "split-KV scratch of this stream needs %zu bytes but %zu are reserved and the stream "
+                "is capturing; call pa_workspace_reserve for this stream before capture",
+                bytes, ws.bytes);
   const size_t grow = (bytes + (size_t(1) << 20) - 1) & ~((size_t(1) << 20) - 1);
-  if (ws.ptr) {
-    if (hipFree(ws.ptr) != hipSuccess) return fail(PA_ERR_HIP, "hipFree of the old scratch failed");
-    ws.ptr = nullptr;
-    ws.bytes = 0;
-  }
   void* p = nullptr;
   if (hipMalloc(&p, grow) != hipSuccess) return fail(PA_ERR_HIP, "hipMalloc(%zu) for scratch failed", grow);
-  // the arrival counters start at zero, for calls on any stream: cleared and
-  // waited for here (outside capture: allocation never happens while `stream`
-  // captures)
+  // the arrival counters start at zero: cleared and waited for here, before
+  // any call can use the buffer (never while `stream` captures)
   if (hipMemsetAsync(p, 0, kCounterRegion, stream) != hipSuccess || hipStreamSynchronize(stream) != hipSuccess) {
     hipFree(p);
     return fail(PA_ERR_HIP, "clearing the scratch's counters failed");
   }
+  if (ws.ptr) g_retired.push_back(ws.ptr);
   ws.ptr = p;
   ws.bytes = grow;
   *out = p;
@@ -222,9 +223,41 @@ struct Variant {
   int32_t num_q_rows = 0;
   int32_t max_seqlen_q = 1;
   bool token_rows = false;                 // token-row cache layout with byte strides
+  // cache addressing in bytes; page layout: 0 = dense (Hkv * 2048 per block, 2048 per kv head)
   int64_t block_stride = 0, token_stride = 0, head_stride = 0;
+  // elements between rows of q and of the block table (0 = dense)
+  int64_t q_row_stride = 0, bt_row_stride = 0;
   pa_attention_options options = {0, 0.0f, nullptr, nullptr, 0};
 };
+
+// The launch a call makes, from shapes alone.
+struct CallPlan {
+  Plan plan;
+  int32_t q_tile;          // query tokens per tile (columns = q_tile * group <= 16)
+  int32_t q_tiles;         // query tiles per sequence
+  int32_t tiles_per_item;  // tiles one work item holds (1 to 3)
+  int32_t q_items;         // work items per (sequence, kv head, partition)
+  bool lpt_in_kernel;      // longest-first order computed inside the work items
+};
+
+int plan_call(int32_t S, int32_t Hq, int32_t Hkv, int32_t W, int32_t cus, int32_t ppp_req, bool mq,
+              int32_t num_q_rows, int32_t max_seqlen_q, bool longest_first, bool token_rows,
+              CallPlan* cp) {
+  const int32_t G = Hq / Hkv;
+  // query tokens per work item: as many as the 16 MFMA columns hold with the group
+  cp->q_tile = mq ? (pa::kMaxGroup / G > 0 ? pa::kMaxGroup / G : 1) : 1;
+  cp->q_tiles = mq ? (max_seqlen_q + cp->q_tile - 1) / cp->q_tile : 1;
+  // query tiles per work item: up to three (one wave holds their accumulators
+  // against the same K/V); four tiles go as two items of two
+  cp->tiles_per_item = cp->q_tiles <= 2 ? cp->q_tiles : (cp->q_tiles == 4 ? 2 : 3);
+  cp->q_items = (cp->q_tiles + cp->tiles_per_item - 1) / cp->tiles_per_item;
+  // longest-first: computed by each work item where its workgroup is one wave
+  // and the sequences few enough, else by the order kernel
+  cp->lpt_in_kernel = PA_LPT_IN_KERNEL && longest_first && !token_rows && S >= 2 &&
+                      S <= kInKernelOrderMaxSeqs;
+  return make_plan(S, Hq, Hkv, W, cus, ppp_req, &cp->plan, cp->q_items, mq ? num_q_rows : S,
+                   longest_first && !cp->lpt_in_kernel);
+}
 
 int decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
            const int32_t* seq_lens, int32_t S, int32_t Hq, int32_t Hkv, int32_t head_size,
@@ -274,8 +307,20 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   if (W == 0 || NB == 0)
     return fail(PA_ERR_SHAPE, "max_blocks_per_seq and num_blocks must be positive when num_seqs > 0");
 
-  const size_t q_bytes = (size_t)(mq ? num_q_rows : S) * Hq * pa::kHeadDim * 2;
-  size_t cache_bytes = (size_t)NB * Hkv * pa::kPageBytes;
+  const int64_t rows = mq ? num_q_rows : S;
+  const int64_t row_elems = (int64_t)Hq * pa::kHeadDim;
+  const int64_t qrs = var.q_row_stride ? var.q_row_stride : row_elems;
+  const int64_t btrs = var.bt_row_stride ? var.bt_row_stride : W;
+  if (qrs < row_elems || (qrs & 7))
+    return fail(PA_ERR_LAYOUT, "q row stride %lld must be a multiple of 8 elements and at least %lld",
+                (long long)qrs, (long long)row_elems);
+  if (btrs < W)
+    return fail(PA_ERR_LAYOUT, "block-table row stride %lld is below max_blocks_per_seq %d",
+                (long long)btrs, W);
+  const size_t out_bytes = (size_t)rows * row_elems * 2;
+  const size_t q_bytes = ((size_t)(rows - 1) * qrs + row_elems) * 2;
+  int64_t bstride = var.block_stride, hstride = var.head_stride;
+  size_t cache_bytes;
   if (var.token_rows) {
     const int64_t bs = var.block_stride, ts = var.token_stride, hs = var.head_stride;
     if (bs <= 0 || ts <= 0 || hs <= 0 || (bs | ts | hs) & 15)
@@ -286,18 +331,29 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
       return fail(PA_ERR_UNSUPPORTED, "token stride %lld exceeds 2^26 bytes", (long long)ts);
     // bytes from the cache base to the end of the last block's last row
     cache_bytes = (size_t)((NB - 1) * bs + (pa::kBlockTokens - 1) * ts + (Hkv - 1) * hs + pa::kHeadDim);
+  } else {
+    if (bstride == 0 && hstride == 0) {
+      bstride = (int64_t)Hkv * pa::kPageBytes;
+      hstride = pa::kPageBytes;
+    }
+    if (bstride <= 0 || hstride <= 0 || (bstride | hstride) & 15)
+      return fail(PA_ERR_LAYOUT, "cache block / kv-head strides must be positive multiples of 16 bytes "
+                                 "(block %lld, head %lld)", (long long)bstride, (long long)hstride);
+    if (slot_scales && (bstride != (int64_t)Hkv * pa::kPageBytes || hstride != pa::kPageBytes))
+      return fail(PA_ERR_LAYOUT, "per-slot scales need dense caches");
+    cache_bytes = (size_t)((NB - 1) * bstride + (Hkv - 1) * hstride + pa::kPageBytes);
   }
-  if (overlaps(out, q_bytes, q, q_bytes) || overlaps(out, q_bytes, k_cache, cache_bytes) ||
-      overlaps(out, q_bytes, v_cache, cache_bytes) ||
-      overlaps(out, q_bytes, block_tables, (size_t)S * W * 4) ||
-      overlaps(out, q_bytes, seq_lens, (size_t)S * 4) || overlaps(out, q_bytes, k_scale, 4) ||
-      (mq && overlaps(out, q_bytes, cu_seqlens_q, (size_t)(S + 1) * 4)) ||
-      overlaps(out, q_bytes, opt.alibi_slopes, opt.alibi_slopes ? (size_t)Hq * 4 : 0) ||
-      overlaps(out, q_bytes, opt.sinks, opt.sinks ? (size_t)Hq * 4 : 0) ||
-      overlaps(out, q_bytes, v_scale, 4))
+  if (overlaps(out, out_bytes, q, q_bytes) || overlaps(out, out_bytes, k_cache, cache_bytes) ||
+      overlaps(out, out_bytes, v_cache, cache_bytes) ||
+      overlaps(out, out_bytes, block_tables, ((size_t)(S - 1) * btrs + W) * 4) ||
+      overlaps(out, out_bytes, seq_lens, (size_t)S * 4) || overlaps(out, out_bytes, k_scale, 4) ||
+      (mq && overlaps(out, out_bytes, cu_seqlens_q, (size_t)(S + 1) * 4)) ||
+      overlaps(out, out_bytes, opt.alibi_slopes, opt.alibi_slopes ? (size_t)Hq * 4 : 0) ||
+      overlaps(out, out_bytes, opt.sinks, opt.sinks ? (size_t)Hq * 4 : 0) ||
+      overlaps(out, out_bytes, v_scale, 4))
     return fail(PA_ERR_ALIAS, "out overlaps an input");
-  if (slot_scales && (overlaps(out, q_bytes, k_scale, (size_t)NB * Hkv * 64) ||
-                      overlaps(out, q_bytes, v_scale, (size_t)NB * Hkv * 64)))
+  if (slot_scales && (overlaps(out, out_bytes, k_scale, (size_t)NB * Hkv * 64) ||
+                      overlaps(out, out_bytes, v_scale, (size_t)NB * Hkv * 64)))
     return fail(PA_ERR_ALIAS, "out overlaps a scale table");
   if (var.token_rows && ((uintptr_t)v_cache & 15))
     return fail(PA_ERR_SHAPE, "misaligned v_cache (token rows: 16 B)");
@@ -310,27 +366,16 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   // --- past this point HIP is called
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice failed");
-  // query tokens per work item: as many as the 16 MFMA columns hold with the group
-  const int32_t q_tile = mq ? (pa::kMaxGroup / G > 0 ? pa::kMaxGroup / G : 1) : 1;
-  const int32_t q_tiles = mq ? (max_seqlen_q + q_tile - 1) / q_tile : 1;
-  Plan plan;
-  // work items per (sequence, kv head, partition): one per pair of query tiles
-  // query tiles per work item: up to three (one wave holds their accumulators
-  // against the same K/V); four tiles go as two items of two
-  const int32_t tiles_per_item = q_tiles <= 2 ? q_tiles : (q_tiles == 4 ? 2 : 3);
-  const int32_t q_items = (q_tiles + tiles_per_item - 1) / tiles_per_item;
-  // longest-first: computed by each work item where its workgroup is one wave
-  // and the sequences few enough, else by the order kernel
-  const bool lpt_in_kernel =
-      PA_LPT_IN_KERNEL && opt.longest_first != 0 && !var.token_rows && S >= 2 && S <= kInKernelOrderMaxSeqs;
-  int rc = make_plan(S, Hq, Hkv, W, device_cus(dev), ppp_req, &plan, q_items, mq ? num_q_rows : S,
-                     opt.longest_first != 0 && !lpt_in_kernel);
+  CallPlan cp;
+  int rc = plan_call(S, Hq, Hkv, W, device_cus(dev), ppp_req, mq, num_q_rows, max_seqlen_q,
+                     opt.longest_first != 0, var.token_rows, &cp);
   if (rc) return rc;
+  const Plan& plan = cp.plan;
   // one 64-lane block per work item, 256 lanes per merged row: keep both grids
   // within 2^32 lanes
   const int64_t units = (int64_t)S * Hkv * plan.num_parts;
-  const int64_t items = mq ? (units + 7) / 8 * 8 * q_items : units;
-  const int64_t merge_rows = (int64_t)(mq ? num_q_rows : S) * Hq;
+  const int64_t items = mq ? (units + 7) / 8 * 8 * cp.q_items : units;
+  const int64_t merge_rows = rows * Hq;
   if (items > (int64_t(1) << 26) || merge_rows > (int64_t(1) << 24))
     return fail(PA_ERR_UNSUPPORTED, "launch too large: %lld work items, %lld merged rows",
                 (long long)items, (long long)merge_rows);
@@ -342,6 +387,8 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   p.v_cache = (const uint8_t*)v_cache;
   p.block_tables = block_tables;
   p.seq_lens = seq_lens;
+  p.q_row_stride = qrs;
+  p.bt_row_stride = btrs;
   p.k_scale = slot_scales ? nullptr : k_scale;
   p.v_scale = slot_scales ? nullptr : v_scale;
   p.k_slot_scales = slot_scales ? k_scale : nullptr;
@@ -365,11 +412,11 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
                        ? 1 : 0;
   p.multi_query = mq ? 1 : 0;
   p.cu_seqlens_q = cu_seqlens_q;
-  p.num_q_rows = mq ? num_q_rows : S;
-  p.q_tile = q_tile;
-  p.num_q_tiles = q_tiles;
+  p.num_q_rows = (int32_t)rows;
+  p.q_tile = cp.q_tile;
+  p.num_q_tiles = cp.q_tiles;
   // more than one tile of queries: two tiles per item share the page reads
-  p.tiles_per_item = tiles_per_item;
+  p.tiles_per_item = cp.tiles_per_item;
   p.window = opt.sliding_window;
   p.softcap = opt.logits_soft_cap;
   p.scale = scale;
@@ -388,24 +435,19 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
         p.kv_group = g;
         break;
       }
-  p.block_stride = var.block_stride;
+  p.block_stride = bstride;
   p.token_stride = var.token_stride;
-  p.head_stride = var.head_stride;
+  p.head_stride = hstride;
   p.seq_order = nullptr;
-  p.order_in_kernel = lpt_in_kernel ? 1 : 0;
+  p.order_in_kernel = cp.lpt_in_kernel ? 1 : 0;
   // longest-first, one query per sequence, one wave per workgroup: slots in
   // snake order over rounds of one work item per CU (measured on MI355X,
   // ragged 1..4000 batches of 256 sequences: 40/8 181 -> 176 us, 32/8
   // 186 -> 180 us, 32/4 111 -> 105 us; 8/1 and uniform contexts unchanged)
   const int64_t items_per_slot = (int64_t)Hkv * plan.num_parts;
-  p.lpt_round_slots = (!mq && !var.token_rows && (lpt_in_kernel || plan.longest_first))
+  p.lpt_round_slots = (!mq && !var.token_rows && (cp.lpt_in_kernel || plan.longest_first))
                           ? (int32_t)std::max<int64_t>(1, device_cus(dev) / items_per_slot)
                           : 0;
-  // two waves per work item where one partition leaves more than one and at
-  // most two items per CU: four waves streaming on a CU instead of two, no
-  // split (measured on MI355X, 512 items: 40/8 ctx 4096 x 64 sequences 95.7 ->
-  // 88.3 us, 20/4 ctx 4096 x 128 96.0 -> 87.8 us, ctx 1024 and 2048 within 1%;
-  // at 3 to 4 items per CU, and with split contexts, it measured 3-10% slower)
   // the last item of a split (sequence, kv head) merges its partitions where
   // they are few (one query per sequence): no merge kernel and no kernel
   // boundary before it
@@ -413,13 +455,18 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
                    (int64_t)G * plan.num_parts <= pa::kFusedMergeMaxLoads && (int64_t)S * Hkv <= kCounterSlots)
                       ? 1 : 0;
   p.unit_count = nullptr;
+  // two waves per work item where one partition leaves more than one and at
+  // most two items per CU: four waves streaming on a CU instead of two, no
+  // split (measured on MI355X, 512 items: 40/8 ctx 4096 x 64 sequences 95.7 ->
+  // 88.3 us, 20/4 ctx 4096 x 128 96.0 -> 87.8 us, ctx 1024 and 2048 within 1%;
+  // at 3 to 4 items per CU, and with split contexts, it measured 3-10% slower)
   const int64_t cus = device_cus(dev);
   p.waves_per_item = (!mq && !slot_scales && !var.token_rows && plan.num_parts == 1 &&
                       units > cus && units <= 2 * cus)
                          ? 2 : 1;
   if (plan.workspace_bytes) {
     void* ws = nullptr;
-    rc = ensure_workspace(dev, plan.workspace_bytes, stream, true, &ws);
+    rc = ensure_workspace(dev, stream, plan.workspace_bytes, &ws);
     if (rc) return rc;
     p.unit_count = (int32_t*)ws;
     if (plan.num_parts > 1) {
@@ -433,9 +480,110 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   return PA_OK;
 }
 
+// --- tensor descriptors (paged_decode_attention_desc)
+
+bool fp8_bytes(int32_t dt) { return dt == PA_DTYPE_FP8_E4M3FN || dt == PA_DTYPE_UINT8; }
+
+// Stride of dim i, or `want` when the dim has one element (its stride is then
+// never used, and frameworks leave it arbitrary).
+int64_t stride_or(const pa_tensor* t, int i, int64_t want) {
+  return t->sizes[i] == 1 ? want : t->strides[i];
+}
+
+bool valid_desc(const pa_tensor* t) {
+  if (t->ndim < 0 || t->ndim > PA_MAX_DIMS) return false;
+  for (int i = 0; i < t->ndim; ++i)
+    if (t->sizes[i] < 0 || t->strides[i] < 0) return false;
+  return true;
+}
+
+int64_t numel(const pa_tensor* t) {
+  int64_t n = 1;
+  for (int i = 0; i < t->ndim; ++i) n *= t->sizes[i];
+  return n;
+}
+
 }  // namespace
 
 extern "C" {
+
+int paged_decode_attention_desc(const pa_tensor* q, const pa_tensor* k_cache, const pa_tensor* v_cache,
+                                const pa_tensor* block_tables, const pa_tensor* seq_lens, float scale,
+                                const pa_tensor* k_scale, const pa_tensor* v_scale, const pa_tensor* out,
+                                void* stream) {
+  g_last_error[0] = '\0';
+  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !k_scale || !v_scale || !out)
+    return fail(PA_ERR_NULL, "a tensor descriptor is NULL");
+  for (const pa_tensor* t : {q, k_cache, v_cache, block_tables, seq_lens, k_scale, v_scale, out})
+    if (!valid_desc(t))
+      return fail(PA_ERR_SHAPE, "a descriptor has ndim outside 0..%d or a negative size or stride",
+                  PA_MAX_DIMS);
+  // dtypes
+  if (q->dtype != PA_DTYPE_BF16 || out->dtype != PA_DTYPE_BF16)
+    return fail(PA_ERR_DTYPE, "q and out must be bf16 (dtypes %d, %d)", q->dtype, out->dtype);
+  if (!fp8_bytes(k_cache->dtype) || !fp8_bytes(v_cache->dtype))
+    return fail(PA_ERR_DTYPE, "k_cache and v_cache must be fp8 e4m3fn (or its uint8 bytes)");
+  if (block_tables->dtype != PA_DTYPE_INT32 || seq_lens->dtype != PA_DTYPE_INT32)
+    return fail(PA_ERR_DTYPE, "block_tables and seq_lens must be int32");
+  if (k_scale->dtype != PA_DTYPE_FP32 || v_scale->dtype != PA_DTYPE_FP32)
+    return fail(PA_ERR_DTYPE, "k_scale and v_scale must be fp32");
+  // ranks and sizes
+  if (q->ndim != 3 || out->ndim != 3)
+    return fail(PA_ERR_SHAPE, "q and out must be [num_seqs, num_heads, head_size]");
+  const int64_t S = q->sizes[0], Hq = q->sizes[1], D = q->sizes[2];
+  for (int i = 0; i < 3; ++i)
+    if (out->sizes[i] != q->sizes[i]) return fail(PA_ERR_SHAPE, "out must have q's sizes");
+  if (D != pa::kHeadDim) return fail(PA_ERR_UNSUPPORTED, "head_size %lld unsupported (only %d)", (long long)D, pa::kHeadDim);
+  if (k_cache->ndim != 5)
+    return fail(PA_ERR_SHAPE, "k_cache must be [num_blocks, num_kv_heads, head_size/16, block_size, 16]");
+  const int64_t NB = k_cache->sizes[0], Hkv = k_cache->sizes[1], BS = k_cache->sizes[3];
+  if (BS != pa::kBlockTokens)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %lld unsupported (only %d)", (long long)BS, pa::kBlockTokens);
+  if (k_cache->sizes[2] * 16 != D || k_cache->sizes[4] != 16)
+    return fail(PA_ERR_SHAPE, "k_cache's inner sizes must be [head_size/16, 16, 16]");
+  const bool v5 = v_cache->ndim == 5;
+  if (!(v_cache->ndim == 4 || (v5 && v_cache->sizes[2] == 1)))
+    return fail(PA_ERR_SHAPE, "v_cache must be [num_blocks, num_kv_heads, head_size, block_size] "
+                              "or [num_blocks, num_kv_heads, 1, head_size, block_size]");
+  const int vd = v5 ? 3 : 2;  // v_cache's head_size dim
+  if (v_cache->sizes[0] != NB || v_cache->sizes[1] != Hkv || v_cache->sizes[vd] != D ||
+      v_cache->sizes[vd + 1] != BS)
+    return fail(PA_ERR_SHAPE, "v_cache's sizes disagree with k_cache");
+  if (block_tables->ndim != 2 || block_tables->sizes[0] != S)
+    return fail(PA_ERR_SHAPE, "block_tables must be [num_seqs, max_blocks_per_seq]");
+  const int64_t W = block_tables->sizes[1];
+  if (seq_lens->ndim != 1 || seq_lens->sizes[0] != S) return fail(PA_ERR_SHAPE, "seq_lens must be [num_seqs]");
+  if (numel(k_scale) != 1 || numel(v_scale) != 1)
+    return fail(PA_ERR_SHAPE, "k_scale and v_scale must hold one element");
+  if (S > INT32_MAX || Hq > INT32_MAX || Hkv > INT32_MAX || W > INT32_MAX || Hkv == 0)
+    return fail(PA_ERR_SHAPE, "sizes out of range");
+  // layouts (strides in elements)
+  if (stride_or(q, 2, 1) != 1 || stride_or(q, 1, D) != D)
+    return fail(PA_ERR_LAYOUT, "q's rows [num_heads, head_size] must be dense");
+  if (stride_or(out, 2, 1) != 1 || stride_or(out, 1, D) != D || stride_or(out, 0, Hq * D) != Hq * D)
+    return fail(PA_ERR_LAYOUT, "out must be dense");
+  if (stride_or(k_cache, 4, 1) != 1 || stride_or(k_cache, 3, 16) != 16 || stride_or(k_cache, 2, 256) != 256)
+    return fail(PA_ERR_LAYOUT, "k_cache's pages [head_size/16, 16, 16] must be dense");
+  if (stride_or(v_cache, vd + 1, 1) != 1 || stride_or(v_cache, vd, BS) != BS)
+    return fail(PA_ERR_LAYOUT, "v_cache's pages [head_size, block_size] must be dense");
+  const int64_t page = D * BS;
+  const int64_t kb = stride_or(k_cache, 0, Hkv * page), kh = stride_or(k_cache, 1, page);
+  const int64_t vb = stride_or(v_cache, 0, Hkv * page), vh = stride_or(v_cache, 1, page);
+  if (kb != vb || kh != vh)
+    return fail(PA_ERR_LAYOUT, "k_cache and v_cache must have the same block and kv-head strides");
+  if (stride_or(block_tables, 1, 1) != 1)
+    return fail(PA_ERR_LAYOUT, "block_tables' rows must be dense");
+  if (stride_or(seq_lens, 0, 1) != 1) return fail(PA_ERR_LAYOUT, "seq_lens must be dense");
+  Variant var;
+  var.block_stride = kb;
+  var.head_stride = kh;
+  var.q_row_stride = stride_or(q, 0, Hq * D);
+  var.bt_row_stride = stride_or(block_tables, 0, W);
+  return decode(q->data, k_cache->data, v_cache->data, (const int32_t*)block_tables->data,
+                (const int32_t*)seq_lens->data, (int32_t)S, (int32_t)Hq, (int32_t)Hkv, (int32_t)D,
+                (int32_t)BS, (int32_t)W, NB, scale, (const float*)k_scale->data,
+                (const float*)v_scale->data, out->data, stream, 0, var);
+}
 
 int paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
@@ -553,12 +701,48 @@ int pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
   return PA_OK;
 }
 
-int pa_decode_reserve_workspace(size_t bytes) {
+int pa_workspace_bytes(int32_t num_seqs, int32_t num_q_tokens, int32_t max_seqlen_q,
+                       int32_t num_heads, int32_t num_kv_heads, int32_t max_blocks_per_seq,
+                       int32_t longest_first, int32_t token_rows, int device, size_t* bytes) {
   g_last_error[0] = '\0';
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice failed");
+  if (!bytes) return fail(PA_ERR_NULL, "bytes is NULL");
+  *bytes = 0;
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_blocks_per_seq < 0 ||
+      num_q_tokens < 0 || max_seqlen_q < 0 || num_heads % num_kv_heads != 0)
+    return fail(PA_ERR_SHAPE, "bad sizes (num_seqs=%d num_q_tokens=%d max_seqlen_q=%d num_heads=%d "
+                              "num_kv_heads=%d max_blocks_per_seq=%d)",
+                num_seqs, num_q_tokens, max_seqlen_q, num_heads, num_kv_heads, max_blocks_per_seq);
+  if (num_heads / num_kv_heads > pa::kMaxGroup)
+    return fail(PA_ERR_UNSUPPORTED, "group size %d exceeds %d", num_heads / num_kv_heads, pa::kMaxGroup);
+  const bool mq = num_q_tokens > 0;
+  if (num_seqs == 0 || (mq && max_seqlen_q == 0)) return PA_OK;
+  int cus = kDefaultCUs;
+  if (device >= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || n <= 0)
+      return fail(PA_ERR_HIP, "cannot read the compute-unit count of device %d", device);
+    cus = n;
+  }
+  CallPlan cp;
+  const int rc = plan_call(num_seqs, num_heads, num_kv_heads, max_blocks_per_seq, cus, 0, mq,
+                           mq ? num_q_tokens : num_seqs, mq ? max_seqlen_q : 1, longest_first != 0,
+                           token_rows != 0, &cp);
+  if (rc) return rc;
+  *bytes = cp.plan.workspace_bytes;
+  return PA_OK;
+}
+
+int pa_workspace_reserve(int device, void* stream, size_t bytes) {
+  g_last_error[0] = '\0';
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice failed");
+  if (device != cur && hipSetDevice(device) != hipSuccess)
+    return fail(PA_ERR_HIP, "hipSetDevice(%d) failed", device);
   void* p = nullptr;
-  return ensure_workspace(dev, bytes, nullptr, false, &p);
+  const int rc = bytes ? ensure_workspace(device, (hipStream_t)stream, bytes, &p) : PA_OK;
+  if (device != cur && hipSetDevice(cur) != hipSuccess && rc == PA_OK)
+    return fail(PA_ERR_HIP, "hipSetDevice(%d) failed", cur);
+  return rc;
 }
 
 int paged_kv_cache_write(const void* key, const void* value, int64_t key_token_stride,
@@ -585,10 +769,10 @@ int paged_kv_cache_write(const void* key, const void* value, int64_t key_token_s
                 "token strides (%lld, %lld) must be even and at least num_kv_heads * 128 = %lld",
                 (long long)key_token_stride, (long long)value_token_stride, (long long)row);
   if (num_blocks == 0) return fail(PA_ERR_SHAPE, "num_blocks must be positive");
-  // one workgroup per (16 tokens, kv head): keep the grid within 2^31 - 1
+  // one 64-lane workgroup per (16 tokens, kv head): keep the grid within 2^32 lanes
   const int64_t cw_items = ((int64_t)num_tokens + pa::kBlockTokens - 1) / pa::kBlockTokens * num_kv_heads;
-  if (cw_items > INT32_MAX)
-    return fail(PA_ERR_UNSUPPORTED, "launch too large: %lld work items (16 tokens x kv head)",
+  if (cw_items > (int64_t(1) << 26))
+    return fail(PA_ERR_UNSUPPORTED, "launch too large: %lld work items (16 tokens x kv head; at most 2^26)",
                 (long long)cw_items);
   if (((uintptr_t)key & 3) || ((uintptr_t)value & 3) || ((uintptr_t)k_cache & 1) ||
       ((uintptr_t)slot_mapping & 7))

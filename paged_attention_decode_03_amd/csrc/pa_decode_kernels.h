@@ -14,16 +14,18 @@ constexpr int kMaxGroup = 16;                         // query heads per kv head
 constexpr int kMaxPagesPerPart = 256;                 // blocks per work item (LDS id buffer)
 
 struct DecodeParams {
-  const uint16_t* q;         // bf16 [S][Hq][128]
-  const uint8_t* k_cache;    // fp8  [NB][Hkv][8][16][16]
-  const uint8_t* v_cache;    // fp8  [NB][Hkv][128][16]
-  const int32_t* block_tables;  // [S][W]
+  const uint16_t* q;         // bf16 rows of [Hq][128], q_row_stride elements apart
+  const uint8_t* k_cache;    // fp8 pages [8][16][16] (or token rows, below)
+  const uint8_t* v_cache;    // fp8 pages [128][16]
+  const int32_t* block_tables;  // [S] rows of W entries, bt_row_stride elements apart
   const int32_t* seq_lens;      // [S]
+  int64_t q_row_stride;      // elements between consecutive q rows (>= Hq * 128)
+  int64_t bt_row_stride;     // elements between consecutive block-table rows (>= W)
   const float* k_scale;      // [1] (per-tensor scales)
   const float* v_scale;      // [1]
   const float* k_slot_scales;  // [NB][Hkv][16] per-slot scales, or null for per-tensor
   const float* v_slot_scales;
-  uint16_t* out;             // bf16 [S][Hq][128]
+  uint16_t* out;             // bf16 [rows][Hq][128], dense
   float* part_acc;           // [S][Hq][P][128] unnormalised partial outputs (P > 1 only)
   float* part_ml;            // [S][Hq][P][2]   (running max in log2 units, sum of weights)
   int32_t num_seqs;
@@ -50,9 +52,10 @@ struct DecodeParams {
   float scale;               // softmax scale (natural units, for the softcap)
   const float* alibi_slopes;  // [Hq]: logit + slope * (t - p)
   const float* sinks;         // [Hq]: extra softmax term exp(sink) with no value
-  // token-row cache layout (token_rows != 0): token j of kv head k in block p
-  // has its 128 dims at p * block_stride + j * token_stride + k * head_stride
-  // bytes from k_cache / v_cache
+  // cache addressing, bytes from k_cache / v_cache: the page of kv head k in
+  // block p at p * block_stride + k * head_stride (page layout); with token
+  // rows (token_rows != 0), token j's 128 dims at p * block_stride +
+  // j * token_stride + k * head_stride
   int32_t token_rows;
   int32_t kv_group;          // token rows: kv heads per workgroup (divides num_kv_heads, <= 8)
   int64_t block_stride;

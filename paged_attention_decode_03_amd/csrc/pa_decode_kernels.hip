@@ -149,10 +149,12 @@ __device__ __forceinline__ float max_over_rows(float x) {
 }
 
 // The value lane I of this lane's quad (lanes 4k .. 4k + 3) holds (DPP quad
-// broadcast).
+// broadcast).  Every lane of a quad is a valid source, so with all rows and
+// banks enabled no lane keeps `old`; it is still given (0), so that no lane
+// can ever read an undefined register.
 template <int I>
 __device__ __forceinline__ uint32_t quad_lane(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x55 * I, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x55 * I, 0xF, 0xF, false);
 }
 
 // The four values lanes 0..3 of this lane's quad hold.
@@ -269,12 +271,13 @@ struct Stage {
 };
 
 // SS: per-slot scale tables instead of per-tensor scales.  K scales multiply
-// the logits token by token; V scales multiply the fp16 weights that feed PV
-// (the denominator keeps the plain weights).  So that p * v_scale stays in
-// fp16's normal range, every weight of a work item is also multiplied by one
-// exact power of two, 2^-e with e the exponent of the item's first V scale,
-// and the epilogue divides it out exactly.  (Scales more than 2^14 above the
-// first one would saturate the fp16 weights.)
+// the logits token by token.  A V scale v_t = f_t 2^E_t (f_t in [0.5, 1))
+// enters the numerator's weights: token t's numerator weight is
+// 2^(z_t + E_t - mv) f_t, where mv is a running max of z_t + E_t (kept next to
+// the denominator's running max m of z_t, with its own rescale of the
+// accumulator), so every fp16 weight lies in [0, 1) and the largest term of
+// the numerator has a weight of at least 1/2, whatever the spread of the
+// scales.  The epilogue multiplies by 2^(mv - m).
 // MQ: several query tokens per sequence (rows cu_seqlens_q[s] ..), causal.  The
 // 16 MFMA columns then hold (query token, head) pairs: q_tile tokens of the
 // tile times the group's heads.  Query i of a sequence with L tokens and q_len
@@ -376,7 +379,7 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
   const int h = kvh * p.group + g;
   int qrow[NT];      // row of q and out
   bool hvalid[NT];   // the column holds a query of this sequence
-  size_t orow[NT];
+  size_t orow[NT];    // element offset of the row in out (dense)
 #pragma unroll
   for (int u = 0; u < NT; ++u) {
     const int qt = qt0 + u;
@@ -391,7 +394,7 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
   // partition's slice of the block-table row (its length is not known yet, so
   // entries past the context are read too and discarded below), the sequence
   // length, and q.
-  const int32_t* bt = p.block_tables + (size_t)s * p.max_blocks;
+  const int32_t* bt = p.block_tables + (size_t)s * p.bt_row_stride;
   const int span = min(ppp, p.max_blocks - pbeg);
   int32_t idv[kMaxPagesPerPart / 64];
 #pragma unroll
@@ -404,7 +407,7 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
 #pragma unroll
   for (int u = 0; u < NT; ++u) {
     if (hvalid[u]) {
-      const uint16_t* qp = p.q + orow[u];
+      const uint16_t* qp = p.q + (size_t)qrow[u] * p.q_row_stride + (size_t)h * kHeadDim;
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
@@ -486,8 +489,8 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
   const float cap_l2 = MQ ? p.softcap * kLog2e : 0.0f;
   const bool biased = MQ && p.alibi_slopes != nullptr;
 
-  const size_t page_stride = TR ? (size_t)p.block_stride : (size_t)p.num_kv_heads * kPageBytes;
-  const size_t head_off = TR ? (size_t)kvh * p.head_stride : (size_t)kvh * kPageBytes;
+  const size_t page_stride = (size_t)p.block_stride;
+  const size_t head_off = (size_t)kvh * p.head_stride;
   const uint8_t* kpage0 = p.k_cache + head_off;
   const uint8_t* vpage0 = p.v_cache + head_off;
   // K: token lane & 15, chunks lane >> 4 (koff) and 4 + (lane >> 4) (koff + khi)
@@ -519,7 +522,7 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
     }
   }
   const f16x4 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
-  float vnorm = 1.0f, vnorm_inv = 1.0f;  // per-slot variant: power-of-two weight factor
+  float mv_run = -INFINITY;  // per-slot variant: running max of z + E(v_scale), the numerator's
 
   // The partition's physical block ids, staged in LDS.  A load of a page past
   // the partition gets a buffer descriptor of zero bytes: it is still issued
@@ -731,22 +734,39 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
       const float m_new = fmaxf(m_run[u], mx);
       if (__builtin_amdgcn_ballot_w64(m_new > m_run[u])) {
         const float alpha = (m_new == m_run[u]) ? 1.0f : __builtin_amdgcn_exp2f(m_run[u] - m_new);
+        if constexpr (!SS) {  // (per-slot: the numerator has a running max of its own)
 #pragma unroll
-        for (int jd = 0; jd < 8; ++jd) acc[u][jd] *= alpha;
+          for (int jd = 0; jd < 8; ++jd) acc[u][jd] *= alpha;
+        }
         accl[u] *= alpha;
         m_run[u] = m_new;
       }
     }
     // P = 2^(z - m) in fp16, then PV
+    // per-slot V scales v = f 2^E: the numerator's logits z + E, their running
+    // max, and the accumulator rescaled when it grows
+    float zv[SS ? PPS : 1][4], vf[SS ? PPS : 1][4];
     if constexpr (SS) {
-      if (stage == 0) {
-        // 2^-e for the exponent e of the item's first V scale (token 0 is always
-        // in the context); clamped so that the factor and its inverse are normal,
-        // and 1 when that scale is zero or subnormal (e.g. a page read as zeros)
-        const uint32_t e0 = (__builtin_amdgcn_readfirstlane(st.vs[0]) >> 23) & 0xFFu;  // lane 0: slot 0
-        const uint32_t eb = e0 == 0u ? 127u : min(e0, 253u);
-        vnorm = __uint_as_float((254u - eb) << 23);
-        vnorm_inv = __uint_as_float(eb << 23);
+      float mxv = -INFINITY;
+#pragma unroll
+      for (int pp = 0; pp < PPS; ++pp) {
+        const u32x4 vsq = quad_gather(st.vs[pp]);  // the lane's four slots' V scales
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float vsc = __uint_as_float(vsq[i]);
+          vf[pp][i] = __builtin_amdgcn_frexp_mantf(vsc);
+          // a zero scale adds exactly nothing: it must not set the numerator's max
+          zv[pp][i] = vf[pp][i] == 0.0f ? -INFINITY : z[0][pp][i] + (float)__builtin_amdgcn_frexp_expf(vsc);
+          mxv = fmaxf(mxv, zv[pp][i]);
+        }
+      }
+      mxv = max_over_rows(mxv);
+      const float mv_new = fmaxf(mv_run, mxv);
+      if (__builtin_amdgcn_ballot_w64(mv_new > mv_run)) {
+        const float beta = (mv_new == mv_run) ? 1.0f : __builtin_amdgcn_exp2f(mv_run - mv_new);
+#pragma unroll
+        for (int jd = 0; jd < 8; ++jd) acc[0][jd] *= beta;
+        mv_run = mv_new;
       }
     }
 #pragma unroll
@@ -758,14 +778,14 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
         vmask = nv >= 4 ? 0xFFFFFFFFu : (nv <= 0 ? 0u : ((1u << (8 * nv)) - 1u));
       }
       if constexpr (SS) {
-        const u32x4 vsq = quad_gather(st.vs[pp]);  // the lane's four slots' V scales
         f16x4 pb, pv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float e = __builtin_amdgcn_exp2f(z[0][pp][i] - m_run[0]);
           pb[i] = (_Float16)e;
-          // masked tokens have e == 0; their scale may be NaN and must not reach PV
-          const float w = e == 0.0f ? 0.0f : fminf(e * __uint_as_float(vsq[i]) * vnorm, 65504.0f);
+          // 2^(z + E - mv) f in [0, 1); tokens past the context (z = -inf; their
+          // scale may be NaN) and zero scales give 0 (mv may still be -inf)
+          const float w = zv[pp][i] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(zv[pp][i] - mv_run) * vf[pp][i];
           pv[i] = (_Float16)w;
         }
 #pragma unroll
@@ -854,7 +874,9 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
     const float lsum = accl[u][0];
     if (direct) {
       // several queries: lsum is 0 for a query that sees no token (more queries than context)
-      const float inv = (!MQ || lsum > 0.0f) ? (SS ? vnorm_inv : scalar_load(p.v_scale)) / lsum : 0.0f;
+      const float inv = (!MQ || lsum > 0.0f)
+                            ? (SS ? __builtin_amdgcn_exp2f(mv_run - m_run[u]) : scalar_load(p.v_scale)) / lsum
+                            : 0.0f;
       uint16_t* o = p.out + orow[u] + rq * 4;
 #pragma unroll
       for (int jd = 0; jd < 8; ++jd) {
@@ -874,13 +896,15 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
       // (wave-uniform), lrow the lane's head; offsets below 16 x P x 512 bytes
       const size_t rbase = ((size_t)s * p.num_heads + (size_t)kvh * p.group) * p.num_parts;
       const int lrow = g * p.num_parts + part;
+      // per-slot scales: the numerator relative to the denominator's max m
+      const float vfold = SS ? __builtin_amdgcn_exp2f(mv_run - m_run[u]) : 1.0f;
       const auto ra = __builtin_amdgcn_make_buffer_rsrc((void*)(p.part_acc + rbase * kHeadDim), (short)0, 0x7FFFFFF0,
                                                         kRsrcWord3);
       const auto rm = __builtin_amdgcn_make_buffer_rsrc((void*)(p.part_ml + rbase * 2), (short)0, 0x7FFFFFF0,
                                                         kRsrcWord3);
 #pragma unroll
       for (int jd = 0; jd < 8; ++jd)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[u][jd] * vnorm_inv), ra,
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[u][jd] * vfold), ra,
                                                (lrow * kHeadDim + rq * 4 + jd * 16) * 4, 0, kAuxSc1);
       if (rq == 0)
         __builtin_amdgcn_raw_buffer_store_b64(

@@ -52,7 +52,8 @@ def bf16_ulp(x):
     return 2.0 ** (np.floor(np.log2(a)) - 7)
 
 
-def compare(gpu_out, ref, label, seqs=None, max_abs=MAX_ABS, mean_abs=MEAN_ABS, relative=False):
+def compare(gpu_out, ref, label, seqs=None, max_abs=MAX_ABS, mean_abs=MEAN_ABS, relative=False,
+            term_scale=None):
     """Check bf16 GPU output against the fp64 oracle.
 
     Max bound, element by element: |gpu - oracle| <= 1e-2 wherever a bf16
@@ -69,6 +70,11 @@ def compare(gpu_out, ref, label, seqs=None, max_abs=MAX_ABS, mean_abs=MEAN_ABS, 
     relative=True (workloads whose outputs are far larger than N(0,1) data's,
     e.g. per-token magnitudes spread over 2^8): every error is divided by
     max(1, |oracle|) before the same bounds are applied.
+
+    term_scale (same shape as ref: the magnitude of the terms each output
+    sums, sum_t p_t |V_t|, from the oracle): every error is divided by
+    max(1, term_scale) instead, for data whose terms spread so far that an
+    output can be a near cancellation of much larger terms.
     """
     g = gpu_out.float().cpu().double().numpy()
     if seqs is not None:
@@ -80,10 +86,18 @@ def compare(gpu_out, ref, label, seqs=None, max_abs=MAX_ABS, mean_abs=MEAN_ABS, 
     floor = np.abs(rne - ref)
     err_rne = np.abs(g - rne)
     ulp = bf16_ulp(ref)
-    denom = np.maximum(1.0, np.abs(ref)) if relative else np.ones_like(ref)
+    if term_scale is not None:
+        ts = np.asarray(term_scale, dtype=np.float64)
+        if seqs is not None and ts.shape != ref.shape:
+            ts = ts[np.asarray(seqs)]
+        assert ts.shape == ref.shape and (ts >= np.abs(ref) * (1 - 1e-12)).all(), "term_scale below |out|"
+        denom = np.maximum(1.0, ts)
+    else:
+        denom = np.maximum(1.0, np.abs(ref)) if relative else np.ones_like(ref)
     err_s, floor_s, err_rne_s = err / denom, floor / denom, err_rne / denom
     reach = floor_s <= max_abs
-    log(f"[{label}]{' (relative)' if relative else ''} vs fp64: max={err_s.max():.3e} mean={err_s.mean():.3e} | "
+    mode = " (relative to the terms)" if term_scale is not None else (" (relative)" if relative else "")
+    log(f"[{label}]{mode} vs fp64: max={err_s.max():.3e} mean={err_s.mean():.3e} | "
         f"vs bf16(oracle): max={err_rne_s.max():.3e} mean={err_rne_s.mean():.3e} | "
         f"bf16 floor: max={floor_s.max():.3e} mean={floor_s.mean():.3e} | "
         f"beyond reach of 1e-2: {int((~reach).sum())} | n={err.size}")

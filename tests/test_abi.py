@@ -27,8 +27,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("paged_decode_attention", "paged_decode_attention_split", "pa_decode_plan",
-              "pa_decode_reserve_workspace", "paged_kv_cache_write",
+    for n in ("paged_decode_attention", "paged_decode_attention_desc",
+              "paged_decode_attention_split", "pa_decode_plan", "pa_workspace_bytes",
+              "pa_workspace_reserve", "paged_kv_cache_write",
               "paged_decode_attention_slot_scales", "paged_multi_query_attention",
               "paged_decode_attention_nhd", "paged_attention_unified", "pa_last_error"):
         assert n in names
@@ -149,9 +150,11 @@ def test_cache_write_rejects_bad_arguments(lib, kw, code):
 
 
 def test_cache_write_rejects_a_grid_past_its_limit(lib):
-    # 2^31 - 1 tokens x 32 kv heads: 2^32 groups of 16 tokens x kv head
-    assert cw(lib, T=2**31 - 1, Hkv=32, ks_=4096, vs_=4096) == -3
+    # one 64-lane workgroup per (16 tokens, kv head), within a 2^32-lane grid:
+    # at most 2^26 workgroups; 2^30 + 16 tokens x 1 kv head is one too many
+    assert cw(lib, T=2**30 + 16, Hkv=1, ks_=128, vs_=128) == -3
     assert "too large" in lib.pa_last_error().decode()
+    assert cw(lib, T=2**31 - 1, Hkv=32, ks_=4096, vs_=4096) == -3
 
 
 def test_cache_write_empty_is_a_noop(lib):
@@ -228,3 +231,159 @@ def test_unified_option_checks(lib):
     assert unified(lib, sinks=FAKE * 80 + 1) == -2
     assert unified(lib, sinks=FAKE * 64 + 64) == -4       # inside out
     assert unified(lib, cu=0, T=3) == -2                  # one query per sequence: T must be 2
+
+
+# ----------------------------------------------------------------------------
+# tensor descriptors: every status code through ctypes, no device touched
+# (a call that passes every check reaches HIP, which reports PA_ERR_HIP on a
+# machine without a GPU)
+
+def desc(data, dtype, sizes, strides=None, ndim=None):
+    import paged_attention_decode_03_amd as pa
+    if strides is None:
+        strides, acc = [], 1
+        for n in reversed(sizes):
+            strides.insert(0, acc)
+            acc *= n
+    d = pa.Tensor()
+    d.data, d.dtype, d.ndim = data, dtype, len(sizes)
+    for i, (n, st) in enumerate(zip(sizes, strides)):
+        d.sizes[i], d.strides[i] = n, st
+    if ndim is not None:
+        d.ndim = ndim
+    return d
+
+
+BF16, FP8, U8, I32, F32 = 1, 2, 3, 4, 5
+
+
+def dcall(lib, **over):
+    S, Hq, Hkv, NB, W = 2, 8, 2, 16, 4
+    t = dict(
+        q=desc(FAKE, BF16, [S, Hq, 128]),
+        k=desc(FAKE * 16, FP8, [NB, Hkv, 8, 16, 16]),
+        v=desc(FAKE * 32, U8, [NB, Hkv, 128, 16]),
+        bt=desc(FAKE * 48, I32, [S, W]),
+        sl=desc(FAKE * 50, I32, [S]),
+        ks=desc(FAKE * 52, F32, [1]),
+        vs=desc(FAKE * 53, F32, []),
+        out=desc(FAKE * 64, BF16, [S, Hq, 128]),
+    )
+    scale = over.pop("scale", 0.088)
+    t.update(over)
+    ref = lambda x: None if x is None else ctypes.byref(x)
+    return lib.paged_decode_attention_desc(ref(t["q"]), ref(t["k"]), ref(t["v"]), ref(t["bt"]),
+                                           ref(t["sl"]), ctypes.c_float(scale), ref(t["ks"]),
+                                           ref(t["vs"]), ref(t["out"]), None)
+
+
+@pytest.mark.parametrize("name,over,code", [
+    ("null descriptor", dict(k=None), -1),
+    ("null data", dict(q=desc(0, BF16, [2, 8, 128])), -1),
+    ("q fp32", dict(q=desc(FAKE, F32, [2, 8, 128])), -7),
+    ("out fp32", dict(out=desc(FAKE * 64, F32, [2, 8, 128])), -7),
+    ("k bf16", dict(k=desc(FAKE * 16, BF16, [16, 2, 8, 16, 16])), -7),
+    ("table int64", dict(bt=desc(FAKE * 48, 6, [2, 4])), -7),
+    ("scale bf16", dict(ks=desc(FAKE * 52, BF16, [1])), -7),
+    ("q rank", dict(q=desc(FAKE, BF16, [2, 1024])), -2),
+    ("rank past 5", dict(q=desc(FAKE, BF16, [2, 8, 128], ndim=6)), -2),
+    ("negative stride", dict(q=desc(FAKE, BF16, [2, 8, 128], [-1024, 128, 1])), -2),
+    ("out sizes", dict(out=desc(FAKE * 64, BF16, [2, 8, 64])), -2),
+    ("k inner sizes", dict(k=desc(FAKE * 16, FP8, [16, 2, 4, 16, 32])), -2),
+    ("v sizes", dict(v=desc(FAKE * 32, U8, [16, 1, 128, 16])), -2),
+    ("v 5-D middle", dict(v=desc(FAKE * 32, U8, [16, 2, 2, 64, 16])), -2),
+    ("table rows", dict(bt=desc(FAKE * 48, I32, [3, 4])), -2),
+    ("seq_lens size", dict(sl=desc(FAKE * 50, I32, [3])), -2),
+    ("two scales", dict(ks=desc(FAKE * 52, F32, [2])), -2),
+    ("head_size 64", dict(q=desc(FAKE, BF16, [2, 8, 64]), out=desc(FAKE * 64, BF16, [2, 8, 64])), -3),
+    ("block_size 32", dict(k=desc(FAKE * 16, FP8, [16, 2, 8, 32, 16])), -3),
+    ("group 32", dict(q=desc(FAKE, BF16, [2, 64, 128]), out=desc(FAKE * 64, BF16, [2, 64, 128])), -3),
+    ("q heads not dense", dict(q=desc(FAKE, BF16, [2, 8, 128], [2048, 256, 1])), -8),
+    ("q dims strided", dict(q=desc(FAKE, BF16, [2, 8, 128], [2048, 256, 2])), -8),
+    ("q row stride odd", dict(q=desc(FAKE, BF16, [2, 8, 128], [1028, 128, 1])), -8),
+    ("out strided", dict(out=desc(FAKE * 64, BF16, [2, 8, 128], [2048, 128, 1])), -8),
+    ("k page not dense", dict(k=desc(FAKE * 16, FP8, [16, 2, 8, 16, 16], [4096, 2048, 256, 32, 1])), -8),
+    ("v page not dense", dict(v=desc(FAKE * 32, U8, [16, 2, 128, 16], [4096, 2048, 32, 1])), -8),
+    ("K/V strides differ", dict(v=desc(FAKE * 32, U8, [16, 2, 128, 16], [8192, 2048, 16, 1])), -8),
+    ("block stride not 16", dict(k=desc(FAKE * 16, FP8, [16, 2, 8, 16, 16], [4104, 2048, 256, 16, 1]),
+                                 v=desc(FAKE * 32, U8, [16, 2, 128, 16], [4104, 2048, 16, 1])), -8),
+    ("table columns strided", dict(bt=desc(FAKE * 48, I32, [2, 4], [8, 2])), -8),
+    ("table row stride short", dict(bt=desc(FAKE * 48, I32, [2, 4], [3, 1])), -8),
+    ("seq_lens strided", dict(sl=desc(FAKE * 50, I32, [2], [2])), -8),
+    ("out over q", dict(out=desc(FAKE + 256, BF16, [2, 8, 128])), -4),
+    ("out over a strided table", dict(bt=desc(FAKE * 48, I32, [2, 4], [1 << 20, 1]),
+                                      out=desc(FAKE * 48 + 2 * (1 << 20), BF16, [2, 8, 128])), -4),
+    ("q misaligned", dict(q=desc(FAKE + 8, BF16, [2, 8, 128])), -2),
+    ("scale inf", dict(scale=float("inf")), -2),
+])
+def test_descriptor_status_codes(lib, name, over, code):
+    assert dcall(lib, **over) == code, name
+    assert lib.pa_last_error().decode() != ""
+
+
+def test_descriptor_accepts_free_strides_and_views(lib):
+    """Everything the descriptor form allows passes every host check and
+    reaches HIP (which, without a GPU, fails with PA_ERR_HIP, not a check's
+    code)."""
+    import torch
+    cases = [
+        {},
+        # q rows apart by more than a row; block-table rows padded; 5-D V view
+        dict(q=desc(FAKE, BF16, [2, 8, 128], [2048, 128, 1]),
+             bt=desc(FAKE * 48, I32, [2, 4], [16, 1]),
+             v=desc(FAKE * 32, FP8, [16, 2, 1, 128, 16])),
+        # caches as halves of one [NB, 2, Hkv, page] tensor: block stride 2 * Hkv * 2048
+        dict(k=desc(FAKE * 16, FP8, [16, 2, 8, 16, 16], [8192, 2048, 256, 16, 1]),
+             v=desc(FAKE * 16 + 4096, FP8, [16, 2, 128, 16], [8192, 2048, 16, 1])),
+        # size-1 dims with arbitrary strides
+        dict(q=desc(FAKE, BF16, [1, 8, 128], [7, 128, 1]), bt=desc(FAKE * 48, I32, [1, 4], [3, 1]),
+             sl=desc(FAKE * 50, I32, [1], [9]), out=desc(FAKE * 64, BF16, [1, 8, 128], [5, 128, 1])),
+    ]
+    has_gpu = torch.cuda.is_available()
+    for over in cases:
+        rc = dcall(lib, **over)
+        assert rc in ((0,) if has_gpu else (-6,)), (over.keys(), rc, lib.pa_last_error().decode())
+
+
+def test_descriptor_empty_batch_is_a_noop(lib):
+    assert dcall(lib, q=desc(FAKE, BF16, [0, 8, 128]), out=desc(FAKE * 64, BF16, [0, 8, 128]),
+                 bt=desc(FAKE * 48, I32, [0, 4]), sl=desc(FAKE * 50, I32, [0])) == 0
+
+
+# ----------------------------------------------------------------------------
+# workspace queries (host only with device = -1)
+
+def wsb(lib, S, Hq, Hkv, W, T=0, maxq=0, lpt=0, tr=0, dev=-1):
+    n = ctypes.c_size_t(12345)
+    rc = lib.pa_workspace_bytes(S, T, maxq, Hq, Hkv, W, lpt, tr, dev, ctypes.byref(n))
+    return rc, n.value
+
+
+def test_workspace_bytes_matches_the_decode_plan(lib):
+    for S, Hq, Hkv, W in [(16, 40, 8, 64), (24, 32, 8, 256), (1, 40, 8, 2048), (256, 40, 8, 256),
+                          (300, 8, 1, 256)]:
+        assert wsb(lib, S, Hq, Hkv, W) == (0, plan(lib, S, Hq, Hkv, W)[3])
+
+
+def test_workspace_bytes_covers_several_queries_and_longest_first(lib):
+    # 4 sequences x 4 queries at 40/8 (G = 5: 3 queries a tile, 2 tiles, one
+    # item of two tiles): 32 units -> 32 partitions of 8 blocks per tile group
+    rc, n = wsb(lib, 4, 40, 8, 256, T=16, maxq=4)
+    rc1, P, ppp, _ = plan(lib, 4, 40, 8, 256)
+    assert rc == 0 and n == 4096 + 16 * 40 * P * 130 * 4
+    # longest-first over 1000 sequences (more than a work item sorts itself):
+    # the order kernel's 4 bytes a sequence after the 256-byte aligned partials
+    rc, n = wsb(lib, 1000, 8, 1, 64, lpt=1)
+    assert rc == 0 and n == 4096 + 1000 * 4
+    # up to 512 sequences the work items sort by themselves: no scratch
+    assert wsb(lib, 300, 16, 1, 128, lpt=1)[1] == plan(lib, 300, 16, 1, 128)[3]
+    # token rows never sort inside the work items
+    assert wsb(lib, 300, 16, 1, 128, lpt=1, tr=1)[1] > plan(lib, 300, 16, 1, 128)[3]
+
+
+def test_workspace_bytes_rejects_bad_shapes(lib):
+    assert wsb(lib, -1, 8, 2, 4)[0] == -2
+    assert wsb(lib, 2, 9, 2, 4)[0] == -2
+    assert wsb(lib, 2, 64, 2, 4)[0] == -3
+    assert wsb(lib, 0, 8, 2, 4) == (0, 0)
+    assert lib.pa_workspace_bytes(2, 0, 0, 8, 2, 4, 0, 0, -1, None) == -1

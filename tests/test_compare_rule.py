@@ -39,3 +39,17 @@ def test_relative_mode_scales_by_magnitude():
     compare(bf16([300.0]), ref, "relative", relative=True)
     with pytest.raises(AssertionError):
         compare(bf16([304.0]), ref, "relative, far", relative=True, mean_abs=1.0)
+
+
+def test_term_scale_mode_scales_by_the_terms_magnitude():
+    # an output of 4 that cancels terms of magnitude 3000: an error of 2 is
+    # 2 / 3000 < 1e-2 of the terms, but half the output
+    ref = np.array([4.0])
+    compare(bf16([6.0]), ref, "cancellation", term_scale=np.array([3000.0]), mean_abs=1.0)
+    with pytest.raises(AssertionError):
+        compare(bf16([6.0]), ref, "same error without the terms", relative=True, mean_abs=1.0)
+    with pytest.raises(AssertionError):
+        compare(bf16([40.0]), ref, "36 / 3000 > 1e-2", term_scale=np.array([3000.0]), mean_abs=1.0)
+    # a term scale below |out| cannot be a sum of |terms|
+    with pytest.raises(AssertionError):
+        compare(bf16([4.0]), ref, "bad term scale", term_scale=np.array([1.0]))

@@ -163,6 +163,8 @@ def test_graph_capture_replays_match_eager():
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
+        step()   # eager on the capture stream: sizes that stream's split-KV scratch
+        torch.cuda.synchronize()
         with torch.cuda.graph(g, stream=s):
             step()
     torch.cuda.synchronize()
@@ -181,12 +183,19 @@ def test_graph_capture_replays_match_eager():
 def test_binding_rejects_bad_cu_seqlens():
     import paged_attention_decode_03_amd as pa
     case = workloads.make_multi_case(8, 2, [10, 20], [2, 3], seed=62).to("cuda")
-    with pytest.raises(TypeError):
+    ks = torch.tensor([case.k_scale], device="cuda")
+    vs = torch.tensor([case.v_scale], device="cuda")
+    with pytest.raises(TypeError, match="cu_seqlens_q"):
         pa.paged_multi_query_attention(case.q, case.cu_seqlens_q[:-1], 3, case.k_cache,
                                        case.v_cache, case.block_tables, case.seq_lens,
-                                       case.scale, case.k_scale, case.v_scale)
-    with pytest.raises(TypeError):
+                                       case.scale, ks, vs)
+    with pytest.raises(TypeError, match="cu_seqlens_q"):
         pa.paged_multi_query_attention(case.q, case.cu_seqlens_q.to(torch.int64), 3, case.k_cache,
+                                       case.v_cache, case.block_tables, case.seq_lens,
+                                       case.scale, ks, vs)
+    # host floats as scales are refused (a per-call copy a graph cannot replay)
+    with pytest.raises(TypeError, match="host float"):
+        pa.paged_multi_query_attention(case.q, case.cu_seqlens_q, 3, case.k_cache,
                                        case.v_cache, case.block_tables, case.seq_lens,
                                        case.scale, case.k_scale, case.v_scale)
 

@@ -172,6 +172,8 @@ def test_graph_capture_replays_match_eager():
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
+        step()   # eager on the capture stream: sizes that stream's split-KV scratch
+        torch.cuda.synchronize()
         with torch.cuda.graph(g, stream=s):
             step()
     torch.cuda.synchronize()
@@ -249,11 +251,14 @@ def run_gpu_slot(case):
     return out
 
 
-def oracle_slot(case, seqs=None):
+def oracle_slot(case, seqs=None, abs_values=False):
+    """fp64 oracle with per-slot scales; abs_values: on |V| (every V code's
+    sign bit cleared), i.e. sum_t p_t |V_t|, the magnitude of the terms."""
     import oracle
     h = case.host()
     idx = np.arange(h.num_seqs) if seqs is None else np.asarray(seqs)
-    return oracle.decode_slot_scales(h.q_bits()[idx], h.k_cache.numpy(), h.v_cache.numpy(),
+    v = h.v_cache.numpy() & 0x7F if abs_values else h.v_cache.numpy()
+    return oracle.decode_slot_scales(h.q_bits()[idx], h.k_cache.numpy(), v,
                                      h.block_tables.numpy()[idx], h.seq_lens.numpy()[idx],
                                      h.scale, h.k_slot_scales.numpy(), h.v_slot_scales.numpy())
 
@@ -292,6 +297,27 @@ def test_slot_scales_ragged_with_poison():
     compare(out, oracle_slot(case, seqs), "slot scales ragged", seqs, relative=True)
 
 
+@pytest.mark.parametrize("num_seqs", [8, 32, 64], ids=lambda n: f"S{n}")
+def test_slot_scales_spread_far_beyond_fp16(num_seqs):
+    """Per-slot V scales spread over 2^40 within every partition, and each
+    sequence's first token's V scale a further 2^-40 below (its V values are
+    tiny): the fp16 weights must neither saturate nor lose the small terms.
+    8, 32 and 64 sequences at 40/8 take the merge kernel (8 partitions), the
+    merge in the decode (4) and no split.
+
+    With terms this far apart, an output can be a near cancellation of terms
+    hundreds of times larger than itself, so the bound is applied relative to
+    the magnitude of the sum's terms, sum_t p_t |V_t|, which the oracle
+    computes on the same case with every V code's sign cleared."""
+    lens = [(1, 5, 16, 17, 300, 1000, 2048, 4096)[i % 8] for i in range(num_seqs)]
+    case = workloads.make_case(40, 8, lens, seed=64 + num_seqs, scale_mode="per_slot",
+                               slot_log2_span=8, v_slot_log2_span=40, tiny_first_v=True,
+                               max_blocks=256)
+    terms = oracle_slot(case, abs_values=True)
+    compare(run_gpu_slot(case), oracle_slot(case), f"slot scales spread 2^40, S={num_seqs}",
+            term_scale=terms)
+
+
 # ---------------------------------------------------------------- caller errors on the device
 
 def test_block_ids_outside_the_caches_read_as_zero_pages():
@@ -306,8 +332,9 @@ def test_block_ids_outside_the_caches_read_as_zero_pages():
     zero_blk = next(b for b in range(NB) if b not in used)
     case.k_cache[zero_blk] = 0
     case.v_cache[zero_blk] = 0
-    case.k_slot_scales[zero_blk] = 1.0
-    case.v_slot_scales[zero_blk] = 1.0
+    # an id outside the caches reads as an all-zero page: zero K, V and slot scales
+    case.k_slot_scales[zero_blk] = 0.0
+    case.v_slot_scales[zero_blk] = 0.0
     bad_ids = [NB, NB + 7, -1, 2**31 - 1]
     spots = [(0, 1), (1, 0), (1, 3), (2, 2)]    # (sequence, table entry) inside each context
     zero_tab = case.block_tables.clone()
@@ -411,6 +438,9 @@ def test_fused_merge_counters_stay_consistent():
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
+    # the capture stream's split-KV scratch, reserved before capture
+    pa.pa_workspace_reserve(pa.pa_workspace_bytes(c.num_seqs, c.num_heads, c.num_kv_heads,
+                                                  c.max_blocks, device=0), stream=s)
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
             for _ in range(2):
@@ -462,6 +492,9 @@ def test_longest_first_order_covers_every_sequence():
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
+    pa.pa_workspace_reserve(pa.pa_workspace_bytes(case.num_seqs, case.num_heads, case.num_kv_heads,
+                                                  case.max_blocks, longest_first=True, device=0),
+                            stream=s)
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
             pa.paged_attention_unified(case.q, None, 1, *args, longest_first=True, out=out)

@@ -164,6 +164,8 @@ def test_graph_capture_replays_match_eager():
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
+        step()   # eager on the capture stream: sizes that stream's split-KV scratch
+        torch.cuda.synchronize()
         with torch.cuda.graph(g, stream=s):
             step()
     torch.cuda.synchronize()

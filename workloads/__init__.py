@@ -137,13 +137,17 @@ def _quantise_per_slot(x: torch.Tensor, layout: str):
 def make_case(num_heads: int, num_kv_heads: int, seq_lens, seed: int = 0, *,
               device="cpu", max_blocks: int | None = None, extra_blocks: int | None = None,
               scale_mode: str = "amax", poison: bool = True, name: str = "case",
-              softmax_scale: float | None = None) -> Case:
+              softmax_scale: float | None = None, slot_log2_span: float = 8.0,
+              v_slot_log2_span: float | None = None, tiny_first_v: bool = False) -> Case:
     """Build one seeded case.  ``seq_lens`` is a list/tensor of per-sequence token counts.
 
     scale_mode: "amax" / "pow2" (per-tensor scales), or "per_slot": each token's
-    K and V get a random magnitude 2^U(-4, 4) and their own scale amax/448 per
-    (block, kv head, slot), returned as k_slot_scales / v_slot_scales (slots
-    outside every context get NaN scales)."""
+    K and V get a random magnitude 2^U(-span/2, span/2) (span = slot_log2_span,
+    default 8; V's v_slot_log2_span when given) and their own scale amax/448 per
+    (block, kv head, slot), returned
+    as k_slot_scales / v_slot_scales (slots outside every context get NaN
+    scales); tiny_first_v also shrinks every sequence's first token's V by
+    2^-40, so its slot scale sits far below the others."""
     device = torch.device(device)
     g = torch.Generator(device=device)
     g.manual_seed(int(seed))
@@ -176,11 +180,16 @@ def make_case(num_heads: int, num_kv_heads: int, seq_lens, seed: int = 0, *,
     if scale_mode == "per_slot":
         n = NB * num_kv_heads * HEAD_DIM * BLOCK
         kx = torch.randn(n, generator=g, device=device).view(NB, num_kv_heads, 8, BLOCK, 16)
-        kx *= torch.exp2(torch.rand(NB, num_kv_heads, 1, BLOCK, 1, generator=g, device=device) * 8 - 4)
+        span = float(slot_log2_span)
+        kx *= torch.exp2(torch.rand(NB, num_kv_heads, 1, BLOCK, 1, generator=g, device=device) * span - span / 2)
         k_codes, ks_tab = _quantise_per_slot(kx.reshape(NB, num_kv_heads, 2048), "k")
         del kx
         vx = torch.randn(n, generator=g, device=device).view(NB, num_kv_heads, HEAD_DIM, BLOCK)
-        vx *= torch.exp2(torch.rand(NB, num_kv_heads, 1, BLOCK, generator=g, device=device) * 8 - 4)
+        vspan = span if v_slot_log2_span is None else float(v_slot_log2_span)
+        vx *= torch.exp2(torch.rand(NB, num_kv_heads, 1, BLOCK, generator=g, device=device) * vspan - vspan / 2)
+        if tiny_first_v:
+            first = bt[:, 0][lens > 0].to(device=device, dtype=torch.int64)
+            vx[first, :, :, 0] *= 2.0 ** -40
         v_codes, vs_tab = _quantise_per_slot(vx.reshape(NB, num_kv_heads, 2048), "v")
         del vx
         k_scale = v_scale = 1.0
