@@ -91,6 +91,9 @@ typedef struct pa_tensor {
   int64_t strides[PA_MAX_DIMS];
 } pa_tensor;
 
+/* Bytes of the fixed split-KV array of paged_decode_attention_noalloc (per GPU). */
+#define PA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
 /*
  * Paged decode attention (see the top of this file for the operation).
  *
@@ -172,6 +175,32 @@ int paged_decode_attention_split(const void* q, const void* k_cache, const void*
                                  int32_t max_blocks_per_seq, int64_t num_blocks,
                                  float scale, const float* k_scale, const float* v_scale,
                                  void* out, void* stream, int32_t pages_per_partition);
+
+/*
+ * paged_decode_attention_split that allocates nothing: for callers that
+ * cannot call hipMalloc (code under HIP graph capture that must not grow a
+ * scratch, tight serving loops, harnesses that forbid allocation).  The
+ * split-KV partials and arrival counters live in a fixed array of
+ * PA_NOALLOC_SCRATCH_BYTES (16 MiB) in the library's device memory, one copy
+ * per GPU, held until the process ends; the caller passes inputs and out.
+ *   pages_per_partition  as for paged_decode_attention_split; 0 = the
+ *                        library's plan, which needs at most 8.5 MiB on a
+ *                        256-CU MI355X
+ * A call whose plan needs more than the array returns PA_ERR_WORKSPACE and
+ * launches nothing.  All calls on one GPU share its array and find it as the
+ * last call left it (the arrival counters back at zero): calls that overlap
+ * on one GPU (two streams, concurrent graph replays) race and must not be
+ * made.  The first call on a GPU that needs the array also enqueues, on
+ * `stream`, one small kernel that clears its counters.  Otherwise (arguments,
+ * result, errors) as paged_decode_attention_split.
+ */
+int paged_decode_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_tables, const int32_t* seq_lens,
+                                   int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
+                                   int64_t num_blocks, float scale, const float* k_scale,
+                                   const float* v_scale, void* out, void* stream,
+                                   int32_t pages_per_partition);
 
 /*
  * Attention of several new query tokens per sequence over the paged cache,

@@ -26,6 +26,7 @@ import torch
 
 __all__ = [
     "paged_decode_attention", "paged_decode_attention_desc", "paged_decode_attention_split",
+    "paged_decode_attention_noalloc",
     "pa_decode_plan", "pa_workspace_bytes", "pa_workspace_reserve", "paged_kv_cache_write",
     "paged_decode_attention_slot_scales", "paged_multi_query_attention",
     "paged_attention_unified", "paged_decode_attention_nhd", "pa_last_error",
@@ -103,6 +104,8 @@ def load_library():
     lib.paged_decode_attention.restype = ctypes.c_int
     lib.paged_decode_attention_split.argtypes = common + [i32]
     lib.paged_decode_attention_split.restype = ctypes.c_int
+    lib.paged_decode_attention_noalloc.argtypes = common + [i32]
+    lib.paged_decode_attention_noalloc.restype = ctypes.c_int
     lib.paged_decode_attention_slot_scales.argtypes = common
     lib.paged_decode_attention_slot_scales.restype = ctypes.c_int
     lib.paged_multi_query_attention.argtypes = [vp, vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, i32,
@@ -261,6 +264,19 @@ def paged_decode_attention_split(q, k_cache, v_cache, block_tables, seq_lens, sc
                                    v_scale, out, stream)
     with torch.cuda.device(dev):
         _check(lib.paged_decode_attention_split(*c_args, int(pages_per_partition)))
+    return out
+
+
+def paged_decode_attention_noalloc(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale,
+                                   v_scale, pages_per_partition: int = 0, out=None, stream=None):
+    """paged_decode_attention_split whose split-KV scratch is the library's
+    fixed per-GPU array (the C call allocates nothing; pass `out` to allocate
+    nothing here either).  Calls that overlap on one GPU race."""
+    lib = load_library()
+    dev, out, c_args, keep = _args(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale,
+                                   v_scale, out, stream)
+    with torch.cuda.device(dev):
+        _check(lib.paged_decode_attention_noalloc(*c_args, int(pages_per_partition)))
     return out
 
 

@@ -211,6 +211,45 @@ int ensure_workspace(int dev, hipStream_t stream, size_t bytes, void** out) {
   return PA_OK;
 }
 
+}  // namespace
+
+// Split-KV scratch of the allocation-free entry point: a fixed array in the
+// library's device memory (each GPU holds its own copy until the process
+// ends).  In host code `scratch` only stands for the symbol: its device
+// address on each GPU comes from hipGetSymbolAddress, kept per device below.
+static __device__ __align__(256) uint8_t scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::vector<void*> g_fixed_scratch;  // per device: the address of `scratch` there
+
+__global__ void clear_words_kernel(uint32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
+// The device address of `scratch` on `dev` (the current device), looked up
+// once per device.  That first time, the arrival counters at its front are
+// cleared by a small kernel enqueued on `stream` (stream-ordered before the
+// caller's decode; under capture it becomes part of the graph, where
+// clearing counters that every call leaves at zero anyway is harmless).
+int fixed_scratch(int dev, hipStream_t stream, void** out) {
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  if ((int)g_fixed_scratch.size() <= dev) g_fixed_scratch.resize(dev + 1, nullptr);
+  if (!g_fixed_scratch[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(PA_ERR_HIP, "hipGetSymbolAddress of the fixed scratch failed: %s", hipGetErrorString(e));
+    hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(256), 0, stream, (uint32_t*)p,
+                       (int)(kCounterRegion / sizeof(uint32_t)));
+    const hipError_t le = hipGetLastError();
+    if (le != hipSuccess) return fail(PA_ERR_HIP, "clearing the fixed scratch failed: %s", hipGetErrorString(le));
+    g_fixed_scratch[dev] = p;
+  }
+  *out = g_fixed_scratch[dev];
+  return PA_OK;
+}
+
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
   return na && nb && a0 < b0 + nb && b0 < a0 + na;
@@ -263,7 +302,7 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
            const int32_t* seq_lens, int32_t S, int32_t Hq, int32_t Hkv, int32_t head_size,
            int32_t block_size, int32_t W, int64_t NB, float scale, const float* k_scale,
            const float* v_scale, void* out, void* stream_ptr, int32_t ppp_req,
-           const Variant& var = Variant()) {
+           const Variant& var = Variant(), bool use_fixed_scratch = false) {
   const bool slot_scales = var.slot_scales;
   const int32_t* cu_seqlens_q = var.cu_seqlens_q;
   const int32_t num_q_rows = var.num_q_rows;
@@ -466,8 +505,18 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
                          ? 2 : 1;
   if (plan.workspace_bytes) {
     void* ws = nullptr;
-    rc = ensure_workspace(dev, stream, plan.workspace_bytes, &ws);
-    if (rc) return rc;
+    if (use_fixed_scratch) {
+      // the fixed array of the allocation-free entry point: never grown
+      if (plan.workspace_bytes > (size_t)PA_NOALLOC_SCRATCH_BYTES)
+        return fail(PA_ERR_WORKSPACE,
+                    "this plan needs %zu bytes of split-KV scratch; the fixed array holds %zu",
+                    plan.workspace_bytes, (size_t)PA_NOALLOC_SCRATCH_BYTES);
+      rc = fixed_scratch(dev, stream, &ws);
+      if (rc) return rc;
+    } else {
+      rc = ensure_workspace(dev, stream, plan.workspace_bytes, &ws);
+      if (rc) return rc;
+    }
     p.unit_count = (int32_t*)ws;
     if (plan.num_parts > 1) {
       p.part_acc = (float*)((char*)ws + kCounterRegion);
@@ -606,6 +655,18 @@ int paged_decode_attention_split(const void* q, const void* k_cache, const void*
   return decode(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads, num_kv_heads,
                 head_size, block_size, max_blocks_per_seq, num_blocks, scale, k_scale, v_scale, out,
                 stream, pages_per_partition);
+}
+
+int paged_decode_attention_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* block_tables, const int32_t* seq_lens,
+                                   int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
+                                   int64_t num_blocks, float scale, const float* k_scale,
+                                   const float* v_scale, void* out, void* stream,
+                                   int32_t pages_per_partition) {
+  return decode(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads, num_kv_heads,
+                head_size, block_size, max_blocks_per_seq, num_blocks, scale, k_scale, v_scale, out,
+                stream, pages_per_partition, Variant(), true);
 }
 
 int paged_multi_query_attention(const void* q, const int32_t* cu_seqlens_q, int32_t num_q_tokens,
