@@ -9,16 +9,24 @@ default workload is 40 query / 8 kv heads, head_dim 128, 256 sequences of
 (2.15 GB of K/V per call, far beyond the 256 MB Infinity Cache, so every call
 streams from HBM).
 
-Prints one JSON line: achieved algorithmic HBM GB/s (value), µs/call, the
-roofline object for the decode kernel (HIP-event timing on its launch stream;
-counter traffic from the committed rocprofv3 summary when it matches the
-current kernel source), and the fp64 CPU oracle timed on a bounded sample.
+Prints one JSON line: achieved algorithmic HBM GB/s (value: the bytes of one
+call over the timed region's time per call, i.e. whole-job throughput), the
+per-call median and mean (HIP events around each call, on the stream the
+kernels run on), the median of graph replays (the pages' timing method), the
+roofline object for the decode kernel (its average launch duration from those
+per-call events; counter traffic from the committed rocprofv3 summary when it
+matches the current kernel source), and the fp64 CPU oracle timed on bounded
+samples (median of three, all host cores and one core).
 
 Other modes:
     --workload all          also print one line per workload of the suite to stderr
                             (decode workloads, and the fp8 cache write for a decode step
                             and for a prefill-sized batch)
     --copy-calibration      time a plain 1 GiB device copy (for scaling PMC counters)
+    --read-ceiling          the bandwidth plain reads reach: a streaming read of 2 GiB
+                            (several grid sizes, with and without the streaming hint)
+                            and the decode's page-gather reads alone on the target
+                            workload (libpa_probe.so)
 """
 from __future__ import annotations
 
@@ -213,8 +221,10 @@ def make_call(case, out, stream=None):
                                              stream=stream)
 
 
-def time_calls(case, steps, warmup):
-    """Average µs per call, HIP events recorded on the stream the kernels run on."""
+def time_calls(case, steps, warmup, per_call=False):
+    """µs per call over the timed region (HIP events recorded on the stream
+    the kernels run on); with per_call, also each call's own duration (an
+    event pair around every call inside the region)."""
     import torch
     dev = case.q.device
     out = torch.empty_like(case.q)
@@ -225,12 +235,21 @@ def time_calls(case, steps, warmup):
     torch.cuda.synchronize(dev)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(steps if per_call else 0)]
     start.record(stream)
-    for _ in range(steps):
+    for i in range(steps):
+        if per_call:
+            pairs[i][0].record(stream)
         call()
+        if per_call:
+            pairs[i][1].record(stream)
     end.record(stream)
     torch.cuda.synchronize(dev)
-    return start.elapsed_time(end) * 1e3 / steps
+    region = start.elapsed_time(end) * 1e3 / steps
+    if not per_call:
+        return region
+    return region, [a.elapsed_time(b) * 1e3 for a, b in pairs]
 
 
 COLD_MIN_BYTES = 512 << 20   # twice the 256 MB Infinity Cache
@@ -286,9 +305,10 @@ def time_calls_cold(case, steps, warmup):
     return us
 
 
-def time_graph(case, replays=50, calls_per_graph=10):
+def time_graph(case, replays=50, calls_per_graph=10, per_replay=False):
     """Average µs per call when `calls_per_graph` calls are captured in one HIP
-    graph and the graph is replayed (the way the pages time impl.forward)."""
+    graph and the graph is replayed (the way the pages time impl.forward);
+    with per_replay, also the µs per call of each replay (events around it)."""
     import torch
     dev = case.q.device
     out = torch.empty_like(case.q)
@@ -297,7 +317,7 @@ def time_graph(case, replays=50, calls_per_graph=10):
     stream.wait_stream(torch.cuda.current_stream(dev))
     with torch.cuda.stream(stream):
         for _ in range(3):
-            call()          # sizes the split-KV scratch before capture
+            call()          # sizes the capture stream's split-KV scratch
     torch.cuda.synchronize(dev)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
@@ -308,12 +328,21 @@ def time_graph(case, replays=50, calls_per_graph=10):
     torch.cuda.synchronize(dev)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(replays if per_replay else 0)]
     start.record()
-    for _ in range(replays):
+    for i in range(replays):
+        if per_replay:
+            pairs[i][0].record()
         g.replay()
+        if per_replay:
+            pairs[i][1].record()
     end.record()
     torch.cuda.synchronize(dev)
-    return start.elapsed_time(end) * 1e3 / (replays * calls_per_graph)
+    mean = start.elapsed_time(end) * 1e3 / (replays * calls_per_graph)
+    if not per_replay:
+        return mean
+    return mean, [a.elapsed_time(b) * 1e3 / calls_per_graph for a, b in pairs]
 
 
 def cache_write_case(num_tokens, num_kv_heads=8, seed=0, prefill=True):
@@ -365,32 +394,113 @@ def time_cache_write(num_tokens, steps, warmup, num_kv_heads=8, prefill=True):
     return start.elapsed_time(end) * 1e3 / steps
 
 
-def cpu_baseline(target_seconds=12.0, max_seqs=256):
-    """The fp64 oracle on a bounded sample of the same workload (host cores):
-    16 sequences first, then as many as about target_seconds of oracle work
-    allow (a multiple of 16, up to the workload's 256), timed on their own."""
+def cpu_baseline(target_seconds=4.0, max_seqs=256):
+    """The fp64 oracle as it stands, on bounded samples of the same workload:
+    on every host core (os.cpu_count() threads), the median of three runs of
+    as many sequences as about target_seconds of work allow (a multiple of 4
+    up to the workload's 256, sized by a first run of 4); and the same on one
+    core, on a sample sized the same way.  Reported in the metric's unit
+    (algorithmic GB/s of the sample)."""
+    import statistics
     import oracle
     import workloads
     hq, hkv, _, ctx = workloads.TARGET
     cores = os.cpu_count() or 1
 
-    def run(n):
+    def run(n, threads):
         case = workloads.dense(hq, hkv, n, ctx, seed=1, device="cpu")
         args = (case.q_bits(), case.k_cache.numpy(), case.v_cache.numpy(), case.block_tables.numpy(),
                 case.seq_lens.numpy(), case.scale, case.k_scale, case.v_scale)
         t0 = time.perf_counter()
-        oracle.decode(*args, num_threads=cores)
+        oracle.decode(*args, num_threads=threads)
         return case.algorithmic_bytes(), time.perf_counter() - t0
 
-    n = 16
-    b, dt = run(n)
-    m = int(min(max_seqs, n * target_seconds / max(dt, 1e-3))) // 16 * 16
-    if m > n:
-        n = m
-        b, dt = run(n)
+    def median_of_three(threads):
+        n = 4
+        _, dt = run(n, threads)
+        n = max(4, int(min(max_seqs, n * target_seconds / max(dt, 1e-3))) // 4 * 4)
+        runs = [run(n, threads) for _ in range(3)]
+        b = runs[0][0]
+        dt = statistics.median(r[1] for r in runs)
+        return n, b, dt, [round(r[1], 2) for r in runs]
+
+    n, b, dt, all_dt = median_of_three(cores)
+    n1, b1, dt1, all_dt1 = median_of_three(1)
     return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"{n} of 256 sequences of the same shape (40/8 heads, ctx {ctx}), all heads; "
-                      f"{dt:.2f} s wall on {cores} threads"}
+                      f"median of 3 runs {all_dt} s on {cores} threads",
+            "one_core": {"value": round(b1 / dt1 / 1e9, 5), "unit": "GB/s", "cores": 1,
+                         "sample": f"{n1} sequences of the same shape; median of 3 runs {all_dt1} s"}}
+
+
+def read_ceiling(steps):
+    """JSON lines: GB/s of a plain streaming read over 2 GiB for several grid
+    sizes and both cache policies, and of the decode's page-gather reads
+    alone on the target workload (K+V pages, table and lengths)."""
+    import ctypes
+    import torch
+    import workloads
+    from paged_attention_decode_03_amd import build as pa_build
+    lib = ctypes.CDLL(pa_build.PROBE_LIB)
+    vp = ctypes.c_void_p
+    lib.pa_probe_read_stream.argtypes = [vp, ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32, vp, vp]
+    lib.pa_probe_page_gather.argtypes = [vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         vp, vp]
+    stream = torch.cuda.Stream()
+
+    def timed(fn):
+        for _ in range(3):
+            assert fn() == 0
+        torch.cuda.synchronize()
+        pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(steps)]
+        for a, b in pairs:
+            a.record(stream)
+            assert fn() == 0
+            b.record(stream)
+        torch.cuda.synchronize()
+        per = sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)
+        return per[len(per) // 2], sum(per) / len(per)
+
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(1 << 16, dtype=torch.int32, device="cuda")
+    best = 0.0
+    for nt in (1, 0):
+        for blocks in (1024, 2048, 4096, 8192, 16384):
+            chunk = nbytes // blocks
+            med, mean = timed(lambda: lib.pa_probe_read_stream(buf.data_ptr(), chunk, blocks, nt,
+                                                               sink.data_ptr(), stream.cuda_stream))
+            gbs = nbytes / med / 1e3
+            best = max(best, gbs)
+            print(json.dumps({"probe": "read_stream", "bytes": nbytes, "workgroups": blocks,
+                              "threads": 256, "nontemporal": nt, "us_median": round(med, 2),
+                              "us_mean": round(mean, 2), "GBps": round(gbs, 1),
+                              "frac_of_peak": round(gbs / PEAK_GBS, 4)}), flush=True)
+    del buf
+    case = make_workload("target", "cuda")
+    S, Hkv, W = case.num_seqs, case.num_kv_heads, case.max_blocks
+    sink = torch.empty(S * Hkv, dtype=torch.int32, device="cuda")
+    med, mean = timed(lambda: lib.pa_probe_page_gather(
+        case.k_cache.data_ptr(), case.v_cache.data_ptr(), case.block_tables.data_ptr(),
+        case.seq_lens.data_ptr(), S, Hkv, W, sink.data_ptr(), stream.cuda_stream))
+    b = case.kv_bytes() + S * W * 4 + 4 * S
+    print(json.dumps({"probe": "page_gather", "workload": "40/8 heads, 256 seqs x ctx 4096",
+                      "bytes": b, "us_median": round(med, 2), "us_mean": round(mean, 2),
+                      "GBps": round(b / med / 1e3, 1), "frac_of_peak": round(b / med / 1e3 / PEAK_GBS, 4)}),
+          flush=True)
+    print(json.dumps({"read_stream_best_GBps": round(best, 1),
+                      "read_stream_best_frac": round(best / PEAK_GBS, 4)}), flush=True)
+
+
+def P_one_launch(case):
+    """Whether one call of `case` is a single launch of the decode kernel (one
+    partition, no order kernel, one query per sequence)."""
+    import paged_attention_decode_03_amd as pa
+    if case.cu_seqlens_q is not None or getattr(case, "longest_first", False) or case.meta.get("options"):
+        return False
+    P, _, _ = pa.pa_decode_plan(case.num_seqs, case.num_heads, case.num_kv_heads, case.max_blocks, 256)
+    return P == 1
 
 
 def copy_calibration(steps):
@@ -418,6 +528,9 @@ def main():
     ap.add_argument("--workload", default="target")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--read-ceiling", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the graph-replay timing (profiler runs: only the timed calls)")
     ap.add_argument("--cold", action="store_true",
                     help="rotate the calls over copies of the inputs in distinct buffers "
                          "(at least 512 MiB touched per round), so a small workload is "
@@ -434,6 +547,9 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     if args.copy_calibration:
         copy_calibration(args.steps)
+        return
+    if args.read_ceiling:
+        read_ceiling(args.steps)
         return
 
     import paged_attention_decode_03_amd as pa
@@ -483,9 +599,24 @@ def main():
         return
 
     case = make_workload(args.workload, "cuda")
-    us = (time_calls_cold if args.cold else time_calls)(case, args.steps, args.warmup)
+    if args.cold:
+        us = time_calls_cold(case, args.steps, args.warmup)
+        per = None
+    else:
+        us, per = time_calls(case, args.steps, args.warmup, per_call=True)
     B = workload_bytes(case)
     gbs = B / us / 1e3
+    import statistics
+    us_med = statistics.median(per) if per else None
+    us_evmean = sum(per) / len(per) if per else None
+    # the graph-replay median, the pages' timing method (not in the timed region)
+    g_mean, g_per = time_graph(case, replays=30, calls_per_graph=10, per_replay=True) \
+        if not (args.cold or args.no_graph) else (None, None)
+    g_med = statistics.median(g_per) if g_per else None
+    # the decode kernel's average launch duration: the per-call mean where a
+    # call is one launch (one partition), else the timed region's average
+    kernel_us = us_evmean if (per and P_one_launch(case)) else us
+    k_gbs = B / kernel_us / 1e3
     P, ppp, _ = pa.pa_decode_plan(case.num_seqs, case.num_heads, case.num_kv_heads, case.max_blocks, 256)
     traffic = counter_traffic() if args.workload == "target" else None
     line = {
@@ -497,6 +628,11 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(us / 1e3, 6),
         "us_per_call": round(us, 3),
+        "value_basis": "algorithmic bytes per call / (timed region / steps): whole-job throughput",
+        "us_per_call_median": None if us_med is None else round(us_med, 3),
+        "us_per_call_mean_of_calls": None if us_evmean is None else round(us_evmean, 3),
+        "us_per_call_graph_median": None if g_med is None else round(g_med, 3),
+        "us_per_call_graph_mean": None if g_mean is None else round(g_mean, 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": round(PAGES_ASM_US / us, 4) if args.workload == "target" else None,
@@ -510,8 +646,9 @@ def main():
                    "num_kv_heads": case.num_kv_heads, "max_blocks_per_seq": case.max_blocks,
                    "partitions": P, "pages_per_partition": ppp, "algorithmic_bytes": B,
                    "inputs": "rotated over copies (cold cache)" if args.cold else "one set"},
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / PEAK_GBS, 4), "traffic": traffic},
+        "roofline": {"bound": "hbm", "achieved": round(k_gbs, 2), "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": round(k_gbs / PEAK_GBS, 4), "traffic": traffic,
+                     "kernel_us_mean": round(kernel_us, 3)},
     }
     del case
     torch.cuda.empty_cache()

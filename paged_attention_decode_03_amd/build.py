@@ -1,4 +1,5 @@
-"""Build libpagedattn.so (HIP, gfx950) in-tree with hipcc.
+"""Build libpagedattn.so (HIP, gfx950) in-tree with hipcc, and the bandwidth
+probes the benchmark uses (libpa_probe.so, not part of the attention library).
 
     python -m paged_attention_decode_03_amd.build
 """
@@ -15,6 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpagedattn.so")
 SOURCES = ["pa_decode_kernels.hip", "pa_cache_write.hip", "pa_api.hip"]
+PROBE_LIB = os.path.join(PKG, "libpa_probe.so")
+PROBE_SOURCES = ["pa_probe.hip"]
 ARCH = "gfx950"
 
 
@@ -35,10 +38,16 @@ def compile_flags() -> list[str]:
 
 
 def build(verbose: bool = False) -> str:
+    _link(SOURCES, LIB, verbose)
+    _link(PROBE_SOURCES, PROBE_LIB, verbose)
+    return LIB
+
+
+def _link(sources, lib, verbose):
     objs = []
     tmpdir = os.path.join(PKG, "_build")
     os.makedirs(tmpdir, exist_ok=True)
-    for src in SOURCES:
+    for src in sources:
         obj = os.path.join(tmpdir, os.path.splitext(src)[0] + ".o")
         cmd = [hipcc(), *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
@@ -48,14 +57,13 @@ def build(verbose: bool = False) -> str:
             sys.stderr.write(r.stdout + r.stderr)
             raise RuntimeError(f"hipcc failed on {src}")
         objs.append(obj)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("linking libpagedattn.so failed")
-    os.replace(tmp, LIB)
-    return LIB
+        raise RuntimeError(f"linking {os.path.basename(lib)} failed")
+    os.replace(tmp, lib)
 
 
 if __name__ == "__main__":

@@ -2,6 +2,8 @@
 binding, run the fp64 oracle on the same bytes, compare."""
 from __future__ import annotations
 
+import json
+import os
 import sys
 
 import numpy as np
@@ -97,6 +99,14 @@ def compare(gpu_out, ref, label, seqs=None, max_abs=MAX_ABS, mean_abs=MEAN_ABS, 
     err_s, floor_s, err_rne_s = err / denom, floor / denom, err_rne / denom
     reach = floor_s <= max_abs
     mode = " (relative to the terms)" if term_scale is not None else (" (relative)" if relative else "")
+    record = {"label": label, "mode": mode.strip(" ()") or "absolute", "n": int(err.size),
+              "max_vs_fp64": float(err_s.max()), "mean_vs_fp64": float(err_s.mean()),
+              "max_vs_bf16_oracle": float(err_rne_s.max()), "mean_vs_bf16_oracle": float(err_rne_s.mean()),
+              "bf16_floor_mean": float(floor_s.mean()), "beyond_reach": int((~reach).sum())}
+    if os.environ.get("PA_PARITY_LOG"):
+        # one JSON line per comparison (the whole-workload error table)
+        with open(os.environ["PA_PARITY_LOG"], "a") as f:
+            f.write(json.dumps(record) + "\n")
     log(f"[{label}]{mode} vs fp64: max={err_s.max():.3e} mean={err_s.mean():.3e} | "
         f"vs bf16(oracle): max={err_rne_s.max():.3e} mean={err_rne_s.mean():.3e} | "
         f"bf16 floor: max={floor_s.max():.3e} mean={floor_s.mean():.3e} | "
@@ -111,16 +121,3 @@ def compare(gpu_out, ref, label, seqs=None, max_abs=MAX_ABS, mean_abs=MEAN_ABS, 
     if floor_s.mean() <= mean_abs / 2:
         assert err_s.mean() <= mean_abs, f"{label}: mean abs error {err_s.mean():.3e} > {mean_abs}"
     return err
-
-
-def sample_seqs(case, n, seed=0):
-    """n sequences spread over the batch, always including the longest and shortest."""
-    S = case.num_seqs
-    if n >= S:
-        return list(range(S))
-    lens = case.seq_lens.cpu().numpy()
-    rng = np.random.default_rng(seed)
-    pick = set(rng.choice(S, size=n - 2, replace=False).tolist())
-    pick.add(int(lens.argmax()))
-    pick.add(int(lens.argmin()))
-    return sorted(pick)

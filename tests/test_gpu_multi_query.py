@@ -17,7 +17,7 @@ import torch
 
 import oracle
 import workloads
-from parity import compare, log, run_gpu, sample_seqs
+from parity import compare, log, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -200,16 +200,15 @@ def test_binding_rejects_bad_cu_seqlens():
                                        case.scale, case.k_scale, case.v_scale)
 
 
-# ---------------------------------------------------------------- full size, sampled
+# ---------------------------------------------------------------- full size, every query row
 
 def test_speculative_decode_target_layout():
     """40/8 heads, 256 sequences of 4096 tokens, 4 new tokens each (one
     accepted token plus three drafts)."""
     S, ctx = 256, 4096
     case = workloads.make_multi_case(40, 8, [ctx] * S, [4] * S, seed=71, device="cuda")
-    seqs = sample_seqs(case, 6, seed=1)
-    log(f"spec decode 40/8 x{S} ctx {ctx} q_len 4, sampled {seqs}")
-    check(case, "spec decode q_len 4", seqs=seqs)
+    log(f"spec decode 40/8 x{S} ctx {ctx} q_len 4")
+    check(case, "spec decode q_len 4")
 
 
 def test_mixed_batch():
@@ -221,6 +220,5 @@ def test_mixed_batch():
     ql = np.where(g.random(S) < 0.6, 1, g.choice([2, 3, 4, 5, 8, 16], size=S))
     ql = np.minimum(ql, lens).tolist()
     case = workloads.make_multi_case(40, 8, lens, ql, seed=81, max_blocks=250, device="cuda")
-    seqs = sample_seqs(case, 8, seed=2)
-    log(f"mixed batch: sampled {seqs}")
-    check(case, "mixed batch", seqs=seqs)
+    log("mixed batch")
+    check(case, "mixed batch")

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import workloads
-from parity import compare, log, run_gpu, sample_seqs
+from parity import compare, log, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -127,15 +127,19 @@ def test_binding_rejects_mismatched_views():
                                       case.v_scale)
 
 
-@pytest.mark.parametrize("layout", ["nhd", "packed"])
-def test_target_shape_sampled(layout):
-    """40/8 heads, 256 sequences x 4096 tokens (the benchmark's shape)."""
+def test_target_shape_every_layout():
+    """40/8 heads, 256 sequences x 4096 tokens (the benchmark's shape) in all
+    three token-row layouts: each equals the page-layout kernel bit for bit
+    and meets the bound against the token-row oracle on every sequence (the
+    oracle's layouts agree bit for bit, so it runs once, on NHD)."""
     hq, hkv, S, ctx = workloads.TARGET
     case = workloads.dense(hq, hkv, S, ctx, seed=3, device="cuda")
-    kv, vv = gpu_views(case, layout)
-    got = run_nhd(case, kv, vv)
     ref_page = run_gpu(case)
-    assert torch.equal(got.view(torch.int16), ref_page.view(torch.int16)), "differs from page layout"
-    seqs = sample_seqs(case, 4, seed=5)
-    log(f"token rows {layout} target, sampled {seqs}")
-    compare(got, oracle_rows(case, layout, seqs), f"token rows {layout} target", seqs=seqs)
+    ref = oracle_rows(case, "nhd")
+    for layout in workloads.TOKEN_ROW_LAYOUTS:
+        kv, vv = gpu_views(case, layout)
+        got = run_nhd(case, kv, vv)
+        del kv, vv
+        log(f"token rows {layout} target")
+        assert torch.equal(got.view(torch.int16), ref_page.view(torch.int16)), f"{layout}: differs from page layout"
+        compare(got, ref, f"token rows {layout} target")

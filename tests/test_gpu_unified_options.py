@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import workloads
-from parity import compare, log, sample_seqs
+from parity import compare, log
 
 pytestmark = pytest.mark.gpu
 
@@ -203,12 +203,11 @@ def test_one_query_per_sequence_without_row_offsets():
     compare(b, ref, "one query per sequence, options", seqs=rows)
 
 
-def test_speculative_decode_with_window_and_sinks_sampled():
+def test_speculative_decode_with_window_and_sinks():
     """40/8 heads, 256 sequences of 4096 tokens, 4 queries each, a 128-token
     window and per-head sinks: only the last pages of each sequence are read."""
     S, ctx = 256, 4096
     case = workloads.make_multi_case(40, 8, [ctx] * S, [4] * S, seed=96, device="cuda")
     sinks = np.linspace(-1.0, 2.0, 40).astype(np.float32)
-    seqs = sample_seqs(case, 4, seed=3)
-    log(f"spec decode with window 128 + sinks, sampled {seqs}")
-    check(case, "spec decode window + sinks", seqs=seqs, sliding_window=128, sinks=sinks)
+    log("spec decode with window 128 + sinks")
+    check(case, "spec decode window + sinks", sliding_window=128, sinks=sinks)
