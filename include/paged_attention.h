@@ -251,9 +251,16 @@ int paged_multi_query_attention(const void* q, const int32_t* cu_seqlens_q, int3
  *                    finds its own sequence by a counting sort of the lengths;
  *                    otherwise, up to 8192 sequences, a small kernel orders them
  *                    first (about 4.6 us more); above that the order stays plain.
- *                    Same results, bit for bit; pays off for ragged contexts
- *                    (256 sequences of 1..4000 tokens at 40/8 heads on MI355X:
- *                    202 -> 185 us) and costs about 3 us when contexts are alike.
+ *                    Where one partition per sequence gives 2 to 4 work items
+ *                    per CU, each item then runs as two waves, so that few
+ *                    items a CU are resident and the rest start longest first
+ *                    as those finish.  Results equal the plain order's bit for
+ *                    bit, except in that case, where the two waves' summation
+ *                    order makes them agree to rounding (one shape still always
+ *                    gives the same bits).  Pays off for ragged contexts (256
+ *                    sequences of 1..4000 tokens on MI355X: 40/8 heads 202 ->
+ *                    185 us, 32/4 heads 111 -> 96 us) and costs 1-8% when
+ *                    contexts are alike.
  *                    The order kernel's scratch (4 bytes per sequence, after the
  *                    split-KV scratch rounded up to 256 bytes) is not in
  *                    pa_decode_plan's figure.

@@ -87,6 +87,15 @@ constexpr int64_t kCounterSlots = kCounterRegion / sizeof(int32_t);
 // contexts are all alike.
 constexpr int kLongestFirstMaxSeqs = 8192;  // what the one-workgroup order kernel holds
 constexpr int kInKernelOrderMaxSeqs = 512;  // what a work item orders by itself (8 per lane)
+// Longest-first launches of up to this many items per CU run two waves per
+// item (one per SIMD), so only two items a CU are resident and the rest start
+// as those finish, longest first: greedy longest-first scheduling.  Measured
+// on MI355X (graph replay, ragged 1..4000 x 256 sequences): 32/4 heads (4
+// items per CU) 110.5 -> 96.1 us and 106.8 -> 89.9 us (seeds 0, 1); at 8
+// items per CU (32/8, 40/8) within +-3%, so the rule stops at 4.  On uniform
+// contexts it costs 1-8% more than longest-first alone (which is off by
+// default for them).
+constexpr int kLptTwoWaveItemsPerCU = 4;
 #ifndef PA_LPT_IN_KERNEL
 #define PA_LPT_IN_KERNEL 1
 #endif
@@ -499,9 +508,11 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   // split (measured on MI355X, 512 items: 40/8 ctx 4096 x 64 sequences 95.7 ->
   // 88.3 us, 20/4 ctx 4096 x 128 96.0 -> 87.8 us, ctx 1024 and 2048 within 1%;
   // at 3 to 4 items per CU, and with split contexts, it measured 3-10% slower)
+  // longest-first: up to kLptTwoWaveItemsPerCU items per CU
   const int64_t cus = device_cus(dev);
-  p.waves_per_item = (!mq && !slot_scales && !var.token_rows && plan.num_parts == 1 &&
-                      units > cus && units <= 2 * cus)
+  const bool lpt_on = cp.lpt_in_kernel || plan.longest_first;
+  p.waves_per_item = (!mq && !slot_scales && !var.token_rows && plan.num_parts == 1 && units > cus &&
+                      units <= (lpt_on ? kLptTwoWaveItemsPerCU : 2) * cus)
                          ? 2 : 1;
   if (plan.workspace_bytes) {
     void* ws = nullptr;

@@ -499,6 +499,33 @@ def test_longest_first_order_covers_every_sequence():
         assert torch.equal(out.view(torch.int16), plain.view(torch.int16)), f"replay {r}"
 
 
+@pytest.mark.parametrize("name", ["ragged_32x4_seed0", "ragged_32x4_seed1", "ragged_8x1_600seqs"])
+def test_longest_first_with_two_waves_per_item(name):
+    """Longest-first launches of 2 to 4 items per CU run two waves per item
+    (ragged 32/4 x 256 sequences: 1024 items; 600 ragged sequences at 8/1:
+    600 items, ordered by the order kernel): every sequence meets the bound
+    against the oracle, the plain order's result too, and a repeat gives the
+    same bits."""
+    import paged_attention_decode_03_amd as pa
+    if name.startswith("ragged_32x4"):
+        case = workloads.ragged(32, 4, seed=int(name[-1]), device="cuda")
+    else:
+        case = workloads.make_case(8, 1, workloads.ragged_lens(600, seed=11), seed=111, device="cuda",
+                                   max_blocks=250)
+    ks = torch.tensor([case.k_scale], device="cuda")
+    vs = torch.tensor([case.v_scale], device="cuda")
+    args = (case.k_cache, case.v_cache, case.block_tables, case.seq_lens, case.scale, ks, vs)
+    lpt = pa.paged_attention_unified(case.q, None, 1, *args, longest_first=True)
+    again = pa.paged_attention_unified(case.q, None, 1, *args, longest_first=True)
+    plain = pa.paged_decode_attention(case.q, *args)
+    torch.cuda.synchronize()
+    log(f"longest first, two waves per item: {name}")
+    assert torch.equal(lpt.view(torch.int16), again.view(torch.int16))
+    ref = run_oracle(case)
+    compare(lpt, ref, f"longest first two waves {name}")
+    compare(plain, ref, f"plain order {name}")
+
+
 def test_cache_policy_does_not_change_results():
     """Working sets within the Infinity Cache are read with the default cache
     policy, larger ones with the streaming hint: two instantiations of the
