@@ -10,13 +10,18 @@ default workload is 40 query / 8 kv heads, head_dim 128, 256 sequences of
 streams from HBM).
 
 Prints one JSON line: achieved algorithmic HBM GB/s (value: the bytes of one
-call over the timed region's time per call, i.e. whole-job throughput), the
-per-call median and mean (HIP events around each call, on the stream the
-kernels run on), the median of graph replays (the pages' timing method), the
-roofline object for the decode kernel (its average launch duration from those
-per-call events; counter traffic from the committed rocprofv3 summary when it
-matches the current kernel source), and the fp64 CPU oracle timed on bounded
-samples (median of three, all host cores and one core).
+call over the timed region's time per call, i.e. whole-job throughput; the
+region's calls run back to back between two HIP events on the stream the
+kernels run on), the per-call median and mean (a second, untimed loop with an
+event pair around each call), the median of graph replays (the pages' timing
+method), the roofline object for the decode kernel (its average launch
+duration: the region's time per call, one launch a call; counter traffic from
+the committed rocprofv3 summary when it matches the current kernel source),
+and the fp64 CPU oracle timed on bounded samples (median of three, all host
+cores and one core).  Before the warm-up calls, untimed calls run for
+--settle-ms (100 ms): the first calls after the inputs are generated run
+slower (the kernel trace shows the first at ~400 µs and the next twenty ~2%
+above the rest).
 
 Other modes:
     --workload all          also print one line per workload of the suite to stderr
@@ -221,35 +226,49 @@ def make_call(case, out, stream=None):
                                              stream=stream)
 
 
-def time_calls(case, steps, warmup, per_call=False):
-    """µs per call over the timed region (HIP events recorded on the stream
-    the kernels run on); with per_call, also each call's own duration (an
-    event pair around every call inside the region)."""
+def time_calls(case, steps, warmup, per_call=False, settle_ms=0.0):
+    """µs per call over the timed region: `steps` calls back to back between
+    two HIP events recorded on the stream the kernels run on, after
+    `warmup` untimed calls (and, with settle_ms, untimed calls for at least
+    that long before them: the first calls after the inputs are generated run
+    slower).  With per_call, also a second, untimed loop of `steps` calls,
+    each between its own event pair (events between calls delay the next
+    launch, so they stay out of the timed region); returns (region µs,
+    per-call µs list, settle calls)."""
     import torch
     dev = case.q.device
     out = torch.empty_like(case.q)
     stream = torch.cuda.Stream(dev)
     call = make_call(case, out, stream)
+    settled = 0
+    if settle_ms > 0:
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < settle_ms:
+            for _ in range(8):
+                call()
+            settled += 8
+            torch.cuda.synchronize(dev)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize(dev)
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(steps if per_call else 0)]
     start.record(stream)
-    for i in range(steps):
-        if per_call:
-            pairs[i][0].record(stream)
+    for _ in range(steps):
         call()
-        if per_call:
-            pairs[i][1].record(stream)
     end.record(stream)
     torch.cuda.synchronize(dev)
     region = start.elapsed_time(end) * 1e3 / steps
     if not per_call:
         return region
-    return region, [a.elapsed_time(b) * 1e3 for a, b in pairs]
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(steps)]
+    for a, b in pairs:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize(dev)
+    return region, [a.elapsed_time(b) * 1e3 for a, b in pairs], settled
 
 
 COLD_MIN_BYTES = 512 << 20   # twice the 256 MB Infinity Cache
@@ -445,7 +464,7 @@ def read_ceiling(steps):
     vp = ctypes.c_void_p
     lib.pa_probe_read_stream.argtypes = [vp, ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32, vp, vp]
     lib.pa_probe_page_gather.argtypes = [vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                         vp, vp]
+                                         ctypes.c_int32, ctypes.c_int32, vp, vp]
     stream = torch.cuda.Stream()
 
     def timed(fn):
@@ -481,14 +500,16 @@ def read_ceiling(steps):
     case = make_workload("target", "cuda")
     S, Hkv, W = case.num_seqs, case.num_kv_heads, case.max_blocks
     sink = torch.empty(S * Hkv, dtype=torch.int32, device="cuda")
-    med, mean = timed(lambda: lib.pa_probe_page_gather(
-        case.k_cache.data_ptr(), case.v_cache.data_ptr(), case.block_tables.data_ptr(),
-        case.seq_lens.data_ptr(), S, Hkv, W, sink.data_ptr(), stream.cuda_stream))
     b = case.kv_bytes() + S * W * 4 + 4 * S
-    print(json.dumps({"probe": "page_gather", "workload": "40/8 heads, 256 seqs x ctx 4096",
-                      "bytes": b, "us_median": round(med, 2), "us_mean": round(mean, 2),
-                      "GBps": round(b / med / 1e3, 1), "frac_of_peak": round(b / med / 1e3 / PEAK_GBS, 4)}),
-          flush=True)
+    for pps, depth in ((2, 2), (1, 2), (1, 3), (1, 4), (2, 3), (2, 4), (4, 2), (4, 3), (4, 4)):
+        med, mean = timed(lambda: lib.pa_probe_page_gather(
+            case.k_cache.data_ptr(), case.v_cache.data_ptr(), case.block_tables.data_ptr(),
+            case.seq_lens.data_ptr(), S, Hkv, W, pps, depth, sink.data_ptr(), stream.cuda_stream))
+        print(json.dumps({"probe": "page_gather", "workload": "40/8 heads, 256 seqs x ctx 4096",
+                          "pages_per_stage": pps, "ring_depth": depth, "bytes": b,
+                          "us_median": round(med, 2), "us_mean": round(mean, 2),
+                          "GBps": round(b / med / 1e3, 1),
+                          "frac_of_peak": round(b / med / 1e3 / PEAK_GBS, 4)}), flush=True)
     print(json.dumps({"read_stream_best_GBps": round(best, 1),
                       "read_stream_best_frac": round(best / PEAK_GBS, 4)}), flush=True)
 
@@ -531,6 +552,12 @@ def main():
     ap.add_argument("--read-ceiling", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replay timing (profiler runs: only the timed calls)")
+    ap.add_argument("--after-suite-workloads", type=int, default=0,
+                    help="first allocate, run and free the suite's first N workloads in this "
+                         "process (the condition the target meets inside --workload all)")
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="untimed calls for at least this long before the warm-up calls "
+                         "(the first calls after input generation run slower)")
     ap.add_argument("--cold", action="store_true",
                     help="rotate the calls over copies of the inputs in distinct buffers "
                          "(at least 512 MiB touched per round), so a small workload is "
@@ -598,12 +625,18 @@ def main():
                           "bytes": b}), flush=True)
         return
 
+    for name in suite_names()[:max(0, args.after_suite_workloads)]:
+        w = make_workload(name, "cuda")
+        time_calls(w, 20, 5)
+        del w
+        torch.cuda.empty_cache()
     case = make_workload(args.workload, "cuda")
     if args.cold:
         us = time_calls_cold(case, args.steps, args.warmup)
         per = None
     else:
-        us, per = time_calls(case, args.steps, args.warmup, per_call=True)
+        us, per, settled = time_calls(case, args.steps, args.warmup, per_call=True,
+                                      settle_ms=args.settle_ms)
     B = workload_bytes(case)
     gbs = B / us / 1e3
     import statistics
@@ -613,10 +646,12 @@ def main():
     g_mean, g_per = time_graph(case, replays=30, calls_per_graph=10, per_replay=True) \
         if not (args.cold or args.no_graph) else (None, None)
     g_med = statistics.median(g_per) if g_per else None
-    # the decode kernel's average launch duration: the per-call mean where a
-    # call is one launch (one partition), else the timed region's average
-    kernel_us = us_evmean if (per and P_one_launch(case)) else us
+    # the decode kernel's average launch duration: the timed region's calls run
+    # back to back, so where a call is one launch (one partition) the region's
+    # average per call is that kernel's average duration
+    kernel_us = us
     k_gbs = B / kernel_us / 1e3
+    one_launch = P_one_launch(case)
     P, ppp, _ = pa.pa_decode_plan(case.num_seqs, case.num_heads, case.num_kv_heads, case.max_blocks, 256)
     traffic = counter_traffic() if args.workload == "target" else None
     line = {
@@ -629,8 +664,10 @@ def main():
         "ms_per_step": round(us / 1e3, 6),
         "us_per_call": round(us, 3),
         "value_basis": "algorithmic bytes per call / (timed region / steps): whole-job throughput",
+        "settle_calls": None if args.cold else settled,
         "us_per_call_median": None if us_med is None else round(us_med, 3),
         "us_per_call_mean_of_calls": None if us_evmean is None else round(us_evmean, 3),
+        "per_call_basis": "a second, untimed loop of the same calls, an event pair around each",
         "us_per_call_graph_median": None if g_med is None else round(g_med, 3),
         "us_per_call_graph_mean": None if g_mean is None else round(g_mean, 3),
         "higher_is_better": True,
@@ -648,7 +685,7 @@ def main():
                    "inputs": "rotated over copies (cold cache)" if args.cold else "one set"},
         "roofline": {"bound": "hbm", "achieved": round(k_gbs, 2), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(k_gbs / PEAK_GBS, 4), "traffic": traffic,
-                     "kernel_us_mean": round(kernel_us, 3)},
+                     "kernel_us_mean": round(kernel_us, 3), "one_launch_per_call": one_launch},
     }
     del case
     torch.cuda.empty_cache()

@@ -7,9 +7,8 @@
 //   pa_probe_page_gather  the decode's own access pattern without its
 //                         arithmetic: one wave per (sequence, kv head) walks
 //                         the block table and reads each 2 KiB K page and
-//                         2 KiB V page (two 16-byte loads a lane per page), the
-//                         pages of one stage in flight while the previous
-//                         stage's bytes are folded
+//                         2 KiB V page (two 16-byte loads a lane per page),
+//                         with a chosen stage size and ring depth
 //
 // Both fold what they read into one word per workgroup (so no load is dead)
 // and write it to `sink`.
@@ -47,11 +46,11 @@ __global__ __launch_bounds__(kStreamThreads) void read_stream_kernel(const uint8
   if (threadIdx.x == 0) sink[blockIdx.x] = part[0] ^ part[1] ^ part[2] ^ part[3];
 }
 
-constexpr int kGatherPagesPerStage = 2;
-
 // One wave per (sequence, kv head) unit; pages of the unit's table row up to
 // ceil(seq_len / 16), dense page layout (K and V pages of 2048 bytes at
-// (block * Hkv + kv head) * 2048).
+// (block * Hkv + kv head) * 2048).  PPS pages a stage, a ring of NB stages
+// (NB - 1 in flight while one is folded).
+template <int PPS, int NB>
 __global__ __launch_bounds__(64) void page_gather_kernel(const uint8_t* k_cache, const uint8_t* v_cache,
                                                          const int32_t* block_tables, const int32_t* seq_lens,
                                                          int num_kv_heads, int max_blocks, uint32_t* sink) {
@@ -63,11 +62,11 @@ __global__ __launch_bounds__(64) void page_gather_kernel(const uint8_t* k_cache,
   const int32_t* bt = block_tables + (size_t)s * max_blocks;
   const size_t page_stride = (size_t)num_kv_heads * 2048;
   u32x4 acc = {0u, 0u, 0u, 0u};
-  u32x4 cur[kGatherPagesPerStage][4];
-  auto load = [&](u32x4 (&st)[kGatherPagesPerStage][4], int stage) {
+  u32x4 ring[NB][PPS][4];
+  auto load = [&](u32x4 (&st)[PPS][4], int stage) {
 #pragma unroll
-    for (int pp = 0; pp < kGatherPagesPerStage; ++pp) {
-      const int i = stage * kGatherPagesPerStage + pp;
+    for (int pp = 0; pp < PPS; ++pp) {
+      const int i = stage * PPS + pp;
       const int pid = __builtin_amdgcn_readfirstlane(i < npages ? bt[i] : 0);
       const int bytes = i < npages ? 2048 : 0;
       const size_t off = (size_t)pid * page_stride + (size_t)kvh * 2048;
@@ -80,19 +79,20 @@ __global__ __launch_bounds__(64) void page_gather_kernel(const uint8_t* k_cache,
       }
     }
   };
-  const int nsteps = (npages + kGatherPagesPerStage - 1) / kGatherPagesPerStage;
-  load(cur, 0);
-  for (int st = 0; st < nsteps; ++st) {
-    u32x4 nxt[kGatherPagesPerStage][4];
-    load(nxt, st + 1);  // past the last page: zero-byte descriptors, no memory touched
+  const int nsteps = (npages + PPS - 1) / PPS;
 #pragma unroll
-    for (int pp = 0; pp < kGatherPagesPerStage; ++pp)
+  for (int k = 0; k < NB - 1; ++k) load(ring[k], k);
+  for (int st = 0; st < nsteps; st += NB) {
 #pragma unroll
-      for (int h = 0; h < 4; ++h) acc ^= cur[pp][h];
+    for (int k = 0; k < NB; ++k) {
+      if (st + k >= nsteps) break;
+      // loads past the last page: zero-byte descriptors, no memory touched
+      load(ring[(k + NB - 1) % NB], st + k + NB - 1);
 #pragma unroll
-    for (int pp = 0; pp < kGatherPagesPerStage; ++pp)
+      for (int pp = 0; pp < PPS; ++pp)
 #pragma unroll
-      for (int h = 0; h < 4; ++h) cur[pp][h] = nxt[pp][h];
+        for (int h = 0; h < 4; ++h) acc ^= ring[k][pp][h];
+    }
   }
   uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
   for (int o = 32; o > 0; o >>= 1) x ^= __shfl_xor(x, o);
@@ -123,16 +123,31 @@ int pa_probe_read_stream(const void* buf, uint64_t chunk, int32_t blocks, int32_
 // The decode's page reads alone, over the same caches, table and lengths
 // (dense page layout; every used block id must lie in the caches, seq_lens
 // at most 16 * max_blocks).  sink holds num_seqs * num_kv_heads words.
+// pages_per_stage: 1, 2 or 4; ring_depth: 2, 3 or 4 stages (depth - 1 in
+// flight while one is folded); the decode itself reads 2 pages a stage in a
+// ring of 2.
 int pa_probe_page_gather(const void* k_cache, const void* v_cache, const int32_t* block_tables,
                          const int32_t* seq_lens, int32_t num_seqs, int32_t num_kv_heads,
-                         int32_t max_blocks, uint32_t* sink, void* stream) {
+                         int32_t max_blocks, int32_t pages_per_stage, int32_t ring_depth, uint32_t* sink,
+                         void* stream) {
   if (!k_cache || !v_cache || !block_tables || !seq_lens || !sink || num_seqs <= 0 || num_kv_heads <= 0 ||
       max_blocks <= 0 || (int64_t)num_seqs * num_kv_heads > INT32_MAX)
     return -2;
-  hipLaunchKernelGGL(page_gather_kernel, dim3(num_seqs * num_kv_heads), dim3(64), 0, (hipStream_t)stream,
-                     (const uint8_t*)k_cache, (const uint8_t*)v_cache, block_tables, seq_lens, num_kv_heads,
-                     max_blocks, sink);
-  return hipGetLastError() == hipSuccess ? 0 : -6;
+  const dim3 grid(num_seqs * num_kv_heads), block(64);
+  hipStream_t st = (hipStream_t)stream;
+  const auto* kc = (const uint8_t*)k_cache;
+  const auto* vc = (const uint8_t*)v_cache;
+#define PA_PROBE_GATHER(P, D)                                                                         \
+  if (pages_per_stage == P && ring_depth == D) {                                                      \
+    hipLaunchKernelGGL((page_gather_kernel<P, D>), grid, block, 0, st, kc, vc, block_tables, seq_lens, \
+                       num_kv_heads, max_blocks, sink);                                               \
+    return hipGetLastError() == hipSuccess ? 0 : -6;                                                  \
+  }
+  PA_PROBE_GATHER(1, 2) PA_PROBE_GATHER(1, 3) PA_PROBE_GATHER(1, 4)
+  PA_PROBE_GATHER(2, 2) PA_PROBE_GATHER(2, 3) PA_PROBE_GATHER(2, 4)
+  PA_PROBE_GATHER(4, 2) PA_PROBE_GATHER(4, 3) PA_PROBE_GATHER(4, 4)
+#undef PA_PROBE_GATHER
+  return -2;
 }
 
 }  // extern "C"
