@@ -32,6 +32,9 @@ Other modes:
                             (several grid sizes, with and without the streaming hint)
                             and the decode's page-gather reads alone on the target
                             workload (libpa_probe.so)
+    --valu-compare          the decode (MFMA for qKᵀ and PV) against the same decode with
+                            its dot products on the vector ALUs (libpa_probe.so), per call,
+                            on the target and on 32/8, 32/4 and 8/1 heads at ctx 4096 x 256
 """
 from __future__ import annotations
 
@@ -456,15 +459,8 @@ def read_ceiling(steps):
     """JSON lines: GB/s of a plain streaming read over 2 GiB for several grid
     sizes and both cache policies, and of the decode's page-gather reads
     alone on the target workload (K+V pages, table and lengths)."""
-    import ctypes
     import torch
-    import workloads
-    from paged_attention_decode_03_amd import build as pa_build
-    lib = ctypes.CDLL(pa_build.PROBE_LIB)
-    vp = ctypes.c_void_p
-    lib.pa_probe_read_stream.argtypes = [vp, ctypes.c_uint64, ctypes.c_int32, ctypes.c_int32, vp, vp]
-    lib.pa_probe_page_gather.argtypes = [vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                         ctypes.c_int32, ctypes.c_int32, vp, vp]
+    lib = probe_library()
     stream = torch.cuda.Stream()
 
     def timed(fn):
@@ -514,6 +510,81 @@ def read_ceiling(steps):
                       "read_stream_best_frac": round(best / PEAK_GBS, 4)}), flush=True)
 
 
+def probe_library():
+    """libpa_probe.so (built with the library; the benchmark's probes only),
+    with its entry points' argument types set."""
+    import ctypes
+    from paged_attention_decode_03_amd import build as pa_build
+    lib = ctypes.CDLL(pa_build.PROBE_LIB)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    lib.pa_probe_read_stream.argtypes = [vp, ctypes.c_uint64, i32, i32, vp, vp]
+    lib.pa_probe_page_gather.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]
+    lib.pa_probe_decode_valu.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.c_int64,
+                                         ctypes.c_float, vp, vp, vp, vp]
+    return lib
+
+
+def valu_decode(lib, case, k_scale, v_scale, out, stream):
+    """The decode with its dot products on the vector ALUs (the probe), into
+    `out`; returns the probe's status."""
+    return lib.pa_probe_decode_valu(case.q.data_ptr(), case.k_cache.data_ptr(), case.v_cache.data_ptr(),
+                                    case.block_tables.data_ptr(), case.seq_lens.data_ptr(), case.num_seqs,
+                                    case.num_heads, case.num_kv_heads, case.max_blocks,
+                                    case.k_cache.shape[0], case.scale, k_scale.data_ptr(),
+                                    v_scale.data_ptr(), out.data_ptr(), stream.cuda_stream)
+
+
+VALU_COMPARE_WORKLOADS = ("target", "dense_32x8_ctx4096_s256", "dense_32x4_ctx4096_s256",
+                          "dense_8x1_ctx4096_s256")
+
+
+def valu_compare(steps, warmup):
+    """JSON lines: the decode (MFMA for qKᵀ and PV) against the same decode
+    with its dot products on the vector ALUs (probe), on the same inputs and
+    stream: per-call median and mean (HIP events around each call on the
+    launch stream) and GB/s, and the largest difference between the two
+    outputs."""
+    import torch
+    import paged_attention_decode_03_amd as pa
+    pa.load_library()
+    lib = probe_library()
+    stream = torch.cuda.Stream()
+    for name in VALU_COMPARE_WORKLOADS:
+        case = make_workload(name, "cuda")
+        ks = torch.tensor([case.k_scale], dtype=torch.float32, device="cuda")
+        vs = torch.tensor([case.v_scale], dtype=torch.float32, device="cuda")
+        out_m, out_v = torch.empty_like(case.q), torch.empty_like(case.q)
+        def mfma():
+            pa.paged_decode_attention(case.q, case.k_cache, case.v_cache, case.block_tables, case.seq_lens,
+                                      case.scale, ks, vs, out=out_m, stream=stream)
+            return 0
+
+        calls = {"mfma": mfma, "valu": lambda: valu_decode(lib, case, ks, vs, out_v, stream)}
+        res = {"workload": name, "group": case.num_heads // case.num_kv_heads,
+               "bytes": case.algorithmic_bytes()}
+        for kind, fn in calls.items():
+            for _ in range(warmup):
+                assert fn() == 0
+            torch.cuda.synchronize()
+            pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                     for _ in range(steps)]
+            for a, b in pairs:
+                a.record(stream)
+                assert fn() == 0
+                b.record(stream)
+            torch.cuda.synchronize()
+            per = sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)
+            med = per[len(per) // 2]
+            res[kind] = {"us_median": round(med, 2), "us_mean": round(sum(per) / len(per), 2),
+                         "GBps": round(res["bytes"] / med / 1e3, 1),
+                         "frac_of_peak": round(res["bytes"] / med / 1e3 / PEAK_GBS, 4)}
+        res["valu_over_mfma"] = round(res["valu"]["us_median"] / res["mfma"]["us_median"], 3)
+        res["max_abs_diff"] = float((out_m.float() - out_v.float()).abs().max())
+        print(json.dumps(res), flush=True)
+        del case, out_m, out_v
+        torch.cuda.empty_cache()
+
+
 def P_one_launch(case):
     """Whether one call of `case` is a single launch of the decode kernel (one
     partition, no order kernel, one query per sequence)."""
@@ -550,6 +621,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--read-ceiling", action="store_true")
+    ap.add_argument("--valu-compare", action="store_true",
+                    help="the decode against the same decode on the vector ALUs (probe)")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replay timing (profiler runs: only the timed calls)")
     ap.add_argument("--after-suite-workloads", type=int, default=0,
@@ -577,6 +650,9 @@ def main():
         return
     if args.read_ceiling:
         read_ceiling(args.steps)
+        return
+    if args.valu_compare:
+        valu_compare(args.steps, args.warmup)
         return
 
     import paged_attention_decode_03_amd as pa

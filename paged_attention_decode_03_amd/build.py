@@ -1,5 +1,6 @@
-"""Build libpagedattn.so (HIP, gfx950) in-tree with hipcc, and the bandwidth
-probes the benchmark uses (libpa_probe.so, not part of the attention library).
+"""Build libpagedattn.so (HIP, gfx950) in-tree with hipcc, and the probes the
+benchmark uses (libpa_probe.so, not part of the attention library: bandwidth
+probes and a decode with its dot products on the vector ALUs).
 
     python -m paged_attention_decode_03_amd.build
 """
@@ -17,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpagedattn.so")
 SOURCES = ["pa_decode_kernels.hip", "pa_cache_write.hip", "pa_api.hip"]
 PROBE_LIB = os.path.join(PKG, "libpa_probe.so")
-PROBE_SOURCES = ["pa_probe.hip"]
+PROBE_SOURCES = ["pa_probe.hip", "pa_probe_valu.hip"]
 ARCH = "gfx950"
 
 
