@@ -703,33 +703,54 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
 #pragma unroll
       for (int pp = 0; pp < PPS; ++pp) ksq[pp] = quad_gather(st.ks[pp]);
     }
-    // scale, mask, running max
+    // scale (and the options: softcap, ALiBi), mask, running max.  Each step
+    // that not every stage needs sits under one wave-uniform branch around
+    // the whole tile, so a stage without options or masking pays for neither.
+    const bool masked = last || causal;
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
-      float mx = -INFINITY;
+      if (MQ && (capped || biased)) {
 #pragma unroll
-      for (int pp = 0; pp < PPS; ++pp) {
+        for (int pp = 0; pp < PPS; ++pp) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float v = z[u][pp][i] * c_log2;
-          if constexpr (SS) v *= __uint_as_float(ksq[pp][i]);
-          if constexpr (MQ) {
-            const int t = (j0 + pp) * kBlockTokens + rq * 4 + i;
+          for (int i = 0; i < 4; ++i) {
+            float v = z[u][pp][i] * c_log2;
             if (capped) {
               // c tanh(z / c) = c (1 - 2 / (e^(2 z / c) + 1)), then in log2 units
               const float e2 = __builtin_amdgcn_exp2f(z[u][pp][i] * c_nat * cap_k);
               v = cap_l2 * (1.0f - 2.0f * __builtin_amdgcn_rcpf(e2 + 1.0f));
             }
-            if (biased) v += slope_l2 * (float)(t - pos_col[u]);
-            if (last || causal) v = (t < tlim[u] && t >= tlo[u]) ? v : -INFINITY;
-          } else if (last) {
-            const int t = (j0 + pp) * kBlockTokens + rq * 4 + i;
-            v = (t < tlim[u]) ? v : -INFINITY;
+            if (biased) v += slope_l2 * (float)((j0 + pp) * kBlockTokens + rq * 4 + i - pos_col[u]);
+            z[u][pp][i] = v;
           }
-          z[u][pp][i] = v;
-          mx = fmaxf(mx, v);
+        }
+      } else {
+#pragma unroll
+        for (int pp = 0; pp < PPS; ++pp) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float v = z[u][pp][i] * c_log2;
+            if constexpr (SS) v *= __uint_as_float(ksq[pp][i]);
+            z[u][pp][i] = v;
+          }
         }
       }
+      if (masked) {
+#pragma unroll
+        for (int pp = 0; pp < PPS; ++pp) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = (j0 + pp) * kBlockTokens + rq * 4 + i;
+            const bool keep = MQ ? (t < tlim[u] && t >= tlo[u]) : t < tlim[u];
+            z[u][pp][i] = keep ? z[u][pp][i] : -INFINITY;
+          }
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int pp = 0; pp < PPS; ++pp)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, z[u][pp][i]);
       mx = max_over_rows(mx);
       const float m_new = fmaxf(m_run[u], mx);
       if (__builtin_amdgcn_ballot_w64(m_new > m_run[u])) {
@@ -796,13 +817,12 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
         f16x4 pb[NT];
 #pragma unroll
         for (int u = 0; u < NT; ++u) {
+          // a column that has seen no token yet (several queries: a causal end
+          // before this item's tokens) has m_run = -inf and every z = -inf:
+          // measured from 0 instead, its weights are 2^-inf = 0
+          const float m_ref = (MQ && m_run[u] == -INFINITY) ? 0.0f : m_run[u];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            // a column that has seen no token yet has m_run = -inf: its weights are 0
-            float e = __builtin_amdgcn_exp2f(z[u][pp][i] - m_run[u]);
-            if constexpr (MQ) e = (z[u][pp][i] == -INFINITY) ? 0.0f : e;
-            pb[u][i] = (_Float16)e;
-          }
+          for (int i = 0; i < 4; ++i) pb[u][i] = (_Float16)__builtin_amdgcn_exp2f(z[u][pp][i] - m_ref);
         }
 #pragma unroll
         for (int jd = 0; jd < 8; ++jd) {
