@@ -296,8 +296,15 @@ int plan_call(int32_t S, int32_t Hq, int32_t Hkv, int32_t W, int32_t cus, int32_
   cp->q_tile = mq ? (pa::kMaxGroup / G > 0 ? pa::kMaxGroup / G : 1) : 1;
   cp->q_tiles = mq ? (max_seqlen_q + cp->q_tile - 1) / cp->q_tile : 1;
   // query tiles per work item: up to three (one wave holds their accumulators
-  // against the same K/V); four tiles go as two items of two
-  cp->tiles_per_item = cp->q_tiles <= 2 ? cp->q_tiles : (cp->q_tiles == 4 ? 2 : 3);
+  // against the same K/V); four tiles go as two items of two.  Three tiles
+  // leave registers for one page a stage, which pays only where most
+  // sequences fill them: the batch's query rows must average more than two
+  // tiles a sequence (measured on MI355X, 40/8 ctx 4096 x 256, graph replay:
+  // 8 queries per sequence 395 us at three tiles an item, 566 us at two; a
+  // mixed batch of 256 ragged sequences, 60% with one query and the rest 2..16,
+  // 770 rows: 458 us at three, 307 us at two, 424 us at one)
+  const bool full_tiles = (int64_t)num_q_rows > (int64_t)2 * cp->q_tile * (S > 0 ? S : 1);
+  cp->tiles_per_item = cp->q_tiles <= 2 ? cp->q_tiles : (cp->q_tiles == 4 || !full_tiles ? 2 : 3);
   cp->q_items = (cp->q_tiles + cp->tiles_per_item - 1) / cp->tiles_per_item;
   // longest-first: computed by each work item where its workgroup is one wave
   // and the sequences few enough, else by the order kernel

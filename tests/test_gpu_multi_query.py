@@ -80,6 +80,7 @@ SMALL = [
     (12, 4, [3, 50, 129], [3, 7, 11]),                         # G=3: 5 per tile, one idle column
     (20, 4, [31, 32, 33, 100], [4, 6, 1, 13]),                 # G=5: 3 per tile
     (40, 8, [1, 100, 1000, 17, 4], [1, 4, 4, 17, 2]),          # G=5, the target layout
+    (40, 8, [100, 64, 1000, 9], [9, 8, 1, 9]),                 # G=5, three tiles an item, one query alone
     (32, 4, [64, 65, 256, 257], [2, 3, 4, 5]),                 # G=8: 2 per tile
     (16, 1, [48, 333, 7], [3, 2, 7]),                          # G=16: 1 per tile
     (8, 2, [40, 70, 90, 5], [0, 12, 0, 5]),                    # sequences without queries
@@ -209,6 +210,16 @@ def test_speculative_decode_target_layout():
     case = workloads.make_multi_case(40, 8, [ctx] * S, [4] * S, seed=71, device="cuda")
     log(f"spec decode 40/8 x{S} ctx {ctx} q_len 4")
     check(case, "spec decode q_len 4")
+
+
+def test_speculative_decode_eight_queries():
+    """40/8 heads, 64 sequences of 4096 tokens, 8 new tokens each: three
+    query tiles a work item (the query rows average more than two tiles a
+    sequence), one read of the pages for all of them."""
+    S, ctx = 64, 4096
+    case = workloads.make_multi_case(40, 8, [ctx] * S, [8] * S, seed=72, device="cuda")
+    log(f"spec decode 40/8 x{S} ctx {ctx} q_len 8")
+    check(case, "spec decode q_len 8")
 
 
 def test_mixed_batch():
