@@ -85,7 +85,7 @@ def counter_traffic():
 def make_workload(name, device):
     import workloads
     if name.endswith("_lpt") and not name.startswith("ragged_"):
-        # any one-query workload with longest-first dispatch
+        # any workload of the suite with longest-first dispatch
         case = make_workload(name[:-4], device)
         case.longest_first = True
         case.name = name
@@ -169,7 +169,7 @@ def suite_names():
     names += ["target", "dense_20x4_ctx4096_s256"]
     names += ["slotscales_40x8_ctx4096_s256"]
     names += [f"specdec_40x8_ctx4096_s256_q{q}" for q in (2, 3, 4, 8)]
-    names += ["mixed_40x8_s256"]
+    names += ["mixed_40x8_s256", "mixed_40x8_s256_lpt"]
     names += [f"tokenrows_{lay}_40x8_ctx4096_s256" for lay in ("nhd", "combined", "packed")]
     names += ["unified_40x8_ctx4096_s256_" + o for o in ("window1024", "softcap30", "alibi", "sinks")]
     names += ["unified_40x8_ctx4096_s256_q4_window128+sinks"]
@@ -229,7 +229,9 @@ def make_call(case, out, stream=None):
                                                   case.block_tables, case.seq_lens, case.scale, ks,
                                                   vs, out=out, stream=stream, **opts)
     if getattr(case, "longest_first", False):
-        return lambda: pa.paged_attention_unified(case.q, None, 1, case.k_cache, case.v_cache,
+        cu = case.cu_seqlens_q
+        max_q = 1 if cu is None else int((cu[1:] - cu[:-1]).max().item())
+        return lambda: pa.paged_attention_unified(case.q, cu, max_q, case.k_cache, case.v_cache,
                                                   case.block_tables, case.seq_lens, case.scale, ks,
                                                   vs, longest_first=True, out=out, stream=stream)
     if case.cu_seqlens_q is not None:
