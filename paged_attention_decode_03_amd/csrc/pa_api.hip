@@ -210,7 +210,7 @@ int ensure_workspace(int dev, hipStream_t stream, size_t bytes, void** out) {
   // the arrival counters start at zero: cleared and waited for here, before
   // any call can use the buffer (never while `stream` captures)
   if (hipMemsetAsync(p, 0, kCounterRegion, stream) != hipSuccess || hipStreamSynchronize(stream) != hipSuccess) {
-    hipFree(p);
+    (void)hipFree(p);
     return fail(PA_ERR_HIP, "clearing the scratch's counters failed");
   }
   if (ws.ptr) g_retired.push_back(ws.ptr);
