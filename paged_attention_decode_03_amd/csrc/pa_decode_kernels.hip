@@ -298,8 +298,13 @@ struct Stage {
 // (max, denominator, accumulator) to wave 0 through LDS at the end, which
 // combines them by the log-sum-exp rule: twice the waves on a CU for the same
 // work items, no second kernel.
+//
+// OPT (several queries): the per-logit options, softcap and ALiBi, compiled
+// in.  Without them the logit loop holds no branch for them (a wave-uniform
+// branch there measured 2.7% on 8 queries per sequence); window and sinks
+// need no per-logit work and run in every several-queries kernel.
 template <int PPS, int NB, bool SS, bool MQ, int AUX = PA_LOAD_AUX, bool TR = false, int NT = 1,
-          bool VL = false, int WPI = 1>
+          bool VL = false, int WPI = 1, bool OPT = false>
 __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64 * WPI)
 __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_EU))) void pa_decode_kernel(const DecodeParams p) {
   const int lane = threadIdx.x & 63;
@@ -483,11 +488,11 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
   // logits in log2 units: z * scale * k_scale * log2(e) (k_scale per slot when SS)
   const float c_log2 = SS ? p.scale_log2e : p.scale_log2e * scalar_load(p.k_scale);
   // softcap: the natural-unit logit z * scale * k_scale, capped, then in log2 units
-  const bool capped = MQ && p.softcap > 0.0f;
+  const bool capped = MQ && OPT && p.softcap > 0.0f;
   const float c_nat = MQ ? p.scale * scalar_load(p.k_scale) : 0.0f;
   const float cap_k = MQ && capped ? 2.0f * kLog2e / p.softcap : 0.0f;
   const float cap_l2 = MQ ? p.softcap * kLog2e : 0.0f;
-  const bool biased = MQ && p.alibi_slopes != nullptr;
+  const bool biased = MQ && OPT && p.alibi_slopes != nullptr;
 
   const size_t page_stride = (size_t)p.block_stride;
   const size_t head_off = (size_t)kvh * p.head_stride;
@@ -709,7 +714,7 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
     const bool masked = last || causal;
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
-      if (MQ && (capped || biased)) {
+      if constexpr (MQ && OPT) {
 #pragma unroll
         for (int pp = 0; pp < PPS; ++pp) {
 #pragma unroll
@@ -1161,6 +1166,8 @@ __global__ __launch_bounds__(kOrderThreads) void pa_order_kernel(const DecodePar
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
+  // per-logit options (several-queries kernels only): the instantiations that hold them
+  const bool opt = p.softcap > 0.0f || p.alibi_slopes != nullptr;
   if (p.seq_order)
     hipLaunchKernelGGL(pa_order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, p);
   const size_t units = (size_t)p.num_seqs * p.num_kv_heads * p.num_parts;
@@ -1175,6 +1182,15 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   // V through LDS where it measured faster on MI355X (40/8 ctx 4096 x 256):
   // two query tiles per item (4 queries: 372.9 -> 369.4 us) and per-slot
   // scales (339.8 -> 335.6 us); one tile per item was 0.5% slower with it
+  else if (p.multi_query && opt && p.tiles_per_item == 3)
+    hipLaunchKernelGGL((pa_decode_kernel<kThreeTilePagesPerStage, kRingDepth, false, true, PA_LOAD_AUX, false, 3, true, 1, true>),
+                       dim3((unsigned)items), dim3(64), kThreeTilePagesPerStage * kPageBytes, stream, p);
+  else if (p.multi_query && opt && p.tiles_per_item == 2)
+    hipLaunchKernelGGL((pa_decode_kernel<kTwoTilePagesPerStage, kRingDepth, false, true, PA_LOAD_AUX, false, 2, true, 1, true>),
+                       dim3((unsigned)items), dim3(64), kTwoTilePagesPerStage * kPageBytes, stream, p);
+  else if (p.multi_query && opt)
+    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, true, PA_LOAD_AUX, false, 1, false, 1, true>),
+                       dim3((unsigned)items), dim3(64), 0, stream, p);
   else if (p.multi_query && p.tiles_per_item == 3)
     hipLaunchKernelGGL((pa_decode_kernel<kThreeTilePagesPerStage, kRingDepth, false, true, PA_LOAD_AUX, false, 3, true>),
                        dim3((unsigned)items), dim3(64), kThreeTilePagesPerStage * kPageBytes, stream, p);
