@@ -708,9 +708,9 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
 #pragma unroll
       for (int pp = 0; pp < PPS; ++pp) ksq[pp] = quad_gather(st.ks[pp]);
     }
-    // scale (and the options: softcap, ALiBi), mask, running max.  Each step
-    // that not every stage needs sits under one wave-uniform branch around
-    // the whole tile, so a stage without options or masking pays for neither.
+    // scale (and the options: softcap, ALiBi), mask, running max.  The mask,
+    // which only stages at a causal end or window start need, sits under one
+    // wave-uniform branch for all tiles.
     const bool masked = last || causal;
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
@@ -740,24 +740,34 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
           }
         }
       }
-      if (masked) {
+    }
+    if (masked) {
 #pragma unroll
-        for (int pp = 0; pp < PPS; ++pp) {
+      for (int u = 0; u < NT; ++u)
+#pragma unroll
+        for (int pp = 0; pp < PPS; ++pp)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int t = (j0 + pp) * kBlockTokens + rq * 4 + i;
             const bool keep = MQ ? (t < tlim[u] && t >= tlo[u]) : t < tlim[u];
             z[u][pp][i] = keep ? z[u][pp][i] : -INFINITY;
           }
-        }
-      }
-      float mx = -INFINITY;
+    }
+    // the tiles' maxima first (their cross-lane steps overlap), then each
+    // tile's rescale where its max grew
+    float mx[NT];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      mx[u] = -INFINITY;
 #pragma unroll
       for (int pp = 0; pp < PPS; ++pp)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, z[u][pp][i]);
-      mx = max_over_rows(mx);
-      const float m_new = fmaxf(m_run[u], mx);
+        for (int i = 0; i < 4; ++i) mx[u] = fmaxf(mx[u], z[u][pp][i]);
+      mx[u] = max_over_rows(mx[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      const float m_new = fmaxf(m_run[u], mx[u]);
       if (__builtin_amdgcn_ballot_w64(m_new > m_run[u])) {
         const float alpha = (m_new == m_run[u]) ? 1.0f : __builtin_amdgcn_exp2f(m_run[u] - m_new);
         if constexpr (!SS) {  // (per-slot: the numerator has a running max of its own)
