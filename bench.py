@@ -171,6 +171,7 @@ def suite_names():
     names += [f"specdec_40x8_ctx4096_s256_q{q}" for q in (2, 3, 4, 8)]
     names += ["mixed_40x8_s256", "mixed_40x8_s256_lpt"]
     names += [f"tokenrows_{lay}_40x8_ctx4096_s256" for lay in ("nhd", "combined", "packed")]
+    names += ["tokenrows_nhd_40x8_ctx4096_s64", "tokenrows_nhd_40x8_ctx1024_s16"]
     names += ["unified_40x8_ctx4096_s256_" + o for o in ("window1024", "softcap30", "alibi", "sinks")]
     names += ["unified_40x8_ctx4096_s256_q4_window128+sinks"]
     names += [f"ragged_{a}x{b}_seed0" for (a, b) in workloads.RAGGED_LAYOUTS]

@@ -336,15 +336,17 @@ int paged_decode_attention_slot_scales(const void* q, const void* k_cache, const
                                        void* out, void* stream);
 
 /*
- * Launch plan of the one-query decode (paged_decode_attention,
- * paged_decode_attention_split, _desc, _slot_scales, _nhd) for the given
- * shapes: host arithmetic only, no device access.
+ * Launch plan of the one-query decode on block-layout caches
+ * (paged_decode_attention, paged_decode_attention_split, _desc, _slot_scales)
+ * for the given shapes: host arithmetic only, no device access.
  * num_compute_units: the device's CU count (256 on MI355X).
  * pages_per_partition: as in paged_decode_attention_split (0 = library's choice).
  * Outputs (any may be NULL): number of partitions per sequence, blocks per
  * partition, and the split-KV scratch bytes that plan needs (0 when it has one
- * partition).  Several queries per sequence and longest-first dispatch change
- * the plan: pa_workspace_bytes covers them.  Returns PA_OK or PA_ERR_SHAPE.
+ * partition).  Token-row caches (paged_decode_attention_nhd, which splits
+ * more where one partition leaves one to eight work items per CU), several
+ * queries per sequence and longest-first dispatch change the plan:
+ * pa_workspace_bytes covers them.  Returns PA_OK or PA_ERR_SHAPE.
  */
 int pa_decode_plan(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                    int32_t max_blocks_per_seq, int32_t num_compute_units,

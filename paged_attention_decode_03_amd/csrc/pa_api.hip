@@ -53,6 +53,18 @@ int fail(int code, const char* fmt, ...) {
 constexpr int kTokenRowMaxKvGroup = PA_TR_MAX_KV_GROUP;  // kv heads walking a sequence together
 constexpr int kItemsPerCU = PA_ITEMS_PER_CU;  // from this many items per CU, no split
 constexpr int kSplitItemsPerCU = PA_SPLIT_ITEMS_PER_CU;  // what a split aims for, per CU
+// Token-row caches have no two-waves-per-item kernel, and a wave of theirs
+// streams less than a page-layout wave: they split into at least the
+// partitions the rule below gives, and further up to eight items per CU, with
+// at most kTokenRowMaxParts partitions.  Measured on MI355X (NHD layout, graph
+// replay, against the page layout's plan): 40/8 ctx 4096 x 64 sequences
+// 169 -> 89 us (four partitions), x 128 178 -> 169 us (two), 32/8 ctx 4096 x
+// 24 55.9 -> 45.8 us (eight), ctx 1024 x 24 19.1 -> 17.1 us (eight), 40/8 ctx
+// 32768 x 4 52.0 -> 48.8 us (64); the packed layout, 64 sequences 168.5 ->
+// 87.6 us.  256 partitions of one sequence lost (1 x 32768: 20.3 -> 21.5 us
+// against 128), hence the cap.
+constexpr int kTokenRowItemsPerCU = 8;
+constexpr int kTokenRowMaxParts = 64;
 // K/V working sets up to this size (about the 256 MB Infinity Cache and a
 // little more) are read with the default cache policy, which lets repeated
 // calls find the pages in that cache; larger ones stream past it (nt).
@@ -114,7 +126,8 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // where that leaves at most one item per CU), whole pipeline stages, and never
 // more than pa::kMaxPagesPerPart blocks.
 int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t W, int32_t num_cus, int32_t ppp_req,
-              Plan* plan, int32_t q_tiles = 1, int64_t q_rows = -1, bool longest_first = false) {
+              Plan* plan, int32_t q_tiles = 1, int64_t q_rows = -1, bool longest_first = false,
+              bool token_rows = false) {
   if (S < 0 || Hq <= 0 || Hkv <= 0 || W < 0 || ppp_req < 0)
     return fail(PA_ERR_SHAPE, "plan: negative or zero size (S=%d Hq=%d Hkv=%d W=%d ppp=%d)", S, Hq,
                 Hkv, W, ppp_req);
@@ -130,6 +143,12 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t W, int32_t num_cus, in
     int64_t parts = 1;
     if (items < cus * kItemsPerCU)
       while (parts * 2 * items <= cus * kSplitItemsPerCU) parts *= 2;
+    if (token_rows) {
+      int64_t tr_parts = 1;
+      while (tr_parts * 2 * items <= cus * kTokenRowItemsPerCU && tr_parts * 2 <= kTokenRowMaxParts)
+        tr_parts *= 2;
+      if (tr_parts > parts) parts = tr_parts;
+    }
     if (parts > Wc) parts = Wc;
     ppp = ceil_div(Wc, parts < 1 ? 1 : parts);
     if (ppp < Wc) {
@@ -311,7 +330,7 @@ int plan_call(int32_t S, int32_t Hq, int32_t Hkv, int32_t W, int32_t cus, int32_
   cp->lpt_in_kernel = PA_LPT_IN_KERNEL && longest_first && !token_rows && S >= 2 &&
                       S <= kInKernelOrderMaxSeqs;
   return make_plan(S, Hq, Hkv, W, cus, ppp_req, &cp->plan, cp->q_items, mq ? num_q_rows : S,
-                   longest_first && !cp->lpt_in_kernel);
+                   longest_first && !cp->lpt_in_kernel, token_rows && !mq);
 }
 
 int decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
@@ -481,15 +500,19 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   // token rows: where the kv heads' rows interleave within a token's row
   // (head stride below token stride, as in [blocks, 16, kv_heads, 128]), the
   // largest divisor of Hkv up to 8 kv heads share a workgroup and read each
-  // block together; a layout that keeps a (block, kv head) together gains
-  // nothing from it
+  // block together, as long as the launch keeps a workgroup per CU (measured on
+  // MI355X, 40/8 NHD ctx 4096 x 16 sequences, 8 partitions: 8 kv heads a
+  // workgroup 40.3 us, 4 30.0 us); a layout that keeps a (block, kv head)
+  // together gains nothing from it
   p.kv_group = 1;
-  if (var.token_rows && var.head_stride < var.token_stride)
+  if (var.token_rows && var.head_stride < var.token_stride) {
+    const int64_t tr_items = (int64_t)S * Hkv * plan.num_parts;
     for (int g = kTokenRowMaxKvGroup; g >= 1; --g)
-      if (Hkv % g == 0) {
+      if (Hkv % g == 0 && (g == 1 || tr_items / g >= device_cus(dev))) {
         p.kv_group = g;
         break;
       }
+  }
   p.block_stride = bstride;
   p.token_stride = var.token_stride;
   p.head_stride = hstride;

@@ -379,6 +379,11 @@ def test_workspace_bytes_covers_several_queries_and_longest_first(lib):
     assert wsb(lib, 300, 16, 1, 128, lpt=1)[1] == plan(lib, 300, 16, 1, 128)[3]
     # token rows never sort inside the work items
     assert wsb(lib, 300, 16, 1, 128, lpt=1, tr=1)[1] > plan(lib, 300, 16, 1, 128)[3]
+    # token rows split where one partition leaves 1..8 items per CU: 64 x 40/8
+    # x 256 blocks (512 units) -> 4 partitions; the block layout keeps one
+    assert wsb(lib, 64, 40, 8, 256) == (0, 0)
+    assert wsb(lib, 64, 40, 8, 256, tr=1) == (0, 4096 + 64 * 40 * 4 * 130 * 4)
+    assert wsb(lib, 256, 40, 8, 256, tr=1) == (0, 0)
 
 
 def test_workspace_bytes_rejects_bad_shapes(lib):

@@ -127,6 +127,39 @@ def test_binding_rejects_mismatched_views():
                                       case.v_scale)
 
 
+@pytest.mark.parametrize("layout", workloads.TOKEN_ROW_LAYOUTS)
+def test_mid_batch_splits_where_the_page_layout_runs_two_waves(layout):
+    """64 sequences x 1024 tokens at 40/8: one partition would leave two work
+    items per CU, which the page layout serves with two waves per item; token
+    rows split into four partitions instead (and still group eight kv heads a
+    workgroup, 256 workgroups).  Bit for bit the page layout's split entry
+    point with the same partitions, and the oracle's result on every
+    sequence."""
+    import paged_attention_decode_03_amd as pa
+    case = workloads.dense(40, 8, 64, 1024, seed=9, device="cuda")
+    assert pa.pa_decode_plan(64, 40, 8, 64, 256)[:2] == (1, 64)
+    kv, vv = gpu_views(case, layout)
+    got = run_nhd(case, kv, vv)
+    del kv, vv
+    ref_split = run_gpu(case, 16)
+    log(f"token rows {layout} 64 x 1024")
+    assert torch.equal(got.view(torch.int16), ref_split.view(torch.int16)), "differs from 4-partition page layout"
+    compare(got, oracle_rows(case, layout), f"token rows {layout} 64 x 1024")
+
+
+def test_small_batch_groups_fewer_kv_heads():
+    """16 sequences x 1024 tokens at 40/8 (8 partitions, 1024 work items): four
+    kv heads a workgroup keep a workgroup per CU; the result is the page
+    layout's bit for bit."""
+    case = workloads.dense(40, 8, 16, 1024, seed=10, device="cuda")
+    kv, vv = gpu_views(case, "nhd")
+    got = run_nhd(case, kv, vv)
+    ref_page = run_gpu(case)
+    log("token rows nhd 16 x 1024")
+    assert torch.equal(got.view(torch.int16), ref_page.view(torch.int16))
+    compare(got, oracle_rows(case, "nhd"), "token rows nhd 16 x 1024")
+
+
 def test_target_shape_every_layout():
     """40/8 heads, 256 sequences x 4096 tokens (the benchmark's shape) in all
     three token-row layouts: each equals the page-layout kernel bit for bit
