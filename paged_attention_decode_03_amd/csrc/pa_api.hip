@@ -127,7 +127,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // more than pa::kMaxPagesPerPart blocks.
 int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t W, int32_t num_cus, int32_t ppp_req,
               Plan* plan, int32_t q_tiles = 1, int64_t q_rows = -1, bool longest_first = false,
-              bool token_rows = false) {
+              bool token_rows = false, bool lpt_requested = false) {
   if (S < 0 || Hq <= 0 || Hkv <= 0 || W < 0 || ppp_req < 0)
     return fail(PA_ERR_SHAPE, "plan: negative or zero size (S=%d Hq=%d Hkv=%d W=%d ppp=%d)", S, Hq,
                 Hkv, W, ppp_req);
@@ -141,7 +141,14 @@ int make_plan(int32_t S, int32_t Hq, int32_t Hkv, int32_t W, int32_t num_cus, in
     // a power of two of partitions, so that (table widths being powers of
     // two in practice) partitions are even and items divide over the CUs
     int64_t parts = 1;
-    if (items < cus * kItemsPerCU)
+    // exactly kItemsPerCU items per CU split in two as well (measured on
+    // MI355X, 512 items, graph replay, two partitions merged in the decode
+    // against two waves per item: 40/8 ctx 4096 x 64 sequences 91.0 -> 84.3
+    // us, 32/8 x 64 92.5 -> 86.1 us, 20/4 x 128 93.8 -> 86.6 us, 32/4 x 128
+    // 90.6 -> 84.8 us; ctx 1024 and 2048 within 1%; per-slot scales, which
+    // have no two-waves form, 142.3 -> 91.0 us); longest-first dispatch keeps
+    // them whole for its two waves per item
+    if (items < cus * kItemsPerCU || (items == cus * kItemsPerCU && !lpt_requested))
       while (parts * 2 * items <= cus * kSplitItemsPerCU) parts *= 2;
     if (token_rows) {
       int64_t tr_parts = 1;
@@ -330,7 +337,7 @@ int plan_call(int32_t S, int32_t Hq, int32_t Hkv, int32_t W, int32_t cus, int32_
   cp->lpt_in_kernel = PA_LPT_IN_KERNEL && longest_first && !token_rows && S >= 2 &&
                       S <= kInKernelOrderMaxSeqs;
   return make_plan(S, Hq, Hkv, W, cus, ppp_req, &cp->plan, cp->q_items, mq ? num_q_rows : S,
-                   longest_first && !cp->lpt_in_kernel, token_rows && !mq);
+                   longest_first && !cp->lpt_in_kernel, token_rows && !mq, longest_first);
 }
 
 int decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
@@ -534,11 +541,12 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
                       ? 1 : 0;
   p.unit_count = nullptr;
   // two waves per work item where one partition leaves more than one and at
-  // most two items per CU: four waves streaming on a CU instead of two, no
-  // split (measured on MI355X, 512 items: 40/8 ctx 4096 x 64 sequences 95.7 ->
-  // 88.3 us, 20/4 ctx 4096 x 128 96.0 -> 87.8 us, ctx 1024 and 2048 within 1%;
-  // at 3 to 4 items per CU, and with split contexts, it measured 3-10% slower)
-  // longest-first: up to kLptTwoWaveItemsPerCU items per CU
+  // most kLptTwoWaveItemsPerCU items per CU under longest-first dispatch
+  // (without it such launches split into two partitions instead: see the
+  // plan).  Measured on MI355X, 512 items, against one wave per item: 40/8
+  // ctx 4096 x 64 sequences 95.7 -> 88.3 us, 20/4 ctx 4096 x 128 96.0 -> 87.8
+  // us (two partitions: 84.3 and 86.6 us); with split contexts two waves
+  // measured 3-10% slower
   const int64_t cus = device_cus(dev);
   const bool lpt_on = cp.lpt_in_kernel || plan.longest_first;
   p.waves_per_item = (!mq && !slot_scales && !var.token_rows && plan.num_parts == 1 && units > cus &&

@@ -71,9 +71,13 @@ def test_plan_split_is_a_power_of_two_within_four_items_per_cu(lib):
     assert plan(lib, 24, 32, 8, 256)[:3] == (0, 4, 64)
     # 4 x ctx 32768: 32 units -> 32 partitions of 64 blocks
     assert plan(lib, 4, 40, 8, 2048)[:3] == (0, 32, 64)
-    # 300 units -> 2 partitions; 512 units (two per CU) -> unsplit
+    # 300 units -> 2 partitions; 512 units (exactly two per CU) -> 2 as well
     assert plan(lib, 300, 8, 1, 256)[:3] == (0, 2, 128)
-    assert plan(lib, 64, 40, 8, 64)[:3] == (0, 1, 64)
+    assert plan(lib, 64, 40, 8, 64)[:3] == (0, 2, 32)
+    assert plan(lib, 128, 40, 8, 256)[:3] == (0, 1, 256)
+    # longest-first keeps exactly two per CU whole (two waves per item), and
+    # orders them inside the work items: no scratch
+    assert wsb(lib, 64, 40, 8, 64, lpt=1) == (0, 0)
     # a width that is no power of two: partitions of whole stages, the last shorter
     assert plan(lib, 256, 8, 1, 250)[:3] == (0, 4, 64)
 
@@ -379,9 +383,9 @@ def test_workspace_bytes_covers_several_queries_and_longest_first(lib):
     assert wsb(lib, 300, 16, 1, 128, lpt=1)[1] == plan(lib, 300, 16, 1, 128)[3]
     # token rows never sort inside the work items
     assert wsb(lib, 300, 16, 1, 128, lpt=1, tr=1)[1] > plan(lib, 300, 16, 1, 128)[3]
-    # token rows split where one partition leaves 1..8 items per CU: 64 x 40/8
-    # x 256 blocks (512 units) -> 4 partitions; the block layout keeps one
-    assert wsb(lib, 64, 40, 8, 256) == (0, 0)
+    # token rows split up to eight items per CU: 64 x 40/8 x 256 blocks (512
+    # units) -> 4 partitions; the block layout takes 2
+    assert wsb(lib, 64, 40, 8, 256) == (0, 4096 + 64 * 40 * 2 * 130 * 4)
     assert wsb(lib, 64, 40, 8, 256, tr=1) == (0, 4096 + 64 * 40 * 4 * 130 * 4)
     assert wsb(lib, 256, 40, 8, 256, tr=1) == (0, 0)
 

@@ -367,28 +367,31 @@ def test_block_ids_outside_the_caches_read_as_zero_pages():
 
 
 def test_two_waves_per_item():
-    """One partition with two work items per CU (64 sequences x 8 kv heads =
-    512 items on 256 CUs) runs two waves per item, each computing every other
-    stage of 4 pages, combined in LDS.  Ragged contexts with empty, one-token,
-    one-stage and one-token-past-a-stage sequences, in both cache-policy
-    instantiations (an 80-block table: cached loads; 256 blocks: streamed, V
-    through LDS), with NaN poison outside the contexts (must equal the clean
-    case bit for bit), must meet the bound; longest-first order must equal the
-    plain order bit for bit."""
+    """Two waves per work item (each computing every other stage of 4 pages,
+    combined in LDS) run where one partition leaves two work items per CU
+    (64 sequences x 8 kv heads = 512 items on 256 CUs) and the contexts stay
+    whole: an explicit partition of the whole table, or longest-first
+    dispatch.  Ragged contexts with empty, one-token, one-stage and
+    one-token-past-a-stage sequences, in both cache-policy instantiations (an
+    80-block table: cached loads; 256 blocks: streamed, V through LDS), with
+    NaN poison outside the contexts (must equal the clean case bit for bit),
+    must meet the bound; longest-first must equal the whole-table call bit
+    for bit.  The library's own plan splits such launches in two (merged in
+    the decode), which must meet the bound as well."""
     import paged_attention_decode_03_amd as pa
     for W, top in ((80, 1280), (256, 4096)):
-        P, ppp, _ = pa.pa_decode_plan(64, 40, 8, W, 256)
-        assert P == 1
+        assert pa.pa_decode_plan(64, 40, 8, W, 256)[:2] == (2, W // 2)
         lens = [0, 1, 15, 16, 17, 63, 64, 65, 127, 128, 129, top, top - 1, 700, 333, 1000] * 4
         cases = [workloads.make_case(40, 8, lens, seed=51 + W, max_blocks=W, poison=p) for p in (True, False)]
         log(f"two waves per item, {W}-block table, poison vs clean")
-        a, b = run_gpu(cases[0]).cpu(), run_gpu(cases[1]).cpu()
+        a, b = run_gpu(cases[0], W).cpu(), run_gpu(cases[1], W).cpu()
         assert torch.isfinite(a.float()).all()
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
         for s in range(64):
             if lens[s] == 0:
                 assert torch.count_nonzero(a[s]) == 0
-        compare(a, run_oracle(cases[1]), f"two waves per item, W={W}")
+        ref = run_oracle(cases[1])
+        compare(a, ref, f"two waves per item, W={W}")
         c = cases[0].to("cuda")
         ks = torch.tensor([c.k_scale], device="cuda")
         vs = torch.tensor([c.v_scale], device="cuda")
@@ -397,6 +400,8 @@ def test_two_waves_per_item():
         torch.cuda.synchronize()
         log(f"two waves per item, {W}-block table, longest first")
         assert torch.equal(lpt.cpu().view(torch.int16), a.view(torch.int16))
+        log(f"two partitions, {W}-block table")
+        compare(run_gpu(cases[0]).cpu(), ref, f"two partitions, W={W}")
 
 
 def test_fused_merge_counters_stay_consistent():

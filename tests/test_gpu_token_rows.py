@@ -128,16 +128,15 @@ def test_binding_rejects_mismatched_views():
 
 
 @pytest.mark.parametrize("layout", workloads.TOKEN_ROW_LAYOUTS)
-def test_mid_batch_splits_where_the_page_layout_runs_two_waves(layout):
+def test_mid_batch_splits_into_eight_items_per_cu(layout):
     """64 sequences x 1024 tokens at 40/8: one partition would leave two work
-    items per CU, which the page layout serves with two waves per item; token
-    rows split into four partitions instead (and still group eight kv heads a
-    workgroup, 256 workgroups).  Bit for bit the page layout's split entry
-    point with the same partitions, and the oracle's result on every
-    sequence."""
+    items per CU; the page layout splits in two, token rows into four (eight
+    items per CU, still eight kv heads a workgroup: 256 workgroups).  Bit for
+    bit the page layout's split entry point with the same partitions, and the
+    oracle's result on every sequence."""
     import paged_attention_decode_03_amd as pa
     case = workloads.dense(40, 8, 64, 1024, seed=9, device="cuda")
-    assert pa.pa_decode_plan(64, 40, 8, 64, 256)[:2] == (1, 64)
+    assert pa.pa_decode_plan(64, 40, 8, 64, 256)[:2] == (2, 32)
     kv, vv = gpu_views(case, layout)
     got = run_nhd(case, kv, vv)
     del kv, vv
