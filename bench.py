@@ -114,15 +114,17 @@ def make_workload(name, device):
         hq, hkv, ctx, s, ql = map(int, m.groups())
         return workloads.make_multi_case(hq, hkv, [ctx] * s, [ql] * s, seed=0, device=device,
                                          name=name)
-    m = re.fullmatch(r"mixed_(\d+)x(\d+)_s(\d+)", name)
+    m = re.fullmatch(r"mixed_(\d+)x(\d+)_s(\d+)(?:_qmax(\d+))?", name)
     if m:
         # decode rows next to short prefill chunks and drafts: contexts uniform in
         # [1, 4000]; 60% of the sequences have one query, the rest 2..5, 8 or 16
+        # (with _qmaxN: those up to N)
         import numpy as np
-        hq, hkv, s = map(int, m.groups())
+        hq, hkv, s = map(int, m.groups()[:3])
+        qmax = int(m.group(4) or 16)
         lens = workloads.ragged_lens(s, seed=3)
         g = np.random.default_rng(81)
-        ql = np.where(g.random(s) < 0.6, 1, g.choice([2, 3, 4, 5, 8, 16], size=s))
+        ql = np.where(g.random(s) < 0.6, 1, g.choice([c for c in (2, 3, 4, 5, 8, 16) if c <= qmax], size=s))
         ql = np.minimum(ql, lens).tolist()
         return workloads.make_multi_case(hq, hkv, lens, ql, seed=81, max_blocks=250, device=device,
                                          name=name)
@@ -169,7 +171,7 @@ def suite_names():
     names += ["target", "dense_20x4_ctx4096_s256"]
     names += ["slotscales_40x8_ctx4096_s256"]
     names += [f"specdec_40x8_ctx4096_s256_q{q}" for q in (2, 3, 4, 8)]
-    names += ["mixed_40x8_s256", "mixed_40x8_s256_lpt"]
+    names += ["mixed_40x8_s256", "mixed_40x8_s256_lpt", "mixed_40x8_s256_qmax8", "mixed_40x8_s256_qmax8_lpt"]
     names += [f"tokenrows_{lay}_40x8_ctx4096_s256" for lay in ("nhd", "combined", "packed")]
     names += ["tokenrows_nhd_40x8_ctx4096_s64", "tokenrows_nhd_40x8_ctx1024_s16"]
     names += ["unified_40x8_ctx4096_s256_" + o for o in ("window1024", "softcap30", "alibi", "sinks")]

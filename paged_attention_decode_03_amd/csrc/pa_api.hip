@@ -64,6 +64,7 @@ constexpr int kSplitItemsPerCU = PA_SPLIT_ITEMS_PER_CU;  // what a split aims fo
 // 87.6 us.  256 partitions of one sequence lost (1 x 32768: 20.3 -> 21.5 us
 // against 128), hence the cap.
 constexpr int kTokenRowItemsPerCU = 8;
+constexpr int kThreeTileUnitsPerCU = 8;  // (sequence, kv head) units for three query tiles an item
 constexpr int kTokenRowMaxParts = 64;
 // K/V working sets up to this size (about the 256 MB Infinity Cache and a
 // little more) are read with the default cache policy, which lets repeated
@@ -322,15 +323,22 @@ int plan_call(int32_t S, int32_t Hq, int32_t Hkv, int32_t W, int32_t cus, int32_
   cp->q_tile = mq ? (pa::kMaxGroup / G > 0 ? pa::kMaxGroup / G : 1) : 1;
   cp->q_tiles = mq ? (max_seqlen_q + cp->q_tile - 1) / cp->q_tile : 1;
   // query tiles per work item: up to three (one wave holds their accumulators
-  // against the same K/V); four tiles go as two items of two.  Three tiles
-  // leave registers for one page a stage, which pays only where most
-  // sequences fill them: the batch's query rows must average more than two
-  // tiles a sequence (measured on MI355X, 40/8 ctx 4096 x 256, graph replay:
-  // 8 queries per sequence 395 us at three tiles an item, 566 us at two; a
-  // mixed batch of 256 ragged sequences, 60% with one query and the rest 2..16,
-  // 770 rows: 458 us at three, 307 us at two, 424 us at one)
-  const bool full_tiles = (int64_t)num_q_rows > (int64_t)2 * cp->q_tile * (S > 0 ? S : 1);
-  cp->tiles_per_item = cp->q_tiles <= 2 ? cp->q_tiles : (cp->q_tiles == 4 || !full_tiles ? 2 : 3);
+  // against the same K/V).  Three, at one page a stage, only where they make
+  // one item of a sequence's three tiles and the (sequence, kv head) units
+  // alone keep two waves per SIMD; otherwise items of two tiles, which for a
+  // three-tile sequence means two items reading its pages.  Measured on
+  // MI355X (graph replay, 40/8 heads, two -> three tiles an item; ragged
+  // contexts 1..4000): 256 sequences with 8 queries in 40% of them (the rest
+  // one) 323 -> 258 us, in 10% 315 -> 250 us, in all 334 -> 271 us, 256 x
+  // 4096 all 8 505 -> 384 us, 64/4 heads x 512 sequences (3 queries in 40%)
+  // 327 -> 271 us; but 128 ragged sequences (8 queries in 40%) 177 -> 194 us
+  // and 64 x 4096 all 8 139 -> 186 us.  Six tiles (16 queries at G = 5): two
+  // tiles an item win (256 ragged sequences, 16 queries in 40%: 325 us against
+  // 432 us at three; 256 x 4096 all 16: 692 against 742 us); five likewise
+  // (14 queries: 415 against 493 us).
+  const int64_t ncus = cus > 0 ? cus : kDefaultCUs;
+  const bool three = cp->q_tiles == 3 && (int64_t)(S > 0 ? S : 1) * Hkv >= kThreeTileUnitsPerCU * ncus;
+  cp->tiles_per_item = cp->q_tiles <= 2 ? cp->q_tiles : (three ? 3 : 2);
   cp->q_items = (cp->q_tiles + cp->tiles_per_item - 1) / cp->tiles_per_item;
   // longest-first: computed by each work item where its workgroup is one wave
   // and the sequences few enough, else by the order kernel

@@ -375,6 +375,12 @@ def test_workspace_bytes_covers_several_queries_and_longest_first(lib):
     rc, n = wsb(lib, 4, 40, 8, 256, T=16, maxq=4)
     rc1, P, ppp, _ = plan(lib, 4, 40, 8, 256)
     assert rc == 0 and n == 4096 + 16 * 40 * P * 130 * 4
+    # 8 queries at 40/8 (three tiles a sequence): below eight (sequence, kv
+    # head) units per CU, items of two tiles, i.e. two items per unit.  16
+    # sequences: 256 items -> 4 partitions (three tiles an item would make
+    # 128 items and 8 partitions); 64 sequences: 1024 items, no split
+    assert wsb(lib, 16, 40, 8, 256, T=128, maxq=8) == (0, 4096 + 128 * 40 * 4 * 130 * 4)
+    assert wsb(lib, 64, 40, 8, 256, T=512, maxq=8) == (0, 0)
     # longest-first over 1000 sequences (more than a work item sorts itself):
     # the order kernel's 4 bytes a sequence after the 256-byte aligned partials
     rc, n = wsb(lib, 1000, 8, 1, 64, lpt=1)

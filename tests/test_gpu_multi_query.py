@@ -213,13 +213,27 @@ def test_speculative_decode_target_layout():
 
 
 def test_speculative_decode_eight_queries():
-    """40/8 heads, 64 sequences of 4096 tokens, 8 new tokens each: three
-    query tiles a work item (the query rows average more than two tiles a
-    sequence), one read of the pages for all of them."""
+    """40/8 heads, 64 sequences of 4096 tokens, 8 new tokens each: three query
+    tiles a sequence, which a batch of 512 (sequence, kv head) units spreads
+    over two items (of two tiles and of one) reading the same pages."""
     S, ctx = 64, 4096
     case = workloads.make_multi_case(40, 8, [ctx] * S, [8] * S, seed=72, device="cuda")
     log(f"spec decode 40/8 x{S} ctx {ctx} q_len 8")
     check(case, "spec decode q_len 8")
+
+
+def test_three_tiles_an_item():
+    """256 sequences at 40/8 (2048 (sequence, kv head) units: eight per CU),
+    ragged contexts in [1, 1000], 8 queries (three tiles) in 40% of them and
+    one in the rest: one item of three tiles per (sequence, kv head), and
+    sequences shorter than their queries' span."""
+    S = 256
+    lens = workloads.ragged_lens(S, hi=1000, seed=5)
+    g = np.random.default_rng(85)
+    ql = np.minimum(np.where(g.random(S) < 0.6, 1, 8), lens).tolist()
+    case = workloads.make_multi_case(40, 8, lens, ql, seed=85, max_blocks=64, device="cuda")
+    log("three tiles an item, 256 ragged sequences")
+    check(case, "three tiles an item")
 
 
 def test_mixed_batch():

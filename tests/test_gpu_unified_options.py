@@ -144,6 +144,21 @@ def test_all_options_together():
           alibi_slopes=slopes_for(40), sinks=np.linspace(-1, 1, 40).astype(np.float32))
 
 
+def test_options_with_three_tiles_an_item():
+    """256 sequences at 40/8 with up to 8 queries each (three tiles, one item
+    of three tiles per (sequence, kv head)): softcap and ALiBi compiled into
+    that item's logit loop, and window with sinks."""
+    S = 256
+    lens = workloads.ragged_lens(S, hi=300, seed=6)
+    g = np.random.default_rng(86)
+    ql = np.minimum(np.where(g.random(S) < 0.5, 1, g.choice([2, 5, 7, 8], size=S)), lens).tolist()
+    case = workloads.make_multi_case(40, 8, lens, ql, seed=86, max_blocks=32, device="cuda")
+    log("options, three tiles an item")
+    check(case, "three tiles: softcap + alibi", softcap=5.0, alibi_slopes=slopes_for(40))
+    check(case, "three tiles: window + sinks", sliding_window=40,
+          sinks=np.linspace(-1.0, 3.0, 40).astype(np.float32))
+
+
 def test_graph_capture_replays_match_eager():
     import paged_attention_decode_03_amd as pa
     case = workloads.make_multi_case(40, 8, [900, 40, 2000, 1], [4, 4, 3, 1], seed=95).to("cuda")
