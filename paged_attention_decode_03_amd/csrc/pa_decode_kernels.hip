@@ -140,10 +140,20 @@ __device__ __forceinline__ f16x4 fp8x4_to_f16(uint32_t v) {
   return r;
 }
 
-// Max of x over lanes l, l^16, l^32, l^48 (the four 16-lane rows).
+// max(a, b) for values that are never NaN: the one instruction.  (fmaxf on
+// values that came through a lane permute first quiets each operand, two
+// more instructions.)
+__device__ __forceinline__ float max_nonnan(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// Max of x over lanes l, l^16, l^32, l^48 (the four 16-lane rows); x is
+// never NaN (logits, or -inf where masked).
 __device__ __forceinline__ float max_over_rows(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  x = max_nonnan(__uint_as_float(r[0]), __uint_as_float(r[1]));
   const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
 }
@@ -166,6 +176,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   const __bf16 x = (__bf16)a;
   const __bf16 y = (__bf16)b;
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+// Byte mask of the first n of a dword's four slots (n <= 0: none, n >= 4: all).
+__device__ __forceinline__ uint32_t slot_bytes(int n) {
+  return n >= 4 ? 0xFFFFFFFFu : (n <= 0 ? 0u : ((1u << (8 * n)) - 1u));
 }
 
 __device__ __forceinline__ int clamp_len(int len, int max_blocks) {
@@ -512,6 +527,11 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
   f32x4 acc[NT][8];  // O^T tiles: dims 16*jd + 4*rq + i for column `col`
   f32x4 accl[NT];    // softmax denominator (same value in every element)
   float m_run[NT];
+  // the max the weights are taken against: m_run, except 0 for a column that
+  // has seen no token yet (several queries: a causal end before this item's
+  // tokens), whose every z is -inf and whose weights 2^-inf are then 0;
+  // updated with m_run
+  float m_ref[NT];
 #pragma unroll
   for (int u = 0; u < NT; ++u) {
 #pragma unroll
@@ -525,6 +545,7 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
         accl[u] = f32x4{1.f, 1.f, 1.f, 1.f};
       }
     }
+    m_ref[u] = (MQ && m_run[u] == -INFINITY) ? 0.0f : m_run[u];
   }
   const f16x4 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
   float mv_run = -INFINITY;  // per-slot variant: running max of z + E(v_scale), the numerator's
@@ -648,8 +669,35 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
     }
   };
 
-  auto compute = [&](const Stage<PPS>& st, int stage, bool last) {
+  auto compute = [&](Stage<PPS>& st, int stage, bool last) {
     const int j0 = pstart + stage * PPS;
+    if (last) {
+      // Slots past the context may hold anything (even NaN): their V bytes are
+      // zeroed here, once, so that no PV operand needs a mask.
+#pragma unroll
+      for (int pp = 0; pp < PPS; ++pp) {
+        const int nv = tend - (j0 + pp) * kBlockTokens;  // tokens of the page to keep
+        if constexpr (TR) {
+          // dwords 4 h .. 4 h + 3: 16 bytes of token 8 h + (lane >> 3)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              st.v[pp][4 * h + e] = 8 * h + (lane >> 3) < nv ? st.v[pp][4 * h + e] : 0u;
+        } else if constexpr (VL) {
+          // dword 4 h + e: slots 4 e .. 4 e + 3 of one dim
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st.v[pp][4 * h + e] &= slot_bytes(nv - 4 * e);
+        } else {
+          // dword jd: slots 4 rq .. 4 rq + 3 of one dim
+          const uint32_t m = slot_bytes(nv - 4 * rq);
+#pragma unroll
+          for (int jd = 0; jd < 8; ++jd) st.v[pp][jd] &= m;
+        }
+      }
+    }
     uint8_t* const vtb = vt + (TR ? (stage & 1) * kVtBytes<PPS> : 0);
     if constexpr (VL) {
       // the stage's V pages, copied as they are (one buffer: the wave's LDS
@@ -776,6 +824,7 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
         }
         accl[u] *= alpha;
         m_run[u] = m_new;
+        m_ref[u] = (MQ && m_new == -INFINITY) ? 0.0f : m_new;
       }
     }
     // P = 2^(z - m) in fp16, then PV
@@ -807,12 +856,6 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
     }
 #pragma unroll
     for (int pp = 0; pp < PPS; ++pp) {
-      uint32_t vmask = 0xFFFFFFFFu;
-      if (last) {
-        // slots past the context may hold anything (even NaN): zero their V bytes
-        const int nv = tend - ((j0 + pp) * kBlockTokens + rq * 4);
-        vmask = nv >= 4 ? 0xFFFFFFFFu : (nv <= 0 ? 0u : ((1u << (8 * nv)) - 1u));
-      }
       if constexpr (SS) {
         f16x4 pb, pv;
 #pragma unroll
@@ -826,22 +869,18 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
         }
 #pragma unroll
         for (int jd = 0; jd < 8; ++jd)
-          acc[0][jd] = __builtin_amdgcn_mfma_f32_16x16x16f16(fp8x4_to_f16(vword(st, vtb, pp, jd) & vmask), pv, acc[0][jd], 0, 0, 0);
+          acc[0][jd] = __builtin_amdgcn_mfma_f32_16x16x16f16(fp8x4_to_f16(vword(st, vtb, pp, jd)), pv, acc[0][jd], 0, 0, 0);
         accl[0] = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, pb, accl[0], 0, 0, 0);
       } else {
         f16x4 pb[NT];
 #pragma unroll
         for (int u = 0; u < NT; ++u) {
-          // a column that has seen no token yet (several queries: a causal end
-          // before this item's tokens) has m_run = -inf and every z = -inf:
-          // measured from 0 instead, its weights are 2^-inf = 0
-          const float m_ref = (MQ && m_run[u] == -INFINITY) ? 0.0f : m_run[u];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) pb[u][i] = (_Float16)__builtin_amdgcn_exp2f(z[u][pp][i] - m_ref);
+          for (int i = 0; i < 4; ++i) pb[u][i] = (_Float16)__builtin_amdgcn_exp2f(z[u][pp][i] - m_ref[u]);
         }
 #pragma unroll
         for (int jd = 0; jd < 8; ++jd) {
-          const f16x4 va = fp8x4_to_f16(vword(st, vtb, pp, jd) & vmask);  // shared by the tiles
+          const f16x4 va = fp8x4_to_f16(vword(st, vtb, pp, jd));  // shared by the tiles
 #pragma unroll
           for (int u = 0; u < NT; ++u) acc[u][jd] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb[u], acc[u][jd], 0, 0, 0);
         }
