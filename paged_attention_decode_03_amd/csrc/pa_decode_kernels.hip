@@ -801,22 +801,19 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
             z[u][pp][i] = keep ? z[u][pp][i] : -INFINITY;
           }
     }
-    // the tiles' maxima first (their cross-lane steps overlap), then each
-    // tile's rescale where its max grew
-    float mx[NT];
+    // Each lane's max over its own rows of the stage first: where no lane's
+    // exceeds the tile's running max, no column max can (the running max is
+    // then unchanged), so the max across the four row groups and the rescale
+    // run only where some lane's does.
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
-      mx[u] = -INFINITY;
+      float mx = -INFINITY;
 #pragma unroll
       for (int pp = 0; pp < PPS; ++pp)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mx[u] = fmaxf(mx[u], z[u][pp][i]);
-      mx[u] = max_over_rows(mx[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < NT; ++u) {
-      const float m_new = fmaxf(m_run[u], mx[u]);
-      if (__builtin_amdgcn_ballot_w64(m_new > m_run[u])) {
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, z[u][pp][i]);
+      if (__builtin_amdgcn_ballot_w64(mx > m_run[u])) {
+        const float m_new = fmaxf(m_run[u], max_over_rows(mx));
         const float alpha = (m_new == m_run[u]) ? 1.0f : __builtin_amdgcn_exp2f(m_run[u] - m_new);
         if constexpr (!SS) {  // (per-slot: the numerator has a running max of its own)
 #pragma unroll
@@ -845,9 +842,8 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
           mxv = fmaxf(mxv, zv[pp][i]);
         }
       }
-      mxv = max_over_rows(mxv);
-      const float mv_new = fmaxf(mv_run, mxv);
-      if (__builtin_amdgcn_ballot_w64(mv_new > mv_run)) {
+      if (__builtin_amdgcn_ballot_w64(mxv > mv_run)) {  // (as for m above)
+        const float mv_new = fmaxf(mv_run, max_over_rows(mxv));
         const float beta = (mv_new == mv_run) ? 1.0f : __builtin_amdgcn_exp2f(mv_run - mv_new);
 #pragma unroll
         for (int jd = 0; jd < 8; ++jd) acc[0][jd] *= beta;
