@@ -39,6 +39,7 @@
 // Several queries per sequence (MQ): the 16 columns hold (query token, head)
 // pairs, and an item holds one or two such tiles against the same K/V.
 // Pages are software-pipelined PPS at a time, one stage ahead.
+#include <float.h>
 #include <limits.h>
 #include <math.h>
 
@@ -502,6 +503,22 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
 
   // logits in log2 units: z * scale * k_scale * log2(e) (k_scale per slot when SS)
   const float c_log2 = SS ? p.scale_log2e : p.scale_log2e * scalar_load(p.k_scale);
+  // Per-tensor scales without per-logit options: the scale enters the
+  // exponent instead, each weight 2^(z |c| - m) by one fma, and the running
+  // max is |c| times the max of the raw products z.  A negative scale is
+  // folded into q beforehand (an exact bf16 negation), so that the raw
+  // products' max is the scaled logits' max.  (|c| = 0: every weight 1.)
+  constexpr bool kFold = !SS && !(MQ && OPT);
+  const float c_abs = kFold ? fmaxf(fabsf(c_log2), FLT_MIN) : 0.0f;
+  if (kFold && c_log2 < 0.0f) {
+#pragma unroll
+    for (int u = 0; u < NT; ++u)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          qop[u][h2][c] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, qop[u][h2][c]) ^ 0x80008000u);
+  }
   // softcap: the natural-unit logit z * scale * k_scale, capped, then in log2 units
   const bool capped = MQ && OPT && p.softcap > 0.0f;
   const float c_nat = MQ ? p.scale * scalar_load(p.k_scale) : 0.0f;
@@ -777,7 +794,7 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
             z[u][pp][i] = v;
           }
         }
-      } else {
+      } else if constexpr (!kFold) {
 #pragma unroll
         for (int pp = 0; pp < PPS; ++pp) {
 #pragma unroll
@@ -812,8 +829,9 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
       for (int pp = 0; pp < PPS; ++pp)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, z[u][pp][i]);
-      if (__builtin_amdgcn_ballot_w64(mx > m_run[u])) {
-        const float m_new = fmaxf(m_run[u], max_over_rows(mx));
+      if (__builtin_amdgcn_ballot_w64((kFold ? mx * c_abs : mx) > m_run[u])) {
+        const float mr = max_over_rows(mx);
+        const float m_new = fmaxf(m_run[u], kFold ? mr * c_abs : mr);
         const float alpha = (m_new == m_run[u]) ? 1.0f : __builtin_amdgcn_exp2f(m_run[u] - m_new);
         if constexpr (!SS) {  // (per-slot: the numerator has a running max of its own)
 #pragma unroll
@@ -872,7 +890,9 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
 #pragma unroll
         for (int u = 0; u < NT; ++u) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) pb[u][i] = (_Float16)__builtin_amdgcn_exp2f(z[u][pp][i] - m_ref[u]);
+          for (int i = 0; i < 4; ++i)
+            pb[u][i] = (_Float16)__builtin_amdgcn_exp2f(kFold ? __builtin_fmaf(z[u][pp][i], c_abs, -m_ref[u])
+                                                              : z[u][pp][i] - m_ref[u]);
         }
 #pragma unroll
         for (int jd = 0; jd < 8; ++jd) {
