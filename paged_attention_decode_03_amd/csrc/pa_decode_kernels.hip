@@ -1244,9 +1244,11 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false, PA_LOAD_AUX, true>),
                        dim3((unsigned)(items / p.kv_group)), dim3(64 * p.kv_group),
                        (unsigned)(p.kv_group * 2 * kVtBytes<kPagesPerStage>), stream, p);
-  // V through LDS where it measured faster on MI355X (40/8 ctx 4096 x 256):
-  // two query tiles per item (4 queries: 372.9 -> 369.4 us) and per-slot
-  // scales (339.8 -> 335.6 us); one tile per item was 0.5% slower with it
+  // V through LDS in every several-queries and per-slot kernel, measured
+  // faster on MI355X (40/8 ctx 4096 x 256): two query tiles per item (4
+  // queries: 372.9 -> 369.4 us), per-slot scales (339.8 -> 335.6 us), one
+  // tile (3 queries 327.3 -> 321.9 us, ALiBi 333.0 -> 327.5, sinks 346.4 ->
+  // 341.5, window 1024 94.0 -> 90.6; 64 x 1024, 2 queries 38.4 -> 36.1)
   else if (p.multi_query && opt && p.tiles_per_item == 3)
     hipLaunchKernelGGL((pa_decode_kernel<kThreeTilePagesPerStage, kRingDepth, false, true, PA_LOAD_AUX, false, 3, true, 1, true>),
                        dim3((unsigned)items), dim3(64), kThreeTilePagesPerStage * kPageBytes, stream, p);
@@ -1254,8 +1256,8 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((pa_decode_kernel<kTwoTilePagesPerStage, kRingDepth, false, true, PA_LOAD_AUX, false, 2, true, 1, true>),
                        dim3((unsigned)items), dim3(64), kTwoTilePagesPerStage * kPageBytes, stream, p);
   else if (p.multi_query && opt)
-    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, true, PA_LOAD_AUX, false, 1, false, 1, true>),
-                       dim3((unsigned)items), dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, true, PA_LOAD_AUX, false, 1, true, 1, true>),
+                       dim3((unsigned)items), dim3(64), kPagesPerStage * kPageBytes, stream, p);
   else if (p.multi_query && p.tiles_per_item == 3)
     hipLaunchKernelGGL((pa_decode_kernel<kThreeTilePagesPerStage, kRingDepth, false, true, PA_LOAD_AUX, false, 3, true>),
                        dim3((unsigned)items), dim3(64), kThreeTilePagesPerStage * kPageBytes, stream, p);
@@ -1266,8 +1268,8 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((pa_decode_kernel<kTwoTilePagesPerStage, kRingDepth, false, true, PA_LOAD_AUX, false, 2, true>),
                        dim3((unsigned)items), dim3(64), kTwoTilePagesPerStage * kPageBytes, stream, p);
   else if (p.multi_query)
-    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, true>), dim3((unsigned)items),
-                       dim3(64), 0, stream, p);
+    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, true, PA_LOAD_AUX, false, 1, true>),
+                       dim3((unsigned)items), dim3(64), kPagesPerStage * kPageBytes, stream, p);
   else if (p.k_slot_scales)
     hipLaunchKernelGGL((pa_decode_kernel<kSlotScalePagesPerStage, kRingDepth, true, false, PA_LOAD_AUX, false, 1, true>),
                        dim3((unsigned)items), dim3(64), kSlotScalePagesPerStage * kPageBytes, stream, p);
