@@ -1274,17 +1274,22 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((pa_decode_kernel<kSlotScalePagesPerStage, kRingDepth, true, false, PA_LOAD_AUX, false, 1, true>),
                        dim3((unsigned)items), dim3(64), kSlotScalePagesPerStage * kPageBytes, stream, p);
   else if (p.waves_per_item == 2 && p.cached_loads)
-    hipLaunchKernelGGL((pa_decode_kernel<kTwoWavePagesPerStage, kTwoWaveRingDepth, false, false, 0, false, 1, false, 2>),
-                       dim3((unsigned)items), dim3(128), 0, stream, p);
+    hipLaunchKernelGGL((pa_decode_kernel<kTwoWavePagesPerStage, kTwoWaveRingDepth, false, false, 0, false, 1, true, 2>),
+                       dim3((unsigned)items), dim3(128), 2 * kTwoWavePagesPerStage * kPageBytes, stream, p);
   else if (p.waves_per_item == 2)
     hipLaunchKernelGGL((pa_decode_kernel<kTwoWavePagesPerStage, kTwoWaveRingDepth, false, false, PA_LOAD_AUX, false, 1, true, 2>),
                        dim3((unsigned)items), dim3(128), 2 * kTwoWavePagesPerStage * kPageBytes, stream, p);
   else if (p.cached_loads)
-    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false, 0>), dim3((unsigned)items),
-                       dim3(64), 0, stream, p);
-  else  // streamed working sets: V through LDS (fewer load instructions; measured on MI355X,
-        // 40/8 ctx 4096: 256 sequences 327.6 -> 326.9 us, ragged 1..4000 216.7 -> 202.5 us,
-        // while a 24-sequence set that stays in the Infinity Cache lost 4% with it)
+    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false, 0, false, 1, true>), dim3((unsigned)items),
+                       dim3(64), kPagesPerStage * kPageBytes, stream, p);
+  else  // V through LDS (two 16-byte loads a page instead of eight dword loads), with
+        // either cache policy: a wave alone on its SIMD streams a page faster, which is
+        // what the long items of a ragged batch are (measured on MI355X, working
+        // sets in the Infinity Cache, graph replay: ragged 1..4000 x 256 at 8/1
+        // 38.8 -> 28.8 us, 40/8 x 32 37.9 -> 27.6 us, 256 x {4000, 100, 100, 100}
+        // 39.0 -> 28.4 us; uniform batches from 7% faster to 6% slower, e.g. 40/8
+        // ctx 1024 x 16 12.0 -> 11.2 us, x 64 24.6 -> 26.2 us; on the streamed
+        // sets: 40/8 ctx 4096 x 256 327.6 -> 326.9 us, ragged 216.7 -> 202.5 us)
     hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false, PA_LOAD_AUX, false, 1, true>),
                        dim3((unsigned)items), dim3(64), kPagesPerStage * kPageBytes, stream, p);
   const size_t rows = p.multi_query ? (size_t)p.num_q_rows : (size_t)p.num_seqs;
