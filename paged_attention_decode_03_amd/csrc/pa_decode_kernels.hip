@@ -27,10 +27,11 @@
 // Loads go from HBM into VGPRs:
 //   K: two fully coalesced 1 KiB dwordx4 loads per page, in the layout the
 //      MFMA wants (lane l: token l & 15, 16-dim chunks l >> 4 and 4 + (l >> 4)),
-//   V: either eight dword loads per page in the operand layout (each a
-//      contiguous 256 B: 16 dims x 16 slots), or (VL) two 1 KiB dwordx4 loads
-//      whose page is copied to LDS and read back one operand dword at a time;
-//      fewer load instructions per page measured faster on streamed sets.
+//   V: two 1 KiB dwordx4 loads per page (lane l: dims l and 64 + l, all 16
+//      slots), the page copied to LDS and read back one operand dword at a
+//      time: two load instructions a page where the operand layout would take
+//      eight dword loads, which measured faster (most where a wave is alone
+//      on its SIMD).
 // Token-row caches (TR: each token's 128 dims contiguous, the flash-style
 // layouts of the API page's unified backend) load K the same way (lane l:
 // 16 B chunks of token l & 15's row) and V as whole 128 B token rows (eight
@@ -281,7 +282,7 @@ __device__ __forceinline__ int snake_slot(int slot, int per_round, int S) {
 template <int PPS>
 struct Stage {
   u32x4 k[PPS][2];     // per page: 16 bytes of chunk (l >> 4) and of chunk 4 + (l >> 4)
-  uint32_t v[PPS][8];  // per page: 4 slots of one dim in each of the 8 16-dim blocks
+  uint32_t v[PPS][8];  // per page: slots 4 e .. 4 e + 3 of dims lane (e < 4) and 64 + lane (token rows: row bytes)
   uint32_t ks[PPS];    // per-slot scale of slot 4 rq + (lane & 3) (per-slot variant only)
   uint32_t vs[PPS];
 };
@@ -305,10 +306,6 @@ struct Stage {
 // registers), so up to NT * q_tile queries of a sequence cost one read of its
 // pages.
 //
-// VL (page layout): V pages are loaded as two 16-byte pieces a lane (dims lane
-// and 64 + lane, all 16 slots: two load instructions a page instead of eight)
-// and copied to LDS, where each PV operand is one dword of the page.
-//
 // WPI (page layout, one query per sequence): waves per work item.  With 2,
 // wave w computes stages w, w + 2, ... of the item and wave 1 hands its
 // (max, denominator, accumulator) to wave 0 through LDS at the end, which
@@ -320,7 +317,7 @@ struct Stage {
 // branch there measured 2.7% on 8 queries per sequence); window and sinks
 // need no per-logit work and run in every several-queries kernel.
 template <int PPS, int NB, bool SS, bool MQ, int AUX = PA_LOAD_AUX, bool TR = false, int NT = 1,
-          bool VL = false, int WPI = 1, bool OPT = false>
+          int WPI = 1, bool OPT = false>
 __global__ __launch_bounds__(TR ? 64 * kMaxKvPerGroup : 64 * WPI)
 __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_EU))) void pa_decode_kernel(const DecodeParams p) {
   const int lane = threadIdx.x & 63;
@@ -534,10 +531,10 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
   const int tstride = TR ? (int)p.token_stride : 0;
   const int koff = TR ? col * tstride + rq * 16 : lane * 16;
   constexpr int khi = TR ? 64 : 1024;
-  // V: page layout: dim col (+16 jd), slots 4 rq .. 4 rq + 3 (one dword per jd);
-  // token rows: bytes 16 (lane & 7) .. +15 of tokens lane >> 3 and 8 + (lane >> 3)
-  // (each load reads eight whole 128-byte rows)
-  const int voff = TR ? (lane >> 3) * tstride + (lane & 7) * 16 : col * 16 + rq * 4;
+  // V (token rows): bytes 16 (lane & 7) .. +15 of tokens lane >> 3 and
+  // 8 + (lane >> 3) (each load reads eight whole 128-byte rows); the page
+  // layout's V loads take dims lane and 64 + lane
+  const int voff = TR ? (lane >> 3) * tstride + (lane & 7) * 16 : 0;
   // bytes a page's descriptor covers
   const int page_bytes = TR ? (kBlockTokens - 1) * tstride + kHeadDim : kPageBytes;
 
@@ -594,8 +591,8 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
   // columns x 4 row groups) hit distinct banks.
   // (dynamic LDS, kv_group * 2 * kVtBytes<PPS> bytes, sized at launch)
   extern __shared__ __attribute__((aligned(16))) uint8_t pa_dyn_lds[];
-  // (VL: one stage of V pages per wave)
-  uint8_t* const vt = pa_dyn_lds + (TR ? wave * 2 * kVtBytes<PPS> : VL ? wave * PPS * kPageBytes : 0);
+  // (page layout: one stage of V pages per wave, PPS * kPageBytes bytes)
+  uint8_t* const vt = pa_dyn_lds + (TR ? wave * 2 * kVtBytes<PPS> : wave * PPS * kPageBytes);
   auto load = [&](Stage<PPS>& st, int stage) {
     const int i0 = stage * PPS;           // page of the item (pages past npg are empty)
     const int32_t* idp = ids + ioff + i0;  // their staged block ids
@@ -655,7 +652,8 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
 #pragma unroll
           for (int e = 0; e < 4; ++e) st.v[pp][4 * h + e] = w[e];
         }
-      } else if constexpr (VL) {
+      } else {
+        // dims lane and 64 + lane, all 16 slots
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const u32x4 w =
@@ -663,10 +661,6 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
 #pragma unroll
           for (int e = 0; e < 4; ++e) st.v[pp][4 * h + e] = w[e];
         }
-      } else {
-#pragma unroll
-        for (int jd = 0; jd < 8; ++jd)
-          st.v[pp][jd] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff + jd * 256, 0, kAux);
       }
     }
     // keep the scheduler from hoisting compute above these loads
@@ -679,10 +673,8 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
       const uint8_t* b = vtb + (pp * kBlockTokens + 4 * rq) * kVRow + 16 * jd + col;
       return (uint32_t)b[0] | ((uint32_t)b[kVRow] << 8) | ((uint32_t)b[2 * kVRow] << 16) |
              ((uint32_t)b[3 * kVRow] << 24);
-    } else if constexpr (VL) {
-      return *(const uint32_t*)(vtb + pp * kPageBytes + (col + 16 * jd) * 16 + 4 * rq);
     } else {
-      return st.v[pp][jd];
+      return *(const uint32_t*)(vtb + pp * kPageBytes + (col + 16 * jd) * 16 + 4 * rq);
     }
   };
 
@@ -701,22 +693,17 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
 #pragma unroll
             for (int e = 0; e < 4; ++e)
               st.v[pp][4 * h + e] = 8 * h + (lane >> 3) < nv ? st.v[pp][4 * h + e] : 0u;
-        } else if constexpr (VL) {
+        } else {
           // dword 4 h + e: slots 4 e .. 4 e + 3 of one dim
 #pragma unroll
           for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int e = 0; e < 4; ++e) st.v[pp][4 * h + e] &= slot_bytes(nv - 4 * e);
-        } else {
-          // dword jd: slots 4 rq .. 4 rq + 3 of one dim
-          const uint32_t m = slot_bytes(nv - 4 * rq);
-#pragma unroll
-          for (int jd = 0; jd < 8; ++jd) st.v[pp][jd] &= m;
         }
       }
     }
     uint8_t* const vtb = vt + (TR ? (stage & 1) * kVtBytes<PPS> : 0);
-    if constexpr (VL) {
+    if constexpr (!TR) {
       // the stage's V pages, copied as they are (one buffer: the wave's LDS
       // operations run in order, so these writes follow the last stage's reads)
 #pragma unroll
@@ -1250,37 +1237,37 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   // tile (3 queries 327.3 -> 321.9 us, ALiBi 333.0 -> 327.5, sinks 346.4 ->
   // 341.5, window 1024 94.0 -> 90.6; 64 x 1024, 2 queries 38.4 -> 36.1)
   else if (p.multi_query && opt && p.tiles_per_item == 3)
-    hipLaunchKernelGGL((pa_decode_kernel<kThreeTilePagesPerStage, kRingDepth, false, true, PA_LOAD_AUX, false, 3, true, 1, true>),
+    hipLaunchKernelGGL((pa_decode_kernel<kThreeTilePagesPerStage, kRingDepth, false, true, PA_LOAD_AUX, false, 3, 1, true>),
                        dim3((unsigned)items), dim3(64), kThreeTilePagesPerStage * kPageBytes, stream, p);
   else if (p.multi_query && opt && p.tiles_per_item == 2)
-    hipLaunchKernelGGL((pa_decode_kernel<kTwoTilePagesPerStage, kRingDepth, false, true, PA_LOAD_AUX, false, 2, true, 1, true>),
+    hipLaunchKernelGGL((pa_decode_kernel<kTwoTilePagesPerStage, kRingDepth, false, true, PA_LOAD_AUX, false, 2, 1, true>),
                        dim3((unsigned)items), dim3(64), kTwoTilePagesPerStage * kPageBytes, stream, p);
   else if (p.multi_query && opt)
-    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, true, PA_LOAD_AUX, false, 1, true, 1, true>),
+    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, true, PA_LOAD_AUX, false, 1, 1, true>),
                        dim3((unsigned)items), dim3(64), kPagesPerStage * kPageBytes, stream, p);
   else if (p.multi_query && p.tiles_per_item == 3)
-    hipLaunchKernelGGL((pa_decode_kernel<kThreeTilePagesPerStage, kRingDepth, false, true, PA_LOAD_AUX, false, 3, true>),
+    hipLaunchKernelGGL((pa_decode_kernel<kThreeTilePagesPerStage, kRingDepth, false, true, PA_LOAD_AUX, false, 3>),
                        dim3((unsigned)items), dim3(64), kThreeTilePagesPerStage * kPageBytes, stream, p);
   else if (p.multi_query && p.tiles_per_item == 2 && p.num_q_tiles > 2)
-    hipLaunchKernelGGL((pa_decode_kernel<kTwoTilePagesPerStage, kRingDepth, false, true, 0, false, 2, true>),
+    hipLaunchKernelGGL((pa_decode_kernel<kTwoTilePagesPerStage, kRingDepth, false, true, 0, false, 2>),
                        dim3((unsigned)items), dim3(64), kTwoTilePagesPerStage * kPageBytes, stream, p);
   else if (p.multi_query && p.tiles_per_item == 2)
-    hipLaunchKernelGGL((pa_decode_kernel<kTwoTilePagesPerStage, kRingDepth, false, true, PA_LOAD_AUX, false, 2, true>),
+    hipLaunchKernelGGL((pa_decode_kernel<kTwoTilePagesPerStage, kRingDepth, false, true, PA_LOAD_AUX, false, 2>),
                        dim3((unsigned)items), dim3(64), kTwoTilePagesPerStage * kPageBytes, stream, p);
   else if (p.multi_query)
-    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, true, PA_LOAD_AUX, false, 1, true>),
+    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, true, PA_LOAD_AUX, false, 1>),
                        dim3((unsigned)items), dim3(64), kPagesPerStage * kPageBytes, stream, p);
   else if (p.k_slot_scales)
-    hipLaunchKernelGGL((pa_decode_kernel<kSlotScalePagesPerStage, kRingDepth, true, false, PA_LOAD_AUX, false, 1, true>),
+    hipLaunchKernelGGL((pa_decode_kernel<kSlotScalePagesPerStage, kRingDepth, true, false, PA_LOAD_AUX, false, 1>),
                        dim3((unsigned)items), dim3(64), kSlotScalePagesPerStage * kPageBytes, stream, p);
   else if (p.waves_per_item == 2 && p.cached_loads)
-    hipLaunchKernelGGL((pa_decode_kernel<kTwoWavePagesPerStage, kTwoWaveRingDepth, false, false, 0, false, 1, true, 2>),
+    hipLaunchKernelGGL((pa_decode_kernel<kTwoWavePagesPerStage, kTwoWaveRingDepth, false, false, 0, false, 1, 2>),
                        dim3((unsigned)items), dim3(128), 2 * kTwoWavePagesPerStage * kPageBytes, stream, p);
   else if (p.waves_per_item == 2)
-    hipLaunchKernelGGL((pa_decode_kernel<kTwoWavePagesPerStage, kTwoWaveRingDepth, false, false, PA_LOAD_AUX, false, 1, true, 2>),
+    hipLaunchKernelGGL((pa_decode_kernel<kTwoWavePagesPerStage, kTwoWaveRingDepth, false, false, PA_LOAD_AUX, false, 1, 2>),
                        dim3((unsigned)items), dim3(128), 2 * kTwoWavePagesPerStage * kPageBytes, stream, p);
   else if (p.cached_loads)
-    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false, 0, false, 1, true>), dim3((unsigned)items),
+    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false, 0, false, 1>), dim3((unsigned)items),
                        dim3(64), kPagesPerStage * kPageBytes, stream, p);
   else  // V through LDS (two 16-byte loads a page instead of eight dword loads), with
         // either cache policy: a wave alone on its SIMD streams a page faster, which is
@@ -1290,7 +1277,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
         // 39.0 -> 28.4 us; uniform batches from 7% faster to 6% slower, e.g. 40/8
         // ctx 1024 x 16 12.0 -> 11.2 us, x 64 24.6 -> 26.2 us; on the streamed
         // sets: 40/8 ctx 4096 x 256 327.6 -> 326.9 us, ragged 216.7 -> 202.5 us)
-    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false, PA_LOAD_AUX, false, 1, true>),
+    hipLaunchKernelGGL((pa_decode_kernel<kPagesPerStage, kRingDepth, false, false, PA_LOAD_AUX, false, 1>),
                        dim3((unsigned)items), dim3(64), kPagesPerStage * kPageBytes, stream, p);
   const size_t rows = p.multi_query ? (size_t)p.num_q_rows : (size_t)p.num_seqs;
   if (p.num_parts > 1 && rows > 0 && !p.fused_merge)
