@@ -385,21 +385,40 @@ def time_graph(case, replays=50, calls_per_graph=10, per_replay=False):
     return mean, [a.elapsed_time(b) * 1e3 / calls_per_graph for a, b in pairs]
 
 
-def cache_write_case(num_tokens, num_kv_heads=8, seed=0, prefill=True):
+def cache_write_case(num_tokens, num_kv_heads=8, seed=0, pattern="prefill"):
     """New keys/values (bf16 N(0,1), per-tensor scale amax/448) for `num_tokens`
-    tokens.  prefill: sequences of 2048 new tokens, each filling its own shuffled
-    blocks in order; otherwise one token per sequence at a random slot (a decode
-    step).  The cache has 25% spare blocks."""
+    tokens.  pattern "prefill": sequences of 2048 new tokens, each filling its
+    own shuffled blocks in order; "chunks": prefill chunks of 1..4095 tokens
+    (about 2048 on average) that each continue a sequence at a random slot of
+    its last block (chunked prefill, prefix caching); "decode": one token per
+    sequence at a random slot (a decode step).  The cache has 25% spare
+    blocks."""
+    import numpy as np
     import torch
     g = torch.Generator(device="cuda")
     g.manual_seed(seed)
     nb = (num_tokens + 15) // 16 * 5 // 4 + 1
     key = torch.randn(num_tokens, num_kv_heads, 128, generator=g, device="cuda").to(torch.bfloat16)
     value = torch.randn(num_tokens, num_kv_heads, 128, generator=g, device="cuda").to(torch.bfloat16)
-    if prefill:
+    if pattern == "prefill":
         blocks = torch.randperm(nb, generator=g, device="cuda")[:(num_tokens + 15) // 16]
         t = torch.arange(num_tokens, device="cuda")
         slots = blocks[t // 16] * 16 + t % 16
+    elif pattern == "chunks":
+        rng = np.random.default_rng(seed + 17)
+        lens, starts = [], []
+        while sum(lens) < num_tokens:
+            lens.append(int(min(rng.integers(1, 4096), num_tokens - sum(lens))))
+            starts.append(int(rng.integers(0, 16)))
+        nb = sum((a + n + 15) // 16 for a, n in zip(starts, lens)) * 5 // 4 + 1
+        perm = torch.randperm(nb, generator=g, device="cuda")
+        parts, b = [], 0
+        for a, n in zip(starts, lens):
+            k = (a + n + 15) // 16
+            t = torch.arange(n, device="cuda") + a
+            parts.append(perm[b:b + k][t // 16] * 16 + t % 16)
+            b += k
+        slots = torch.cat(parts)
     else:
         slots = torch.randperm(nb * 16, generator=g, device="cuda")[:num_tokens]
     slots = slots.to(torch.int64)
@@ -416,10 +435,10 @@ def cache_write_bytes(num_tokens, num_kv_heads=8):
     return num_tokens * num_kv_heads * 128 * (2 + 2 + 1 + 1) + 8 * num_tokens + 8
 
 
-def time_cache_write(num_tokens, steps, warmup, num_kv_heads=8, prefill=True):
+def time_cache_write(num_tokens, steps, warmup, num_kv_heads=8, pattern="prefill"):
     import torch
     import paged_attention_decode_03_amd as pa
-    key, value, kc, vc, slots, ks, vs = cache_write_case(num_tokens, num_kv_heads, prefill=prefill)
+    key, value, kc, vc, slots, ks, vs = cache_write_case(num_tokens, num_kv_heads, pattern=pattern)
     stream = torch.cuda.Stream()
     for _ in range(warmup):
         pa.paged_kv_cache_write(key, value, kc, vc, slots, ks, vs, stream=stream)
@@ -698,9 +717,10 @@ def main():
             print(json.dumps(row), file=sys.stderr, flush=True)
             del case
             torch.cuda.empty_cache()
-        for name, T, pre in (("cache_write_decode_256x8", 256, False),
-                             ("cache_write_prefill_32768x8", 32768, True)):
-            us = time_cache_write(T, args.steps, args.warmup, prefill=pre)
+        for name, T, pattern in (("cache_write_decode_256x8", 256, "decode"),
+                                 ("cache_write_prefill_32768x8", 32768, "prefill"),
+                                 ("cache_write_chunks_32768x8", 32768, "chunks")):
+            us = time_cache_write(T, args.steps, args.warmup, pattern=pattern)
             b = cache_write_bytes(T)
             print(json.dumps({"workload": name, "us_per_call": round(us, 2),
                               "GBps": round(b / us / 1e3, 1),
@@ -708,11 +728,10 @@ def main():
                   file=sys.stderr, flush=True)
         args.workload = "target"
 
-    m = re.fullmatch(r"cache_write_(prefill|decode)_(\d+)x(\d+)", args.workload)
+    m = re.fullmatch(r"cache_write_(prefill|chunks|decode)_(\d+)x(\d+)", args.workload)
     if m:   # one workload of the cache write, for profiling runs
         T, hkv = int(m.group(2)), int(m.group(3))
-        us = time_cache_write(T, args.steps, args.warmup, num_kv_heads=hkv,
-                              prefill=m.group(1) == "prefill")
+        us = time_cache_write(T, args.steps, args.warmup, num_kv_heads=hkv, pattern=m.group(1))
         b = cache_write_bytes(T, hkv)
         print(json.dumps({"workload": args.workload, "us_per_call": round(us, 2),
                           "GBps": round(b / us / 1e3, 1), "frac_of_peak": round(b / us / 1e3 / PEAK_GBS, 4),

@@ -9,13 +9,16 @@
 // lishuoshuo-amd/vllm #3 (Details > Layout): K [head_size/16][16 slots][16],
 // V [head_size][16 slots] per (block, kv head).
 //
-// One wavefront per (group of 16 consecutive tokens, kv head).  When the group
-// fills one block in order (the usual prefill pattern) the wave writes the two
-// 2 KiB pages whole: each lane converts 2 tokens x 16 dims of K and 16 tokens x
-// 2 dims of V and stores 32 contiguous bytes of each page.  Otherwise it walks
-// the group token by token, two dims per lane: K as 2-byte stores into 16-byte
-// slot rows, V as single bytes (a V page keeps a dim's 16 slots together, so
-// one token touches a byte of every dim row).
+// One wavefront per (group of 16 consecutive tokens, kv head).  Each lane
+// converts one token's 32 dims of K and 2 dims of all 16 tokens' V.  K goes
+// out as whole 16-byte rows (chunk, slot) of the K pages, whatever the slots;
+// V rows keep a dim's 16 slots together, so the group is cut into runs of
+// tokens whose slots follow each other in one block (one run filling a block
+// in a prefill that starts on a block; two pieces of blocks where it starts
+// inside one or where a sequence ends), and each run's bytes of a dim row go
+// out in the widest aligned stores that cover them.  Rows of the key/value
+// inputs without 16-byte alignment take a token-by-token walk instead (K as
+// 2-byte stores, V as single bytes).
 // A negative slot is a token that is not cached; a slot past the caches is
 // skipped too (the host cannot see device data to reject it).
 #include <math.h>
@@ -126,11 +129,10 @@ __device__ __forceinline__ void write_token(const CacheWriteParams& p, int kvh, 
   vp[kBlockTokens] = (uint8_t)(vc >> 8);
 }
 
-// Sixteen tokens that fill block `block` in slot order: whole-page writes.
-// K page bytes [32 l, 32 l + 32): chunk c = l / 8 (dims 16c..16c+15), slots
-// 2(l%8), 2(l%8)+1; V page bytes [32 l, 32 l + 32): dims 2l and 2l+1, all 16
-// slots of each.  The codes are made without NaN handling unless a NaN is in
-// the wave's inputs (or the division path, where the scale may be one).
+// The lane's codes: kout[u] the 16 fp8 codes of kin[u] (16 dims of one
+// token), vout[0] / vout[1] the codes of dims 2l / 2l + 1 of the group's 16
+// tokens (byte t = token t).  The codes are made without NaN handling unless a
+// NaN is in the wave's inputs (or the division path, where the scale may be one).
 template <bool FAST, bool WITH_NAN>
 __device__ __forceinline__ void block_codes(const uint32_t (&kin)[2][8], const uint32_t (&vin)[kGroup],
                                             const Scale& ks, const Scale& vs, uint4 (&kout)[2], uint4 (&vout)[2]) {
@@ -155,17 +157,70 @@ __device__ __forceinline__ void block_codes(const uint32_t (&kin)[2][8], const u
   vout[1] = make_uint4(b[0], b[1], b[2], b[3]);
 }
 
+// Bytes [x, x + 8) of a 16-byte row held as two 64-bit halves (x wave-uniform,
+// 0 <= x <= 15; bytes past the row read as 0).
+__device__ __forceinline__ uint64_t row_bytes(uint64_t lo, uint64_t hi, int x) {
+  if (x >= 8) return hi >> (8 * (x - 8));
+  if (x == 0) return lo;
+  return (lo >> (8 * x)) | (hi << (64 - 8 * x));
+}
+
+// Slots [a, a + len) of two V page rows (dims d and d + 1: `row` and row + 16,
+// 16-byte aligned) from the codes of tokens [o, o + len) of the group, held in
+// token order (byte t = token t) as (la, ha) and (lb, hb).  The widest aligned
+// stores that cover the range; a, len and o are wave-uniform, a + len <= 16.
+__device__ __forceinline__ void store_rows(uint8_t* row, uint64_t la, uint64_t ha, uint64_t lb, uint64_t hb,
+                                           int a, int len, int o) {
+  if (a == 0 && len == kBlockTokens) {  // (then o = 0) the whole rows
+    *(uint4*)row = make_uint4((uint32_t)la, (uint32_t)(la >> 32), (uint32_t)ha, (uint32_t)(ha >> 32));
+    *(uint4*)(row + kBlockTokens) =
+        make_uint4((uint32_t)lb, (uint32_t)(lb >> 32), (uint32_t)hb, (uint32_t)(hb >> 32));
+    return;
+  }
+  const int end = a + len;
+  for (int pos = a; pos < end;) {
+    const uint64_t va = row_bytes(la, ha, pos - a + o);
+    const uint64_t vb = row_bytes(lb, hb, pos - a + o);
+    if ((pos & 7) == 0 && pos + 8 <= end) {
+      *(uint64_t*)(row + pos) = va;
+      *(uint64_t*)(row + kBlockTokens + pos) = vb;
+      pos += 8;
+    } else if ((pos & 3) == 0 && pos + 4 <= end) {
+      *(uint32_t*)(row + pos) = (uint32_t)va;
+      *(uint32_t*)(row + kBlockTokens + pos) = (uint32_t)vb;
+      pos += 4;
+    } else if ((pos & 1) == 0 && pos + 2 <= end) {
+      *(uint16_t*)(row + pos) = (uint16_t)va;
+      *(uint16_t*)(row + kBlockTokens + pos) = (uint16_t)vb;
+      pos += 2;
+    } else {
+      row[pos] = (uint8_t)va;
+      row[kBlockTokens + pos] = (uint8_t)vb;
+      pos += 1;
+    }
+  }
+}
+
+// Any slot pattern, rows that allow 16-byte loads.  K: lane l converts token
+// l & 15's dims of chunks l >> 4 and 4 + (l >> 4) and stores each as the
+// whole 16-byte row (chunk, slot) of its page.  V: lane l converts dims 2l and
+// 2l + 1 of all 16 tokens, and the group is cut into runs (tokens whose slots
+// follow each other in one block: a whole block in a prefill that starts on a
+// block, two pieces of blocks where it does not); each run's slots of the two
+// dim rows are written with the widest aligned stores.  Runs of one block may
+// come from two groups (a run that crosses a group boundary): each writes
+// only its own tokens' bytes.
 template <bool FAST>
-__device__ __forceinline__ void write_block(const CacheWriteParams& p, int t0, int kvh, int64_t block,
-                                            int lane, const Scale& ks, const Scale& vs) {
-  const size_t page = ((size_t)block * p.num_kv_heads + kvh) * kPageBytes;
-  const int c = lane >> 3;
-  const int j0 = 2 * (lane & 7);
-  const int d = 2 * lane;
+__device__ __forceinline__ void write_runs(const CacheWriteParams& p, int t0, int n, int kvh, int lane,
+                                           int64_t my_slot, const Scale& ks, const Scale& vs) {
+  const int jt = lane & 15;  // K: the lane's token; the lane of token jt in each row of 16
+  const int c0 = lane >> 4;  // K: chunks c0 and c0 + 4
+  const int d = 2 * lane;    // V: dims d and d + 1
   uint32_t kin[2][8], vin[kGroup];
+  const int tk = t0 + min(jt, n - 1);
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const uint16_t* src = p.key + (size_t)(t0 + j0 + u) * p.key_stride + kvh * kHeadDim + 16 * c;
+    const uint16_t* src = p.key + (size_t)tk * p.key_stride + kvh * kHeadDim + 16 * (c0 + 4 * u);
     const uint4 lo = *(const uint4*)src;        // dims +0..7
     const uint4 hi = *(const uint4*)(src + 8);  // dims +8..15
     kin[u][0] = lo.x, kin[u][1] = lo.y, kin[u][2] = lo.z, kin[u][3] = lo.w;
@@ -173,7 +228,7 @@ __device__ __forceinline__ void write_block(const CacheWriteParams& p, int t0, i
   }
 #pragma unroll
   for (int j = 0; j < kGroup; ++j)
-    vin[j] = *(const uint32_t*)(p.value + (size_t)(t0 + j) * p.value_stride + kvh * kHeadDim + d);
+    vin[j] = *(const uint32_t*)(p.value + (size_t)(t0 + min(j, n - 1)) * p.value_stride + kvh * kHeadDim + d);
   bool nan = true;
   if constexpr (FAST) {
     uint64_t m = 0;
@@ -192,12 +247,37 @@ __device__ __forceinline__ void write_block(const CacheWriteParams& p, int t0, i
     block_codes<FAST, true>(kin, vin, ks, vs, kout, vout);
   else
     block_codes<FAST, false>(kin, vin, ks, vs, kout, vout);
-  uint4* kdst = (uint4*)(p.k_cache + page + c * 256 + j0 * 16);
-  kdst[0] = kout[0];
-  kdst[1] = kout[1];
-  uint4* vdst = (uint4*)(p.v_cache + page + (size_t)d * kBlockTokens);
-  vdst[0] = vout[0];
-  vdst[1] = vout[1];
+
+  const int64_t cap = p.num_blocks * kBlockTokens;
+  const bool valid = jt < n && my_slot >= 0 && my_slot < cap;
+  if (valid) {
+    uint8_t* kp = p.k_cache + ((size_t)(my_slot / kBlockTokens) * p.num_kv_heads + kvh) * kPageBytes +
+                  (my_slot % kBlockTokens) * 16;
+    *(uint4*)(kp + c0 * 256) = kout[0];
+    *(uint4*)(kp + (c0 + 4) * 256) = kout[1];
+  }
+  // the previous token's slot (lane jt - 1 of the row of 16; none for token 0)
+  const uint32_t prev_lo = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)(uint32_t)my_slot, 0x111, 0xF, 0xF, false);
+  const uint32_t prev_hi = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)(uint32_t)(my_slot >> 32), 0x111, 0xF, 0xF, false);
+  const int64_t prev = (int64_t)(((uint64_t)prev_hi << 32) | prev_lo);
+  // token jt continues the run of token jt - 1: the next slot of the same block
+  const bool cont = valid && jt > 0 && prev >= 0 && my_slot == prev + 1 && (my_slot % kBlockTokens) != 0;
+  uint64_t starts = __builtin_amdgcn_ballot_w64(lane < kGroup && valid && !cont);
+  const uint64_t conts = __builtin_amdgcn_ballot_w64(lane < kGroup && cont);
+  const uint64_t la = (uint64_t)vout[0].x | ((uint64_t)vout[0].y << 32);
+  const uint64_t ha = (uint64_t)vout[0].z | ((uint64_t)vout[0].w << 32);
+  const uint64_t lb = (uint64_t)vout[1].x | ((uint64_t)vout[1].y << 32);
+  const uint64_t hb = (uint64_t)vout[1].z | ((uint64_t)vout[1].w << 32);
+  while (starts) {
+    const int o = __builtin_ctzll(starts);
+    starts &= starts - 1;
+    const int len = 1 + __builtin_ctzll(~(conts >> (o + 1)));
+    const int64_t s = (int64_t)(uint32_t)__builtin_amdgcn_readlane((int)(my_slot & 0xFFFFFFFF), o) |
+                      ((int64_t)__builtin_amdgcn_readlane((int)(my_slot >> 32), o) << 32);
+    uint8_t* row = p.v_cache + ((size_t)(s / kBlockTokens) * p.num_kv_heads + kvh) * kPageBytes +
+                   (size_t)d * kBlockTokens;
+    store_rows(row, la, ha, lb, hb, (int)(s % kBlockTokens), len, o);
+  }
 }
 
 template <bool FAST>
@@ -212,18 +292,15 @@ __device__ __forceinline__ void cache_write_group(const CacheWriteParams& p, con
   const int kvh = (int)(item % p.num_kv_heads);
   const int n = min(kGroup, p.num_tokens - t0);
 
-  // slot of token t0 + lane (lanes past the group: -1)
-  const int64_t my_slot = (lane < n) ? p.slot_mapping[t0 + lane] : -1;
-  const int64_t s0 = (int64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(my_slot & 0xFFFFFFFF)) |
-                     ((int64_t)__builtin_amdgcn_readfirstlane((int)(my_slot >> 32)) << 32);
-  const bool in_order = (lane >= kGroup) || (my_slot == s0 + lane);
-  const bool whole = p.vec16 && n == kGroup && s0 >= 0 && (s0 % kBlockTokens) == 0 &&
-                     s0 < p.num_blocks * kBlockTokens && __builtin_amdgcn_ballot_w64(!in_order) == 0;
-  if (whole) {
-    write_block<FAST>(p, t0, kvh, s0 / kBlockTokens, lane, ks, vs);
+  if (p.vec16) {
+    // slot of token t0 + (lane & 15) (tokens past the group: -1)
+    const int64_t slot16 = ((lane & 15) < n) ? p.slot_mapping[t0 + (lane & 15)] : -1;
+    write_runs<FAST>(p, t0, n, kvh, lane, slot16, ks, vs);
     return;
   }
-  // Any slot pattern: read every token's two dims first (the cache stores may
+  // slot of token t0 + lane (lanes past the group: -1)
+  const int64_t my_slot = (lane < n) ? p.slot_mapping[t0 + lane] : -1;
+  // Rows without 16-byte alignment: read every token's two dims first (the cache stores may
   // alias the inputs as far as the compiler knows, so loads interleaved with
   // them would wait for each store), then convert and store token by token.
   uint32_t kw[kGroup], vw[kGroup];

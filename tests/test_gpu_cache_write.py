@@ -170,6 +170,31 @@ def test_whole_block_runs(pattern):
     assert_same(vc, ov, "v_cache")
 
 
+def test_sequences_of_every_length_and_start():
+    """A batch of prefill chunks of 1..40 tokens, each continuing its
+    sequence at every slot 0..15 of a block (its earlier tokens already
+    cached): runs of every start slot and length, sequence boundaries inside
+    the groups of 16 tokens, runs that cross a group boundary and blocks
+    written from two groups."""
+    Hkv, NB = 2, 400
+    g = torch.Generator().manual_seed(41)
+    perm = torch.randperm(NB, generator=g).tolist()
+    slots, b = [], 0
+    for i, (length, start) in enumerate((l, s) for l in range(1, 41) for s in (0, 1, 5, 8, 15) if (l + s) % 3 != 1):
+        nblk = (start + length + 15) // 16
+        blocks = perm[b:b + nblk]
+        b += nblk
+        slots += [blocks[(start + t) // 16] * 16 + (start + t) % 16 for t in range(length)]
+    slots = torch.tensor(slots, dtype=torch.int64)
+    T = slots.numel()
+    key = torch.randn(T, Hkv, 128, generator=g).to(torch.bfloat16)
+    value = torch.randn(T, Hkv, 128, generator=g).to(torch.bfloat16)
+    log(f"prefill chunks: {T} tokens, {b} blocks")
+    kc, vc, ok, ov = run_both(key, value, slots, NB, 0.013, 0.017, seed=5)
+    assert_same(kc, ok, "k_cache")
+    assert_same(vc, ov, "v_cache")
+
+
 # scales taking the short correctly rounded quotient, and ones outside its
 # range (tiny, huge, subnormal, negative) that take the division
 QUOTIENT_SCALES = [0.0173, 1.0 / 3.0, 3.0, 0.99999994, 7.3e-3, 1.1e2, 2.0 ** -60, 2.0 ** 60,
