@@ -109,6 +109,21 @@ constexpr int kInKernelOrderMaxSeqs = 512;  // what a work item orders by itself
 // contexts it costs 1-8% more than longest-first alone (which is off by
 // default for them).
 constexpr int kLptTwoWaveItemsPerCU = 4;
+// Longest-first without being asked, computed in the work items (no
+// scratch): batches of at most kAutoLptMaxSeqs sequences with tables of at
+// least kAutoLptMinBlocks blocks and at least eight (sequence, kv head) units
+// per CU (where the plan is the same either way).  The items read their plain
+// sequence's data while the order is made and keep it where every length
+// falls in one bin, so a batch of equal lengths pays little.  Measured on
+// MI355X (graph replay, plain -> this): ragged 1..4000 x 256 at 40/8 202.9 ->
+// 184.5 us, 32/8 198.7 -> 181.1 us, the mixed batch 257.9 -> 233.2 us, at
+// most 8 queries 230.9 -> 213.7 us; uniform 40/8 ctx 4096 x 256 329.8 ->
+// 330.8 us, 32/8 324.7 -> 325.4 us, 3 queries 334.9 -> 336.3 us.  Outside
+// these bounds the order cost more (ctx 1024 x 256 85.2 -> 87.0 us without
+// the shortcut).  Results are bit-identical either way.
+constexpr int kAutoLptUnitsPerCU = 8;
+constexpr int kAutoLptMaxSeqs = 256;
+constexpr int kAutoLptMinBlocks = 192;
 #ifndef PA_LPT_IN_KERNEL
 #define PA_LPT_IN_KERNEL 1
 #endif
@@ -341,8 +356,11 @@ int plan_call(int32_t S, int32_t Hq, int32_t Hkv, int32_t W, int32_t cus, int32_
   cp->tiles_per_item = cp->q_tiles <= 2 ? cp->q_tiles : (three ? 3 : 2);
   cp->q_items = (cp->q_tiles + cp->tiles_per_item - 1) / cp->tiles_per_item;
   // longest-first: computed by each work item where its workgroup is one wave
-  // and the sequences few enough, else by the order kernel
-  cp->lpt_in_kernel = PA_LPT_IN_KERNEL && longest_first && !token_rows && S >= 2 &&
+  // and the sequences few enough, else by the order kernel; by default on
+  // large batches of long tables (kAutoLptUnitsPerCU)
+  const bool auto_lpt = PA_LPT_IN_KERNEL && !token_rows && S >= 2 && S <= kAutoLptMaxSeqs &&
+                        W >= kAutoLptMinBlocks && (int64_t)S * Hkv >= kAutoLptUnitsPerCU * ncus;
+  cp->lpt_in_kernel = PA_LPT_IN_KERNEL && (longest_first || auto_lpt) && !token_rows && S >= 2 &&
                       S <= kInKernelOrderMaxSeqs;
   return make_plan(S, Hq, Hkv, W, cus, ppp_req, &cp->plan, cp->q_items, mq ? num_q_rows : S,
                    longest_first && !cp->lpt_in_kernel, token_rows && !mq, longest_first);

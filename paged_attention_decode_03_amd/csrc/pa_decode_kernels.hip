@@ -202,12 +202,10 @@ constexpr int kInKernelOrderPer = 8;
 // sequences in bin order and, within a bin, in index order (a stable counting
 // sort, so every wave of the grid computes the same permutation).  The bin
 // histogram lives in this wave's LDS; a wave's LDS operations run in order.
-__device__ __forceinline__ int lpt_sequence(const DecodeParams& p, int slot, int lane) {
+__device__ __forceinline__ int lpt_sequence(const DecodeParams& p, int slot, int plain, int lane) {
   __shared__ int cnt[kOrderBins];
   const int S = p.num_seqs;
   const int wmax = p.max_blocks > 0 ? p.max_blocks : 1;
-#pragma unroll
-  for (int b = 0; b < kOrderBins / 64; ++b) cnt[b * 64 + lane] = 0;
   int bin[kInKernelOrderPer];
 #pragma unroll
   for (int k = 0; k < kInKernelOrderPer; ++k) {
@@ -220,6 +218,15 @@ __device__ __forceinline__ int lpt_sequence(const DecodeParams& p, int slot, int
     }
     bin[k] = b;
   }
+  // every length in one bin (a batch of equal lengths): no order to make, the
+  // item keeps its sequence of the plain order (`plain`)
+  const int b0 = __builtin_amdgcn_readfirstlane(bin[0]);
+  uint64_t other = 0;
+#pragma unroll
+  for (int k = 0; k < kInKernelOrderPer; ++k) other |= __builtin_amdgcn_ballot_w64(bin[k] >= 0 && bin[k] != b0);
+  if (other == 0) return plain;
+#pragma unroll
+  for (int b = 0; b < kOrderBins / 64; ++b) cnt[b * 64 + lane] = 0;
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 #pragma unroll
   for (int k = 0; k < kInKernelOrderPer; ++k)
@@ -361,86 +368,101 @@ __attribute__((amdgpu_waves_per_eu(WPI == 2 ? kTwoWaveWavesPerEU : PA_WAVES_PER_
   const int kvh = TR ? (rest % kv_units) * p.kv_group + wave : rest % kv_units;
   // longest-first: the sequence of this slot, from the order kernel or computed
   // here (one-wave workgroups only)
-  const int slot = p.lpt_round_slots > 0 ? snake_slot(rest / kv_units, p.lpt_round_slots, p.num_seqs)
-                                         : rest / kv_units;
-  int s_pick = 0;
+  const int plain = rest / kv_units;
+  const int slot = p.lpt_round_slots > 0 ? snake_slot(plain, p.lpt_round_slots, p.num_seqs) : plain;
+  const int ppp = p.pages_per_part;
+  const int pbeg = part * ppp;  // < max_blocks: the planner never makes an empty partition range
+  const int span = min(ppp, p.max_blocks - pbeg);
+  // The sequence.  With the order computed here, the prologue's reads start
+  // with the plain order's sequence (what a batch whose lengths all share one
+  // bin keeps, found without a histogram) while the order is computed, and
+  // are made again where it picks another sequence.
+  int s = (!TR && p.order_in_kernel) ? plain : p.seq_order ? scalar_load(p.seq_order + slot) : slot;
+
+  // column -> (query token of the tile, head of the group)
+  int qi = 0, g = col, q0 = s, q_len = 1;
+  int qrow[NT];      // row of q and out
+  bool hvalid[NT];   // the column holds a query of this sequence
+  size_t orow[NT];    // element offset of the row in out (dense)
+  int32_t idv[kMaxPagesPerPart / 64];
+  // B operand of QK^T: q^T, 8 dims per MFMA.  Element e of qop[h2][c] is dim
+  // 16 * (4 * h2 + rq) + 8 * c + e, matching the K bytes this lane loads.
+  bf16x8 qop[NT][2][2];
+  int len_raw = 0;
+  // Start the independent reads of the prologue together: this partition's
+  // slice of the block-table row (its length is not known yet, so entries
+  // past the context are read too and discarded below), the sequence length,
+  // and q.
+  // (false: the item's tiles hold no query of the sequence, nothing is read)
+  auto prologue = [&](int sq) -> bool {
+    q0 = sq;
+    q_len = 1;
+    if constexpr (MQ) {
+      qi = col / p.group;
+      g = col - qi * p.group;
+      // no row offsets: one query per sequence (the options without several queries)
+      q0 = p.cu_seqlens_q ? scalar_load(p.cu_seqlens_q + sq) : sq;
+      q_len = p.cu_seqlens_q ? scalar_load(p.cu_seqlens_q + sq + 1) - q0 : 1;
+      if (qt0 * p.q_tile >= q_len) return false;
+    }
+    const int hh = kvh * p.group + g;
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      const int qt = qt0 + u;
+      qrow[u] = q0 + qt * p.q_tile + qi;
+      hvalid[u] = MQ ? (col < p.q_tile * p.group && qt < p.num_q_tiles && qt * p.q_tile + qi < q_len &&
+                        qrow[u] >= 0 && qrow[u] < p.num_q_rows)
+                     : col < p.group;
+      orow[u] = ((size_t)qrow[u] * p.num_heads + hh) * kHeadDim;
+    }
+    const int32_t* bt = p.block_tables + (size_t)sq * p.bt_row_stride;
+#pragma unroll
+    for (int k = 0; k < kMaxPagesPerPart / 64; ++k)
+      idv[k] = (k * 64 < span) ? bt[pbeg + min(k * 64 + lane, span - 1)] : 0;
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      if (hvalid[u]) {
+        const uint16_t* qp = p.q + (size_t)qrow[u] * p.q_row_stride + (size_t)hh * kHeadDim;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+            qop[u][h2][c] = *(const bf16x8*)(qp + 16 * (4 * h2 + rq) + 8 * c);
+      } else {
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+            qop[u][h2][c] = bf16x8{};
+      }
+    }
+    len_raw = scalar_load(p.seq_lens + sq);
+    return true;
+  };
+  bool has_work = prologue(s);
   if (!TR && p.order_in_kernel) {
+    int s_pick;
     if constexpr (WPI == 1) {
-      s_pick = __builtin_amdgcn_readfirstlane(lpt_sequence(p, slot, lane));
+      s_pick = __builtin_amdgcn_readfirstlane(lpt_sequence(p, slot, plain, lane));
     } else {
       // one wave sorts (the histogram in LDS is its own); the other reads its pick
       __shared__ int lpt_pick;
       if (wave == 0) {
-        const int v = lpt_sequence(p, slot, lane);
+        const int v = lpt_sequence(p, slot, plain, lane);
         if (lane == 0) lpt_pick = v;
       }
       __syncthreads();
       s_pick = __builtin_amdgcn_readfirstlane(lpt_pick);
     }
-  }
-  const int s = (!TR && p.order_in_kernel) ? s_pick
-                : p.seq_order                ? scalar_load(p.seq_order + slot)
-                                             : slot;
-  const int ppp = p.pages_per_part;
-  const int pbeg = part * ppp;  // < max_blocks: the planner never makes an empty partition range
-
-  // column -> (query token of the tile, head of the group)
-  int qi = 0, g = col, q0 = s, q_len = 1;
-  if constexpr (MQ) {
-    qi = col / p.group;
-    g = col - qi * p.group;
-    // no row offsets: one query per sequence (the options without several queries)
-    q0 = p.cu_seqlens_q ? scalar_load(p.cu_seqlens_q + s) : s;
-    q_len = p.cu_seqlens_q ? scalar_load(p.cu_seqlens_q + s + 1) - q0 : 1;
-    if (qt0 * p.q_tile >= q_len) return;  // no query of this sequence in the item's tiles
-  }
-  const int h = kvh * p.group + g;
-  int qrow[NT];      // row of q and out
-  bool hvalid[NT];   // the column holds a query of this sequence
-  size_t orow[NT];    // element offset of the row in out (dense)
-#pragma unroll
-  for (int u = 0; u < NT; ++u) {
-    const int qt = qt0 + u;
-    qrow[u] = q0 + qt * p.q_tile + qi;
-    hvalid[u] = MQ ? (col < p.q_tile * p.group && qt < p.num_q_tiles && qt * p.q_tile + qi < q_len &&
-                      qrow[u] >= 0 && qrow[u] < p.num_q_rows)
-                   : col < p.group;
-    orow[u] = ((size_t)qrow[u] * p.num_heads + h) * kHeadDim;
-  }
-
-  // Start the three independent reads of the prologue together: this
-  // partition's slice of the block-table row (its length is not known yet, so
-  // entries past the context are read too and discarded below), the sequence
-  // length, and q.
-  const int32_t* bt = p.block_tables + (size_t)s * p.bt_row_stride;
-  const int span = min(ppp, p.max_blocks - pbeg);
-  int32_t idv[kMaxPagesPerPart / 64];
-#pragma unroll
-  for (int k = 0; k < kMaxPagesPerPart / 64; ++k)
-    idv[k] = (k * 64 < span) ? bt[pbeg + min(k * 64 + lane, span - 1)] : 0;
-
-  // B operand of QK^T: q^T, 8 dims per MFMA.  Element e of qop[h2][c] is dim
-  // 16 * (4 * h2 + rq) + 8 * c + e, matching the K bytes this lane loads.
-  bf16x8 qop[NT][2][2];
-#pragma unroll
-  for (int u = 0; u < NT; ++u) {
-    if (hvalid[u]) {
-      const uint16_t* qp = p.q + (size_t)qrow[u] * p.q_row_stride + (size_t)h * kHeadDim;
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-          qop[u][h2][c] = *(const bf16x8*)(qp + 16 * (4 * h2 + rq) + 8 * c);
-    } else {
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-          qop[u][h2][c] = bf16x8{};
+    if (s_pick != s) {
+      s = s_pick;
+      has_work = prologue(s);
     }
   }
+  if (!has_work) return;  // no query of this sequence in the item's tiles
+  const int h = kvh * p.group + g;
 
-  const int Lseq = clamp_len(scalar_load(p.seq_lens + s), p.max_blocks);
+  const int Lseq = clamp_len(len_raw, p.max_blocks);
   // tokens this item's queries can see: all of them for one query per sequence;
   // up to the tile's last query's position otherwise
   int L = Lseq, pos_first = Lseq - 1;
