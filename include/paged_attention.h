@@ -261,11 +261,12 @@ int paged_multi_query_attention(const void* q, const int32_t* cu_seqlens_q, int3
  *                    sequences of 1..4000 tokens on MI355X: 40/8 heads 202 ->
  *                    185 us, 32/4 heads 111 -> 96 us) and costs 1-8% when
  *                    contexts are alike.  Every call of the
- *                    block layout (paged_decode_attention included) orders
- *                    longest first by itself, bit for bit the same results,
- *                    where num_seqs <= 256, max_blocks_per_seq >= 192 and
- *                    num_seqs * num_kv_heads >= 8 per compute unit; a batch
- *                    whose lengths are alike then keeps the plain order.
+ *                    block layout (paged_decode_attention included) with no
+ *                    sliding window orders longest first by itself, bit for
+ *                    bit the same results, where num_seqs <= 256,
+ *                    max_blocks_per_seq >= 192 and num_seqs * num_kv_heads >= 8
+ *                    per compute unit; a batch whose lengths are alike then
+ *                    keeps the plain order.
  *                    The order kernel's scratch (4 bytes per sequence, after the
  *                    split-KV scratch rounded up to 256 bytes) is not in
  *                    pa_decode_plan's figure.

@@ -504,6 +504,53 @@ def test_longest_first_order_covers_every_sequence():
         assert torch.equal(out.view(torch.int16), plain.view(torch.int16)), f"replay {r}"
 
 
+@pytest.mark.parametrize("kind", ["ragged", "one_bin", "two_bins", "several_queries"])
+def test_default_longest_first_matches_plain_order(kind):
+    """256 sequences at 40/8 heads with 250-block tables are ordered longest
+    first by default (each work item sorts the lengths; where they all fall in
+    one bin it keeps the plain order without sorting), and 257 sequences are
+    not (more than the default order's 256).  The per-sequence arithmetic is
+    the same either way, so the 256-sequence call must equal the first 256
+    sequences of the 257-sequence call bit for bit: ragged lengths, lengths of
+    one bin (250 pages: 3985..4000 tokens), two bins, and several queries per
+    sequence."""
+    import paged_attention_decode_03_amd as pa
+    S = 257
+    if kind == "one_bin":
+        lens = [3985 + (i * 7) % 16 for i in range(S)]
+    elif kind == "two_bins":
+        lens = [4000 if i % 3 else 1990 + i % 11 for i in range(S)]
+    else:
+        lens = workloads.ragged_lens(S, seed=23)
+    ql = [min(1 + (i * 5) % 6, lens[i]) for i in range(S)] if kind == "several_queries" else None
+    if ql is None:
+        case = workloads.make_case(40, 8, lens, seed=123, max_blocks=250, device="cuda")
+    else:
+        case = workloads.make_multi_case(40, 8, lens, ql, seed=124, max_blocks=250, device="cuda")
+    ks = torch.tensor([case.k_scale], device="cuda")
+    vs = torch.tensor([case.v_scale], device="cuda")
+    tail = (case.scale, ks, vs)
+    if ql is None:
+        full = pa.paged_decode_attention(case.q, case.k_cache, case.v_cache, case.block_tables,
+                                         case.seq_lens, *tail)
+        part = pa.paged_decode_attention(case.q[:256].contiguous(), case.k_cache, case.v_cache,
+                                         case.block_tables[:256].contiguous(),
+                                         case.seq_lens[:256].contiguous(), *tail)
+        rows = 256
+    else:
+        cu = case.cu_seqlens_q
+        rows = int(cu[256])
+        full = pa.paged_attention_unified(case.q, cu, 6, case.k_cache, case.v_cache,
+                                          case.block_tables, case.seq_lens, *tail)
+        part = pa.paged_attention_unified(case.q[:rows].contiguous(), cu[:257].contiguous(), 6,
+                                          case.k_cache, case.v_cache,
+                                          case.block_tables[:256].contiguous(),
+                                          case.seq_lens[:256].contiguous(), *tail)
+    torch.cuda.synchronize()
+    log(f"default order {kind}")
+    assert torch.equal(part.view(torch.int16), full[:rows].view(torch.int16))
+
+
 @pytest.mark.parametrize("name", ["ragged_32x4_seed0", "ragged_32x4_seed1", "ragged_8x1_600seqs"])
 def test_longest_first_with_two_waves_per_item(name):
     """Longest-first launches of 2 to 4 items per CU run two waves per item
