@@ -216,7 +216,7 @@ __device__ __forceinline__ void store_rows(uint8_t* row, uint64_t la, uint64_t h
 // only its own tokens' bytes.
 template <bool FAST>
 __device__ __forceinline__ void write_runs(const CacheWriteParams& p, int t0, int n, int kvh, int lane,
-                                           int64_t my_slot, const Scale& ks, const Scale& vs) {
+                                           const Scale& ks, const Scale& vs) {
   const int jt = lane & 15;  // K: the lane's token; the lane of token jt in each row of 16
   const int c0 = lane >> 4;  // K: chunks c0 and c0 + 4
   const int d = 2 * lane;    // V: dims d and d + 1
@@ -233,6 +233,13 @@ __device__ __forceinline__ void write_runs(const CacheWriteParams& p, int t0, in
 #pragma unroll
   for (int j = 0; j < kGroup; ++j)
     vin[j] = *(const uint32_t*)(p.value + (size_t)(t0 + min(j, n - 1)) * p.value_stride + kvh * kHeadDim + d);
+  // The slot of token t0 + jt (tokens past the group: -1), read after the
+  // inputs: read first, the wave waited for it before issuing them (measured
+  // on MI355X, back to back, 32768 tokens x 8 kv heads in whole blocks 39.2
+  // -> 35.4 us, 8 sequences of 3000-5000 44.5 -> 41.6 us, chunks starting
+  // inside blocks 48.8 -> 46.3 us; with the unaligned-row walk in a kernel of
+  // its own)
+  const int64_t my_slot = (jt < n) ? p.slot_mapping[t0 + jt] : -1;
   bool nan = true;
   if constexpr (FAST) {
     uint64_t m = 0;
@@ -300,7 +307,7 @@ __device__ __forceinline__ void write_runs(const CacheWriteParams& p, int t0, in
   }
 }
 
-template <bool FAST>
+template <bool FAST, bool VEC16>
 __device__ __forceinline__ void cache_write_group(const CacheWriteParams& p, const Scale& ks, const Scale& vs) {
   const int lane = threadIdx.x & 63;
   // (the wave index read as wave-uniform: the token and head of the item, and
@@ -312,14 +319,10 @@ __device__ __forceinline__ void cache_write_group(const CacheWriteParams& p, con
   const int kvh = (int)(item % p.num_kv_heads);
   const int n = min(kGroup, p.num_tokens - t0);
 
-  if (p.vec16) {
-    // slot of token t0 + (lane & 15) (tokens past the group: -1)
-    const int64_t slot16 = ((lane & 15) < n) ? p.slot_mapping[t0 + (lane & 15)] : -1;
-    write_runs<FAST>(p, t0, n, kvh, lane, slot16, ks, vs);
+  if constexpr (VEC16) {
+    write_runs<FAST>(p, t0, n, kvh, lane, ks, vs);
     return;
   }
-  // slot of token t0 + lane (lanes past the group: -1)
-  const int64_t my_slot = (lane < n) ? p.slot_mapping[t0 + lane] : -1;
   // Rows without 16-byte alignment: read every token's two dims first (the cache stores may
   // alias the inputs as far as the compiler knows, so loads interleaved with
   // them would wait for each store), then convert and store token by token.
@@ -330,6 +333,8 @@ __device__ __forceinline__ void cache_write_group(const CacheWriteParams& p, con
     kw[i] = *(const uint32_t*)(p.key + t * p.key_stride + kvh * kHeadDim + 2 * lane);
     vw[i] = *(const uint32_t*)(p.value + t * p.value_stride + kvh * kHeadDim + 2 * lane);
   }
+  // slot of token t0 + lane (lanes past the group: -1), after the inputs
+  const int64_t my_slot = (lane < n) ? p.slot_mapping[t0 + lane] : -1;
 #pragma unroll
   for (int i = 0; i < kGroup; ++i) {
     if (i >= n) break;
@@ -343,16 +348,23 @@ __device__ __forceinline__ void cache_write_group(const CacheWriteParams& p, con
 // negative scales, 0, subnormals, infinities and NaN.
 __device__ __forceinline__ bool quotient_scale(float x) { return x >= 0x1p-60f && x <= 0x1p60f; }
 
-__global__ __launch_bounds__(64 * kWavesPerBlock) void pa_cache_write_kernel(const CacheWriteParams p) {
+// VEC16: rows that allow 16-byte loads (p.vec16), else the token walk.
+// Registers for three waves per SIMD (168 VGPRs, no spills; four would spill):
+// measured on MI355X against two, back to back, 32768 tokens x 8 kv heads in
+// whole blocks 35.7 -> 32.5 us, 8 sequences of 3000-5000 41.0 -> 36.5 us, 64
+// of 200-800 42.5 -> 38.3 us, chunks starting inside blocks 46.2 -> 44.0 us.
+template <bool VEC16>
+__global__ __launch_bounds__(64 * kWavesPerBlock) __attribute__((amdgpu_waves_per_eu(3))) void pa_cache_write_kernel(
+    const CacheWriteParams p) {
   const float ks = scalar_load(p.k_scale);
   const float vs = scalar_load(p.v_scale);
   const Scale kq = {ks, 1.0f / ks, 512.0f * ks};
   const Scale vq = {vs, 1.0f / vs, 512.0f * vs};
   // usable scales: the short quotient; anything else takes the division
   if (quotient_scale(ks) && quotient_scale(vs))
-    cache_write_group<true>(p, kq, vq);
+    cache_write_group<true, VEC16>(p, kq, vq);
   else
-    cache_write_group<false>(p, kq, vq);
+    cache_write_group<false, VEC16>(p, kq, vq);
 }
 
 }  // namespace
@@ -360,7 +372,10 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void pa_cache_write_kernel(con
 hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t stream) {
   const int64_t items = ((int64_t)p.num_tokens + kGroup - 1) / kGroup * p.num_kv_heads;
   const int64_t blocks = (items + kWavesPerBlock - 1) / kWavesPerBlock;
-  hipLaunchKernelGGL(pa_cache_write_kernel, dim3((unsigned)blocks), dim3(64 * kWavesPerBlock), 0, stream, p);
+  if (p.vec16)
+    hipLaunchKernelGGL(pa_cache_write_kernel<true>, dim3((unsigned)blocks), dim3(64 * kWavesPerBlock), 0, stream, p);
+  else
+    hipLaunchKernelGGL(pa_cache_write_kernel<false>, dim3((unsigned)blocks), dim3(64 * kWavesPerBlock), 0, stream, p);
   return hipGetLastError();
 }
 
