@@ -504,7 +504,8 @@ def test_longest_first_order_covers_every_sequence():
         assert torch.equal(out.view(torch.int16), plain.view(torch.int16)), f"replay {r}"
 
 
-@pytest.mark.parametrize("kind", ["ragged", "one_bin", "two_bins", "several_queries"])
+@pytest.mark.parametrize("kind", ["ragged", "one_bin", "two_bins", "several_queries", "options",
+                                  "several_queries_options"])
 def test_default_longest_first_matches_plain_order(kind):
     """256 sequences at 40/8 heads with 250-block tables are ordered longest
     first by default (each work item sorts the lengths; where they all fall in
@@ -512,17 +513,22 @@ def test_default_longest_first_matches_plain_order(kind):
     not (more than the default order's 256).  The per-sequence arithmetic is
     the same either way, so the 256-sequence call must equal the first 256
     sequences of the 257-sequence call bit for bit: ragged lengths, lengths of
-    one bin (250 pages: 3985..4000 tokens), two bins, and several queries per
-    sequence."""
+    one bin (250 pages: 3985..4000 tokens), two bins, several queries per
+    sequence, and the unified call's softcap, ALiBi and sinks with one query
+    and with several."""
     import paged_attention_decode_03_amd as pa
     S = 257
+    opts = {}
+    if kind.endswith("options"):
+        opts = dict(softcap=25.0, alibi_slopes=torch.linspace(-0.05, 0.02, 40, device="cuda"),
+                    sinks=torch.linspace(-1.0, 2.0, 40, device="cuda"))
     if kind == "one_bin":
         lens = [3985 + (i * 7) % 16 for i in range(S)]
     elif kind == "two_bins":
         lens = [4000 if i % 3 else 1990 + i % 11 for i in range(S)]
     else:
         lens = workloads.ragged_lens(S, seed=23)
-    ql = [min(1 + (i * 5) % 6, lens[i]) for i in range(S)] if kind == "several_queries" else None
+    ql = [min(1 + (i * 5) % 6, lens[i]) for i in range(S)] if kind.startswith("several") else None
     if ql is None:
         case = workloads.make_case(40, 8, lens, seed=123, max_blocks=250, device="cuda")
     else:
@@ -530,7 +536,14 @@ def test_default_longest_first_matches_plain_order(kind):
     ks = torch.tensor([case.k_scale], device="cuda")
     vs = torch.tensor([case.v_scale], device="cuda")
     tail = (case.scale, ks, vs)
-    if ql is None:
+    if ql is None and opts:
+        full = pa.paged_attention_unified(case.q, None, 1, case.k_cache, case.v_cache,
+                                          case.block_tables, case.seq_lens, *tail, **opts)
+        part = pa.paged_attention_unified(case.q[:256].contiguous(), None, 1, case.k_cache,
+                                          case.v_cache, case.block_tables[:256].contiguous(),
+                                          case.seq_lens[:256].contiguous(), *tail, **opts)
+        rows = 256
+    elif ql is None:
         full = pa.paged_decode_attention(case.q, case.k_cache, case.v_cache, case.block_tables,
                                          case.seq_lens, *tail)
         part = pa.paged_decode_attention(case.q[:256].contiguous(), case.k_cache, case.v_cache,
@@ -541,11 +554,11 @@ def test_default_longest_first_matches_plain_order(kind):
         cu = case.cu_seqlens_q
         rows = int(cu[256])
         full = pa.paged_attention_unified(case.q, cu, 6, case.k_cache, case.v_cache,
-                                          case.block_tables, case.seq_lens, *tail)
+                                          case.block_tables, case.seq_lens, *tail, **opts)
         part = pa.paged_attention_unified(case.q[:rows].contiguous(), cu[:257].contiguous(), 6,
                                           case.k_cache, case.v_cache,
                                           case.block_tables[:256].contiguous(),
-                                          case.seq_lens[:256].contiguous(), *tail)
+                                          case.seq_lens[:256].contiguous(), *tail, **opts)
     torch.cuda.synchronize()
     log(f"default order {kind}")
     assert torch.equal(part.view(torch.int16), full[:rows].view(torch.int16))

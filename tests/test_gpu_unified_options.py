@@ -218,6 +218,23 @@ def test_one_query_per_sequence_without_row_offsets():
     compare(b, ref, "one query per sequence, options", seqs=rows)
 
 
+def test_options_on_a_ragged_batch_ordered_longest_first():
+    """40/8 heads, 256 sequences of 1..4000 tokens with 250-block tables: the
+    shape on which calls order longest first by themselves (the work items
+    sort the lengths).  Softcap, ALiBi and sinks, one query per sequence and
+    two to four, every row against the oracle."""
+    S = 256
+    lens = workloads.ragged_lens(S, seed=12)
+    one = workloads.make_multi_case(40, 8, lens, [1] * S, seed=97, max_blocks=250, device="cuda")
+    opts = dict(softcap=30.0, alibi_slopes=slopes_for(40), sinks=np.linspace(-1.0, 2.0, 40).astype(np.float32))
+    log("options, ragged 256, one query")
+    check(one, "ragged ordered: softcap + alibi + sinks", **opts)
+    ql = [min(2 + i % 3, lens[i]) for i in range(S)]
+    several = workloads.make_multi_case(40, 8, lens, ql, seed=98, max_blocks=250, device="cuda")
+    log("options, ragged 256, 2..4 queries")
+    check(several, "ragged ordered, 2..4 queries: softcap + sinks", softcap=30.0, sinks=opts["sinks"])
+
+
 def test_speculative_decode_with_window_and_sinks():
     """40/8 heads, 256 sequences of 4096 tokens, 4 queries each, a 128-token
     window and per-head sinks: only the last pages of each sequence are read."""
