@@ -263,10 +263,12 @@ int paged_multi_query_attention(const void* q, const int32_t* cu_seqlens_q, int3
  *                    it costs 0.2-0.6% with one wave per item and 1-8% with
  *                    two.  Every call of the
  *                    block layout (paged_decode_attention included) with no
- *                    sliding window orders longest first by itself, bit for
- *                    bit the same results, where num_seqs <= 256,
- *                    max_blocks_per_seq >= 192 and num_seqs * num_kv_heads >= 8
- *                    per compute unit; a batch whose lengths are alike then
+ *                    sliding window orders longest first by itself where
+ *                    num_seqs <= 256, max_blocks_per_seq >= 192 and
+ *                    num_seqs * num_kv_heads >= 4 per compute unit: bit for
+ *                    bit the plain order's results from 8 units per CU, and
+ *                    at 4 (two waves per item, as above) the same to
+ *                    rounding; a batch whose lengths all fall in one bin
  *                    keeps the plain order.
  *                    The order kernel's scratch (4 bytes per sequence, after the
  *                    split-KV scratch rounded up to 256 bytes) is not in

@@ -106,8 +106,7 @@ constexpr int kInKernelOrderMaxSeqs = 512;  // what a work item orders by itself
 // on MI355X (graph replay, ragged 1..4000 x 256 sequences): 32/4 heads (4
 // items per CU) 110.5 -> 96.1 us and 106.8 -> 89.9 us (seeds 0, 1); at 8
 // items per CU (32/8, 40/8) within +-3%, so the rule stops at 4.  On uniform
-// contexts it costs 1-8% more than longest-first alone; the default order
-// below needs 8 units per CU, so it never runs two waves.
+// contexts it costs 1-8% more than longest-first alone.
 constexpr int kLptTwoWaveItemsPerCU = 4;
 // Longest-first without being asked, computed in the work items (no
 // scratch): batches of at most kAutoLptMaxSeqs sequences with tables of at
@@ -120,8 +119,14 @@ constexpr int kLptTwoWaveItemsPerCU = 4;
 // most 8 queries 230.9 -> 213.7 us; uniform 40/8 ctx 4096 x 256 329.8 ->
 // 330.8 us, 32/8 324.7 -> 325.4 us, 3 queries 334.9 -> 336.3 us.  Outside
 // these bounds the order cost more (ctx 1024 x 256 85.2 -> 87.0 us without
-// the shortcut).  Results are bit-identical either way.
-constexpr int kAutoLptUnitsPerCU = 8;
+// the shortcut).  Results are bit-identical either way from 8 units per CU;
+// at 4 (up to kLptTwoWaveItemsPerCU) the items run as two waves, whose sums
+// agree with the plain order to rounding: ragged 1..4000 x 256 at 32/4 103.0
+// -> 94.8, 99.3 -> 86.7, 102.8 -> 93.3 us (seeds 0-2), but equal lengths
+// 1.7-3% slower (32/4 x 256 x 4096 168.2 -> 173.2 us, 40/8 x 128 x 4096
+// 169.1 -> 172.0 us, 20/4 x 256 x 4096 169.6 -> 174.2 us); serving batches
+// are ragged.
+constexpr int kAutoLptUnitsPerCU = 4;
 constexpr int kAutoLptMaxSeqs = 256;
 constexpr int kAutoLptMinBlocks = 192;
 #ifndef PA_LPT_IN_KERNEL

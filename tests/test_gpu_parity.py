@@ -564,6 +564,34 @@ def test_default_longest_first_matches_plain_order(kind):
     assert torch.equal(part.view(torch.int16), full[:rows].view(torch.int16))
 
 
+def test_default_longest_first_with_two_waves_per_item():
+    """256 sequences at 32/4 heads (1024 (sequence, kv head) units: four per
+    CU) with 250-block tables are ordered longest first by default and run
+    two waves per item, whose partial sums combine in another order: the
+    256-sequence call agrees with the first 256 sequences of the 257-sequence
+    call (plain order, one wave per item) to rounding, and repeats itself bit
+    for bit."""
+    import paged_attention_decode_03_amd as pa
+    S = 257
+    lens = workloads.ragged_lens(S, seed=24)
+    case = workloads.make_case(32, 4, lens, seed=125, max_blocks=250, device="cuda")
+    tail = (case.scale, torch.tensor([case.k_scale], device="cuda"), torch.tensor([case.v_scale], device="cuda"))
+    full = pa.paged_decode_attention(case.q, case.k_cache, case.v_cache, case.block_tables,
+                                     case.seq_lens, *tail)
+    sub = (case.q[:256].contiguous(), case.k_cache, case.v_cache, case.block_tables[:256].contiguous(),
+           case.seq_lens[:256].contiguous())
+    part = pa.paged_decode_attention(*sub, *tail)
+    again = pa.paged_decode_attention(*sub, *tail)
+    torch.cuda.synchronize()
+    log("default order, two waves per item, 32/4 x 256")
+    assert torch.equal(part.view(torch.int16), again.view(torch.int16))
+    d = (part.float() - full[:256].float()).abs()
+    ref = full[:256].float().abs()
+    # one bf16 rounding apart at most: 2^-8 relative, or absolute near zero
+    assert bool((d <= torch.clamp(ref, min=2.0 ** -6) * 2.0 ** -7).all()), float(d.max())
+    assert float(d.mean()) < 1e-4
+
+
 @pytest.mark.parametrize("name", ["ragged_32x4_seed0", "ragged_32x4_seed1", "ragged_8x1_600seqs"])
 def test_longest_first_with_two_waves_per_item(name):
     """Longest-first launches of 2 to 4 items per CU run two waves per item
