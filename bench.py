@@ -576,8 +576,8 @@ VALU_COMPARE_WORKLOADS = ("target", "dense_32x8_ctx4096_s256", "dense_32x4_ctx40
 
 
 def valu_compare(steps, warmup):
-    """JSON lines: the decode (MFMA for qKᵀ and PV) against the same decode
-    with its dot products on the vector ALUs (probe), on the same inputs and
+    """JSON lines: the decode (MFMA for qKᵀ and PV, in plain order) against the
+    same decode with its dot products on the vector ALUs (probe), on the same inputs and
     stream: per-call median and mean (HIP events around each call on the
     launch stream) and GB/s, and the largest difference between the two
     outputs."""
@@ -592,8 +592,10 @@ def valu_compare(steps, warmup):
         vs = torch.tensor([case.v_scale], dtype=torch.float32, device="cuda")
         out_m, out_v = torch.empty_like(case.q), torch.empty_like(case.q)
         def mfma():
-            pa.paged_decode_attention(case.q, case.k_cache, case.v_cache, case.block_tables, case.seq_lens,
-                                      case.scale, ks, vs, out=out_m, stream=stream)
+            # the plain order, one wave per (sequence, kv head), like the probe
+            pa.paged_attention_unified(case.q, None, 1, case.k_cache, case.v_cache, case.block_tables,
+                                       case.seq_lens, case.scale, ks, vs, longest_first=-1, out=out_m,
+                                       stream=stream)
             return 0
 
         calls = {"mfma": mfma, "valu": lambda: valu_decode(lib, case, ks, vs, out_v, stream)}

@@ -246,7 +246,9 @@ int paged_multi_query_attention(const void* q, const int32_t* cu_seqlens_q, int3
  *   sinks            NULL: off; else device fp32 [num_heads]: one more softmax
  *                    term exp(sinks[h]) that carries no value
  * and, for any call:
- *   longest_first    0: off; 1: work items are dispatched longest sequence first.
+ *   longest_first    1: work items are dispatched longest sequence first;
+ *                    0: the default order (longest first on the shapes given
+ *                    below, else plain); -1: the plain order always.
  *                    Up to 512 sequences (block-table caches) each work item
  *                    finds its own sequence by a counting sort of the lengths;
  *                    otherwise, up to 8192 sequences, a small kernel orders them
@@ -263,7 +265,9 @@ int paged_multi_query_attention(const void* q, const int32_t* cu_seqlens_q, int3
  *                    it costs 0.2-0.6% with one wave per item and 1-8% with
  *                    two.  Every call of the
  *                    block layout (paged_decode_attention included) with no
- *                    sliding window orders longest first by itself where
+ *                    sliding window and longest_first 0 orders longest first
+ *                    by itself (paged_attention_unified with longest_first -1
+ *                    and no row offsets is the decode in plain order) where
  *                    num_seqs <= 256, max_blocks_per_seq >= 192 and
  *                    num_seqs * num_kv_heads >= 4 per compute unit: bit for
  *                    bit the plain order's results from 8 units per CU, and

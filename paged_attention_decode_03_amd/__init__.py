@@ -330,7 +330,9 @@ def paged_attention_unified(q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache, blo
     """paged_multi_query_attention with the unified backend's options:
     sliding_window (tokens ending at each query, 0 = off), softcap (0 = off),
     alibi_slopes / sinks (float32 [num_heads] tensors on the q device, or None),
-    and longest_first dispatch.  cu_seqlens_q=None: one query per sequence."""
+    and the dispatch order: longest_first True (or 1) longest sequence first,
+    False (0) the library's default order, -1 the plain order always.
+    cu_seqlens_q=None: one query per sequence."""
     lib = load_library()
     dev, out, c_args, keep = _args(q, k_cache, v_cache, block_tables, seq_lens, scale, k_scale,
                                    v_scale, out, stream, q_rows_free=True)
@@ -345,8 +347,11 @@ def paged_attention_unified(q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache, blo
         if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != (q.shape[1],)
                               or t.device != dev or not t.is_contiguous()):
             raise TypeError(f"{name} must be a contiguous float32 [num_heads] tensor on the q device")
+    order = int(longest_first)
+    if order not in (-1, 0, 1):
+        raise ValueError("longest_first must be True / 1, False / 0 or -1")
     opts = AttentionOptions(int(sliding_window), float(softcap), _ptr(alibi_slopes), _ptr(sinks),
-                            1 if longest_first else 0)
+                            order)
     (_, kc, vc, bt, sl, _, Hq, Hkv, D, bs, W, NB, sc, ks, vs, _, handle) = c_args
     with torch.cuda.device(dev):
         _check(lib.paged_attention_unified(
@@ -410,7 +415,7 @@ def pa_workspace_bytes(num_seqs, num_heads, num_kv_heads, max_blocks_per_seq, nu
     lib = load_library()
     n = ctypes.c_size_t()
     _check(lib.pa_workspace_bytes(num_seqs, num_q_tokens, max_seqlen_q, num_heads, num_kv_heads,
-                                  max_blocks_per_seq, 1 if longest_first else 0,
+                                  max_blocks_per_seq, int(longest_first),
                                   1 if token_rows else 0, int(device), ctypes.byref(n)))
     return n.value
 

@@ -337,7 +337,7 @@ struct CallPlan {
 
 int plan_call(int32_t S, int32_t Hq, int32_t Hkv, int32_t W, int32_t cus, int32_t ppp_req, bool mq,
               int32_t num_q_rows, int32_t max_seqlen_q, bool longest_first, bool token_rows,
-              bool windowed, CallPlan* cp) {
+              bool no_default_order, CallPlan* cp) {
   const int32_t G = Hq / Hkv;
   // query tokens per work item: as many as the 16 MFMA columns hold with the group
   cp->q_tile = mq ? (pa::kMaxGroup / G > 0 ? pa::kMaxGroup / G : 1) : 1;
@@ -362,10 +362,11 @@ int plan_call(int32_t S, int32_t Hq, int32_t Hkv, int32_t W, int32_t cus, int32_
   cp->q_items = (cp->q_tiles + cp->tiles_per_item - 1) / cp->tiles_per_item;
   // longest-first: computed by each work item where its workgroup is one wave
   // and the sequences few enough, else by the order kernel; by default on
-  // large batches of long tables (kAutoLptUnitsPerCU), unless a sliding
-  // window bounds every item's pages (the order ranks whole lengths; 40/8 x 256
-  // x 4096, window 1024: 84.7 -> 86.1 us with it)
-  const bool auto_lpt = PA_LPT_IN_KERNEL && !token_rows && !windowed && S >= 2 && S <= kAutoLptMaxSeqs &&
+  // large batches of long tables (kAutoLptUnitsPerCU), unless the caller
+  // asks for the plain order or a sliding window bounds every item's pages
+  // (the order ranks whole lengths; 40/8 x 256 x 4096, window 1024: 84.7 ->
+  // 86.1 us with it)
+  const bool auto_lpt = PA_LPT_IN_KERNEL && !token_rows && !no_default_order && S >= 2 && S <= kAutoLptMaxSeqs &&
                         W >= kAutoLptMinBlocks && (int64_t)S * Hkv >= kAutoLptUnitsPerCU * ncus;
   cp->lpt_in_kernel = PA_LPT_IN_KERNEL && (longest_first || auto_lpt) && !token_rows && S >= 2 &&
                       S <= kInKernelOrderMaxSeqs;
@@ -482,7 +483,8 @@ int decode(const void* q, const void* k_cache, const void* v_cache, const int32_
   if (hipGetDevice(&dev) != hipSuccess) return fail(PA_ERR_HIP, "hipGetDevice failed");
   CallPlan cp;
   int rc = plan_call(S, Hq, Hkv, W, device_cus(dev), ppp_req, mq, num_q_rows, max_seqlen_q,
-                     opt.longest_first != 0, var.token_rows, opt.sliding_window > 0, &cp);
+                     opt.longest_first > 0, var.token_rows, opt.sliding_window > 0 || opt.longest_first < 0,
+                     &cp);
   if (rc) return rc;
   const Plan& plan = cp.plan;
   // one 64-lane block per work item, 256 lanes per merged row: keep both grids
@@ -868,7 +870,7 @@ int pa_workspace_bytes(int32_t num_seqs, int32_t num_q_tokens, int32_t max_seqle
   }
   CallPlan cp;
   const int rc = plan_call(num_seqs, num_heads, num_kv_heads, max_blocks_per_seq, cus, 0, mq,
-                           mq ? num_q_tokens : num_seqs, mq ? max_seqlen_q : 1, longest_first != 0,
+                           mq ? num_q_tokens : num_seqs, mq ? max_seqlen_q : 1, longest_first > 0,
                            token_rows != 0, false, &cp);
   if (rc) return rc;
   *bytes = cp.plan.workspace_bytes;

@@ -394,6 +394,10 @@ def test_workspace_bytes_covers_several_queries_and_longest_first(lib):
     assert wsb(lib, 64, 40, 8, 256) == (0, 4096 + 64 * 40 * 2 * 130 * 4)
     assert wsb(lib, 64, 40, 8, 256, tr=1) == (0, 4096 + 64 * 40 * 4 * 130 * 4)
     assert wsb(lib, 256, 40, 8, 256, tr=1) == (0, 0)
+    # the plain order asked for (-1) plans like the default (0): no order
+    # kernel, so no scratch for it
+    assert wsb(lib, 1000, 8, 1, 64, lpt=-1) == wsb(lib, 1000, 8, 1, 64, lpt=0)
+    assert wsb(lib, 256, 32, 4, 250, lpt=-1) == wsb(lib, 256, 32, 4, 250) == (0, 0)
 
 
 def test_workspace_bytes_rejects_bad_shapes(lib):

@@ -570,7 +570,8 @@ def test_default_longest_first_with_two_waves_per_item():
     two waves per item, whose partial sums combine in another order: the
     256-sequence call agrees with the first 256 sequences of the 257-sequence
     call (plain order, one wave per item) to rounding, and repeats itself bit
-    for bit."""
+    for bit; asked for the plain order (longest_first -1), the 256-sequence
+    call equals the 257-sequence one bit for bit."""
     import paged_attention_decode_03_amd as pa
     S = 257
     lens = workloads.ragged_lens(S, seed=24)
@@ -582,9 +583,12 @@ def test_default_longest_first_with_two_waves_per_item():
            case.seq_lens[:256].contiguous())
     part = pa.paged_decode_attention(*sub, *tail)
     again = pa.paged_decode_attention(*sub, *tail)
+    # longest_first = -1: the plain order, one wave per item, as with 257 sequences
+    plain = pa.paged_attention_unified(sub[0], None, 1, *sub[1:], *tail, longest_first=-1)
     torch.cuda.synchronize()
     log("default order, two waves per item, 32/4 x 256")
     assert torch.equal(part.view(torch.int16), again.view(torch.int16))
+    assert torch.equal(plain.view(torch.int16), full[:256].view(torch.int16))
     d = (part.float() - full[:256].float()).abs()
     ref = full[:256].float().abs()
     # one bf16 rounding apart at most: 2^-8 relative, or absolute near zero
