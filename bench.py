@@ -13,7 +13,8 @@ Prints one JSON line: achieved algorithmic HBM GB/s (value: the bytes of one
 call over the timed region's time per call, i.e. whole-job throughput; the
 region's calls run back to back between two HIP events on the stream the
 kernels run on), the per-call median and mean (a second, untimed loop with an
-event pair around each call), the median of graph replays (the pages' timing
+event pair around each call), the median of graph replays (five runs of ten
+replays of ten calls back to back, after six untimed runs: the pages' timing
 method), the roofline object for the decode kernel (its average launch
 duration: the region's time per call, one launch a call; counter traffic from
 the committed rocprofv3 summary when it matches the current kernel source),
@@ -757,10 +758,18 @@ def main():
     import statistics
     us_med = statistics.median(per) if per else None
     us_evmean = sum(per) / len(per) if per else None
-    # the graph-replay median, the pages' timing method (not in the timed region)
-    g_mean, g_per = time_graph(case, replays=30, calls_per_graph=10, per_replay=True) \
-        if not (args.cold or args.no_graph) else (None, None)
+    # graph replay, the pages' timing method (not in the timed region): five
+    # runs of 10 replays back to back (an event pair around each replay would
+    # leave the GPU idle between replays), their per-call averages.  The
+    # the first graphs a process replays run slower than later ones (measured
+    # on MI355X, graphs of 10 calls replayed 10 times: the first five
+    # 336.3-337.5 us a call, the sixth 330.3, then 324.8-325.3, with the timed
+    # region at 326.2), so six are replayed untimed first.
+    g_per = None
+    if not (args.cold or args.no_graph):
+        g_per = [time_graph(case, replays=10, calls_per_graph=10) for _ in range(11)][6:]
     g_med = statistics.median(g_per) if g_per else None
+    g_mean = sum(g_per) / len(g_per) if g_per else None
     # the decode kernel's average launch duration: the timed region's calls run
     # back to back, so where a call is one launch (one partition) the region's
     # average per call is that kernel's average duration
